@@ -1,0 +1,274 @@
+"""CPU oracle for MiniMax Sparse Attention (MSA): block indexer scores, block top-k
+selection and exact softmax attention over the selected 128-token KV blocks.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import or call this
+module: only the tests, the smoke check and the benchmark's CPU-baseline leg do.
+It shares no code, header, table or helper with the HIP library.
+
+Plain NumPy in float64. Inputs may be float32 or float64 arrays (bf16 inputs are
+passed as their exact float32 upcast); every product and sum here is float64.
+
+Sources (the pages this follows):
+  [dd]   daily.dev, "MiniMax M3: 1M-token multimodal reasoning model now available
+         with NVIDIA and vLLM support": sections "Summary" and "What makes M3
+         different" (128-token KV blocks, top blocks kept per query).
+  [feat] models.inteligile.com, "MiniMax-M3" feature page, table "Checked in its
+         code": rows "Indexer-selected sparse attention (DeepSeek Sparse
+         Attention)" (indexer scores keys per head, pools into blocks,
+         topk = min(topk_blocks, num_key_blocks), -inf selections become -1),
+         "Grouped-query attention" (64 query heads share 4 KV heads through
+         repeat_kv) and "Learnable attention sink" (plain fp32 softmax, no sink).
+  [vllm] 24-ai.news, "MiniMax M3 in vLLM: Day-0-Unterstuetzung ...", section
+         "Warum ist ein Million-Token-Kontext eine Serving-Herausforderung?"
+         (each query or GQA query group scores all blocks; KV-block-major layout).
+
+Where the pages leave a step open this module takes these readings:
+  * score of a (query, key) pair for selection group g = sum over the group's
+    indexer heads of the raw dot product q_idx . k_idx (no scale, no softmax);
+  * block score = max over the block's keys and over the unit's queries;
+  * a unit is (request, 128-aligned query tile, group) in prefill and
+    (sequence, group) in decode; its "diagonal" block is the block that holds its
+    queries and is always kept; blocks after it are masked (causal);
+  * ties in block score go to the lower block id; ids are returned ascending and
+    padded with -1;
+  * query head i reads KV head i // (H_q / H_kv); with n_sel == H_kv selection
+    group g drives KV head g, with n_sel == 1 one selection serves every KV head.
+
+Cache layout (block-major, paged): cache[phys_block][head][token_in_block][dim],
+block_table[r][logical_block] = phys_block, seq_lens[r] = tokens of request r
+including its new ones.
+"""
+
+import math
+
+import numpy as np
+
+BLOCK = 128
+
+
+# ----------------------------------------------------------------------------
+# units
+# ----------------------------------------------------------------------------
+
+def prefill_units(seq_lens, q_lens):
+    """Units of a (chunked) prefill batch.
+
+    Request r has seq_lens[r] tokens in its cache, the last q_lens[r] of which are
+    its new queries, at positions seq_lens[r]-q_lens[r] ... seq_lens[r]-1, stored
+    contiguously in the query arrays after those of requests 0..r-1. Queries are
+    grouped by the 128-token block holding their position; that block is the
+    unit's diagonal block tau.
+
+    Returns a list of dicts with r, tau, row0, row1 (query rows [row0, row1)) and
+    pos0 (the position of row0).
+    """
+    units = []
+    row = 0
+    for r, (L, n) in enumerate(zip(seq_lens, q_lens)):
+        L, n = int(L), int(n)
+        assert 0 <= n <= L
+        first = L - n
+        p = first
+        while p < L:
+            tau = p // BLOCK
+            end = min((tau + 1) * BLOCK, L)
+            units.append(dict(r=r, tau=tau, row0=row + (p - first),
+                              row1=row + (end - first), pos0=p))
+            p = end
+        row += n
+    return units
+
+
+def decode_units(seq_lens):
+    """One unit per sequence: its single new query sits at position L-1."""
+    return [dict(r=r, tau=(int(L) - 1) // BLOCK, row0=r, row1=r + 1, pos0=int(L) - 1)
+            for r, L in enumerate(seq_lens)]
+
+
+# ----------------------------------------------------------------------------
+# paged cache access
+# ----------------------------------------------------------------------------
+
+def logical_block(cache, bt_row, b, heads=None):
+    """All 128 tokens of logical block b, float64 [128][heads][dim]."""
+    blk = np.asarray(cache[int(bt_row[b])], dtype=np.float64)   # [heads][128][dim]
+    if heads is not None:
+        blk = blk[heads]
+    return np.transpose(blk, (1, 0, 2))
+
+
+# ----------------------------------------------------------------------------
+# step 1: indexer block scores
+# ----------------------------------------------------------------------------
+
+def unit_block_scores(q_idx_rows, k_idx_cache, bt_row, tau, n_sel, row_len):
+    """Block scores of one unit, float64 [n_sel][row_len].
+
+    For candidate block b < tau:
+        S_g(b) = max over the unit's queries t and the block's keys s of
+                 sum over indexer heads h of group g of q_idx[t,h,:] . k_idx[s,h,:]
+    ([feat] "scores keys per head and pools into blocks"; the group sum and the
+    max pooling are the readings listed in the module docstring.)
+    S_g(tau) = +inf marks the always-kept diagonal block; blocks after tau and
+    entries past the request's last block are -inf (causal masking, the -inf
+    convention of [feat]).
+    """
+    q_idx_rows = np.asarray(q_idx_rows, dtype=np.float64)
+    T, H_i, D_i = q_idx_rows.shape
+    assert H_i % n_sel == 0
+    H_s = H_i // n_sel
+    S = np.full((n_sel, row_len), -np.inf)
+    for g in range(n_sel):
+        heads = slice(g * H_s, (g + 1) * H_s)
+        # the group's heads concatenated: one dot product of length H_s * D_i
+        qg = q_idx_rows[:, heads, :].reshape(T, H_s * D_i)
+        for b in range(tau):
+            kg = logical_block(k_idx_cache, bt_row, b, heads).reshape(BLOCK, H_s * D_i)
+            pair = qg @ kg.T                      # [T][128] pair scores
+            S[g, b] = pair.max()
+        S[g, tau] = np.inf
+    return S
+
+
+def index_scores(units, q_idx, k_idx_cache, block_table, n_sel, row_len):
+    """Scores for every unit: float64 [U][n_sel][row_len]."""
+    out = np.empty((len(units), n_sel, row_len))
+    for u, un in enumerate(units):
+        out[u] = unit_block_scores(q_idx[un["row0"]:un["row1"]], k_idx_cache,
+                                   block_table[un["r"]], un["tau"], n_sel, row_len)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# step 2: block selection
+# ----------------------------------------------------------------------------
+
+def select_blocks(scores_g, tau, topk):
+    """Kept blocks of one (unit, group) row, ascending, padded with -1.
+
+    K = min(topk, tau + 1) blocks are kept ([feat]: topk = min(topk_blocks,
+    num_key_blocks), with the tau + 1 causally visible blocks as the key
+    blocks): the diagonal tau plus the K - 1 candidates b < tau of highest score,
+    equal scores ordered by lower block id.
+    """
+    K = min(topk, tau + 1)
+    candidates = sorted(range(tau), key=lambda b: (-float(scores_g[b]), b))
+    kept = sorted([tau] + candidates[:K - 1])
+    return kept + [-1] * (topk - len(kept))
+
+
+def select(scores, units, topk):
+    """ids int32 [U][n_sel][topk] for all units."""
+    U, n_sel, _ = scores.shape
+    ids = np.empty((U, n_sel, topk), dtype=np.int32)
+    for u in range(U):
+        for g in range(n_sel):
+            ids[u, g] = select_blocks(scores[u, g], units[u]["tau"], topk)
+    return ids
+
+
+# ----------------------------------------------------------------------------
+# step 3: exact softmax attention over the kept blocks
+# ----------------------------------------------------------------------------
+
+def unit_attention(q_rows, pos0, ids_unit, k_cache, v_cache, bt_row, seq_len, n_sel,
+                   scale=None):
+    """Exact attention of one unit's queries over its kept blocks.
+
+    q_rows [T][H_q][D]; query row t sits at position pos0 + t.
+    ids_unit [n_sel][topk]. Query head i reads KV head j = i // G with G = H_q/H_kv
+    ([feat] "Grouped-query attention": repeat_kv); the selection row used is group
+    j when n_sel == H_kv and group 0 when n_sel == 1.
+
+    Visible keys of query t: every token s of a kept block with s <= pos0 + t and
+    s < seq_len. Logits z_s = scale * q . k_s (scale 1/sqrt(D) by default);
+    out = sum_s softmax(z)_s v_s and lse = log sum_s exp(z_s), natural log.
+    The softmax is plain, with no sink logit and no output gate ([feat] row
+    "Learnable attention sink").
+    Returns out [T][H_q][D] and lse [T][H_q], float64.
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    T, H_q, D = q_rows.shape
+    H_kv = k_cache.shape[1]
+    G = H_q // H_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = np.zeros((T, H_q, D))
+    lse = np.zeros((T, H_q))
+    positions = pos0 + np.arange(T)
+    for j in range(H_kv):
+        g = j if n_sel == H_kv else 0
+        blocks = [int(b) for b in ids_unit[g] if b >= 0]
+        keys = np.concatenate([np.arange(b * BLOCK, min((b + 1) * BLOCK, seq_len))
+                               for b in blocks])
+        # K/V rows line up with `keys`: both walk the kept blocks in the same
+        # order, each block cut at seq_len.
+        K, V = _trim_blocks(k_cache, v_cache, bt_row, blocks, seq_len, j)
+        visible = keys[None, :] <= positions[:, None]          # [T][nkeys]
+        for i in range(j * G, (j + 1) * G):
+            z = scale * (q_rows[:, i, :] @ K.T)                 # [T][nkeys]
+            z = np.where(visible, z, -np.inf)
+            m = z.max(axis=1, keepdims=True)
+            e = np.exp(z - m)
+            ssum = e.sum(axis=1, keepdims=True)
+            out[:, i, :] = (e / ssum) @ V
+            lse[:, i] = (m + np.log(ssum))[:, 0]
+    return out, lse
+
+
+def _trim_blocks(k_cache, v_cache, bt_row, blocks, seq_len, j):
+    """K and V rows (float64 [nkeys][D]) of KV head j over the kept blocks, in
+    block order, each block cut at seq_len."""
+    ks, vs = [], []
+    for b in blocks:
+        n = min(BLOCK, seq_len - b * BLOCK)
+        ks.append(logical_block(k_cache, bt_row, b, slice(j, j + 1))[:n, 0, :])
+        vs.append(logical_block(v_cache, bt_row, b, slice(j, j + 1))[:n, 0, :])
+    return np.concatenate(ks), np.concatenate(vs)
+
+
+def attention(units, ids, q, k_cache, v_cache, block_table, seq_lens, n_sel, scale=None):
+    """out [rows][H_q][D] and lse [rows][H_q] over all units."""
+    q = np.asarray(q)
+    rows = max(un["row1"] for un in units)
+    out = np.zeros((rows,) + q.shape[1:])
+    lse = np.zeros((rows, q.shape[1]))
+    for u, un in enumerate(units):
+        o, l = unit_attention(q[un["row0"]:un["row1"]], un["pos0"], ids[u], k_cache,
+                              v_cache, block_table[un["r"]], int(seq_lens[un["r"]]),
+                              n_sel, scale)
+        out[un["row0"]:un["row1"]] = o
+        lse[un["row0"]:un["row1"]] = l
+    return out, lse
+
+
+# ----------------------------------------------------------------------------
+# whole path
+# ----------------------------------------------------------------------------
+
+def max_blocks(seq_lens):
+    return max((int(L) + BLOCK - 1) // BLOCK for L in seq_lens)
+
+
+def run_prefill(q, q_idx, k_cache, v_cache, k_idx_cache, block_table, seq_lens, q_lens,
+                n_sel, topk, scale=None, row_len=None):
+    """Index, select and attend for a chunked prefill batch."""
+    units = prefill_units(seq_lens, q_lens)
+    row_len = row_len or block_table.shape[1]
+    scores = index_scores(units, q_idx, k_idx_cache, block_table, n_sel, row_len)
+    ids = select(scores, units, topk)
+    out, lse = attention(units, ids, q, k_cache, v_cache, block_table, seq_lens, n_sel,
+                         scale)
+    return dict(units=units, scores=scores, ids=ids, out=out, lse=lse)
+
+
+def run_decode(q, q_idx, k_cache, v_cache, k_idx_cache, block_table, seq_lens, n_sel,
+               topk, scale=None, row_len=None):
+    """Index, select and attend for one decode step (one query per sequence)."""
+    units = decode_units(seq_lens)
+    row_len = row_len or block_table.shape[1]
+    scores = index_scores(units, q_idx, k_idx_cache, block_table, n_sel, row_len)
+    ids = select(scores, units, topk)
+    out, lse = attention(units, ids, q, k_cache, v_cache, block_table, seq_lens, n_sel,
+                         scale)
+    return dict(units=units, scores=scores, ids=ids, out=out, lse=lse)

@@ -1,0 +1,448 @@
+"""Pins of the CPU oracle against facts fixed outside it: hand-worked examples,
+closed forms, library routines on special cases, brute force on tiny inputs and
+invariants of the definition. CPU only."""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import msa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+BLK = 128
+
+
+def _f(x):
+    return float(x) if not isinstance(x, str) else float(x.replace("inf", "Infinity")
+                                                         .replace("Infinity", "inf"))
+
+
+# ----------------------------------------------------------------------------
+# test-side helpers (independent of the oracle's code)
+# ----------------------------------------------------------------------------
+
+def paged(rng, seq_lens, heads, dim, permute=True, fill=None):
+    """A random paged cache [P][heads][128][dim] and its block table."""
+    nbs = [(L + BLK - 1) // BLK for L in seq_lens]
+    P = sum(nbs) + 2                    # two spare physical blocks never referenced
+    cache = rng.standard_normal((P, heads, BLK, dim)) if fill is None else fill((P, heads, BLK, dim))
+    perm = rng.permutation(P) if permute else np.arange(P)
+    bt = np.zeros((len(seq_lens), max(nbs)), dtype=np.int32)
+    base = 0
+    for r, nb in enumerate(nbs):
+        bt[r, :nb] = perm[base:base + nb]
+        base += nb
+    return cache, bt
+
+
+def logical(cache, bt_row, L):
+    """[L][heads][dim] by fancy indexing the block table."""
+    nb = (L + BLK - 1) // BLK
+    x = cache[bt_row[:nb]]                                  # [nb][H][128][dim]
+    return np.transpose(x, (0, 2, 1, 3)).reshape(nb * BLK, x.shape[1], x.shape[3])[:L]
+
+
+def dense_reference(q, k_log, v_log, positions, scale):
+    """Dense causal GQA attention with torch SDPA in float64, and lse with scipy."""
+    T, Hq, D = q.shape
+    Hkv = k_log.shape[1]
+    G = Hq // Hkv
+    qt = torch.from_numpy(q).permute(1, 0, 2)                       # [Hq][T][D]
+    kt = torch.from_numpy(k_log).permute(1, 0, 2).repeat_interleave(G, 0)
+    vt = torch.from_numpy(v_log).permute(1, 0, 2).repeat_interleave(G, 0)
+    keys = np.arange(k_log.shape[0])
+    mask = torch.from_numpy(keys[None, :] <= np.asarray(positions)[:, None])
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=mask, scale=scale).permute(1, 0, 2).numpy()
+    logits = (torch.matmul(qt, kt.transpose(1, 2)) * scale).numpy()   # [Hq][T][L]
+    logits = np.where(mask.numpy()[None], logits, -np.inf)
+    lse = scipy.special.logsumexp(logits, axis=2).T                    # [T][Hq]
+    return out, lse
+
+
+CASES = [
+    # seq_lens, q_lens, Hq, Hkv
+    ([1], [1], 1, 1),
+    ([5], [5], 4, 1),
+    ([127], [127], 2, 1),
+    ([128], [128], 4, 2),
+    ([129], [129], 4, 2),
+    ([300], [300], 8, 2),
+    ([1000], [1000], 4, 4),
+    ([700, 260, 129], [300, 260, 1], 8, 2),
+    ([513, 384], [1, 200], 4, 1),
+]
+
+
+@pytest.mark.parametrize("seq_lens,q_lens,Hq,Hkv", CASES)
+@pytest.mark.parametrize("sel", ["kv", "one"])
+def test_dense_when_topk_covers_all_blocks(seq_lens, q_lens, Hq, Hkv, sel):
+    """k >= number of blocks: MSA is exactly dense causal GQA attention."""
+    rng = np.random.default_rng(11)
+    D, Hi, Di = 16, 2 * Hkv, 8
+    nsel = Hkv if sel == "kv" else 1
+    kc, bt = paged(rng, seq_lens, Hkv, D)
+    vc = rng.standard_normal(kc.shape)
+    ki = rng.standard_normal((kc.shape[0], Hi, BLK, Di))
+    T = sum(q_lens)
+    q = rng.standard_normal((T, Hq, D))
+    qi = rng.standard_normal((T, Hi, Di))
+    topk = bt.shape[1] + 3
+    res = O.run_prefill(q, qi, kc, vc, ki, bt, seq_lens, q_lens, nsel, topk)
+    row = 0
+    for r, (L, n) in enumerate(zip(seq_lens, q_lens)):
+        pos = np.arange(L - n, L)
+        out, lse = dense_reference(q[row:row + n], logical(kc, bt[r], L),
+                                   logical(vc, bt[r], L), pos, 1 / math.sqrt(D))
+        np.testing.assert_allclose(res["out"][row:row + n], out, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(res["lse"][row:row + n], lse, rtol=1e-12, atol=1e-12)
+        row += n
+
+
+@pytest.mark.parametrize("L", [1, 77, 128])
+def test_single_block_is_plain_softmax(L):
+    """One block: plain causal softmax attention over that block (any k)."""
+    rng = np.random.default_rng(3)
+    D = 32
+    kc, bt = paged(rng, [L], 2, D)
+    vc = rng.standard_normal(kc.shape)
+    ki = rng.standard_normal((kc.shape[0], 2, BLK, 8))
+    q = rng.standard_normal((L, 4, D))
+    qi = rng.standard_normal((L, 2, 8))
+    res = O.run_prefill(q, qi, kc, vc, ki, bt, [L], [L], 2, 1)
+    assert (res["ids"][:, :, 0] == 0).all()
+    out, lse = dense_reference(q, logical(kc, bt[0], L), logical(vc, bt[0], L),
+                               np.arange(L), 1 / math.sqrt(D))
+    np.testing.assert_allclose(res["out"], out, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(res["lse"], lse, rtol=1e-12, atol=1e-12)
+
+
+def test_topk_one_attends_only_the_diagonal_block():
+    """k = 1 keeps only the query's own block: plain softmax over its prefix."""
+    rng = np.random.default_rng(4)
+    L, n, D = 700, 300, 32
+    kc, bt = paged(rng, [L], 1, D)
+    vc = rng.standard_normal(kc.shape)
+    ki = rng.standard_normal((kc.shape[0], 1, BLK, 8))
+    q = rng.standard_normal((n, 2, D))
+    qi = rng.standard_normal((n, 1, 8))
+    res = O.run_prefill(q, qi, kc, vc, ki, bt, [L], [n], 1, 1)
+    k_log, v_log = logical(kc, bt[0], L), logical(vc, bt[0], L)
+    for t in range(0, n, 37):
+        p = L - n + t
+        b0 = (p // BLK) * BLK
+        out, lse = dense_reference(q[t:t + 1], k_log[b0:p + 1], v_log[b0:p + 1],
+                                   [p - b0], 1 / math.sqrt(D))
+        np.testing.assert_allclose(res["out"][t], out[0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(res["lse"][t], lse[0], rtol=1e-12, atol=1e-12)
+
+
+def test_zero_query_gives_mean_of_visible_values():
+    """q = 0: uniform weights, out = mean of V over the visible keys, lse = ln|V_t|."""
+    rng = np.random.default_rng(5)
+    L, n, D, topk = 900, 420, 16, 3
+    kc, bt = paged(rng, [L], 2, D)
+    vc = rng.standard_normal(kc.shape)
+    ki = rng.standard_normal((kc.shape[0], 4, BLK, 8))
+    q = np.zeros((n, 4, D))
+    qi = rng.standard_normal((n, 4, 8))
+    res = O.run_prefill(q, qi, kc, vc, ki, bt, [L], [n], 2, topk)
+    v_log = logical(vc, bt[0], L)
+    for u, un in enumerate(res["units"]):
+        for t in range(un["row0"], un["row1"]):
+            p = un["pos0"] + (t - un["row0"])
+            for i in range(4):
+                j = i // 2
+                kept = [b for b in res["ids"][u, j] if b >= 0]
+                vis = [s for b in kept for s in range(b * BLK, min(b * BLK + BLK, p + 1))]
+                assert len(vis) == sum(BLK for b in kept if b < un["tau"]) + p - un["tau"] * BLK + 1
+                np.testing.assert_allclose(res["out"][t, i], v_log[vis, j].mean(0), atol=1e-12)
+                assert abs(res["lse"][t, i] - math.log(len(vis))) < 1e-12
+
+
+def test_constant_values_pass_through():
+    rng = np.random.default_rng(6)
+    L, n, D = 600, 600, 16
+    kc, bt = paged(rng, [L], 1, D)
+    c = rng.standard_normal(D)
+    vc = np.broadcast_to(c, kc.shape).copy()
+    ki = rng.standard_normal((kc.shape[0], 1, BLK, 8))
+    q = rng.standard_normal((n, 2, D)) * 3
+    qi = rng.standard_normal((n, 1, 8))
+    res = O.run_prefill(q, qi, kc, vc, ki, bt, [L], [n], 1, 2)
+    np.testing.assert_allclose(res["out"], np.broadcast_to(c, res["out"].shape), atol=1e-12)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    rng = np.random.default_rng(7)
+    L, n, D, G = 640, 250, 16, 4
+    kc, bt = paged(rng, [L], 2, D)
+    vc = rng.standard_normal(kc.shape)
+    ki = rng.standard_normal((kc.shape[0], 4, BLK, 8))
+    q = rng.standard_normal((n, 2 * G, D))
+    qi = rng.standard_normal((n, 4, 8))
+    gqa = O.run_prefill(q, qi, kc, vc, ki, bt, [L], [n], 1, 2)
+    mha = O.run_prefill(q, qi, np.repeat(kc, G, axis=1), np.repeat(vc, G, axis=1), ki, bt,
+                        [L], [n], 1, 2)
+    assert (gqa["ids"] == mha["ids"]).all()
+    np.testing.assert_allclose(gqa["out"], mha["out"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(gqa["lse"], mha["lse"], rtol=1e-13, atol=1e-13)
+
+
+def test_prefill_row_equals_decode_with_same_ids():
+    rng = np.random.default_rng(8)
+    L, n, D = 1000, 500, 16
+    kc, bt = paged(rng, [L], 2, D)
+    vc = rng.standard_normal(kc.shape)
+    ki = rng.standard_normal((kc.shape[0], 2, BLK, 8))
+    q = rng.standard_normal((n, 4, D))
+    qi = rng.standard_normal((n, 2, 8))
+    res = O.run_prefill(q, qi, kc, vc, ki, bt, [L], [n], 2, 3)
+    for u, un in enumerate(res["units"]):
+        t = un["row0"] + (un["row1"] - un["row0"]) // 2
+        p = un["pos0"] + t - un["row0"]
+        o, l = O.unit_attention(q[t:t + 1], p, res["ids"][u], kc, vc, bt[0], p + 1, 2)
+        np.testing.assert_allclose(o[0], res["out"][t], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(l[0], res["lse"][t], rtol=1e-13, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# indexer scores
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nsel", [1, 2])
+def test_scores_brute_force_loops(nsel):
+    """Explicit loops over queries, keys, heads and dims on a tiny chunked case."""
+    rng = np.random.default_rng(9)
+    seq_lens, q_lens, Hi, Di = [300, 200], [50, 130], 4, 3
+    ki, bt = paged(rng, seq_lens, Hi, Di)
+    qi = rng.standard_normal((sum(q_lens), Hi, Di))
+    units = O.prefill_units(seq_lens, q_lens)
+    S = O.index_scores(units, qi, ki, bt, nsel, bt.shape[1])
+    Hs = Hi // nsel
+    for u, un in enumerate(units):
+        for g in range(nsel):
+            for b in range(bt.shape[1]):
+                if b > un["tau"] or b >= (seq_lens[un["r"]] + BLK - 1) // BLK:
+                    assert S[u, g, b] == -np.inf
+                    continue
+                if b == un["tau"]:
+                    assert S[u, g, b] == np.inf
+                    continue
+                best = -np.inf
+                for t in range(un["row0"], un["row1"]):
+                    for s in range(b * BLK, b * BLK + BLK):
+                        blk, row = bt[un["r"], s // BLK], s % BLK
+                        acc = 0.0
+                        for h in range(g * Hs, g * Hs + Hs):
+                            for d in range(Di):
+                                acc += qi[t, h, d] * ki[blk, h, row, d]
+                        best = max(best, acc)
+                assert abs(S[u, g, b] - best) <= 1e-12 * max(1.0, abs(best))
+
+
+def test_scores_constant_block_closed_form():
+    """k_idx constant within a block: S_g(b) = max_t sum_h q_idx[t,h] . c_h(b)."""
+    rng = np.random.default_rng(10)
+    L, n, Hi, Di = 900, 200, 4, 8
+    nb = (L + BLK - 1) // BLK
+    c = rng.standard_normal((nb, Hi, Di))
+    bt = np.arange(nb, dtype=np.int32)[None][:, ::-1].copy()         # reversed layout
+    ki = np.empty((nb, Hi, BLK, Di))
+    for b in range(nb):
+        ki[bt[0, b]] = c[b][:, None, :]
+    qi = rng.standard_normal((n, Hi, Di))
+    units = O.prefill_units([L], [n])
+    S = O.index_scores(units, qi, ki, bt, 2, nb)
+    for u, un in enumerate(units):
+        rows = qi[un["row0"]:un["row1"]]
+        for g in range(2):
+            for b in range(un["tau"]):
+                want = max(float(np.sum(rows[t, 2 * g:2 * g + 2] * c[b, 2 * g:2 * g + 2]))
+                           for t in range(len(rows)))
+                assert abs(S[u, g, b] - want) < 1e-12
+
+
+def test_zero_keys_tie_to_lowest_ids():
+    """All-zero indexer keys: every candidate scores exactly 0, so the kept blocks
+    are the lowest ids 0..K-2 plus the diagonal."""
+    rng = np.random.default_rng(12)
+    L, n = 1500, 400
+    ki, bt = paged(rng, [L], 2, 8, fill=np.zeros)
+    qi = rng.standard_normal((n, 2, 8))
+    units = O.prefill_units([L], [n])
+    S = O.index_scores(units, qi, ki, bt, 1, bt.shape[1])
+    ids = O.select(S, units, 4)
+    for u, un in enumerate(units):
+        tau = un["tau"]
+        assert (S[u, 0, :tau] == 0).all()
+        K = min(4, tau + 1)
+        assert list(ids[u, 0]) == list(range(K - 1)) + [tau] + [-1] * (4 - K)
+
+
+def test_group_isolation():
+    """Only group 1's indexer heads carry signal: group 0 scores are exactly 0."""
+    rng = np.random.default_rng(13)
+    L, n = 700, 300
+    ki, bt = paged(rng, [L], 4, 8)
+    qi = rng.standard_normal((n, 4, 8))
+    qi[:, :2] = 0.0
+    units = O.prefill_units([L], [n])
+    S = O.index_scores(units, qi, ki, bt, 2, bt.shape[1])
+    for u, un in enumerate(units):
+        assert (S[u, 0, :un["tau"]] == 0).all()
+        assert (S[u, 1, :un["tau"]] != 0).all()
+
+
+def test_planted_dominant_block_is_kept():
+    rng = np.random.default_rng(14)
+    L, n = 2000, 600
+    ki, bt = paged(rng, [L], 2, 16)
+    qi = rng.standard_normal((n, 2, 16))
+    direction = qi.sum(axis=0)                       # shared direction of the queries
+    planted = 3
+    ki[bt[0, planted]] = 50.0 * direction[:, None, :] / np.linalg.norm(direction)
+    qi += 2.0 * direction / np.linalg.norm(direction)
+    units = O.prefill_units([L], [n])
+    ids = O.select(O.index_scores(units, qi, ki, bt, 1, bt.shape[1]), units, 2)
+    for u, un in enumerate(units):
+        if un["tau"] > planted:
+            assert planted in ids[u, 0]
+
+
+def test_positive_scaling_keeps_selection():
+    rng = np.random.default_rng(15)
+    L, n = 1600, 500
+    ki, bt = paged(rng, [L], 2, 8)
+    qi = rng.standard_normal((n, 2, 8))
+    units = O.prefill_units([L], [n])
+    a = O.select(O.index_scores(units, qi, ki, bt, 2, bt.shape[1]), units, 3)
+    b = O.select(O.index_scores(units, 2.5 * qi, ki, bt, 2, bt.shape[1]), units, 3)
+    assert (a == b).all()
+
+
+def test_block_table_permutation_is_exact():
+    rng = np.random.default_rng(16)
+    seq_lens, q_lens, D = [800, 300], [400, 300], 16
+    ident = {}
+    for permute in (False, True):
+        r2 = np.random.default_rng(17)
+        kc, bt = paged(r2, seq_lens, 2, D, permute=False)
+        vc = r2.standard_normal(kc.shape)
+        ki = r2.standard_normal((kc.shape[0], 2, BLK, 8))
+        if permute:
+            perm = rng.permutation(kc.shape[0])
+            inv = np.argsort(perm)
+            kc, vc, ki = kc[perm], vc[perm], ki[perm]
+            bt = inv[bt].astype(np.int32)
+        q = r2.standard_normal((sum(q_lens), 4, D))
+        qi = r2.standard_normal((sum(q_lens), 2, 8))
+        ident[permute] = O.run_prefill(q, qi, kc, vc, ki, bt, seq_lens, q_lens, 2, 3)
+    for key in ("scores", "ids", "out", "lse"):
+        assert np.array_equal(ident[False][key], ident[True][key]), key
+
+
+# ----------------------------------------------------------------------------
+# selection
+# ----------------------------------------------------------------------------
+
+def generic_row_rule(row, topk):
+    """Top-k of a row by (score desc, index asc) over entries above -inf, ascending."""
+    valid = [b for b in range(len(row)) if row[b] != -np.inf]
+    kept = sorted(sorted(valid, key=lambda b: (-row[b], b))[:topk])
+    return kept + [-1] * (topk - len(kept))
+
+
+def test_select_matches_generic_row_rule():
+    rng = np.random.default_rng(18)
+    for _ in range(400):
+        n = int(rng.integers(1, 40))
+        tau = int(rng.integers(0, n))
+        row = np.full(n, -np.inf)
+        row[:tau] = rng.integers(-3, 4, size=tau).astype(float)   # many ties
+        row[tau] = np.inf
+        topk = int(rng.integers(1, n + 3))
+        want = generic_row_rule(row, topk)
+        got = O.select_blocks(row, tau, topk)
+        assert got == want
+        kept = [b for b in got if b >= 0]
+        assert tau in kept and kept == sorted(set(kept)) and len(kept) == min(topk, tau + 1)
+        out = [b for b in range(tau) if b not in kept]
+        for a in kept:
+            for b in out:
+                assert (row[a], -a) > (row[b], -b)
+
+
+def test_select_golden_cases():
+    cases = json.load(open(os.path.join(GOLDEN, "select_cases.json")))["cases"]
+    for c in cases:
+        row = np.array([_f(x) for x in c["scores"]])
+        tau = int(np.where(row == np.inf)[0][0])
+        assert O.select_blocks(row, tau, c["topk"]) == c["expected"], c
+
+
+# ----------------------------------------------------------------------------
+# hand-worked example
+# ----------------------------------------------------------------------------
+
+def _hand_cache():
+    ki = np.zeros((3, 2, BLK, 2))
+    ki[0, 0, :, :] = [1.0, 0.0]
+    ki[0, 1, :, :] = [0.0, 1.0]
+    ki[0, 0, 5, :] = [2.0, 0.0]
+    ki[1, 0, 2, :] = [0.0, 3.0]
+    ki[2] = 1.0
+    return ki
+
+
+def test_hand_example_indexer():
+    g = json.load(open(os.path.join(GOLDEN, "hand_example.json")))["indexer"]
+    ki = _hand_cache()
+    bt = np.array([[0, 1, 2]], dtype=np.int32)
+    qi = np.array(g["q_idx"])[None]
+    units = O.decode_units([g["seq_len"]])
+    assert units[0]["pos0"] == g["query_pos"]
+    for nsel in (1, 2):
+        S = O.index_scores(units, qi, ki, bt, nsel, 3)
+        want = np.array([[_f(x) for x in row] for row in g[f"expected_scores_nsel{nsel}"]])
+        assert np.array_equal(S[0], want)
+        for k, ids in g[f"expected_ids_nsel{nsel}"].items():
+            assert O.select(S, units, int(k))[0].tolist() == ids
+
+
+def test_hand_example_attention():
+    g = json.load(open(os.path.join(GOLDEN, "hand_example.json")))["attention"]
+    kc = np.zeros((1, 1, BLK, 1))
+    vc = np.zeros((1, 1, BLK, 1))
+    kc[0, 0, :3, 0] = g["keys"]
+    vc[0, 0, :3, 0] = g["values"]
+    q = np.full((3, 1, 1), g["q"])
+    out, lse = O.unit_attention(q, 0, np.array([[0]]), kc, vc, np.array([0]), 3, 1,
+                                scale=g["scale"])
+    np.testing.assert_allclose(out[:, 0, 0], g["expected_out"], rtol=1e-14)
+    np.testing.assert_allclose(lse[:, 0], g["expected_lse"], rtol=1e-14, atol=1e-15)
+
+
+def test_hand_example_units():
+    g = json.load(open(os.path.join(GOLDEN, "hand_example.json")))["units"]
+    assert O.prefill_units(g["seq_lens"], g["q_lens"]) == g["expected"]
+
+
+def test_planted_pins_would_catch_a_transposed_group():
+    """Sanity of the pins themselves: a mistaken group slicing (heads taken
+    interleaved instead of contiguous) changes the scores of the isolation case."""
+    rng = np.random.default_rng(19)
+    ki, bt = paged(rng, [400], 4, 8)
+    qi = rng.standard_normal((100, 4, 8))
+    qi[:, :2] = 0.0
+    units = O.prefill_units([400], [100])
+    un = units[0]
+    wrong = max(float(np.max(qi[t, 0::2].reshape(-1) @ O.logical_block(ki, bt[0], 0, slice(0, 4, 2))
+                             .reshape(BLK, -1).T)) for t in range(un["row0"], un["row1"]))
+    assert wrong != 0.0
