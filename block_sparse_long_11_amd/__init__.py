@@ -1,0 +1,366 @@
+"""Python binding of libmsa (include/msa.h): MiniMax Sparse Attention on MI355X.
+
+Argument marshalling only. Every step of the path runs in the HIP kernels of
+libmsa.so; torch supplies device memory and the current stream. There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+
+Entry points (same names as the C ABI):
+  msa_prefill_plan, msa_index_scores, msa_select_topk_blocks,
+  msa_sparse_attn_prefill, msa_decode_workspace_size, msa_sparse_attn_decode
+plus two helpers that allocate outputs and run the whole path:
+  prefill(...) and decode(...).
+"""
+
+import ctypes
+import dataclasses
+import pathlib
+
+import numpy as np
+import torch
+
+_LIB_PATH = pathlib.Path(__file__).resolve().parent / "libmsa.so"
+_lib = None
+
+MSA_F32, MSA_BF16 = 0, 1
+BLOCK = 128
+
+
+class MsaError(RuntimeError):
+    """A libmsa call returned a non-zero status."""
+
+    def __init__(self, status, message):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+class _Geom(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_q_heads", "num_kv_heads", "head_dim", "num_idx_heads", "idx_head_dim",
+        "num_sel_groups", "block_size", "dtype")]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("k_idx_cache", ctypes.c_void_p), ("num_phys_blocks", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("max_blocks_per_seq", ctypes.c_int32),
+                ("seq_lens", ctypes.c_void_p), ("num_seqs", ctypes.c_int32)]
+
+
+class _Unit(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("r", "tau", "row0", "num_rows", "pos0")]
+
+
+class _Batch(ctypes.Structure):
+    _fields_ = [("units", ctypes.c_void_p), ("total_units", ctypes.c_int32),
+                ("total_q", ctypes.c_int32)]
+
+
+EXPORTS = {
+    # name: (restype, argtypes)
+    "msa_prefill_plan": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
+    "msa_index_scores": (ctypes.c_int, [ctypes.POINTER(_Geom), ctypes.POINTER(_Cache),
+                                        ctypes.POINTER(_Batch), ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]),
+    "msa_select_topk_blocks": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
+    "msa_sparse_attn_prefill": (ctypes.c_int, [ctypes.POINTER(_Geom), ctypes.POINTER(_Cache),
+                                               ctypes.POINTER(_Batch), ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+                                               ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_void_p]),
+    "msa_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(_Geom), ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.c_int32]),
+    "msa_sparse_attn_decode": (ctypes.c_int, [ctypes.POINTER(_Geom), ctypes.POINTER(_Cache),
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                              ctypes.c_float, ctypes.c_int32, ctypes.c_void_p,
+                                              ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p]),
+    "msa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "msa_last_error": (ctypes.c_char_p, []),
+    "msa_version": (ctypes.c_int32, []),
+}
+
+
+def lib():
+    """The loaded libmsa.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not _LIB_PATH.exists():
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with "
+                "`python -m block_sparse_long_11_amd.build` (there is no fallback path)")
+        handle = ctypes.CDLL(str(_LIB_PATH))
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+def _status_name(status):
+    try:
+        return lib().msa_status_string(status).decode()
+    except Exception:   # library unavailable while formatting an error
+        return f"status {status}"
+
+
+def _check(status):
+    if status != 0:
+        raise MsaError(status, lib().msa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+@dataclasses.dataclass
+class Geometry:
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    num_idx_heads: int
+    idx_head_dim: int
+    num_sel_groups: int
+    dtype: str = "bf16"          # "bf16" or "f32"
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def c(self):
+        return _Geom(self.num_q_heads, self.num_kv_heads, self.head_dim, self.num_idx_heads,
+                     self.idx_head_dim, self.num_sel_groups, BLOCK,
+                     MSA_BF16 if self.dtype == "bf16" else MSA_F32)
+
+
+@dataclasses.dataclass
+class Cache:
+    """Block-major paged caches on one device (see include/msa.h)."""
+    k_cache: torch.Tensor        # [P][H_kv][128][D]
+    v_cache: torch.Tensor        # [P][H_kv][128][D]
+    k_idx_cache: torch.Tensor    # [P][H_i][128][D_i]
+    block_table: torch.Tensor    # int32 [B][max_blocks]
+    seq_lens: torch.Tensor       # int32 [B]
+
+    def check(self, geom: Geometry):
+        dt, dev = geom.torch_dtype, self.block_table.device
+        _need(self.k_cache, "k_cache", dt, 4, dev)
+        _need(self.v_cache, "v_cache", dt, 4, dev)
+        _need(self.k_idx_cache, "k_idx_cache", dt, 4, dev)
+        _need(self.block_table, "block_table", torch.int32, 2, dev)
+        _need(self.seq_lens, "seq_lens", torch.int32, 1, dev)
+        P = self.k_cache.shape[0]
+        if tuple(self.k_cache.shape) != (P, geom.num_kv_heads, BLOCK, geom.head_dim) or \
+                self.v_cache.shape != self.k_cache.shape:
+            raise ValueError("k_cache / v_cache must be [P][H_kv][128][D]")
+        if tuple(self.k_idx_cache.shape) != (P, geom.num_idx_heads, BLOCK, geom.idx_head_dim):
+            raise ValueError("k_idx_cache must be [P][H_i][128][D_i]")
+        if self.seq_lens.shape[0] != self.block_table.shape[0]:
+            raise ValueError("seq_lens and block_table disagree on the number of sequences")
+
+    @property
+    def num_seqs(self):
+        return self.block_table.shape[0]
+
+    @property
+    def max_blocks(self):
+        return self.block_table.shape[1]
+
+    def c(self):
+        return _Cache(self.k_cache.data_ptr(), self.v_cache.data_ptr(),
+                      self.k_idx_cache.data_ptr(), self.k_cache.shape[0],
+                      self.block_table.data_ptr(), self.block_table.shape[1],
+                      self.seq_lens.data_ptr(), self.block_table.shape[0])
+
+
+@dataclasses.dataclass
+class Batch:
+    """A planned prefill batch: `units` (host int32 [U][5]) and its device copy."""
+    units_host: np.ndarray
+    units: torch.Tensor          # int32 [U][5] on the device
+    total_q: int
+
+    @property
+    def total_units(self):
+        return int(self.units_host.shape[0])
+
+    def c(self):
+        return _Batch(self.units.data_ptr() if self.total_units else None,
+                      self.total_units, self.total_q)
+
+
+# ----------------------------------------------------------------------------
+# C-ABI wrappers
+# ----------------------------------------------------------------------------
+
+def msa_prefill_plan(seq_lens, q_lens):
+    """Host plan of a prefill batch: int32 [U][5] rows (r, tau, row0, num_rows, pos0)."""
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    ql = np.ascontiguousarray(q_lens, dtype=np.int32)
+    if sl.shape != ql.shape or sl.ndim != 1:
+        raise ValueError("seq_lens and q_lens must be 1-D and of equal length")
+    n = ctypes.c_int32(0)
+    _check(lib().msa_prefill_plan(sl.ctypes.data, ql.ctypes.data, len(sl), None, 0,
+                                  ctypes.byref(n)))
+    units = np.zeros((n.value, 5), dtype=np.int32)
+    _check(lib().msa_prefill_plan(sl.ctypes.data, ql.ctypes.data, len(sl),
+                                  units.ctypes.data if n.value else None, n.value,
+                                  ctypes.byref(n)))
+    return units
+
+
+def make_batch(seq_lens, q_lens, device):
+    units = msa_prefill_plan(seq_lens, q_lens)
+    return Batch(units, torch.from_numpy(units).to(device), int(np.sum(q_lens)))
+
+
+def msa_index_scores(geom: Geometry, cache: Cache, batch, q_idx, scores, stream=None):
+    """Step 1. batch=None is decode. scores: fp32 [U][n_sel][max_blocks]."""
+    cache.check(geom)
+    dev = cache.block_table.device
+    _need(q_idx, "q_idx", geom.torch_dtype, 3, dev)
+    _need(scores, "scores", torch.float32, 3, dev)
+    U = cache.num_seqs if batch is None else batch.total_units
+    rows_q = cache.num_seqs if batch is None else batch.total_q
+    if tuple(q_idx.shape) != (rows_q, geom.num_idx_heads, geom.idx_head_dim):
+        raise ValueError(f"q_idx must be [{rows_q}][H_i][D_i], got {tuple(q_idx.shape)}")
+    if tuple(scores.shape) != (U, geom.num_sel_groups, cache.max_blocks):
+        raise ValueError(f"scores must be [{U}][n_sel][{cache.max_blocks}]")
+    g, c = geom.c(), cache.c()
+    b = None if batch is None else ctypes.pointer(batch.c())
+    _check(lib().msa_index_scores(ctypes.byref(g), ctypes.byref(c), b, _ptr(q_idx),
+                                  _ptr(scores), _stream(stream)))
+
+
+def msa_select_topk_blocks(scores, topk, ids, stream=None):
+    """Step 2 over the rows of scores (any leading shape); ids int32 [..., topk]."""
+    _need(scores, "scores", torch.float32)
+    _need(ids, "ids", torch.int32, None, scores.device)
+    row_len = scores.shape[-1]
+    rows = scores.numel() // row_len
+    if ids.numel() != rows * topk or ids.shape[-1] != topk:
+        raise ValueError("ids must hold [rows][topk]")
+    _check(lib().msa_select_topk_blocks(_ptr(scores), rows, row_len, topk, _ptr(ids),
+                                        _stream(stream)))
+
+
+def msa_sparse_attn_prefill(geom: Geometry, cache: Cache, batch: Batch, q, ids, topk, out,
+                            lse=None, softmax_scale=0.0, stream=None):
+    """Step 3 for prefill. q/out [total_q][H_q][D], lse fp32 [total_q][H_q] or None."""
+    cache.check(geom)
+    dev = cache.block_table.device
+    _need(q, "q", geom.torch_dtype, 3, dev)
+    _need(out, "out", geom.torch_dtype, 3, dev)
+    _need(ids, "ids", torch.int32, 3, dev)
+    shape = (batch.total_q, geom.num_q_heads, geom.head_dim)
+    if tuple(q.shape) != shape or tuple(out.shape) != shape:
+        raise ValueError(f"q and out must be {shape}")
+    if tuple(ids.shape) != (batch.total_units, geom.num_sel_groups, topk):
+        raise ValueError("ids must be [U][n_sel][topk]")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+        if tuple(lse.shape) != shape[:2]:
+            raise ValueError("lse must be [total_q][H_q]")
+    g, c, b = geom.c(), cache.c(), batch.c()
+    _check(lib().msa_sparse_attn_prefill(ctypes.byref(g), ctypes.byref(c), ctypes.byref(b),
+                                         _ptr(q), _ptr(ids), topk, float(softmax_scale),
+                                         _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def msa_decode_workspace_size(geom: Geometry, num_seqs, topk, num_splits=0):
+    g = geom.c()
+    return int(lib().msa_decode_workspace_size(ctypes.byref(g), num_seqs, topk, num_splits))
+
+
+def msa_sparse_attn_decode(geom: Geometry, cache: Cache, q, ids, topk, out, workspace,
+                           lse=None, num_splits=0, softmax_scale=0.0, stream=None):
+    """Steps 3+4 for decode. q/out [B][H_q][D]; workspace a uint8 device tensor."""
+    cache.check(geom)
+    dev = cache.block_table.device
+    B = cache.num_seqs
+    _need(q, "q", geom.torch_dtype, 3, dev)
+    _need(out, "out", geom.torch_dtype, 3, dev)
+    _need(ids, "ids", torch.int32, 3, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    shape = (B, geom.num_q_heads, geom.head_dim)
+    if tuple(q.shape) != shape or tuple(out.shape) != shape:
+        raise ValueError(f"q and out must be {shape}")
+    if tuple(ids.shape) != (B, geom.num_sel_groups, topk):
+        raise ValueError("ids must be [B][n_sel][topk]")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+    g, c = geom.c(), cache.c()
+    _check(lib().msa_sparse_attn_decode(ctypes.byref(g), ctypes.byref(c), _ptr(q), _ptr(ids),
+                                        topk, float(softmax_scale), num_splits, _ptr(workspace),
+                                        workspace.numel(), _ptr(out), _ptr(lse),
+                                        _stream(stream)))
+
+
+def workspace(nbytes, device):
+    """A 256-byte aligned uint8 device buffer of at least nbytes."""
+    raw = torch.empty(max(1, nbytes) + 256, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % 256
+    return raw[off:off + max(1, nbytes)]
+
+
+# ----------------------------------------------------------------------------
+# whole-path helpers (allocate outputs, call the four entry points in order)
+# ----------------------------------------------------------------------------
+
+def prefill(geom: Geometry, cache: Cache, batch: Batch, q, q_idx, topk, softmax_scale=0.0,
+            stream=None):
+    """Index, select and attend for a prefill batch. Returns dict of device tensors."""
+    dev = q.device
+    U = batch.total_units
+    scores = torch.empty((U, geom.num_sel_groups, cache.max_blocks), dtype=torch.float32,
+                         device=dev)
+    ids = torch.empty((U, geom.num_sel_groups, topk), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    msa_index_scores(geom, cache, batch, q_idx, scores, stream)
+    msa_select_topk_blocks(scores, topk, ids, stream)
+    msa_sparse_attn_prefill(geom, cache, batch, q, ids, topk, out, lse, softmax_scale, stream)
+    return dict(scores=scores, ids=ids, out=out, lse=lse)
+
+
+def decode(geom: Geometry, cache: Cache, q, q_idx, topk, num_splits=0, softmax_scale=0.0,
+           stream=None, ws=None):
+    """Index, select and attend for one decode step. Returns dict of device tensors."""
+    dev = q.device
+    B = cache.num_seqs
+    scores = torch.empty((B, geom.num_sel_groups, cache.max_blocks), dtype=torch.float32,
+                         device=dev)
+    ids = torch.empty((B, geom.num_sel_groups, topk), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(msa_decode_workspace_size(geom, B, topk, num_splits), dev)
+    msa_index_scores(geom, cache, None, q_idx, scores, stream)
+    msa_select_topk_blocks(scores, topk, ids, stream)
+    msa_sparse_attn_decode(geom, cache, q, ids, topk, out, ws, lse, num_splits, softmax_scale,
+                           stream)
+    return dict(scores=scores, ids=ids, out=out, lse=lse)

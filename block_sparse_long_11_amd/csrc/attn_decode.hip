@@ -1,0 +1,268 @@
+// Split-KV sparse decode attention and its log-sum-exp combine (steps 3 and 4 of
+// MSA, decode).
+//
+// [dd] daily.dev "MiniMax M3 ...", section "Serving options": decode kernels for
+// sparse GQA. [feat] models.inteligile.com "MiniMax-M3", method list "Two-phase
+// forward" and "LSE fusion": the kept blocks are attended in independent parts
+// whose partial results are merged through their logsumexp; "query
+// concatenation": the G query heads that share a KV head are stacked against
+// each KV block. Row "Grouped-query attention": query head i reads KV head i / G.
+//
+// Phase 1: one work-group (4 waves) per (sequence, KV head j, split). Its G <= 16
+// query heads form the N = 16 columns of MFMA 16x16x32 bf16 products; each wave
+// takes 32 keys of every kept block of the split:
+//   S^T = K . Q^T    (A = K rows read straight from HBM, 16-byte loads;
+//                     B = the stacked queries in registers)
+//   O^T += V^T . P^T (A = V^T from LDS, B = probabilities from S^T's registers)
+// In the accumulator, lane l register i of 16-key tile tt holds key
+// 16tt + 4(l/16) + i; as a B operand lane l supplies k-index 8(l/16) + 4tt + i,
+// so V^T is stored in LDS in that same key order. The waves' partial (max, sum,
+// O) are merged in LDS and written normalised, with their natural-log lse, to
+// the workspace.
+// Phase 2: per (sequence, query head) the parts are merged:
+//   lse = log sum_s exp(lse_s),  out = sum_s exp(lse_s - lse) o_s.
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+hipError_t launch_attn_f32(const Geom &g, const msa_cache_t &c, const msa_unit_t *units,
+                           int num_units, const void *q, const int32_t *ids, int topk,
+                           float scale, void *out, float *lse, hipStream_t st);
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kDecThreads = 256;
+constexpr int kVtRow = 40;       // LDS row of V^T: 32 keys + 8 pad (elements)
+
+__device__ __forceinline__ int dec_kappa(int kl) {   // key (0..31) -> k-index
+  return 8 * ((kl % 16) / 4) + 4 * (kl / 16) + (kl % 4);
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ vc, const int32_t *__restrict__ block_table,
+    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ ids, int topk,
+    int max_blocks, int Hq, int Hkv, int nsel, int num_splits, int per_split,
+    float scale_log2, float *__restrict__ o_part, float *__restrict__ lse_part) {
+  constexpr int KS = D / 32;   // k steps of S^T
+  constexpr int DT = D / 16;   // d tiles of O^T
+  // V^T of the current block per wave; after the last block the same bytes hold
+  // the waves' partial outputs for the merge.
+  constexpr int kVtBytes = 4 * D * kVtRow * 2;
+  constexpr int kOwBytes = 4 * 16 * (D + 1) * 4;
+  static_assert(kOwBytes <= kVtBytes, "merge buffer must fit in the V^T buffer");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kVtBytes];
+  __shared__ float Mw[4][16], Lw[4][16];
+  auto Vt = reinterpret_cast<uint16_t (*)[D * kVtRow]>(smem);
+  auto Ow = reinterpret_cast<float (*)[16][D + 1]>(smem);
+
+  const int r = blockIdx.x / Hkv, j = blockIdx.x % Hkv, sp = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int g = (nsel == Hkv) ? j : 0;
+  const int32_t *sel = ids + (static_cast<size_t>(r) * nsel + g) * topk;
+  const int32_t *bt = block_table + static_cast<size_t>(r) * max_blocks;
+  const int qpos = seq_lens[r] - 1;
+  const int slot0 = sp * per_split, slot1 = min(topk, slot0 + per_split);
+
+  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+  const int n = lane % 16;               // stacked query head (column)
+  const int qd = (lane / 16) * 8;        // this lane's 8 d inside a k step
+
+  bf16x8 qb[KS];
+  {
+    const bool live = n < G;
+    const uint16_t *qp = q + (static_cast<size_t>(r) * Hq + j * G + (live ? n : 0)) * D + qd;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = *reinterpret_cast<const uint4 *>(qp + ks * 32);
+      if (!live) v = uint4{0, 0, 0, 0};
+      qb[ks] = as_bf16x8(v);
+    }
+  }
+  f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{};
+  float m_run = -1e30f, l_run = 0.f;
+  bool any = false;
+
+  for (int slot = slot0; slot < slot1; ++slot) {
+    const int b = sel[slot];
+    if (b < 0) break;
+    any = true;
+    const int64_t phys = bt[b];
+    const size_t off = (static_cast<size_t>(phys) * Hkv + j) * kBlk * D;
+    __syncthreads();                       // previous block's V^T fully read
+    // stage V^T: 16-byte chunk c = (key, d chunk); lanes of a row are consecutive
+    for (int c = t; c < kBlk * D / 8; c += kDecThreads) {
+      const int key = c / (D / 8), dc = c % (D / 8);
+      const uint4 v = *reinterpret_cast<const uint4 *>(vc + off + key * D + dc * 8);
+      uint16_t *dst = &Vt[key / 32][dc * 8 * kVtRow + dec_kappa(key % 32)];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e * kVtRow] = (w[e / 2] >> ((e % 2) * 16)) & 0xffffu;
+    }
+    // S^T for this wave's 32 keys: 2 tiles of 16 keys x 16 heads
+    f32x4 s[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      s[tt] = f32x4{};
+      const uint16_t *kr = kc + off + (wave * 32 + tt * 16 + n) * D + qd;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(kr + ks * 32));
+        s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], s[tt], 0, 0, 0);
+      }
+    }
+    float mx = -1e30f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = wave * 32 + tt * 16 + (lane / 16) * 4 + i;
+        float x = s[tt][i] * scale_log2;
+        if (b * kBlk + key > qpos) x = neg_inf();
+        s[tt][i] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float p[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[tt * 4 + i] = exp2f(s[tt][i] - m_new);
+        psum += p[tt * 4 + i];
+      }
+    l_run = l_run * alpha + psum;
+    const bf16x8 pb = as_bf16x8(uint4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
+    __syncthreads();                       // V^T staged
+    const uint16_t *vr = &Vt[wave][n * kVtRow + qd];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      o[dt] *= alpha;
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(vr + dt * 16 * kVtRow));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
+    }
+  }
+
+  // merge the 4 waves: per column n the waves hold (m, partial l, O^T)
+  __syncthreads();                         // V^T no longer read
+  float l_w = l_run + __shfl_xor(l_run, 16, kWave);
+  l_w += __shfl_xor(l_w, 32, kWave);
+  if (lane < 16) {
+    Mw[wave][n] = m_run;
+    Lw[wave][n] = l_w;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ow[wave][n][dt * 16 + (lane / 16) * 4 + i] = o[dt][i];
+  __syncthreads();
+  const size_t part0 = static_cast<size_t>(r) * Hq * num_splits;
+  for (int e = t; e < G * D; e += kDecThreads) {
+    const int hn = e / D, d = e % D;
+    const size_t pi = part0 + static_cast<size_t>(j * G + hn) * num_splits + sp;
+    if (!any) {
+      o_part[pi * D + d] = 0.f;
+      if (d == 0) lse_part[pi] = neg_inf();
+      continue;
+    }
+    const float M = fmaxf(fmaxf(Mw[0][hn], Mw[1][hn]), fmaxf(Mw[2][hn], Mw[3][hn]));
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = exp2f(Mw[w][hn] - M);
+      L += Lw[w][hn] * f;
+      acc += Ow[w][hn][d] * f;
+    }
+    o_part[pi * D + d] = acc / L;
+    if (d == 0) lse_part[pi] = (M + log2f(L)) * kLn2;
+  }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(D) void combine_kernel(const float *__restrict__ o_part,
+                                                    const float *__restrict__ lse_part,
+                                                    int num_splits, void *__restrict__ out,
+                                                    float *__restrict__ lse) {
+  const size_t row = blockIdx.x;   // sequence * Hq + head
+  const int d = threadIdx.x;
+  const float *lp = lse_part + row * num_splits;
+  float M = neg_inf();
+  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, lp[s]);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < num_splits; ++s) {
+    const float ls = lp[s];
+    if (ls == neg_inf()) continue;
+    const float w = __expf(ls - M);
+    L += w;
+    acc += w * o_part[(row * num_splits + s) * D + d];
+  }
+  const float v = acc / L;
+  if constexpr (BF16)
+    static_cast<uint16_t *>(out)[row * D + d] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+  else
+    static_cast<float *>(out)[row * D + d] = v;
+  if (lse != nullptr && d == 0) lse[row] = M + __logf(L);
+}
+
+}  // namespace
+
+int decode_auto_splits(const Geom &g, int num_seqs, int topk) {
+  const int units = num_seqs * g.Hkv;
+  int s = (2048 + units - 1) / units;
+  s = s < 1 ? 1 : (s > topk ? topk : s);
+  const int per = (topk + s - 1) / s;
+  return (topk + per - 1) / per;
+}
+
+size_t decode_workspace_bytes(const Geom &g, int num_seqs, int num_splits) {
+  const size_t parts = static_cast<size_t>(num_seqs) * g.Hq * num_splits;
+  const size_t o_bytes = (parts * g.D * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  return o_bytes + ((parts * sizeof(float) + 255) & ~static_cast<size_t>(255));
+}
+
+hipError_t launch_attn_decode(const Geom &g, const msa_cache_t &c, const void *q,
+                              const int32_t *ids, int topk, float scale, int num_splits,
+                              void *workspace, void *out, float *lse, hipStream_t st) {
+  if (c.num_seqs == 0) return hipSuccess;
+  if (!g.bf16)
+    return launch_attn_f32(g, c, nullptr, c.num_seqs, q, ids, topk, scale, out, lse, st);
+  const int per = (topk + num_splits - 1) / num_splits;
+  const size_t parts = static_cast<size_t>(c.num_seqs) * g.Hq * num_splits;
+  float *o_part = static_cast<float *>(workspace);
+  float *lse_part = reinterpret_cast<float *>(
+      static_cast<char *>(workspace) +
+      ((parts * g.D * sizeof(float) + 255) & ~static_cast<size_t>(255)));
+  const dim3 grid(c.num_seqs * g.Hkv, num_splits);
+  const uint16_t *qb = static_cast<const uint16_t *>(q);
+  const uint16_t *kb = static_cast<const uint16_t *>(c.k_cache);
+  const uint16_t *vb = static_cast<const uint16_t *>(c.v_cache);
+  const float sl2 = scale * kLog2e;
+  if (g.D == 64) {
+    attn_decode_bf16_kernel<64><<<grid, kDecThreads, 0, st>>>(
+        qb, kb, vb, c.block_table, c.seq_lens, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
+        g.nsel, num_splits, per, sl2, o_part, lse_part);
+    combine_kernel<64, true><<<c.num_seqs * g.Hq, 64, 0, st>>>(o_part, lse_part, num_splits,
+                                                                out, lse);
+  } else {
+    attn_decode_bf16_kernel<128><<<grid, kDecThreads, 0, st>>>(
+        qb, kb, vb, c.block_table, c.seq_lens, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
+        g.nsel, num_splits, per, sl2, o_part, lse_part);
+    combine_kernel<128, true><<<c.num_seqs * g.Hq, 128, 0, st>>>(o_part, lse_part,
+                                                                  num_splits, out, lse);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,244 @@
+// C-ABI entry points of libmsa: host-side validation, then kernel launches.
+// Every check here runs before anything is enqueued; see msa.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "msa.h"
+#include "msa_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+msa_status_t fail(msa_status_t st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+msa_status_t ok() {
+  g_last_error.clear();
+  return MSA_OK;
+}
+
+msa_status_t hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MSA_REQUIRE(cond, st, ...) \
+  do {                             \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+// Geometry checks shared by every call. Fills `out` on success.
+msa_status_t check_geom(const msa_geom_t *g, msa::Geom *out) {
+  MSA_REQUIRE(g != nullptr, MSA_ERR_INVALID_ARG, "geom is NULL");
+  MSA_REQUIRE(g->num_q_heads > 0 && g->num_kv_heads > 0 && g->head_dim > 0 &&
+                  g->num_idx_heads > 0 && g->idx_head_dim > 0 && g->num_sel_groups > 0,
+              MSA_ERR_INVALID_ARG, "geometry sizes must be positive");
+  MSA_REQUIRE(g->num_q_heads % g->num_kv_heads == 0, MSA_ERR_INVALID_ARG,
+              "num_q_heads (%d) is not a multiple of num_kv_heads (%d)", g->num_q_heads,
+              g->num_kv_heads);
+  MSA_REQUIRE(g->num_sel_groups == 1 || g->num_sel_groups == g->num_kv_heads,
+              MSA_ERR_INVALID_ARG, "num_sel_groups (%d) must be 1 or num_kv_heads (%d)",
+              g->num_sel_groups, g->num_kv_heads);
+  MSA_REQUIRE(g->num_idx_heads % g->num_sel_groups == 0, MSA_ERR_INVALID_ARG,
+              "num_idx_heads (%d) is not a multiple of num_sel_groups (%d)",
+              g->num_idx_heads, g->num_sel_groups);
+  MSA_REQUIRE(g->block_size == MSA_BLOCK_SIZE, MSA_ERR_UNSUPPORTED,
+              "block_size %d unsupported (only 128)", g->block_size);
+  MSA_REQUIRE(g->dtype == MSA_F32 || g->dtype == MSA_BF16, MSA_ERR_UNSUPPORTED,
+              "dtype %d unsupported", g->dtype);
+  MSA_REQUIRE(g->head_dim == 64 || g->head_dim == 128, MSA_ERR_UNSUPPORTED,
+              "head_dim %d unsupported (64 or 128)", g->head_dim);
+  MSA_REQUIRE(g->idx_head_dim == 32 || g->idx_head_dim == 64, MSA_ERR_UNSUPPORTED,
+              "idx_head_dim %d unsupported (32 or 64)", g->idx_head_dim);
+  const int hs = g->num_idx_heads / g->num_sel_groups;
+  MSA_REQUIRE(hs == 1 || hs == 2 || hs == 4 || hs == 8, MSA_ERR_UNSUPPORTED,
+              "indexer heads per selection group (%d) must be 1, 2, 4 or 8", hs);
+  MSA_REQUIRE(hs * g->idx_head_dim <= 512, MSA_ERR_UNSUPPORTED,
+              "indexer group width %d exceeds 512", hs * g->idx_head_dim);
+  MSA_REQUIRE(g->num_sel_groups <= 16, MSA_ERR_UNSUPPORTED, "more than 16 selection groups");
+  MSA_REQUIRE(g->dtype != MSA_BF16 || g->num_q_heads / g->num_kv_heads <= 16,
+              MSA_ERR_UNSUPPORTED, "bf16 needs at most 16 query heads per KV head");
+  out->Hq = g->num_q_heads;
+  out->Hkv = g->num_kv_heads;
+  out->D = g->head_dim;
+  out->Hi = g->num_idx_heads;
+  out->Di = g->idx_head_dim;
+  out->nsel = g->num_sel_groups;
+  out->bf16 = g->dtype == MSA_BF16;
+  return ok();
+}
+
+msa_status_t check_cache(const msa_cache_t *c, bool need_kv, bool need_kidx) {
+  MSA_REQUIRE(c != nullptr, MSA_ERR_INVALID_ARG, "cache is NULL");
+  MSA_REQUIRE(!need_kv || (c->k_cache != nullptr && c->v_cache != nullptr),
+              MSA_ERR_INVALID_ARG, "k_cache / v_cache is NULL");
+  MSA_REQUIRE(!need_kidx || c->k_idx_cache != nullptr, MSA_ERR_INVALID_ARG,
+              "k_idx_cache is NULL");
+  MSA_REQUIRE(c->block_table != nullptr && c->seq_lens != nullptr, MSA_ERR_INVALID_ARG,
+              "block_table / seq_lens is NULL");
+  MSA_REQUIRE(c->num_phys_blocks > 0 && c->max_blocks_per_seq > 0 && c->num_seqs > 0,
+              MSA_ERR_INVALID_ARG, "cache sizes must be positive");
+  return ok();
+}
+
+msa_status_t check_batch(const msa_batch_t *b) {
+  MSA_REQUIRE(b != nullptr, MSA_ERR_INVALID_ARG, "batch is NULL");
+  MSA_REQUIRE(b->total_units >= 0 && b->total_q >= 0, MSA_ERR_INVALID_ARG,
+              "batch sizes must be non-negative");
+  MSA_REQUIRE(b->total_units == 0 || b->units != nullptr, MSA_ERR_INVALID_ARG,
+              "batch units is NULL");
+  return ok();
+}
+
+float resolve_scale(float s, int D) { return s > 0.f ? s : 1.0f / std::sqrt(float(D)); }
+
+}  // namespace
+
+extern "C" {
+
+msa_status_t msa_prefill_plan(const int32_t *h_seq_lens, const int32_t *h_q_lens,
+                              int32_t num_seqs, msa_unit_t *h_units, int32_t capacity,
+                              int32_t *h_num_units) {
+  MSA_REQUIRE(h_seq_lens != nullptr && h_q_lens != nullptr && h_num_units != nullptr,
+              MSA_ERR_INVALID_ARG, "plan: NULL argument");
+  MSA_REQUIRE(num_seqs > 0, MSA_ERR_INVALID_ARG, "plan: num_seqs must be positive");
+  int64_t count = 0;
+  for (int r = 0; r < num_seqs; ++r) {
+    const int L = h_seq_lens[r], n = h_q_lens[r];
+    MSA_REQUIRE(L > 0 && n >= 0 && n <= L, MSA_ERR_INVALID_ARG,
+                "plan: request %d has seq_len %d and q_len %d", r, L, n);
+    if (n > 0) count += (L - 1) / MSA_BLOCK_SIZE - (L - n) / MSA_BLOCK_SIZE + 1;
+  }
+  MSA_REQUIRE(count <= 2147483647, MSA_ERR_INVALID_ARG, "plan: too many units");
+  if (h_units != nullptr) {
+    MSA_REQUIRE(capacity >= count, MSA_ERR_INVALID_ARG,
+                "plan: capacity %d < %lld units", capacity, static_cast<long long>(count));
+    int64_t u = 0, row = 0;
+    for (int r = 0; r < num_seqs; ++r) {
+      const int L = h_seq_lens[r], n = h_q_lens[r], first = L - n;
+      for (int p = first; p < L;) {
+        const int tau = p / MSA_BLOCK_SIZE;
+        const int end = (tau + 1) * MSA_BLOCK_SIZE < L ? (tau + 1) * MSA_BLOCK_SIZE : L;
+        h_units[u++] = msa_unit_t{r, tau, static_cast<int32_t>(row + (p - first)), end - p, p};
+        p = end;
+      }
+      row += n;
+    }
+  }
+  *h_num_units = static_cast<int32_t>(count);
+  return ok();
+}
+
+msa_status_t msa_index_scores(const msa_geom_t *geom, const msa_cache_t *cache,
+                              const msa_batch_t *batch, const void *q_idx, float *scores,
+                              void *stream) {
+  msa::Geom g;
+  msa_status_t st = check_geom(geom, &g);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache(cache, false, true)) != MSA_OK) return st;
+  MSA_REQUIRE(q_idx != nullptr && scores != nullptr, MSA_ERR_INVALID_ARG,
+              "q_idx / scores is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (batch == nullptr) return hip_status(msa::launch_index_decode(g, *cache, q_idx, scores, s),
+                                          "index_decode");
+  if ((st = check_batch(batch)) != MSA_OK) return st;
+  return hip_status(msa::launch_index_prefill(g, *cache, *batch, q_idx, scores, s),
+                    "index_prefill");
+}
+
+msa_status_t msa_select_topk_blocks(const float *scores, int32_t num_rows, int32_t row_len,
+                                    int32_t topk, int32_t *ids, void *stream) {
+  MSA_REQUIRE(scores != nullptr && ids != nullptr, MSA_ERR_INVALID_ARG, "scores / ids is NULL");
+  MSA_REQUIRE(num_rows >= 0, MSA_ERR_INVALID_ARG, "num_rows must be non-negative");
+  MSA_REQUIRE(row_len >= 1, MSA_ERR_INVALID_ARG, "row_len must be positive");
+  MSA_REQUIRE(topk >= 1, MSA_ERR_INVALID_ARG, "topk must be positive");
+  return hip_status(msa::launch_topk(scores, num_rows, row_len, topk, ids,
+                                     static_cast<hipStream_t>(stream)),
+                    "select_topk_blocks");
+}
+
+msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *cache,
+                                     const msa_batch_t *batch, const void *q,
+                                     const int32_t *ids, int32_t topk, float softmax_scale,
+                                     void *out, float *lse, void *stream) {
+  msa::Geom g;
+  msa_status_t st = check_geom(geom, &g);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache(cache, true, false)) != MSA_OK) return st;
+  if ((st = check_batch(batch)) != MSA_OK) return st;
+  MSA_REQUIRE(q != nullptr && ids != nullptr && out != nullptr, MSA_ERR_INVALID_ARG,
+              "q / ids / out is NULL");
+  MSA_REQUIRE(topk >= 1, MSA_ERR_INVALID_ARG, "topk must be positive");
+  MSA_REQUIRE(!(softmax_scale != softmax_scale), MSA_ERR_INVALID_ARG, "softmax_scale is NaN");
+  return hip_status(msa::launch_attn_prefill(g, *cache, *batch, q, ids, topk,
+                                             resolve_scale(softmax_scale, g.D), out, lse,
+                                             static_cast<hipStream_t>(stream)),
+                    "sparse_attn_prefill");
+}
+
+size_t msa_decode_workspace_size(const msa_geom_t *geom, int32_t num_seqs, int32_t topk,
+                                 int32_t num_splits) {
+  msa::Geom g;
+  if (check_geom(geom, &g) != MSA_OK || num_seqs <= 0 || topk <= 0) return 0;
+  const int s = num_splits > 0 ? (num_splits < topk ? num_splits : topk)
+                               : msa::decode_auto_splits(g, num_seqs, topk);
+  return msa::decode_workspace_bytes(g, num_seqs, s);
+}
+
+msa_status_t msa_sparse_attn_decode(const msa_geom_t *geom, const msa_cache_t *cache,
+                                    const void *q, const int32_t *ids, int32_t topk,
+                                    float softmax_scale, int32_t num_splits,
+                                    void *workspace, size_t workspace_bytes, void *out,
+                                    float *lse, void *stream) {
+  msa::Geom g;
+  msa_status_t st = check_geom(geom, &g);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache(cache, true, false)) != MSA_OK) return st;
+  MSA_REQUIRE(q != nullptr && ids != nullptr && out != nullptr, MSA_ERR_INVALID_ARG,
+              "q / ids / out is NULL");
+  MSA_REQUIRE(topk >= 1, MSA_ERR_INVALID_ARG, "topk must be positive");
+  MSA_REQUIRE(!(softmax_scale != softmax_scale), MSA_ERR_INVALID_ARG, "softmax_scale is NaN");
+  const int s = num_splits > 0 ? (num_splits < topk ? num_splits : topk)
+                               : msa::decode_auto_splits(g, cache->num_seqs, topk);
+  if (g.bf16) {
+    const size_t need = msa::decode_workspace_bytes(g, cache->num_seqs, s);
+    MSA_REQUIRE(workspace != nullptr, MSA_ERR_INVALID_ARG, "workspace is NULL");
+    MSA_REQUIRE(reinterpret_cast<uintptr_t>(workspace) % 256 == 0, MSA_ERR_INVALID_ARG,
+                "workspace must be 256-byte aligned");
+    MSA_REQUIRE(workspace_bytes >= need, MSA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  }
+  return hip_status(msa::launch_attn_decode(g, *cache, q, ids, topk,
+                                            resolve_scale(softmax_scale, g.D), s, workspace,
+                                            out, lse, static_cast<hipStream_t>(stream)),
+                    "sparse_attn_decode");
+}
+
+const char *msa_status_string(msa_status_t status) {
+  switch (status) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+    case MSA_ERR_WORKSPACE_TOO_SMALL: return "MSA_ERR_WORKSPACE_TOO_SMALL";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+const char *msa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t msa_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// Block top-k selection (step 2 of MSA).
+//
+// [feat] models.inteligile.com "MiniMax-M3", table "Checked in its code", row
+// "Indexer-selected sparse attention": topk = min(topk_blocks, num_key_blocks) and
+// selections whose score is -inf become -1. Method list "Exp-free TopK kernel":
+// raw scores are ranked directly, no softmax.
+//
+// One work-group per row. Scores are mapped to order-preserving uint32 keys and
+// the K-th largest key is found exactly by a 4-pass radix select (8 bits per
+// pass, LDS histograms with integer atomics, so the result does not depend on
+// thread timing). The kept entries (key above the threshold, plus the lowest
+// indices among those equal to it) are then written in ascending index order by
+// two block-wide prefix scans. Entries equal to -inf are never kept.
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+namespace {
+
+constexpr int kTopkThreads = 512;
+
+// -0.0 and +0.0 are the same score (ties go to the lower index), so both map to
+// the key of +0.0.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = (f == 0.f) ? 0u : __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+constexpr uint32_t kNegInfKey = 0x007fffffu;   // order_key(-inf)
+
+// Exclusive prefix sum over the work-group; also returns the total.
+__device__ int block_exclusive_scan(int v, int *tmp, int &total) {
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) tmp[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < kTopkThreads / kWave; ++w) {
+    const int s = tmp[w];
+    base += (w < wave) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return base + x - v;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
+    const float *__restrict__ scores, int row_len, int topk, int32_t *__restrict__ ids) {
+  __shared__ int hist[256];
+  __shared__ int sfx[256];
+  __shared__ int tmp[kTopkThreads / kWave];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_remaining;
+
+  const int t = threadIdx.x;
+  const float *row = scores + static_cast<size_t>(blockIdx.x) * row_len;
+  int32_t *out = ids + static_cast<size_t>(blockIdx.x) * topk;
+
+  // number of kept entries K = min(topk, #(score > -inf))
+  int nvalid = 0;
+  for (int i = t; i < row_len; i += kTopkThreads) nvalid += order_key(row[i]) > kNegInfKey;
+  int total;
+  (void)block_exclusive_scan(nvalid, tmp, total);
+  const int K = min(topk, total);
+
+  uint32_t prefix = 0, mask = 0;
+  int remaining = K;   // how many still to take at or below the current prefix
+  if (K > 0) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (t < 256) hist[t] = 0;
+      __syncthreads();
+      for (int i = t; i < row_len; i += kTopkThreads) {
+        const uint32_t k = order_key(row[i]);
+        if (k > kNegInfKey && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      // suffix sums: sfx[d] = #entries in bins >= d
+      if (t < 256) sfx[t] = hist[t];
+      __syncthreads();
+      for (int o = 1; o < 256; o <<= 1) {
+        int v = 0;
+        if (t < 256 && t + o < 256) v = sfx[t + o];
+        __syncthreads();
+        if (t < 256) sfx[t] += v;
+        __syncthreads();
+      }
+      if (t < 256) {
+        const int above = (t < 255) ? sfx[t + 1] : 0;
+        if (above < remaining && remaining <= sfx[t]) {
+          s_prefix = prefix | (static_cast<uint32_t>(t) << shift);
+          s_remaining = remaining - above;
+        }
+      }
+      __syncthreads();
+      prefix = s_prefix;
+      remaining = s_remaining;
+      mask |= 255u << shift;
+      __syncthreads();
+    }
+  }
+  // prefix is now the exact key of the K-th largest entry; `remaining` entries
+  // equal to it are taken, lowest index first.
+  const uint32_t thr = prefix;
+  const int chunk = (row_len + kTopkThreads - 1) / kTopkThreads;
+  const int i0 = min(row_len, t * chunk), i1 = min(row_len, i0 + chunk);
+  int n_eq = 0;
+  if (K > 0)
+    for (int i = i0; i < i1; ++i) n_eq += order_key(row[i]) == thr;
+  const int eq_before = block_exclusive_scan(n_eq, tmp, total);
+  int n_sel = 0;
+  if (K > 0) {
+    int e = eq_before;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t k = order_key(row[i]);
+      if (k > thr) ++n_sel;
+      else if (k == thr) { n_sel += e < remaining; ++e; }
+    }
+  }
+  int pos = block_exclusive_scan(n_sel, tmp, total);
+  if (K > 0) {
+    int e = eq_before;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t k = order_key(row[i]);
+      bool take = false;
+      if (k > thr) take = true;
+      else if (k == thr) { take = e < remaining; ++e; }
+      if (take) out[pos++] = i;
+    }
+  }
+  for (int i = K + t; i < topk; i += kTopkThreads) out[i] = -1;
+}
+
+}  // namespace
+
+hipError_t launch_topk(const float *scores, int rows, int row_len, int topk, int32_t *ids,
+                       hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  topk_rows_kernel<<<rows, kTopkThreads, 0, st>>>(scores, row_len, topk, ids);
+  return hipGetLastError();
+}
+
+}  // namespace msa

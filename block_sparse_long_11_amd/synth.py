@@ -1,0 +1,264 @@
+"""Seeded synthetic inputs for the MSA path: queries, indexer queries, the
+block-major K/V/indexer-key caches, block tables and sequence lengths.
+
+This module draws random numbers and lays them out. It holds none of the
+method's arithmetic (no scoring, no selection, no attention), so both the HIP
+path and the CPU oracle can be fed from it.
+
+Workloads (shapes of the long-context prefill and decode settings the MSA pages
+describe: 128-token KV blocks, 64 query heads over 4 KV heads, up to 1M tokens
+of context):
+
+  tiny_prefill_fp32   fp32, 1 x 2048 tokens, 4 q / 1 kv heads, D 64, indexer
+                      1 x 32, top-k 4, 2 planted blocks per group
+  prefill_32k         bf16, 1 x 32768 tokens, 64/4 heads, D 128, indexer 8 x 64,
+                      top-k 16, 8 planted blocks per 32-block span
+  decode_128k_b64     bf16, 64 sequences x 131072 cached tokens, 1 query each,
+                      top-k 33 (32 + diagonal), 32 planted blocks per sequence
+  decode_1m_b8        bf16, 8 sequences x 1048576 cached tokens, top-k 64,
+                      63 planted blocks per sequence
+  chunked_prefill     bf16, 4 requests, each an 8192-token chunk after cached
+                      prefixes of 1M / 512k / 128k / 32k tokens, top-k 64,
+                      8 planted blocks per 32-block span
+
+Planting ("relevant blocks"): for every (sequence, selection group g) a seeded
+unit direction u_h is drawn per indexer head h of the group; a * u_h is added to
+that head's indexer query of every query token of the sequence and to that head's
+indexer key of every token of each planted block. The mean lift of a planted
+pair's group score is then H_s * a^2; a is chosen so that this equals twice the
+standard deviation sqrt(H_s * D_i) of an unplanted pair score. Values are drawn
+N(0,1) in fp32, planted, then rounded once to the storage dtype.
+"""
+
+import dataclasses
+import math
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+BLOCK = 128
+
+# stream ids of the seeded draws
+_T_Q, _T_K, _T_V, _T_QIDX, _T_KIDX, _T_PLANT_POS, _T_PLANT_DIR, _T_PERM = range(8)
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    dtype: str                      # "f32" or "bf16"
+    seq_lens: List[int]             # cached tokens per request, new ones included
+    q_lens: Optional[List[int]]     # new query tokens per request; None = decode
+    num_q_heads: int = 64
+    num_kv_heads: int = 4
+    head_dim: int = 128
+    num_idx_heads: int = 8
+    idx_head_dim: int = 64
+    num_sel_groups: int = 4
+    topk: int = 16
+    plant_count: int = 8            # planted blocks per span per (seq, group)
+    plant_span: Optional[int] = 32  # span in blocks; None = whole context
+    seed: int = 0
+
+    @property
+    def is_decode(self):
+        return self.q_lens is None
+
+    @property
+    def num_seqs(self):
+        return len(self.seq_lens)
+
+    def blocks(self, r):
+        return (self.seq_lens[r] + BLOCK - 1) // BLOCK
+
+    @property
+    def max_blocks(self):
+        return max(self.blocks(r) for r in range(self.num_seqs))
+
+    @property
+    def num_phys_blocks(self):
+        return sum(self.blocks(r) for r in range(self.num_seqs))
+
+    @property
+    def total_q(self):
+        return self.num_seqs if self.is_decode else sum(self.q_lens)
+
+    def replace(self, **kw):
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny_prefill_fp32": Workload(
+        "tiny_prefill_fp32", "f32", [2048], [2048], num_q_heads=4, num_kv_heads=1,
+        head_dim=64, num_idx_heads=1, idx_head_dim=32, num_sel_groups=1, topk=4,
+        plant_count=2, plant_span=None, seed=1001),
+    "prefill_32k": Workload(
+        "prefill_32k", "bf16", [32768], [32768], topk=16, plant_count=8,
+        plant_span=32, seed=1002),
+    "decode_128k_b64": Workload(
+        "decode_128k_b64", "bf16", [131072] * 64, None, topk=33, plant_count=32,
+        plant_span=None, seed=1003),
+    "decode_1m_b8": Workload(
+        "decode_1m_b8", "bf16", [1048576] * 8, None, topk=64, plant_count=63,
+        plant_span=None, seed=1004),
+    "chunked_prefill": Workload(
+        "chunked_prefill", "bf16",
+        [1048576 + 8192, 524288 + 8192, 131072 + 8192, 32768 + 8192], [8192] * 4,
+        topk=64, plant_count=8, plant_span=32, seed=1005),
+}
+
+
+def plant_amplitude(w: Workload) -> float:
+    """a with H_s * a^2 = 2 * sqrt(H_s * D_i)."""
+    hs = w.num_idx_heads // w.num_sel_groups
+    return math.sqrt(2.0 * math.sqrt(w.idx_head_dim / hs))
+
+
+def _np_rng(w, *stream):
+    return np.random.default_rng([w.seed, *stream])
+
+
+def planted_blocks(w: Workload, r: int, g: int) -> np.ndarray:
+    """Logical ids of the planted blocks of (sequence r, group g), sorted.
+
+    Blocks are drawn uniformly without replacement within each span of
+    plant_span blocks (or over the whole context). In decode the last block,
+    which holds the query, is never a candidate and is not planted."""
+    nb = w.blocks(r)
+    limit = nb - 1 if w.is_decode else nb
+    rng = _np_rng(w, _T_PLANT_POS, r, g)
+    span = w.plant_span or limit
+    out = []
+    for s0 in range(0, limit, span):
+        n = min(span, limit - s0)
+        c = min(w.plant_count, n)
+        out.extend((s0 + rng.choice(n, size=c, replace=False)).tolist())
+    return np.array(sorted(out), dtype=np.int64)
+
+
+def plant_directions(w: Workload, r: int, g: int) -> np.ndarray:
+    """Unit directions [H_s][D_i] (float32) of (sequence r, group g)."""
+    hs = w.num_idx_heads // w.num_sel_groups
+    d = _np_rng(w, _T_PLANT_DIR, r, g).standard_normal((hs, w.idx_head_dim))
+    d /= np.linalg.norm(d, axis=1, keepdims=True)
+    return d.astype(np.float32)
+
+
+def physical_permutation(w: Workload, permute=False) -> np.ndarray:
+    """perm[i] = physical block holding the i-th block of the packed order
+    (request 0's blocks, then request 1's, ...). Identity unless permute."""
+    P = w.num_phys_blocks
+    return _np_rng(w, _T_PERM).permutation(P) if permute else np.arange(P)
+
+
+def block_table(w: Workload, permute=False) -> np.ndarray:
+    """int32 [B][max_blocks]: request r's logical block b -> physical block.
+
+    The packed order lays the requests' blocks one after another; permute=True
+    scatters them with a seeded permutation of the physical blocks (the logical
+    content is the same either way). Entries past a request's last block point at
+    physical block 0 and are never read."""
+    perm = physical_permutation(w, permute)
+    bt = np.zeros((w.num_seqs, w.max_blocks), dtype=np.int32)
+    base = 0
+    for r in range(w.num_seqs):
+        nb = w.blocks(r)
+        bt[r, :nb] = perm[base:base + nb]
+        base += nb
+    return bt
+
+
+def _torch_dtype(w):
+    return torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+
+def _randn(gen, shape, device):
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+
+
+def _gen(w, stream, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(w.seed) * 1000 + stream)
+    return g
+
+
+def make_inputs(w: Workload, device="cpu", permute=False, chunk_blocks=2048):
+    """All inputs of a workload as torch tensors on `device`.
+
+    Returns a dict with q [T][H_q][D], q_idx [T][H_i][D_i], k_cache and v_cache
+    [P][H_kv][128][D], k_idx_cache [P][H_i][128][D_i] (all in the workload dtype),
+    block_table int32 [B][max_blocks], seq_lens int32 [B], q_lens int32 [B]
+    (decode: ones) and cu_q_lens int32 [B+1]. The caches are drawn chunk by chunk
+    of physical blocks so that only one fp32 chunk is alive at a time."""
+    dt = _torch_dtype(w)
+    B, P = w.num_seqs, w.num_phys_blocks
+    T = w.total_q
+    H_q, H_kv, D = w.num_q_heads, w.num_kv_heads, w.head_dim
+    H_i, D_i, n_sel = w.num_idx_heads, w.idx_head_dim, w.num_sel_groups
+    hs = H_i // n_sel
+    a = plant_amplitude(w)
+    bt = block_table(w, permute)
+    perm = physical_permutation(w, permute)
+    q_lens = [1] * B if w.is_decode else list(w.q_lens)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+
+    # packed block index of (request, logical block): base[r] + b
+    base = np.concatenate([[0], np.cumsum([w.blocks(r) for r in range(B)])]).astype(np.int64)
+    plants = {}            # (r, g) -> (planted logical ids, directions)
+    for r in range(B):
+        for g in range(n_sel):
+            plants[(r, g)] = (planted_blocks(w, r, g), plant_directions(w, r, g))
+
+    out = {}
+    out["q"] = _randn(_gen(w, _T_Q, device), (T, H_q, D), device).to(dt)
+
+    qi = _randn(_gen(w, _T_QIDX, device), (T, H_i, D_i), device)
+    for r in range(B):
+        for g in range(n_sel):
+            u = torch.from_numpy(plants[(r, g)][1]).to(device)
+            qi[cu[r]:cu[r + 1], g * hs:(g + 1) * hs, :] += a * u
+    out["q_idx"] = qi.to(dt)
+
+    def cache(stream, heads, dim, plant):
+        # drawn in packed order, chunk by chunk, then scattered to physical blocks
+        gen = _gen(w, stream, device)
+        res = torch.empty((P, heads, BLOCK, dim), dtype=dt, device=device)
+        for c0 in range(0, P, chunk_blocks):
+            c1 = min(P, c0 + chunk_blocks)
+            x = _randn(gen, (c1 - c0, heads, BLOCK, dim), device)
+            if plant:
+                for (r, g), (ids, u) in plants.items():
+                    packed = base[r] + ids
+                    sel = packed[(packed >= c0) & (packed < c1)] - c0
+                    if len(sel):
+                        idx = torch.from_numpy(sel).to(device)
+                        ut = torch.from_numpy(u).to(device)[None, :, None, :]
+                        x[idx, g * hs:(g + 1) * hs] += a * ut
+            dst = torch.from_numpy(perm[c0:c1]).to(device)
+            res[dst] = x.to(dt)
+            del x
+        return res
+
+    out["k_cache"] = cache(_T_K, H_kv, D, False)
+    out["v_cache"] = cache(_T_V, H_kv, D, False)
+    out["k_idx_cache"] = cache(_T_KIDX, H_i, D_i, True)
+    out["block_table"] = torch.from_numpy(bt).to(device)
+    out["seq_lens"] = torch.tensor(w.seq_lens, dtype=torch.int32, device=device)
+    out["q_lens"] = torch.tensor(q_lens, dtype=torch.int32, device=device)
+    out["cu_q_lens"] = torch.from_numpy(cu).to(device)
+    return out
+
+
+def to_host_f32(t: torch.Tensor) -> np.ndarray:
+    """Exact float32 NumPy copy of a float32/bf16 tensor (for the CPU side)."""
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def small_workload(dtype="bf16", seq_lens=(700,), q_lens=(300,), **kw) -> Workload:
+    """A small case for parity tests: defaults to a 4 q / 2 kv head layout."""
+    base = dict(num_q_heads=8, num_kv_heads=2, head_dim=128, num_idx_heads=4,
+                idx_head_dim=64, num_sel_groups=2, topk=3, plant_count=2,
+                plant_span=8, seed=7)
+    base.update(kw)
+    return Workload("small", dtype, list(seq_lens),
+                    None if q_lens is None else list(q_lens), **base)

@@ -1,0 +1,199 @@
+/*
+ * msa.h - MiniMax Sparse Attention (MSA) hot path on AMD Instinct MI355X (gfx950).
+ *
+ * MSA splits the KV cache into 128-token blocks, scores every block with a light
+ * indexer for each query tile or GQA query group, keeps the top-k blocks and runs
+ * exact softmax attention over those blocks only. Pages this follows:
+ *   [dd]   daily.dev, "MiniMax M3: 1M-token multimodal reasoning model now available
+ *          with NVIDIA and vLLM support", sections "Summary", "What makes M3
+ *          different" and "Serving options" (128-token KV blocks, top blocks per
+ *          query, prefill/decode kernels for sparse GQA, KV-block-major prefill).
+ *   [feat] models.inteligile.com, "MiniMax-M3" feature page, table "Checked in its
+ *          code", rows "Indexer-selected sparse attention (DeepSeek Sparse
+ *          Attention)", "Grouped-query attention" and "Learnable attention sink";
+ *          method list "Two-phase forward", "LSE fusion", "Exp-free TopK kernel".
+ *   [vllm] 24-ai.news, "MiniMax M3 in vLLM: Day-0-Unterstuetzung ...", section
+ *          "Warum ist ein Million-Token-Kontext eine Serving-Herausforderung?"
+ *          (each query or GQA query group scores all blocks with light indexer
+ *          kernels; KV-block-major layout).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless the name starts with h_ (host memory).
+ *     Arrays are dense, row-major, with the shapes given below, 16-byte aligned.
+ *   - The caller owns every buffer. The library never allocates, frees or
+ *     synchronizes; each call only enqueues kernels on `stream` (a hipStream_t,
+ *     NULL for the default stream) and returns.
+ *   - Arguments are validated on the host before anything is enqueued. On an
+ *     error nothing is enqueued and no output is written; msa_last_error() then
+ *     describes the problem (thread-local string). Launch failures are reported
+ *     as MSA_ERR_HIP. Device-side values (seq_lens, block_table, ids) are not
+ *     checked: out-of-range entries are undefined behaviour.
+ *   - Calls are re-entrant and thread-safe.
+ *
+ * Data layout (block-major paged caches, [dd] "Serving options", [vllm]):
+ *   k_cache, v_cache   [num_phys_blocks][H_kv][128][D]     (dtype)
+ *   k_idx_cache        [num_phys_blocks][H_i][128][D_i]    (dtype)
+ *   block_table        int32 [num_seqs][max_blocks_per_seq], logical -> physical
+ *   seq_lens           int32 [num_seqs], tokens in the cache INCLUDING the new
+ *                      queries (their K/V/k_idx are inserted before these calls)
+ *   Token s of sequence r lives in physical block block_table[r][s / 128], row
+ *   s % 128. Byte offsets are 64-bit.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_BLOCK_SIZE 128
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = 1,          /* null pointer, bad size or inconsistent shape */
+  MSA_ERR_UNSUPPORTED = 2,          /* valid but not built: dtype, D, D_i, block size */
+  MSA_ERR_WORKSPACE_TOO_SMALL = 3,  /* decode workspace smaller than required */
+  MSA_ERR_HIP = 4                   /* a HIP launch failed */
+} msa_status_t;
+
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype_t;
+
+/* Head geometry ([feat] "Grouped-query attention": 64 query heads share 4 KV heads;
+ * query head i reads KV head i / (num_q_heads / num_kv_heads)).
+ *   num_q_heads % num_kv_heads == 0, (num_q_heads / num_kv_heads) <= 16 for bf16
+ *   head_dim in {64, 128}; idx_head_dim in {32, 64}
+ *   num_sel_groups is num_kv_heads (group g sums indexer heads
+ *     [g*H_s, (g+1)*H_s), H_s = num_idx_heads / num_sel_groups, and selects the
+ *     blocks of KV head g) or 1 (the sum over all indexer heads selects for every
+ *     KV head); num_idx_heads % num_sel_groups == 0, H_s * idx_head_dim <= 512
+ *   block_size must be 128.
+ *   dtype applies to q, q_idx, the three caches and out. */
+typedef struct {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t num_idx_heads;
+  int32_t idx_head_dim;
+  int32_t num_sel_groups;
+  int32_t block_size;
+  int32_t dtype;                    /* msa_dtype_t */
+} msa_geom_t;
+
+typedef struct {
+  const void *k_cache;
+  const void *v_cache;
+  const void *k_idx_cache;
+  int64_t num_phys_blocks;
+  const int32_t *block_table;       /* [num_seqs][max_blocks_per_seq] */
+  int32_t max_blocks_per_seq;
+  const int32_t *seq_lens;          /* [num_seqs] */
+  int32_t num_seqs;
+} msa_cache_t;
+
+/* One prefill unit: the new queries of request r whose positions fall in the
+ * 128-token block tau (its diagonal block). Rows [row0, row0 + num_rows) of q and
+ * q_idx, positions [pos0, pos0 + num_rows). Built by msa_prefill_plan. */
+typedef struct {
+  int32_t r, tau, row0, num_rows, pos0;
+} msa_unit_t;
+
+/* A (chunked) prefill batch. Request r's q_lens[r] new queries are the last
+ * q_lens[r] tokens of its cache, stored in q/q_idx after those of requests
+ * 0..r-1 (total_q rows in all). units is the DEVICE copy of the plan. */
+typedef struct {
+  const msa_unit_t *units;          /* [total_units], device */
+  int32_t total_units;
+  int32_t total_q;
+} msa_batch_t;
+
+/* Host-side plan of a prefill batch: splits each request's new queries at
+ * 128-position boundaries ([dd]: 128-token blocks; the first unit of a chunk that
+ * starts mid-block is partial). With h_units == NULL only *h_num_units is set.
+ * Otherwise up to `capacity` units are written in request order, tiles ascending.
+ * Needs 0 <= h_q_lens[r] <= h_seq_lens[r]. Pure host code. */
+msa_status_t msa_prefill_plan(const int32_t *h_seq_lens, const int32_t *h_q_lens,
+                              int32_t num_seqs, msa_unit_t *h_units, int32_t capacity,
+                              int32_t *h_num_units);
+
+/* Step 1, indexer block scores ([feat] row "Indexer-selected sparse attention":
+ * a lightning indexer scores keys per head and pools them into blocks; [vllm]:
+ * each query or GQA query group scores every available block).
+ *   q_idx   prefill: [batch->total_q][H_i][D_i]; decode (batch == NULL):
+ *           [num_seqs][H_i][D_i], the one new query of sequence r at position
+ *           seq_lens[r] - 1.
+ *   scores  fp32 [U][num_sel_groups][max_blocks_per_seq], U = total_units
+ *           (prefill) or num_seqs (decode). For unit u with diagonal block tau
+ *           and group g:
+ *             b <  tau : max over the unit's queries t and block b's 128 keys s of
+ *                        sum_{h in g} q_idx[t,h,:] . k_idx[s,h,:] (fp32 accumulate)
+ *             b == tau : +inf (the diagonal block is always kept)
+ *             b >  tau : -inf (causal: future blocks are never kept)
+ * Prefill runs on bf16 MFMA for bf16 inputs; decode streams k_idx once. */
+msa_status_t msa_index_scores(const msa_geom_t *geom, const msa_cache_t *cache,
+                              const msa_batch_t *batch, const void *q_idx,
+                              float *scores, void *stream);
+
+/* Step 2, block top-k ([feat]: topk = min(topk_blocks, num_key_blocks), -inf
+ * selections become -1; [feat] method "Exp-free TopK kernel": raw scores are
+ * ranked, no softmax). Generic over rows:
+ *   scores fp32 [num_rows][row_len]; ids int32 [num_rows][topk].
+ * Per row, the K = min(topk, #entries > -inf) entries of highest score are kept,
+ * equal scores ordered by lower index; their indices are written in ascending
+ * order and the remaining topk - K slots are set to -1. NaN scores are undefined.
+ * Requires 1 <= topk, 1 <= row_len. */
+msa_status_t msa_select_topk_blocks(const float *scores, int32_t num_rows,
+                                    int32_t row_len, int32_t topk, int32_t *ids,
+                                    void *stream);
+
+/* Step 3, sparse prefill attention ([dd] "Serving options": prefill kernel for
+ * sparse GQA; [feat] rows "Grouped-query attention", "Learnable attention sink":
+ * plain softmax, no sink, no output gate).
+ *   q    [total_q][H_q][D];  ids int32 [total_units][num_sel_groups][topk] (the
+ *        output of step 2, ascending, -1 padded)
+ *   out  [total_q][H_q][D] (dtype, rounded to nearest even);
+ *   lse  fp32 [total_q][H_q] natural-log logsumexp of the logits, or NULL.
+ * Query t of unit u, head i (KV head j = i / G, selection group g = j or 0)
+ * attends to every key s of the blocks ids[u][g][*] with s <= pos(t):
+ *   out = softmax(softmax_scale * q . k) . v  (fp32 softmax).
+ * softmax_scale <= 0 selects 1/sqrt(D). bf16 runs on MFMA with fp32 accumulation;
+ * probabilities are rounded to bf16 for the P.V product. */
+msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *cache,
+                                     const msa_batch_t *batch, const void *q,
+                                     const int32_t *ids, int32_t topk,
+                                     float softmax_scale, void *out, float *lse,
+                                     void *stream);
+
+/* Bytes of device workspace msa_sparse_attn_decode needs. num_splits <= 0 picks
+ * the library's own split count for this shape (the same one the decode call
+ * picks for num_splits <= 0). */
+size_t msa_decode_workspace_size(const msa_geom_t *geom, int32_t num_seqs,
+                                 int32_t topk, int32_t num_splits);
+
+/* Steps 3+4 for decode, split-KV with a log-sum-exp combine ([dd] "Serving
+ * options": decode kernel for sparse GQA; [feat] methods "Two-phase forward" and
+ * "LSE fusion").
+ *   q   [num_seqs][H_q][D], the new query of sequence r at position seq_lens[r]-1
+ *   ids int32 [num_seqs][num_sel_groups][topk]
+ *   workspace >= msa_decode_workspace_size(...) bytes, device, 256-byte aligned
+ *   out [num_seqs][H_q][D] (dtype); lse fp32 [num_seqs][H_q] or NULL.
+ * The selected slots are split into num_splits parts (<= 0: automatic), each
+ * part is attended separately and the parts are merged by their logsumexp; the
+ * result equals one softmax over all selected keys up to fp32 rounding. */
+msa_status_t msa_sparse_attn_decode(const msa_geom_t *geom, const msa_cache_t *cache,
+                                    const void *q, const int32_t *ids, int32_t topk,
+                                    float softmax_scale, int32_t num_splits,
+                                    void *workspace, size_t workspace_bytes, void *out,
+                                    float *lse, void *stream);
+
+const char *msa_status_string(msa_status_t status);
+const char *msa_last_error(void);
+int32_t msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

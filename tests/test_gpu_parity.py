@@ -1,0 +1,293 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on MI355X.
+
+Small cases are compared in full; the full-size workloads are compared on a
+seeded sample of units (units are independent, so the oracle computes each
+sampled unit alone from the same inputs)."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_11_amd as msa
+from block_sparse_long_11_amd import synth
+from oracle import msa_oracle as O
+import parity as P
+
+pytestmark = pytest.mark.gpu
+BLK = 128
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def geometry(w):
+    return msa.Geometry(w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_idx_heads,
+                        w.idx_head_dim, w.num_sel_groups, w.dtype)
+
+
+def setup(w, dev, permute=False):
+    inp = synth.make_inputs(w, dev, permute=permute)
+    cache = msa.Cache(inp["k_cache"], inp["v_cache"], inp["k_idx_cache"],
+                      inp["block_table"], inp["seq_lens"])
+    return inp, geometry(w), cache
+
+
+def run_gpu(w, inp, geom, cache, dev, num_splits=0):
+    if w.is_decode:
+        res = msa.decode(geom, cache, inp["q"], inp["q_idx"], w.topk, num_splits)
+    else:
+        batch = msa.make_batch(w.seq_lens, w.q_lens, dev)
+        res = msa.prefill(geom, cache, batch, inp["q"], inp["q_idx"], w.topk)
+    torch.cuda.synchronize()
+    return {k: v.cpu() for k, v in res.items()}
+
+
+def host(t):
+    return synth.to_host_f32(t)
+
+
+def full_parity(w, inp, res, where):
+    q, qi = host(inp["q"]), host(inp["q_idx"])
+    kc, vc, ki = host(inp["k_cache"]), host(inp["v_cache"]), host(inp["k_idx_cache"])
+    bt = inp["block_table"].cpu().numpy()
+    units = O.decode_units(w.seq_lens) if w.is_decode else O.prefill_units(w.seq_lens, w.q_lens)
+    ref = O.index_scores(units, qi, ki, bt, w.num_sel_groups, bt.shape[1])
+    tol = P.score_tolerance(qi, ki, w.num_sel_groups)
+    P.check_scores(res["scores"].numpy(), ref, tol, where)
+    ids = res["ids"].numpy()
+    P.check_ids(ids, ref, units, w.topk, where)
+    out, lse = O.attention(units, ids, q, kc, vc, bt, w.seq_lens, w.num_sel_groups)
+    return P.check_attention(host(res["out"]), res["lse"].numpy(), out, lse, w.dtype, where)
+
+
+SMALL_PREFILL = {
+    "one_request": dict(seq_lens=(700,), q_lens=(300,)),
+    "ragged_permuted": dict(seq_lens=(1000, 260, 129, 5), q_lens=(1000, 200, 1, 5), topk=4,
+                            permute=True),
+    "one_selection_group": dict(seq_lens=(900,), q_lens=(650,), num_sel_groups=1),
+    "g16_d64_di32": dict(seq_lens=(1300,), q_lens=(700,), num_q_heads=16, num_kv_heads=1,
+                         head_dim=64, num_idx_heads=2, idx_head_dim=32, num_sel_groups=1),
+    "mha_g1": dict(seq_lens=(600,), q_lens=(600,), num_q_heads=4, num_kv_heads=4,
+                   num_idx_heads=4, num_sel_groups=4),
+    "topk_covers_all": dict(seq_lens=(1000,), q_lens=(1000,), topk=16),
+    "topk_one": dict(seq_lens=(1000,), q_lens=(500,), topk=1),
+    "m3_heads": dict(seq_lens=(1100,), q_lens=(600,), num_q_heads=64, num_kv_heads=4,
+                     num_idx_heads=8, num_sel_groups=4, topk=5),
+    "m3_heads_one_group": dict(seq_lens=(1500, 300), q_lens=(400, 300), num_q_heads=64,
+                               num_kv_heads=4, num_idx_heads=8, num_sel_groups=1, topk=6),
+    "f32_ragged": dict(dtype="f32", seq_lens=(700, 300), q_lens=(300, 300), num_q_heads=4,
+                       num_kv_heads=1, head_dim=64, num_idx_heads=2, idx_head_dim=32,
+                       num_sel_groups=1),
+    "f32_d128": dict(dtype="f32", seq_lens=(520,), q_lens=(400,)),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_PREFILL))
+def test_small_prefill_parity(name, gpu_device):
+    kw = dict(SMALL_PREFILL[name])
+    permute = kw.pop("permute", False)
+    w = synth.small_workload(**kw)
+    say(f"prefill {name}")
+    inp, geom, cache = setup(w, gpu_device, permute)
+    res = run_gpu(w, inp, geom, cache, gpu_device)
+    full_parity(w, inp, res, name)
+
+
+SMALL_DECODE = {
+    "mixed_lengths": dict(seq_lens=(700, 1000, 129, 5, 128, 1024, 4000), topk=4),
+    "m3_heads": dict(seq_lens=(20000, 3000, 131, 9000), num_q_heads=64, num_kv_heads=4,
+                     num_idx_heads=8, num_sel_groups=4, topk=9),
+    "one_selection_group_g16_d64": dict(seq_lens=(5000, 777), num_q_heads=16, num_kv_heads=1,
+                                        head_dim=64, num_idx_heads=4, idx_head_dim=32,
+                                        num_sel_groups=1, topk=7),
+    "topk_covers_all": dict(seq_lens=(900, 300), topk=12),
+    "f32": dict(dtype="f32", seq_lens=(3000, 700), num_q_heads=4, num_kv_heads=1,
+                head_dim=64, num_idx_heads=1, idx_head_dim=32, num_sel_groups=1, topk=4),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_DECODE))
+def test_small_decode_parity(name, gpu_device):
+    w = synth.small_workload(q_lens=None, **SMALL_DECODE[name])
+    say(f"decode {name}")
+    inp, geom, cache = setup(w, gpu_device, permute=True)
+    res = run_gpu(w, inp, geom, cache, gpu_device)
+    full_parity(w, inp, res, name)
+
+
+def test_decode_split_counts_agree(gpu_device):
+    w = synth.small_workload(q_lens=None, seq_lens=(20000, 3000, 131, 9000), num_q_heads=64,
+                             num_kv_heads=4, num_idx_heads=8, num_sel_groups=4, topk=9)
+    inp, geom, cache = setup(w, gpu_device)
+    outs = {}
+    for s in (1, 2, 7, 0, 9):
+        say(f"decode splits={s}")
+        outs[s] = run_gpu(w, inp, geom, cache, gpu_device, num_splits=s)
+    for s in (2, 7, 0, 9):
+        assert torch.equal(outs[s]["ids"], outs[1]["ids"])
+        d = (outs[s]["out"].float() - outs[1]["out"].float()).abs().max().item()
+        assert d <= 2 * 2.0 ** -8, f"splits={s}: {d}"       # two bf16 roundings apart at most
+        assert (outs[s]["lse"] - outs[1]["lse"]).abs().max().item() < 1e-5
+
+
+def test_tiny_prefill_fp32_workload(gpu_device):
+    w = synth.WORKLOADS["tiny_prefill_fp32"]
+    say("tiny_prefill_fp32")
+    inp, geom, cache = setup(w, gpu_device)
+    res = run_gpu(w, inp, geom, cache, gpu_device)
+    full_parity(w, inp, res, w.name)
+
+
+def test_determinism_and_layout_invariance(gpu_device):
+    """Two runs are bit-identical; a permuted physical layout is bit-identical."""
+    for kw in (dict(seq_lens=(1500, 700), q_lens=(800, 700), num_q_heads=64, num_kv_heads=4,
+                    num_idx_heads=8, num_sel_groups=4, topk=5),
+               dict(seq_lens=(9000, 2000), q_lens=None, num_q_heads=64, num_kv_heads=4,
+                    num_idx_heads=8, num_sel_groups=4, topk=9)):
+        w = synth.small_workload(**kw)
+        say(f"determinism {'decode' if w.is_decode else 'prefill'}")
+        inp, geom, cache = setup(w, gpu_device)
+        a = run_gpu(w, inp, geom, cache, gpu_device)
+        b = run_gpu(w, inp, geom, cache, gpu_device)
+        inp2, geom2, cache2 = setup(w, gpu_device, permute=True)
+        c = run_gpu(w, inp2, geom2, cache2, gpu_device)
+        for k in ("scores", "ids", "out", "lse"):
+            assert torch.equal(a[k], b[k]), k
+            assert torch.equal(a[k], c[k]), k
+
+
+def generic_row_rule(row, topk):
+    valid = [b for b in range(len(row)) if row[b] != -np.inf]
+    key = lambda b: (-(row[b] + 0.0), b)          # -0.0 and +0.0 tie
+    kept = sorted(sorted(valid, key=key)[:topk])
+    return kept + [-1] * (topk - len(kept))
+
+
+def test_topk_rows_exact(gpu_device):
+    rng = np.random.default_rng(5)
+    rows = []
+    rows.append(np.array([3, 1, 3, 2, np.inf, -np.inf, -np.inf], np.float32))
+    rows.append(np.array([-0.0, 0.0, -1e-30, 1e-30, np.inf], np.float32))
+    rows.append(np.full(9, -np.inf, np.float32))                    # nothing to keep
+    for n in (1, 2, 31, 128, 1000, 8256, 20011):
+        r = rng.integers(-4, 5, size=n).astype(np.float32)           # heavy ties
+        r[rng.integers(0, n)] = np.inf
+        r[rng.random(n) < 0.2] = -np.inf
+        rows.append(r)
+        rows.append(rng.standard_normal(n).astype(np.float32) * 1e3)
+        rows.append((rng.standard_normal(n) * 1e-38).astype(np.float32))   # denormals
+    for topk in (1, 4, 33, 64, 300):
+        for r in rows:
+            say(f"topk n={len(r)} k={topk}")
+            s = torch.from_numpy(r).to(gpu_device)[None]
+            ids = torch.empty((1, topk), dtype=torch.int32, device=gpu_device)
+            msa.msa_select_topk_blocks(s, topk, ids)
+            assert ids.cpu().numpy()[0].tolist() == generic_row_rule(r.astype(np.float64), topk)
+
+
+def test_empty_prefill_batch_launches_nothing(gpu_device):
+    w = synth.small_workload(seq_lens=(300, 200), q_lens=(1, 1))
+    inp, geom, cache = setup(w, gpu_device)
+    batch = msa.make_batch([300, 200], [0, 0], gpu_device)
+    assert batch.total_units == 0
+    scores = torch.empty((0, 2, cache.max_blocks), dtype=torch.float32, device=gpu_device)
+    msa.msa_index_scores(geom, cache, batch, inp["q_idx"][:0], scores)
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------
+# full-size workloads, sampled units
+# ----------------------------------------------------------------------------
+
+def _mini_cache(cache_t, bt_row, blocks, heads):
+    """Host float32 copy of the given logical blocks and heads of one request, with
+    a block table mapping those logical ids to rows of the copy."""
+    idx = torch.as_tensor(np.asarray(bt_row)[blocks].astype(np.int64), device=cache_t.device)
+    mini = host(cache_t.index_select(0, idx)[:, heads])
+    bt = np.zeros(max(blocks) + 1, dtype=np.int64)
+    bt[blocks] = np.arange(len(blocks))
+    return mini, bt
+
+
+def sampled_parity(w, inp, res, units, picks, rows_per_unit=16, seed=0):
+    rng = np.random.default_rng(seed)
+    bt_all = inp["block_table"].cpu().numpy()
+    nsel, Hs = w.num_sel_groups, w.num_idx_heads // w.num_sel_groups
+    G = w.num_q_heads // w.num_kv_heads
+    scores, ids = res["scores"].numpy(), res["ids"].numpy()
+    q_all, qi_all = inp["q"], inp["q_idx"]
+    worst = [0.0, 0.0]
+    for u in picks:
+        un = units[u]
+        r, tau = un["r"], un["tau"]
+        say(f"{w.name} unit {u} (r={r}, tau={tau})")
+        rows = slice(un["row0"], un["row1"])
+        for g in range(nsel):
+            heads = slice(g * Hs, (g + 1) * Hs)
+            cand = list(range(tau)) if tau > 0 else [0]
+            ki, btm = _mini_cache(inp["k_idx_cache"], bt_all[r], cand, heads)
+            qi = host(qi_all[rows, heads])
+            ref = O.unit_block_scores(qi, ki, btm, tau, 1, scores.shape[2])
+            tol = P.score_tolerance(qi, ki, 1)
+            P.check_scores(scores[u, g][None, None], ref[None], tol, f"{w.name} u{u} g{g}")
+            ok, _ = P.ids_acceptable(ids[u, g], ref[0], tau, w.topk)
+            assert ok, f"{w.name} u{u} g{g}: ids {ids[u, g]}"
+        # attention on a sample of the unit's rows, every query head
+        n = un["row1"] - un["row0"]
+        pick_rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, rows_per_unit)]))
+        for j in range(w.num_kv_heads):
+            g = j if nsel == w.num_kv_heads else 0
+            kept = [int(b) for b in ids[u, g] if b >= 0]
+            kc, btm = _mini_cache(inp["k_cache"], bt_all[r], kept, slice(j, j + 1))
+            vc, _ = _mini_cache(inp["v_cache"], bt_all[r], kept, slice(j, j + 1))
+            qh = host(q_all[un["row0"]:un["row1"], j * G:(j + 1) * G])
+            for t in pick_rows:
+                o, l = O.unit_attention(qh[t:t + 1], un["pos0"] + t, ids[u, g][None], kc, vc,
+                                        btm, int(w.seq_lens[r]), 1)
+                go = host(res["out"][un["row0"] + t, j * G:(j + 1) * G])[None]
+                gl = res["lse"][un["row0"] + t, j * G:(j + 1) * G].numpy()[None]
+                d = P.check_attention(go, gl, o, l, w.dtype, f"{w.name} u{u} row{t} kv{j}")
+                worst = [max(worst[0], d[0]), max(worst[1], d[1])]
+    return worst
+
+
+def _sample_units(units, n, seed):
+    rng = np.random.default_rng(seed)
+    U = len(units)
+    picks = {0, U - 1} | set(rng.choice(U, size=min(n, U), replace=False).tolist())
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name", ["prefill_32k", "chunked_prefill"])
+def test_full_size_prefill_sampled(name, gpu_device):
+    w = synth.WORKLOADS[name]
+    say(f"{name} generate")
+    inp, geom, cache = setup(w, gpu_device)
+    say(f"{name} run")
+    res = run_gpu(w, inp, geom, cache, gpu_device)
+    units = O.prefill_units(w.seq_lens, w.q_lens)
+    picks = _sample_units(units, 4, 1)
+    # the first and last tile of every request
+    for r in range(w.num_seqs):
+        ur = [i for i, un in enumerate(units) if un["r"] == r]
+        picks += [ur[0], ur[-1]]
+    sampled_parity(w, inp, res, units, sorted(set(picks)), rows_per_unit=8)
+    del inp, cache
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["decode_128k_b64", "decode_1m_b8"])
+def test_full_size_decode_sampled(name, gpu_device):
+    w = synth.WORKLOADS[name]
+    say(f"{name} generate")
+    inp, geom, cache = setup(w, gpu_device)
+    say(f"{name} run")
+    res = run_gpu(w, inp, geom, cache, gpu_device)
+    units = O.decode_units(w.seq_lens)
+    sampled_parity(w, inp, res, units, _sample_units(units, 2, 2), rows_per_unit=1)
+    # every row of scores has the diagonal +inf at the last block and no -inf before it
+    sc = res["scores"].numpy()
+    assert np.isposinf(sc[:, :, -1]).all() and np.isfinite(sc[:, :, :-1]).all()
+    del inp, cache
+    torch.cuda.empty_cache()
