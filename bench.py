@@ -1,0 +1,310 @@
+"""Benchmark of the MSA hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input that is
+already resident in HBM: indexer scores -> block top-k -> sparse attention
+(prefill), or indexer -> top-k -> split-KV decode attention -> combine (decode).
+Default workload: the 32k-token prefill (64 q / 4 kv heads, D 128, indexer 8 x 64,
+top-k 16); the 1M-context decode (8 x 1,048,576 tokens, top-k 64) is measured in
+the same run as a second line item.
+
+Prints ONE JSON line. `value` is selected-KV tokens per second: the sum over
+(query token, KV head) of the selected keys that query can see, per second.
+`roofline` is for the step's dominant kernel, with its average launch duration
+measured by HIP events recorded on the launch stream around every launch in the
+timed region. `cpu_baseline` times the CPU oracle on a bounded sample of units.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_sparse_long_11_amd as msa            # noqa: E402
+from block_sparse_long_11_amd import synth         # noqa: E402
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+BLK = 128
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def geometry(w):
+    return msa.Geometry(w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_idx_heads,
+                        w.idx_head_dim, w.num_sel_groups, w.dtype)
+
+
+# ----------------------------------------------------------------------------
+# work accounting
+# ----------------------------------------------------------------------------
+
+def selected_kv_tokens(w, ids, units):
+    """Sum over (query token, KV head) of visible selected keys."""
+    total = 0
+    nsel = w.num_sel_groups
+    for u, un in enumerate(units):
+        tau, n = un["tau"], un["num_rows"]
+        for j in range(w.num_kv_heads):
+            g = j if nsel == w.num_kv_heads else 0
+            kept = ids[u, g]
+            full = int(np.sum((kept >= 0) & (kept < tau))) * BLK
+            # diagonal: query at pos0 + t sees pos0 + t - 128 tau + 1 keys of it
+            first = un["pos0"] - tau * BLK + 1
+            diag = n * first + n * (n - 1) // 2
+            total += n * full + diag
+    return total
+
+
+def plan_units(w):
+    if w.is_decode:
+        return [dict(r=r, tau=(L - 1) // BLK, pos0=L - 1, num_rows=1)
+                for r, L in enumerate(w.seq_lens)]
+    plan = msa.msa_prefill_plan(w.seq_lens, w.q_lens)
+    return [dict(r=int(p[0]), tau=int(p[1]), row0=int(p[2]), num_rows=int(p[3]),
+                 pos0=int(p[4])) for p in plan]
+
+
+def index_decode_bytes(w):
+    """Indexer keys every non-diagonal block must stream, plus q_idx and scores."""
+    per_block = w.num_idx_heads * BLK * w.idx_head_dim * 2
+    blocks = sum(w.blocks(r) - 1 for r in range(w.num_seqs))
+    q = w.num_seqs * w.num_idx_heads * w.idx_head_dim * 2
+    scores = w.num_seqs * w.num_sel_groups * w.max_blocks * 4
+    return blocks * per_block + q + scores
+
+
+# ----------------------------------------------------------------------------
+# timed runs
+# ----------------------------------------------------------------------------
+
+class Runner:
+    """Holds a workload's resident inputs and outputs and launches one step,
+    recording HIP events around each launch on the current stream."""
+
+    def __init__(self, w, dev):
+        self.w, self.dev = w, dev
+        log(f"{w.name}: generating inputs on {dev}")
+        self.inp = synth.make_inputs(w, dev)
+        self.geom = geometry(w)
+        self.cache = msa.Cache(self.inp["k_cache"], self.inp["v_cache"],
+                               self.inp["k_idx_cache"], self.inp["block_table"],
+                               self.inp["seq_lens"])
+        U = w.num_seqs if w.is_decode else len(msa.msa_prefill_plan(w.seq_lens, w.q_lens))
+        self.batch = None if w.is_decode else msa.make_batch(w.seq_lens, w.q_lens, dev)
+        self.scores = torch.empty((U, w.num_sel_groups, self.cache.max_blocks),
+                                  dtype=torch.float32, device=dev)
+        self.ids = torch.empty((U, w.num_sel_groups, w.topk), dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(self.inp["q"])
+        self.lse = torch.empty(self.inp["q"].shape[:2], dtype=torch.float32, device=dev)
+        if w.is_decode:
+            self.ws = msa.workspace(msa.msa_decode_workspace_size(self.geom, w.num_seqs,
+                                                                  w.topk, 0), dev)
+        self.names = ["index_scores", "select_topk_blocks",
+                      "sparse_attn_decode" if w.is_decode else "sparse_attn_prefill"]
+
+    def step(self, events=None):
+        w, i = self.w, self.inp
+        ev = events or [None] * 4
+        if ev[0] is not None:
+            ev[0].record()
+        msa.msa_index_scores(self.geom, self.cache, self.batch, i["q_idx"], self.scores)
+        if ev[1] is not None:
+            ev[1].record()
+        msa.msa_select_topk_blocks(self.scores, w.topk, self.ids)
+        if ev[2] is not None:
+            ev[2].record()
+        if w.is_decode:
+            msa.msa_sparse_attn_decode(self.geom, self.cache, i["q"], self.ids, w.topk,
+                                       self.out, self.ws, self.lse)
+        else:
+            msa.msa_sparse_attn_prefill(self.geom, self.cache, self.batch, i["q"], self.ids,
+                                        w.topk, self.out, self.lse)
+        if ev[3] is not None:
+            ev[3].record()
+
+    def timed(self, steps, warmup):
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for e in evs:
+            self.step(e)
+        stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        total_ms = start.elapsed_time(stop)
+        per = {n: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs]))
+               for k, n in enumerate(self.names)}
+        return total_ms / steps, per, wall
+
+
+def measure(w, dev, steps, warmup):
+    r = Runner(w, dev)
+    ms, per, wall = r.timed(steps, warmup)
+    units = plan_units(w)
+    ids = r.ids.cpu().numpy()
+    tokens = selected_kv_tokens(w, ids, units)
+    G = w.num_q_heads // w.num_kv_heads
+    res = dict(workload=w.name, ms_per_step=ms, kernel_ms=per, wall_s=wall,
+               selected_kv_tokens_per_step=tokens, value=tokens / (ms * 1e-3))
+    if w.is_decode:
+        nbytes = index_decode_bytes(w)
+        t = per["index_scores"] * 1e-3
+        res["roofline"] = dict(kernel="index_scores (decode)", bound="hbm",
+                               achieved=nbytes / t / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                               frac=nbytes / t / 1e9 / HBM_PEAK_GBS, traffic=None,
+                               algorithmic_bytes=nbytes)
+        # whole decode step against HBM: the algorithmic bytes of all four launches
+        kv = tokens * w.head_dim * 2 * 2            # K and V rows of the selected keys
+        step_bytes = nbytes + kv + 2 * w.num_seqs * w.num_q_heads * w.head_dim * 2
+        res["step_hbm_frac"] = step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+        res["step_algorithmic_bytes"] = step_bytes
+    else:
+        flops = 4.0 * w.head_dim * G * tokens       # QK^T and PV over the visible pairs
+        t = per["sparse_attn_prefill"] * 1e-3
+        res["roofline"] = dict(kernel="sparse_attn_prefill", bound="mfma",
+                               achieved=flops / t / 1e12, peak=MFMA_BF16_PEAK_TFLOPS,
+                               unit="TFLOP/s", frac=flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                               traffic=None, algorithmic_flops=flops)
+    res["_runner"] = r
+    return res
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of units
+# ----------------------------------------------------------------------------
+
+def _mini(cache_t, bt_row, blocks):
+    """Host float32 copy of some logical blocks of one request and the block
+    table that maps those logical ids to rows of the copy."""
+    idx = torch.as_tensor(np.asarray(bt_row)[blocks].astype(np.int64), device=cache_t.device)
+    mini = synth.to_host_f32(cache_t.index_select(0, idx))
+    bt = np.zeros(max(blocks) + 1, dtype=np.int64)
+    bt[blocks] = np.arange(len(blocks))
+    return mini, bt
+
+
+def cpu_baseline(w, runner, budget_s=15.0):
+    """The oracle as it stands, timed on this host's cores over a seeded sample of
+    units (the copies of each unit's inputs to the host are not timed)."""
+    from oracle import msa_oracle as O
+    units = plan_units(w)
+    order = np.random.default_rng(0).permutation(len(units))
+    inp = runner.inp
+    bt = inp["block_table"].cpu().numpy()
+    cores = len(os.sched_getaffinity(0))
+    done, tokens, t_used = 0, 0, 0.0
+    for u in order:
+        un = units[u]
+        r, tau = un["r"], un["tau"]
+        rows = slice(r, r + 1) if w.is_decode else slice(un["row0"], un["row0"] + un["num_rows"])
+        q, qi = synth.to_host_f32(inp["q"][rows]), synth.to_host_f32(inp["q_idx"][rows])
+        ki, bti = _mini(inp["k_idx_cache"], bt[r], list(range(max(tau, 1))))
+        t0 = time.perf_counter()
+        S = O.unit_block_scores(qi, ki, bti, tau, w.num_sel_groups, bt.shape[1])
+        ids = np.array([O.select_blocks(S[g], tau, w.topk)
+                        for g in range(w.num_sel_groups)], dtype=np.int32)
+        t_used += time.perf_counter() - t0
+        kept = sorted({int(b) for b in ids.reshape(-1) if b >= 0})
+        kc, btk = _mini(inp["k_cache"], bt[r], kept)
+        vc, _ = _mini(inp["v_cache"], bt[r], kept)
+        t0 = time.perf_counter()
+        O.unit_attention(q, un["pos0"], ids, kc, vc, btk, int(w.seq_lens[r]), w.num_sel_groups)
+        t_used += time.perf_counter() - t0
+        tokens += selected_kv_tokens(w, ids[None], [un])
+        done += 1
+        if t_used > budget_s:
+            break
+    return dict(value=tokens / t_used, unit="selected-KV tokens/s", cores=cores, kind="oracle",
+                sample=f"{done} of {len(units)} units of {w.name} (seeded order), whole oracle "
+                       f"path per unit (scores, top-k, attention) in float64, {t_used:.1f} s "
+                       f"of oracle time")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_32k", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--second", default="decode_1m_b8",
+                    help="second workload measured in the same run ('none' to skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(sequences and KV heads shard with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    msa.lib()
+
+    w = synth.WORKLOADS[args.workload]
+    main_res = measure(w, dev, args.steps, args.warmup)
+    log(f"{w.name}: {main_res['ms_per_step']:.3f} ms/step, kernels {main_res['kernel_ms']}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        cpu = cpu_baseline(w, main_res["_runner"], args.cpu_budget)
+    del main_res["_runner"]
+    torch.cuda.empty_cache()
+
+    second = None
+    if args.second != "none" and args.second != args.workload:
+        w2 = synth.WORKLOADS[args.second]
+        second = measure(w2, dev, args.steps, args.warmup)
+        log(f"{w2.name}: {second['ms_per_step']:.3f} ms/step, kernels {second['kernel_ms']}")
+        del second["_runner"]
+        torch.cuda.empty_cache()
+
+    config = dict(workload=w.name, batch=w.num_seqs,
+                  seq_lens=w.seq_lens if len(set(w.seq_lens)) > 1 else w.seq_lens[0],
+                  q_per_seq=(w.q_lens[0] if w.q_lens else 1), q_heads=w.num_q_heads,
+                  kv_heads=w.num_kv_heads, head_dim=w.head_dim, block=BLK, topk=w.topk,
+                  indexer=f"{w.num_idx_heads}x{w.idx_head_dim}",
+                  selection_groups=w.num_sel_groups)
+    line = {
+        "metric": "selected-KV tokens/sec",
+        "value": main_res["value"],
+        "unit": "selected-KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) with planted blocks), inputs resident in HBM",
+        "config": config,
+        "kernel_ms": main_res["kernel_ms"],
+        "roofline": main_res["roofline"],
+        "cpu_baseline": cpu,
+    }
+    if second is not None:
+        line["second_workload"] = {k: second[k] for k in (
+            "workload", "value", "ms_per_step", "kernel_ms", "roofline", "step_hbm_frac")
+            if k in second}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -148,22 +148,26 @@ msa_status_t msa_index_scores(const msa_geom_t *geom, const msa_cache_t *cache,
   msa_status_t st = check_geom(geom, &g);
   if (st != MSA_OK) return st;
   if ((st = check_cache(cache, false, true)) != MSA_OK) return st;
+  if (batch != nullptr) {
+    if ((st = check_batch(batch)) != MSA_OK) return st;
+    if (batch->total_units == 0) return ok();   // nothing to score
+  }
   MSA_REQUIRE(q_idx != nullptr && scores != nullptr, MSA_ERR_INVALID_ARG,
               "q_idx / scores is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (batch == nullptr) return hip_status(msa::launch_index_decode(g, *cache, q_idx, scores, s),
                                           "index_decode");
-  if ((st = check_batch(batch)) != MSA_OK) return st;
   return hip_status(msa::launch_index_prefill(g, *cache, *batch, q_idx, scores, s),
                     "index_prefill");
 }
 
 msa_status_t msa_select_topk_blocks(const float *scores, int32_t num_rows, int32_t row_len,
                                     int32_t topk, int32_t *ids, void *stream) {
-  MSA_REQUIRE(scores != nullptr && ids != nullptr, MSA_ERR_INVALID_ARG, "scores / ids is NULL");
   MSA_REQUIRE(num_rows >= 0, MSA_ERR_INVALID_ARG, "num_rows must be non-negative");
   MSA_REQUIRE(row_len >= 1, MSA_ERR_INVALID_ARG, "row_len must be positive");
   MSA_REQUIRE(topk >= 1, MSA_ERR_INVALID_ARG, "topk must be positive");
+  if (num_rows == 0) return ok();
+  MSA_REQUIRE(scores != nullptr && ids != nullptr, MSA_ERR_INVALID_ARG, "scores / ids is NULL");
   return hip_status(msa::launch_topk(scores, num_rows, row_len, topk, ids,
                                      static_cast<hipStream_t>(stream)),
                     "select_topk_blocks");
@@ -178,9 +182,10 @@ msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *
   if (st != MSA_OK) return st;
   if ((st = check_cache(cache, true, false)) != MSA_OK) return st;
   if ((st = check_batch(batch)) != MSA_OK) return st;
+  MSA_REQUIRE(topk >= 1, MSA_ERR_INVALID_ARG, "topk must be positive");
+  if (batch->total_units == 0) return ok();     // no queries
   MSA_REQUIRE(q != nullptr && ids != nullptr && out != nullptr, MSA_ERR_INVALID_ARG,
               "q / ids / out is NULL");
-  MSA_REQUIRE(topk >= 1, MSA_ERR_INVALID_ARG, "topk must be positive");
   MSA_REQUIRE(!(softmax_scale != softmax_scale), MSA_ERR_INVALID_ARG, "softmax_scale is NaN");
   return hip_status(msa::launch_attn_prefill(g, *cache, *batch, q, ids, topk,
                                              resolve_scale(softmax_scale, g.D), out, lse,

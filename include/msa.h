@@ -131,7 +131,8 @@ msa_status_t msa_prefill_plan(const int32_t *h_seq_lens, const int32_t *h_q_lens
  *                        sum_{h in g} q_idx[t,h,:] . k_idx[s,h,:] (fp32 accumulate)
  *             b == tau : +inf (the diagonal block is always kept)
  *             b >  tau : -inf (causal: future blocks are never kept)
- * Prefill runs on bf16 MFMA for bf16 inputs; decode streams k_idx once. */
+ * Prefill runs on bf16 MFMA for bf16 inputs; decode streams k_idx once.
+ * A prefill batch with no units enqueues nothing (q_idx and scores may be NULL). */
 msa_status_t msa_index_scores(const msa_geom_t *geom, const msa_cache_t *cache,
                               const msa_batch_t *batch, const void *q_idx,
                               float *scores, void *stream);
@@ -143,7 +144,7 @@ msa_status_t msa_index_scores(const msa_geom_t *geom, const msa_cache_t *cache,
  * Per row, the K = min(topk, #entries > -inf) entries of highest score are kept,
  * equal scores ordered by lower index; their indices are written in ascending
  * order and the remaining topk - K slots are set to -1. NaN scores are undefined.
- * Requires 1 <= topk, 1 <= row_len. */
+ * Requires 1 <= topk, 1 <= row_len; num_rows == 0 enqueues nothing. */
 msa_status_t msa_select_topk_blocks(const float *scores, int32_t num_rows,
                                     int32_t row_len, int32_t topk, int32_t *ids,
                                     void *stream);
@@ -159,7 +160,8 @@ msa_status_t msa_select_topk_blocks(const float *scores, int32_t num_rows,
  * attends to every key s of the blocks ids[u][g][*] with s <= pos(t):
  *   out = softmax(softmax_scale * q . k) . v  (fp32 softmax).
  * softmax_scale <= 0 selects 1/sqrt(D). bf16 runs on MFMA with fp32 accumulation;
- * probabilities are rounded to bf16 for the P.V product. */
+ * probabilities are rounded to bf16 for the P.V product. A batch with no units
+ * enqueues nothing (q, ids and out may be NULL). */
 msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *cache,
                                      const msa_batch_t *batch, const void *q,
                                      const int32_t *ids, int32_t topk,

@@ -41,8 +41,8 @@ def check_scores(gpu, ref, tol, where=""):
     gpu = np.asarray(gpu, dtype=np.float64)
     inf = ~np.isfinite(ref)
     assert np.array_equal(gpu[inf], ref[inf]), f"{where}: +-inf pattern differs"
-    err = np.abs(gpu - ref)
-    err[inf] = 0
+    err = np.zeros_like(ref)
+    err[~inf] = np.abs(gpu[~inf] - ref[~inf])
     worst = (err / tol[None, :, None]).max() if err.size else 0.0
     assert worst <= 1.0, f"{where}: score error {err.max():.3e} exceeds the bound " \
                          f"(ratio {worst:.3f})"

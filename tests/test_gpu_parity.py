@@ -193,6 +193,10 @@ def test_empty_prefill_batch_launches_nothing(gpu_device):
     assert batch.total_units == 0
     scores = torch.empty((0, 2, cache.max_blocks), dtype=torch.float32, device=gpu_device)
     msa.msa_index_scores(geom, cache, batch, inp["q_idx"][:0], scores)
+    ids = torch.empty((0, 2, w.topk), dtype=torch.int32, device=gpu_device)
+    msa.msa_select_topk_blocks(scores, w.topk, ids)
+    out = torch.empty_like(inp["q"][:0])
+    msa.msa_sparse_attn_prefill(geom, cache, batch, inp["q"][:0], ids, w.topk, out)
     torch.cuda.synchronize()
 
 
@@ -204,7 +208,7 @@ def _mini_cache(cache_t, bt_row, blocks, heads):
     """Host float32 copy of the given logical blocks and heads of one request, with
     a block table mapping those logical ids to rows of the copy."""
     idx = torch.as_tensor(np.asarray(bt_row)[blocks].astype(np.int64), device=cache_t.device)
-    mini = host(cache_t.index_select(0, idx)[:, heads])
+    mini = host(cache_t[:, heads].index_select(0, idx))
     bt = np.zeros(max(blocks) + 1, dtype=np.int64)
     bt[blocks] = np.arange(len(blocks))
     return mini, bt
