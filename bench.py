@@ -221,7 +221,7 @@ def cpu_baseline(w, runner, budget_s=15.0):
         t_used += time.perf_counter() - t0
         kept = sorted({int(b) for b in ids.reshape(-1) if b >= 0})
         kc, btk = _mini(inp["k_cache"], bt[r], kept)
-        vc, _ = _mini(inp["v_cache"], bt[r], kept)
+        vc, _ = _mini(synth.v_token_major(inp["v_cache"]), bt[r], kept)
         t0 = time.perf_counter()
         O.unit_attention(q, un["pos0"], ids, kc, vc, btk, int(w.seq_lens[r]), w.num_sel_groups)
         t_used += time.perf_counter() - t0

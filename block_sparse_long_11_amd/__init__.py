@@ -161,7 +161,7 @@ class Geometry:
 class Cache:
     """Block-major paged caches on one device (see include/msa.h)."""
     k_cache: torch.Tensor        # [P][H_kv][128][D]
-    v_cache: torch.Tensor        # [P][H_kv][128][D]
+    v_cache: torch.Tensor        # [P][H_kv][D][128] (each block d-major)
     k_idx_cache: torch.Tensor    # [P][H_i][128][D_i]
     block_table: torch.Tensor    # int32 [B][max_blocks]
     seq_lens: torch.Tensor       # int32 [B]
@@ -174,9 +174,10 @@ class Cache:
         _need(self.block_table, "block_table", torch.int32, 2, dev)
         _need(self.seq_lens, "seq_lens", torch.int32, 1, dev)
         P = self.k_cache.shape[0]
-        if tuple(self.k_cache.shape) != (P, geom.num_kv_heads, BLOCK, geom.head_dim) or \
-                self.v_cache.shape != self.k_cache.shape:
-            raise ValueError("k_cache / v_cache must be [P][H_kv][128][D]")
+        if tuple(self.k_cache.shape) != (P, geom.num_kv_heads, BLOCK, geom.head_dim):
+            raise ValueError("k_cache must be [P][H_kv][128][D]")
+        if tuple(self.v_cache.shape) != (P, geom.num_kv_heads, geom.head_dim, BLOCK):
+            raise ValueError("v_cache must be [P][H_kv][D][128] (d-major blocks)")
         if tuple(self.k_idx_cache.shape) != (P, geom.num_idx_heads, BLOCK, geom.idx_head_dim):
             raise ValueError("k_idx_cache must be [P][H_i][128][D_i]")
         if self.seq_lens.shape[0] != self.block_table.shape[0]:

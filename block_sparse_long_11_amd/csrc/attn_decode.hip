@@ -10,15 +10,15 @@
 //
 // Phase 1: one work-group (4 waves) per (sequence, KV head j, split). Its G <= 16
 // query heads form the N = 16 columns of MFMA 16x16x32 bf16 products; each wave
-// takes 32 keys of every kept block of the split:
-//   S^T = K . Q^T    (A = K rows read straight from HBM, 16-byte loads;
-//                     B = the stacked queries in registers)
-//   O^T += V^T . P^T (A = V^T from LDS, B = probabilities from S^T's registers)
-// In the accumulator, lane l register i of 16-key tile tt holds key
-// 16tt + 4(l/16) + i; as a B operand lane l supplies k-index 8(l/16) + 4tt + i,
-// so V^T is stored in LDS in that same key order. The waves' partial (max, sum,
-// O) are merged in LDS and written normalised, with their natural-log lse, to
-// the workspace.
+// takes 32 keys of every kept block of the split and reads its operands straight
+// from HBM with 16-byte loads (K rows token-major, V rows d-major):
+//   S^T = K . Q^T    (A = 16 K rows per tile, B = the stacked queries in registers)
+//   O^T += V^T . P^T (A = V^T rows, B = probabilities from S^T's registers)
+// Tile tt's A row m is fed key 8(m/4) + 4tt + m%4 of the wave's 32, so that lane l
+// ends up holding keys 8(l/16) .. 8(l/16)+7: the k-indices it supplies to the
+// P^T operand, in natural order, matching one contiguous 16-byte V^T read.
+// The waves' partial (max, sum, O) are merged in LDS and written normalised, with
+// their natural-log lse, to the workspace.
 // Phase 2: per (sequence, query head) the parts are merged:
 //   lse = log sum_s exp(lse_s),  out = sum_s exp(lse_s - lse) o_s.
 #include "msa_device.h"
@@ -35,30 +35,24 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kDecThreads = 256;
-constexpr int kVtRow = 40;       // LDS row of V^T: 32 keys + 8 pad (elements)
+constexpr float kSlack = 8.f;
 
-__device__ __forceinline__ int dec_kappa(int kl) {   // key (0..31) -> k-index
-  return 8 * ((kl % 16) / 4) + 4 * (kl / 16) + (kl % 4);
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, bf16x2));
 }
 
 template <int D>
 __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
-    const uint16_t *__restrict__ vc, const int32_t *__restrict__ block_table,
+    const uint16_t *__restrict__ vtc, const int32_t *__restrict__ block_table,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ ids, int topk,
-    int max_blocks, int Hq, int Hkv, int nsel, int num_splits, int per_split,
-    float scale_log2, float *__restrict__ o_part, float *__restrict__ lse_part) {
+    int max_blocks, int Hq, int Hkv, int nsel, int num_splits, int per_split, float c,
+    float *__restrict__ o_part, float *__restrict__ lse_part) {
   constexpr int KS = D / 32;   // k steps of S^T
   constexpr int DT = D / 16;   // d tiles of O^T
-  // V^T of the current block per wave; after the last block the same bytes hold
-  // the waves' partial outputs for the merge.
-  constexpr int kVtBytes = 4 * D * kVtRow * 2;
-  constexpr int kOwBytes = 4 * 16 * (D + 1) * 4;
-  static_assert(kOwBytes <= kVtBytes, "merge buffer must fit in the V^T buffer");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kVtBytes];
+  __shared__ float Ow[4][16][D + 1];
   __shared__ float Mw[4][16], Lw[4][16];
-  auto Vt = reinterpret_cast<uint16_t (*)[D * kVtRow]>(smem);
-  auto Ow = reinterpret_cast<float (*)[16][D + 1]>(smem);
 
   const int r = blockIdx.x / Hkv, j = blockIdx.x % Hkv, sp = blockIdx.y;
   const int G = Hq / Hkv;
@@ -70,12 +64,13 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
 
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   const int n = lane % 16;               // stacked query head (column)
-  const int qd = (lane / 16) * 8;        // this lane's 8 d inside a k step
+  const int q4 = lane / 16;              // lane quarter: 8 d (or 8 keys) per k step
 
   bf16x8 qb[KS];
   {
     const bool live = n < G;
-    const uint16_t *qp = q + (static_cast<size_t>(r) * Hq + j * G + (live ? n : 0)) * D + qd;
+    const uint16_t *qp =
+        q + (static_cast<size_t>(r) * Hq + j * G + (live ? n : 0)) * D + q4 * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = *reinterpret_cast<const uint4 *>(qp + ks * 32);
@@ -86,7 +81,7 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
   f32x4 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{};
-  float m_run = -1e30f, l_run = 0.f;
+  float m_ref = neg_inf(), l_run = 0.f;
   bool any = false;
 
   for (int slot = slot0; slot < slot1; ++slot) {
@@ -95,78 +90,70 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
     any = true;
     const int64_t phys = bt[b];
     const size_t off = (static_cast<size_t>(phys) * Hkv + j) * kBlk * D;
-    __syncthreads();                       // previous block's V^T fully read
-    // stage V^T: 16-byte chunk c = (key, d chunk); lanes of a row are consecutive
-    for (int c = t; c < kBlk * D / 8; c += kDecThreads) {
-      const int key = c / (D / 8), dc = c % (D / 8);
-      const uint4 v = *reinterpret_cast<const uint4 *>(vc + off + key * D + dc * 8);
-      uint16_t *dst = &Vt[key / 32][dc * 8 * kVtRow + dec_kappa(key % 32)];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dst[e * kVtRow] = (w[e / 2] >> ((e % 2) * 16)) & 0xffffu;
-    }
-    // S^T for this wave's 32 keys: 2 tiles of 16 keys x 16 heads
+    // S^T: 2 tiles of 16 keys x 16 heads over this wave's 32 keys
     f32x4 s[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       s[tt] = f32x4{};
-      const uint16_t *kr = kc + off + (wave * 32 + tt * 16 + n) * D + qd;
+      const int key = wave * 32 + 8 * (n / 4) + 4 * tt + (n % 4);
+      const uint16_t *kr = kc + off + key * D + q4 * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(kr + ks * 32));
         s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], s[tt], 0, 0, 0);
       }
     }
-    float mx = -1e30f;
+    // register i of tile tt holds key wave*32 + 8*q4 + 4*tt + i
+    const int lim = qpos - b * kBlk - (wave * 32 + 8 * q4);
+    float mx = neg_inf();
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = wave * 32 + tt * 16 + (lane / 16) * 4 + i;
-        float x = s[tt][i] * scale_log2;
-        if (b * kBlk + key > qpos) x = neg_inf();
-        s[tt][i] = x;
-        mx = fmaxf(mx, x);
+        if (4 * tt + i > lim) s[tt][i] = neg_inf();
+        mx = fmaxf(mx, s[tt][i]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c;
+    const bool need = mx > m_ref + kSlack;
+    if (__any(need)) {
+      const float nm = need ? mx : m_ref;
+      const float al = __builtin_amdgcn_exp2f(m_ref - nm);
+      m_ref = nm;
+      l_run *= al;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
+    }
     float p[8];
-    float psum = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[tt * 4 + i] = exp2f(s[tt][i] - m_new);
-        psum += p[tt * 4 + i];
+        p[tt * 4 + i] = (m_ref == neg_inf()) ? 0.f
+                        : __builtin_amdgcn_exp2f(fmaf(s[tt][i], c, -m_ref));
+        l_run += p[tt * 4 + i];
       }
-    l_run = l_run * alpha + psum;
-    const bf16x8 pb = as_bf16x8(uint4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
-    __syncthreads();                       // V^T staged
-    const uint16_t *vr = &Vt[wave][n * kVtRow + qd];
+    const bf16x8 pb = as_bf16x8(uint4{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]),
+                                      cvt_pk_bf16(p[4], p[5]), cvt_pk_bf16(p[6], p[7])});
+    const uint16_t *vr = vtc + off + n * kBlk + wave * 32 + q4 * 8;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      o[dt] *= alpha;
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(vr + dt * 16 * kVtRow));
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(vr + dt * 16 * kBlk));
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
     }
   }
 
   // merge the 4 waves: per column n the waves hold (m, partial l, O^T)
-  __syncthreads();                         // V^T no longer read
   float l_w = l_run + __shfl_xor(l_run, 16, kWave);
   l_w += __shfl_xor(l_w, 32, kWave);
   if (lane < 16) {
-    Mw[wave][n] = m_run;
+    Mw[wave][n] = m_ref;
     Lw[wave][n] = l_w;
   }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Ow[wave][n][dt * 16 + (lane / 16) * 4 + i] = o[dt][i];
+    for (int i = 0; i < 4; ++i) Ow[wave][n][dt * 16 + q4 * 4 + i] = o[dt][i];
   __syncthreads();
   const size_t part0 = static_cast<size_t>(r) * Hq * num_splits;
   for (int e = t; e < G * D; e += kDecThreads) {
@@ -181,12 +168,12 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
     float L = 0.f, acc = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float f = exp2f(Mw[w][hn] - M);
+      const float f = (Mw[w][hn] == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(Mw[w][hn] - M);
       L += Lw[w][hn] * f;
       acc += Ow[w][hn][d] * f;
     }
     o_part[pi * D + d] = acc / L;
-    if (d == 0) lse_part[pi] = (M + log2f(L)) * kLn2;
+    if (d == 0) lse_part[pi] = (M + __builtin_log2f(L)) * kLn2;
   }
 }
 

@@ -12,18 +12,21 @@
 // s <= pos(t). Only the diagonal block needs the causal test: every other kept
 // block lies entirely before the unit's first query.
 //
-// bf16 path (MFMA 32x32x16, fp32 accumulate). A work-group of 8 waves owns
-// (unit, KV head j, 2 query heads): 2 heads x 128 token rows = 256 query rows, one
-// wave per (head, 32 rows). For each kept block the group stages K as [key][d]
-// and V transposed as [d][key] in LDS, then every wave computes
-//   S^T = K . Q^T           (A = K from LDS, B = its Q rows held in registers)
-//   O^T += V^T . P^T        (A = V^T from LDS, B = P taken straight from S^T)
-// Computing the transposed products keeps each query in one lane pair, so the
-// online-softmax row statistics need a single cross-lane exchange, and lets the
-// probabilities feed the second product without an LDS round trip. For that the
-// accumulator's key order inside each 16-key group (lane half a, register
-// 8h+jj holds key 16h + 8(jj/4) + 4a + jj%4) is mirrored by storing V^T with
-// keys 4-7 and 8-11 of every 16-key group swapped.
+// bf16 path (MFMA 32x32x16, fp32 accumulate). A work-group of 8 waves (two per
+// SIMD, so one wave's softmax arithmetic overlaps the other's MFMAs) owns (unit,
+// KV head j, 2 query heads): 128 token rows x 2 heads, one wave per (head, 32
+// tokens). Per kept block the group stages K ([key][d]) and V ([d][key], the
+// cache's d-major blocks) in LDS by direct global->LDS loads, 16-byte chunks
+// XOR-swizzled by row, into one of two buffers while the other is being read.
+// Per 32-key tile each wave computes
+//   S^T = K . Q^T           (A = K rows from LDS, B = Q held in registers)
+//   O^T += V^T . P^T        (A = V^T rows from LDS, B = P from S^T's registers)
+// The S^T row m of a tile is fed key (m with bits 2 and 3 swapped): then lane
+// half a, register 8h+jj holds key 16h + 8a + jj, which is exactly the k-index
+// the P^T operand needs, so V^T is read in natural key order.
+// Online softmax in log2 units with a lazy reference maximum: O and the row sum
+// are rescaled only when a row's maximum grows by more than 8 (probabilities
+// stay <= 2^8); the result is exact after the final division by the row sum.
 //
 // fp32 path: plain FMA, one thread per (query, head); for small exact checks.
 #include "msa_device.h"
@@ -35,171 +38,201 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kPrefThreads = 512;
+constexpr float kSlack = 8.f;
 
-// Position of key k (0..127) in the swapped order used for V^T rows.
-__device__ __forceinline__ int vt_pos(int k) {
-  const int grp = (k >> 2) & 3;                    // 4-key group inside 16
-  const int sw = (grp == 1) ? 2 : (grp == 2) ? 1 : grp;
-  return (k & ~15) | (sw << 2) | (k & 3);
+// S^T tile row m (0..31) -> key inside the 32-key tile: swap bits 2 and 3.
+__device__ __forceinline__ int srow_key(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, bf16x2));
 }
 
 template <int D>
-__global__ __launch_bounds__(kPrefThreads) void attn_prefill_bf16_kernel(
+__global__ __launch_bounds__(kPrefThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
-    const uint16_t *__restrict__ vc, const int32_t *__restrict__ block_table,
+    const uint16_t *__restrict__ vtc, const int32_t *__restrict__ block_table,
     const msa_unit_t *__restrict__ units, const int32_t *__restrict__ ids, int topk,
-    int max_blocks, int Hq, int Hkv, int nsel, float scale_log2,
+    int max_blocks, int Hq, int Hkv, int nsel, int num_uj, int pairs, float c,
     uint16_t *__restrict__ out, float *__restrict__ lse) {
-  constexpr int KS = D / 16;        // k steps of S^T = K Q^T
-  constexpr int DT = D / 32;        // d tiles of O^T
-  constexpr int KROW = D + 8;       // padded LDS row (elements) of K
-  constexpr int VROW = kBlk + 8;    // padded LDS row (elements) of V^T
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlk * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VROW];
+  constexpr int KS = D / 16;              // 16-wide d steps of S^T
+  constexpr int DT = D / 32;              // 32-row d tiles of O^T
+  constexpr int CH = D / 8;               // 16-byte chunks per K row
+  constexpr int NW = kPrefThreads / kWave;
+  constexpr int KCH = kBlk * CH / kPrefThreads;
+  constexpr int VCH = D * 16 / kPrefThreads;
+  // Two LDS buffers per operand, filled by direct global->LDS loads while the
+  // other one is being read. K: chunk c of row r at c ^ (r % CH). V^T: chunk c of
+  // row d at c ^ (d % 16).
+  __shared__ u32x4 Ks0[kBlk * CH], Ks1[kBlk * CH];
+  __shared__ u32x4 Vs0[D * 16], Vs1[D * 16];
 
-  const int G = Hq / Hkv;
-  const int pairs = (G + 1) / 2;
-  const int u = blockIdx.x;
-  const int j = blockIdx.y / pairs, hp = blockIdx.y % pairs;
+  // XCD-aware order: the `pairs` work-groups of one (unit, KV head) get ids that
+  // are equal mod 8 (same XCD, same L2) and adjacent in that XCD's dispatch order;
+  // (unit, KV head) pairs are taken from the last unit down (most blocks first).
+  const int id = blockIdx.x;
+  const int uj_rev = 8 * (id / (8 * pairs)) + id % 8;
+  const int hp = (id / 8) % pairs;
+  if (uj_rev >= num_uj) return;
+  const int uj = num_uj - 1 - uj_rev;
+  const int u = uj / Hkv, j = uj % Hkv;
   const msa_unit_t un = units[u];
+  const int G = Hq / Hkv;
   const int g = (nsel == Hkv) ? j : 0;
   const int32_t *sel = ids + (static_cast<size_t>(u) * nsel + g) * topk;
   const int32_t *bt = block_table + static_cast<size_t>(un.r) * max_blocks;
 
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
-  const int hl = 2 * hp + wave / 4;                // head inside the group
-  const int slab = wave % 4;                       // 32-row slab of the tile
+  const int a = lane / 32, n = lane % 32;
+  const int hl = 2 * hp + wave / 4;       // head inside the group
+  const int slab = wave % 4;              // 32-token slab of the tile
   const bool active = hl < G && slab * 32 < un.num_rows;
   const int head = j * G + min(hl, G - 1);
-  const int row_in_tile = slab * 32 + (lane % 32);
+  const int row_in_tile = slab * 32 + n;
   const bool row_ok = row_in_tile < un.num_rows;
   const int qrow = un.row0 + min(row_in_tile, un.num_rows - 1);
   const int qpos = row_ok ? un.pos0 + row_in_tile : 0x7fffffff;
 
-  // B operand of S^T: this lane's query row, 8 d at (l/32)*8 of each k step
-  bf16x8 qb[KS];
+  bf16x8 qf[KS];
   {
-    const uint16_t *qp = q + (static_cast<size_t>(qrow) * Hq + head) * D + (lane / 32) * 8;
+    const uint16_t *pq = q + (static_cast<size_t>(qrow) * Hq + head) * D + a * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qb[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(qp + ks * 16));
+      qf[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(pq + ks * 16));
   }
+
+  // Enqueue the direct loads of block b into (Kd, Vd). Instruction i of wave w
+  // fills LDS chunks (NW i + w) * 64 + lane; each lane fetches the global chunk
+  // that the swizzle places there.
+  auto issue = [&](int b, u32x4 *Kd, u32x4 *Vd) {
+    const size_t off = (static_cast<size_t>(bt[b]) * Hkv + j) * kBlk * D;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int base = (NW * i + wave) * 64;
+      const int p = base + lane, r = p / CH, ch = (p % CH) ^ (r % CH);
+      __builtin_amdgcn_global_load_lds(
+          kc + off + r * D + ch * 8,
+          (__attribute__((address_space(3))) void *)(Kd + base), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int base = (NW * i + wave) * 64;
+      const int p = base + lane, r = p / 16, ch = (p % 16) ^ (r % 16);
+      __builtin_amdgcn_global_load_lds(
+          vtc + off + r * kBlk + ch * 8,
+          (__attribute__((address_space(3))) void *)(Vd + base), 16, 0, 0);
+    }
+  };
 
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
-  float m_run = -1e30f;   // running max (log2 domain); finite so alpha is never NaN
-  float l_run = 0.f;      // this lane's share of the row sum
+  float m_ref = neg_inf();                // reference maximum, log2 units
+  float l_run = 0.f;                      // this lane's share of the row sum
 
-  for (int slot = 0; slot < topk; ++slot) {
-    const int b = sel[slot];
-    if (b < 0) break;                              // ids ascending, -1 at the tail
-    const int64_t phys = bt[b];
-    const size_t head_off = (static_cast<size_t>(phys) * Hkv + j) * kBlk * D;
-    __syncthreads();                               // previous block fully consumed
-    // stage K: [key][d], 16-byte chunks
-    for (int c = t; c < kBlk * D / 8; c += kPrefThreads) {
-      const int key = c / (D / 8), dc = c % (D / 8);
-      *reinterpret_cast<uint4 *>(&Ks[key * KROW + dc * 8]) =
-          *reinterpret_cast<const uint4 *>(kc + head_off + key * D + dc * 8);
-    }
-    // stage V^T: a thread takes 4 consecutive keys x 8 d and writes 8 rows of 4 keys
-    for (int c = t; c < (kBlk / 4) * (D / 8); c += kPrefThreads) {
-      const int ka = c % (kBlk / 4), dc = c / (kBlk / 4);
-      uint4 vv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vv[i] = *reinterpret_cast<const uint4 *>(vc + head_off + (ka * 4 + i) * D + dc * 8);
-      const int p = vt_pos(ka * 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e / 2, sh = (e % 2) * 16;
-        auto pick = [&](const uint4 &x) -> uint32_t {
-          const uint32_t word = (w == 0) ? x.x : (w == 1) ? x.y : (w == 2) ? x.z : x.w;
-          return (word >> sh) & 0xffffu;
-        };
-        uint2 pk;
-        pk.x = pick(vv[0]) | (pick(vv[1]) << 16);
-        pk.y = pick(vv[2]) | (pick(vv[3]) << 16);
-        *reinterpret_cast<uint2 *>(&Vt[(dc * 8 + e) * VROW + p]) = pk;
-      }
-    }
-    __syncthreads();
-    if (!active) continue;
-
-    // S^T tiles: 4 x (32 keys x 32 queries)
-    f32x16 s[4];
+  auto compute = [&](int b, const u32x4 *Kb, const u32x4 *Vb) {
+    const bool diag = (b == un.tau);
+    const int lim = qpos - b * kBlk;      // keys with offset > lim are masked
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      s[kt] = f32x16{};
-      const uint16_t *kr = &Ks[(kt * 32 + lane % 32) * KROW + (lane / 32) * 8];
+      f32x16 s = f32x16{};
+      const int krow = kt * 32 + srow_key(n);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(kr + ks * 16));
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], s[kt], 0, 0, 0);
+        const int ch = 2 * ks + a;
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, Kb[krow * CH + (ch ^ (krow % CH))]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
       }
-    }
-    // scale, causal mask on the diagonal block, row max
-    const bool diag = (b == un.tau);
-    float mx = -1e30f;
+      if (diag) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kt * 32 + (i / 4) * 8 + (lane / 32) * 4 + (i % 4);
-        float x = s[kt][i] * scale_log2;
-        if (diag && b * kBlk + key > qpos) x = neg_inf();
-        s[kt][i] = x;
-        mx = fmaxf(mx, x);
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt * 32 + 16 * (i / 8) + 8 * a + (i % 8);
+          if (key > lim) s[i] = neg_inf();
+        }
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
-    bf16x8 pb[8];
+      float x = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int i = 3; i < 15; i += 2) x = fmaxf(fmaxf(x, s[i]), s[i + 1]);
+      x = fmaxf(x, s[15]);
+      x = fmaxf(x, __shfl_xor(x, 32, kWave)) * c;
+      const bool need = x > m_ref + kSlack;
+      if (__any(need)) {
+        const float nm = need ? x : m_ref;
+        const float al = __builtin_amdgcn_exp2f(m_ref - nm);
+        m_ref = nm;
+        l_run *= al;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
+      }
+      bf16x8 pf[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         uint32_t w[4];
 #pragma unroll
         for (int jj = 0; jj < 8; jj += 2) {
-          const float p0 = exp2f(s[kt][8 * h + jj] - m_new);
-          const float p1 = exp2f(s[kt][8 * h + jj + 1] - m_new);
-          psum += p0 + p1;
-          w[jj / 2] = pack_bf16x2(p0, p1);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj], c, -m_ref));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj + 1], c, -m_ref));
+          l_run += p0 + p1;
+          w[jj / 2] = cvt_pk_bf16(p0, p1);
         }
-        pb[kt * 2 + h] = as_bf16x8(uint4{w[0], w[1], w[2], w[3]});
+        pf[h] = as_bf16x8(uint4{w[0], w[1], w[2], w[3]});
       }
-    l_run = l_run * alpha + psum;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      o[dt] *= alpha;
-      const uint16_t *vr = &Vt[(dt * 32 + lane % 32) * VROW + (lane / 32) * 8];
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = dt * 32 + n;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(vr + ks * 16));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], o[dt], 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+          const int ch = 4 * kt + 2 * h + a;
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, Vb[d * 16 + (ch ^ (d % 16))]);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[h], o[dt], 0, 0, 0);
+        }
       }
     }
+  };
+
+  // Blocks alternate between the two buffers. At the top of each step only that
+  // block's loads are outstanding; after the barrier every wave has finished with
+  // the other buffer, which then receives the next block.
+  int slot = 0;
+  issue(sel[0], Ks0, Vs0);                // the diagonal is always kept: sel[0] >= 0
+  for (;;) {
+    int b = sel[slot];
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this block's loads landed
+    __syncthreads();
+    int nb = (slot + 1 < topk) ? sel[slot + 1] : -1;
+    if (nb >= 0) issue(nb, Ks1, Vs1);
+    if (active) compute(b, Ks0, Vs0);
+    if (nb < 0) break;
+    ++slot;
+    b = nb;
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    nb = (slot + 1 < topk) ? sel[slot + 1] : -1;
+    if (nb >= 0) issue(nb, Ks0, Vs0);
+    if (active) compute(b, Ks1, Vs1);
+    if (nb < 0) break;
+    ++slot;
   }
-  if (!active || !row_ok) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-  const float inv = 1.f / l_tot;
+  if (!active) return;
+  const float sum = l_run + __shfl_xor(l_run, 32, kWave);
+  if (!row_ok) return;
+  const float inv = 1.f / sum;
   uint16_t *op = out + (static_cast<size_t>(qrow) * Hq + head) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = dt * 32 + i4 * 8 + (lane / 32) * 4;
-      uint2 pk;
-      pk.x = pack_bf16x2(o[dt][i4 * 4 + 0] * inv, o[dt][i4 * 4 + 1] * inv);
-      pk.y = pack_bf16x2(o[dt][i4 * 4 + 2] * inv, o[dt][i4 * 4 + 3] * inv);
-      *reinterpret_cast<uint2 *>(op + d) = pk;
+      const int d = dt * 32 + i4 * 8 + a * 4;
+      uint2 w;
+      w.x = cvt_pk_bf16(o[dt][i4 * 4 + 0] * inv, o[dt][i4 * 4 + 1] * inv);
+      w.y = cvt_pk_bf16(o[dt][i4 * 4 + 2] * inv, o[dt][i4 * 4 + 3] * inv);
+      *reinterpret_cast<uint2 *>(op + d) = w;
     }
-  if (lse != nullptr && lane < 32)
-    lse[static_cast<size_t>(qrow) * Hq + head] = (m_run + log2f(l_tot)) * kLn2;
+  if (lse != nullptr && a == 0)
+    lse[static_cast<size_t>(qrow) * Hq + head] = (m_ref + __builtin_log2f(sum)) * kLn2;
 }
 
 }  // namespace
@@ -208,7 +241,7 @@ __global__ __launch_bounds__(kPrefThreads) void attn_prefill_bf16_kernel(
 // per sequence at position seq_len - 1). One thread per (query row, head).
 template <int D>
 __global__ __launch_bounds__(128) void attn_f32_kernel(
-    const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc,
+    const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vtc,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
     const msa_unit_t *__restrict__ units, const int32_t *__restrict__ ids, int topk,
     int max_blocks, int Hq, int Hkv, int nsel, float scale, float *__restrict__ out,
@@ -239,7 +272,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
     if (b < 0) break;
     const int64_t phys = bt[b];
     const float *kb = kc + (static_cast<size_t>(phys) * Hkv + j) * kBlk * D;
-    const float *vb = vc + (static_cast<size_t>(phys) * Hkv + j) * kBlk * D;
+    const float *vb = vtc + (static_cast<size_t>(phys) * Hkv + j) * D * kBlk;
     for (int key = 0; key < kBlk; ++key) {
       if (b * kBlk + key > qpos) break;
       float x = 0.f;
@@ -249,7 +282,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
       const float alpha = expf(m - m_new);
       const float p = expf(x - m_new);
       l = l * alpha + p;
-      for (int d = 0; d < D; ++d) acc[d] = acc[d] * alpha + p * vb[key * D + d];
+      for (int d = 0; d < D; ++d) acc[d] = acc[d] * alpha + p * vb[d * kBlk + key];
       m = m_new;
     }
   }
@@ -283,7 +316,9 @@ hipError_t launch_attn_prefill(const Geom &g, const msa_cache_t &c, const msa_ba
   if (!g.bf16)
     return launch_attn_f32(g, c, b.units, b.total_units, q, ids, topk, scale, out, lse, st);
   const int pairs = (g.G() + 1) / 2;
-  const dim3 grid(b.total_units, g.Hkv * pairs);
+  const int num_uj = b.total_units * g.Hkv;
+  const int groups8 = (num_uj + 7) / 8;
+  const dim3 grid(groups8 * 8 * pairs);
   const uint16_t *qb = static_cast<const uint16_t *>(q);
   const uint16_t *kb = static_cast<const uint16_t *>(c.k_cache);
   const uint16_t *vb = static_cast<const uint16_t *>(c.v_cache);
@@ -292,11 +327,11 @@ hipError_t launch_attn_prefill(const Geom &g, const msa_cache_t &c, const msa_ba
   if (g.D == 64)
     attn_prefill_bf16_kernel<64><<<grid, kPrefThreads, 0, st>>>(
         qb, kb, vb, c.block_table, b.units, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
-        g.nsel, sl2, ob, lse);
+        g.nsel, num_uj, pairs, sl2, ob, lse);
   else
     attn_prefill_bf16_kernel<128><<<grid, kPrefThreads, 0, st>>>(
         qb, kb, vb, c.block_table, b.units, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
-        g.nsel, sl2, ob, lse);
+        g.nsel, num_uj, pairs, sl2, ob, lse);
   return hipGetLastError();
 }
 

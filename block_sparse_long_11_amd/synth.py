@@ -185,8 +185,9 @@ def _gen(w, stream, device):
 def make_inputs(w: Workload, device="cpu", permute=False, chunk_blocks=2048):
     """All inputs of a workload as torch tensors on `device`.
 
-    Returns a dict with q [T][H_q][D], q_idx [T][H_i][D_i], k_cache and v_cache
-    [P][H_kv][128][D], k_idx_cache [P][H_i][128][D_i] (all in the workload dtype),
+    Returns a dict with q [T][H_q][D], q_idx [T][H_i][D_i], k_cache
+    [P][H_kv][128][D], v_cache [P][H_kv][D][128] (each block's values stored
+    d-major), k_idx_cache [P][H_i][128][D_i] (all in the workload dtype),
     block_table int32 [B][max_blocks], seq_lens int32 [B], q_lens int32 [B]
     (decode: ones) and cu_q_lens int32 [B+1]. The caches are drawn chunk by chunk
     of physical blocks so that only one fp32 chunk is alive at a time."""
@@ -219,10 +220,12 @@ def make_inputs(w: Workload, device="cpu", permute=False, chunk_blocks=2048):
             qi[cu[r]:cu[r + 1], g * hs:(g + 1) * hs, :] += a * u
     out["q_idx"] = qi.to(dt)
 
-    def cache(stream, heads, dim, plant):
-        # drawn in packed order, chunk by chunk, then scattered to physical blocks
+    def cache(stream, heads, dim, plant, d_major=False):
+        # drawn in packed order, chunk by chunk, then scattered to physical blocks;
+        # d_major stores each block's [128][dim] rows transposed as [dim][128]
         gen = _gen(w, stream, device)
-        res = torch.empty((P, heads, BLOCK, dim), dtype=dt, device=device)
+        shape = (P, heads, dim, BLOCK) if d_major else (P, heads, BLOCK, dim)
+        res = torch.empty(shape, dtype=dt, device=device)
         for c0 in range(0, P, chunk_blocks):
             c1 = min(P, c0 + chunk_blocks)
             x = _randn(gen, (c1 - c0, heads, BLOCK, dim), device)
@@ -235,18 +238,23 @@ def make_inputs(w: Workload, device="cpu", permute=False, chunk_blocks=2048):
                         ut = torch.from_numpy(u).to(device)[None, :, None, :]
                         x[idx, g * hs:(g + 1) * hs] += a * ut
             dst = torch.from_numpy(perm[c0:c1]).to(device)
-            res[dst] = x.to(dt)
+            res[dst] = (x.transpose(2, 3) if d_major else x).to(dt)
             del x
         return res
 
     out["k_cache"] = cache(_T_K, H_kv, D, False)
-    out["v_cache"] = cache(_T_V, H_kv, D, False)
+    out["v_cache"] = cache(_T_V, H_kv, D, False, d_major=True)
     out["k_idx_cache"] = cache(_T_KIDX, H_i, D_i, True)
     out["block_table"] = torch.from_numpy(bt).to(device)
     out["seq_lens"] = torch.tensor(w.seq_lens, dtype=torch.int32, device=device)
     out["q_lens"] = torch.tensor(q_lens, dtype=torch.int32, device=device)
     out["cu_q_lens"] = torch.from_numpy(cu).to(device)
     return out
+
+
+def v_token_major(v_cache: torch.Tensor) -> torch.Tensor:
+    """View of a d-major V cache [P][H][D][128] as [P][H][128][D]."""
+    return v_cache.transpose(2, 3)
 
 
 def to_host_f32(t: torch.Tensor) -> np.ndarray:

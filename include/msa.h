@@ -31,8 +31,11 @@
  *   - Calls are re-entrant and thread-safe.
  *
  * Data layout (block-major paged caches, [dd] "Serving options", [vllm]):
- *   k_cache, v_cache   [num_phys_blocks][H_kv][128][D]     (dtype)
- *   k_idx_cache        [num_phys_blocks][H_i][128][D_i]    (dtype)
+ *   k_cache            [num_phys_blocks][H_kv][128][D]     (dtype), token-major
+ *   v_cache            [num_phys_blocks][H_kv][D][128]     (dtype), d-major: each
+ *                      block of values is stored transposed, so that the P.V
+ *                      contraction over a block's keys reads contiguous rows
+ *   k_idx_cache        [num_phys_blocks][H_i][128][D_i]    (dtype), token-major
  *   block_table        int32 [num_seqs][max_blocks_per_seq], logical -> physical
  *   seq_lens           int32 [num_seqs], tokens in the cache INCLUDING the new
  *                      queries (their K/V/k_idx are inserted before these calls)

@@ -49,7 +49,8 @@ def host(t):
 
 def full_parity(w, inp, res, where):
     q, qi = host(inp["q"]), host(inp["q_idx"])
-    kc, vc, ki = host(inp["k_cache"]), host(inp["v_cache"]), host(inp["k_idx_cache"])
+    kc, ki = host(inp["k_cache"]), host(inp["k_idx_cache"])
+    vc = host(synth.v_token_major(inp["v_cache"]))
     bt = inp["block_table"].cpu().numpy()
     units = O.decode_units(w.seq_lens) if w.is_decode else O.prefill_units(w.seq_lens, w.q_lens)
     ref = O.index_scores(units, qi, ki, bt, w.num_sel_groups, bt.shape[1])
@@ -244,7 +245,8 @@ def sampled_parity(w, inp, res, units, picks, rows_per_unit=16, seed=0):
             g = j if nsel == w.num_kv_heads else 0
             kept = [int(b) for b in ids[u, g] if b >= 0]
             kc, btm = _mini_cache(inp["k_cache"], bt_all[r], kept, slice(j, j + 1))
-            vc, _ = _mini_cache(inp["v_cache"], bt_all[r], kept, slice(j, j + 1))
+            vc, _ = _mini_cache(synth.v_token_major(inp["v_cache"]), bt_all[r], kept,
+                                slice(j, j + 1))
             qh = host(q_all[un["row0"]:un["row1"], j * G:(j + 1) * G])
             for t in pick_rows:
                 o, l = O.unit_attention(qh[t:t + 1], un["pos0"] + t, ids[u, g][None], kc, vc,
