@@ -104,7 +104,8 @@ __global__ __launch_bounds__(256) void index_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// prefill, bf16: MFMA 32x32x16, one work-group per (unit, group, block chunk)
+// prefill, bf16, group width above 128: MFMA 32x32x16, one work-group per
+// (unit, group, block chunk), keys read straight from L2
 // ---------------------------------------------------------------------------
 //
 // Each of the 4 waves holds 32 query rows of the tile as the A operand
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(256) void index_decode_kernel(
 constexpr int kChunk = 16;   // blocks per work-group
 
 template <int DI, int HS>
-__global__ __launch_bounds__(256) void index_prefill_bf16_kernel(
+__global__ __launch_bounds__(256) void index_prefill_wide_kernel(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const int32_t *__restrict__ block_table, const msa_unit_t *__restrict__ units,
     int max_blocks, int nsel, float *__restrict__ scores) {
@@ -186,6 +187,160 @@ __global__ __launch_bounds__(256) void index_prefill_bf16_kernel(
     out[b0 + t] = (b0 + t == un.tau) ? pos_inf() : neg_inf();
 }
 
+
+// ---------------------------------------------------------------------------
+// prefill, bf16, group width <= 128: MFMA 32x32x16 on LDS-staged keys
+// ---------------------------------------------------------------------------
+//
+// A work-group handles two adjacent query tiles of one request (128 query rows
+// each) and one selection group, over a chunk of kChunk2 candidate blocks. Tiles
+// pair up inside a request: a unit with even tau leads and takes the next unit
+// when it belongs to the same request; a unit with odd tau that opens its request
+// leads alone; every other unit is taken by its leader. Each block's group keys
+// (128 keys x GD, the group's indexer heads side by side) are staged in LDS by
+// direct global->LDS loads, 16-byte chunks XOR-swizzled by key, double-buffered so
+// the next block is in flight while this one is scored. Wave w owns 64 rows (two
+// 32-row MFMA tiles) of tile w/2: every key fragment read from LDS feeds two
+// MFMAs. A = query rows in registers, B = key rows from LDS; the accumulators are
+// max-pooled straight away (the layout of a max does not matter).
+
+constexpr int kChunk2 = 16;   // blocks per work-group
+
+template <int DI, int HS>
+__global__ __launch_bounds__(256) void index_prefill_bf16_kernel(
+    const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
+    const int32_t *__restrict__ block_table, const msa_unit_t *__restrict__ units,
+    int num_units, int max_blocks, int nsel, float *__restrict__ scores) {
+  constexpr int GD = HS * DI;            // group width
+  constexpr int KS = GD / 16;            // k steps
+  constexpr int CHG = GD / 8;            // 16-byte chunks per staged key row
+  constexpr int CPH = DI / 8;            // chunks per head
+  constexpr int NLD = kBlk * CHG / 256;  // direct loads per thread per block
+  static_assert(GD <= 128 && NLD >= 1, "group width");
+  __shared__ u32x4 Kb0[kBlk * CHG], Kb1[kBlk * CHG];
+  __shared__ float red[4][kChunk2];
+
+  const int u0 = blockIdx.x, g = blockIdx.z;
+  const msa_unit_t un0 = units[u0];
+  const bool first = (u0 == 0) || (units[u0 - 1].r != un0.r);
+  if ((un0.tau & 1) && !first) return;           // taken by its leader
+  const bool pair = !(un0.tau & 1) && (u0 + 1 < num_units) && (units[u0 + 1].r == un0.r);
+  const msa_unit_t un1 = pair ? units[u0 + 1] : un0;
+  const int Hi = nsel * HS;
+  const int tau_max = pair ? un1.tau : un0.tau;
+  const int b0 = blockIdx.y * kChunk2;
+  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+
+  // the +inf / -inf entries of both tiles inside this chunk
+  for (int e = t; e < 2 * kChunk2; e += 256) {
+    const int tt = e / kChunk2, b = b0 + e % kChunk2;
+    if (tt == 1 && !pair) continue;
+    const int tau = tt ? un1.tau : un0.tau;
+    if (b >= tau && b < max_blocks)
+      scores[(static_cast<size_t>(tt ? u0 + 1 : u0) * nsel + g) * max_blocks + b] =
+          (b == tau) ? pos_inf() : neg_inf();
+  }
+  if (b0 >= tau_max) return;
+  const int nblk = min(kChunk2, tau_max - b0);
+
+  // this wave's tile and its two 32-row MFMA tiles
+  const int tt = wave / 2;
+  const int my_rows = tt ? un1.num_rows : un0.num_rows;
+  const int my_row0 = tt ? un1.row0 : un0.row0;
+  const int my_tau = tt ? un1.tau : un0.tau;
+  const bool wave_live = (tt == 0 || pair) && (wave % 2) * 64 < my_rows;
+  bf16x8 qa[KS], qb[KS];
+  uint32_t valid = 0;                    // bit i: accumulator row of register i is real
+  {
+    const int r0 = (wave % 2) * 64 + (lane % 32), r1 = r0 + 32;
+    const int q0 = my_row0 + min(r0, my_rows - 1);
+    const int q1 = my_row0 + min(r1, my_rows - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int kk = ks * 16 + (lane / 32) * 8;
+      const int h = g * HS + kk / DI, d = kk % DI;
+      qa[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+          q_idx + (static_cast<size_t>(q0) * Hi + h) * DI + d));
+      qb[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+          q_idx + (static_cast<size_t>(q1) * Hi + h) * DI + d));
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = (i / 4) * 8 + (lane / 32) * 4 + (i % 4);
+      valid |= ((wave % 2) * 64 + row < my_rows ? 1u : 0u) << i;
+      valid |= ((wave % 2) * 64 + 32 + row < my_rows ? 1u : 0u) << (16 + i);
+    }
+  }
+
+  const int32_t *bt = block_table + static_cast<size_t>(un0.r) * max_blocks;
+  auto issue = [&](int b, u32x4 *dst) {
+    const uint16_t *kb = k_idx + static_cast<size_t>(bt[b]) * Hi * kBlk * DI;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int base = (4 * i + wave) * 64;
+      const int p = base + lane, key = p / CHG, c = (p % CHG) ^ (key % CHG);
+      const int h = g * HS + c / CPH, d = (c % CPH) * 8;
+      __builtin_amdgcn_global_load_lds(
+          kb + (static_cast<size_t>(h) * kBlk + key) * DI + d,
+          (__attribute__((address_space(3))) void *)(dst + base), 16, 0, 0);
+    }
+  };
+  auto score = [&](int bi, const u32x4 *src) {
+    const int b = b0 + bi;
+    float m = neg_inf();
+    if (wave_live && b < my_tau) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int key = nt * 32 + lane % 32;
+        f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int c = 2 * ks + lane / 32;
+          const bf16x8 kf = __builtin_bit_cast(bf16x8, src[key * CHG + (c ^ (key % CHG))]);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], kf, acc1, 0, 0, 0);
+        }
+        if (valid == 0xffffffffu) {
+#pragma unroll
+          for (int i = 0; i < 16; i += 2)
+            m = fmaxf(fmaxf(m, fmaxf(acc0[i], acc0[i + 1])), fmaxf(acc1[i], acc1[i + 1]));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            if (valid & (1u << i)) m = fmaxf(m, acc0[i]);
+            if (valid & (1u << (16 + i))) m = fmaxf(m, acc1[i]);
+          }
+        }
+      }
+    }
+    m = group_max<kWave>(m);
+    if (lane == 0) red[wave][bi] = m;
+  };
+
+  issue(b0, Kb0);
+  for (int bi = 0;;) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this block's keys landed
+    __syncthreads();
+    if (bi + 1 < nblk) issue(b0 + bi + 1, Kb1);
+    score(bi, Kb0);
+    if (++bi >= nblk) break;
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    if (bi + 1 < nblk) issue(b0 + bi + 1, Kb0);
+    score(bi, Kb1);
+    if (++bi >= nblk) break;
+  }
+  __syncthreads();
+  // finished rows: tile 0 owns blocks b < tau0, tile 1 blocks b < tau1
+  for (int e = t; e < 2 * nblk; e += 256) {
+    const int tile = e / nblk, bi = e % nblk, b = b0 + bi;
+    if (tile == 1 && !pair) continue;
+    if (b >= (tile ? un1.tau : un0.tau)) continue;
+    scores[(static_cast<size_t>(tile ? u0 + 1 : u0) * nsel + g) * max_blocks + b] =
+        fmaxf(red[2 * tile][bi], red[2 * tile + 1][bi]);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // prefill, fp32: plain FMA, one work-group of 128 threads per (unit, group, block)
 // ---------------------------------------------------------------------------
@@ -243,17 +398,33 @@ hipError_t dispatch_decode_hs(const Geom &g, const msa_cache_t &c, const void *q
 template <int DI>
 hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                  const void *q_idx, float *scores, hipStream_t st) {
-  const dim3 grid(b.total_units, (c.max_blocks_per_seq + kChunk - 1) / kChunk, g.nsel);
   const uint16_t *q = static_cast<const uint16_t *>(q_idx);
   const uint16_t *k = static_cast<const uint16_t *>(c.k_idx_cache);
-  switch (g.Hs()) {
+  const int hs = g.Hs();
+  if (hs * DI <= 128) {
+    const dim3 grid(b.total_units, (c.max_blocks_per_seq + kChunk2 - 1) / kChunk2, g.nsel);
+    switch (hs) {
 #define MSA_CASE(HS)                                                                     \
   case HS:                                                                               \
-    if (HS * DI > 512) return hipErrorInvalidValue;                                      \
-    index_prefill_bf16_kernel<DI, HS><<<grid, 256, 0, st>>>(                             \
+    if constexpr (HS * DI <= 128)                                                        \
+      index_prefill_bf16_kernel<DI, HS><<<grid, 256, 0, st>>>(                           \
+          q, k, c.block_table, b.units, b.total_units, c.max_blocks_per_seq, g.nsel,     \
+          scores);                                                                       \
+    break;
+      MSA_CASE(1) MSA_CASE(2) MSA_CASE(4)
+#undef MSA_CASE
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  const dim3 grid(b.total_units, (c.max_blocks_per_seq + kChunk - 1) / kChunk, g.nsel);
+  switch (hs) {
+#define MSA_CASE(HS)                                                                     \
+  case HS:                                                                               \
+    index_prefill_wide_kernel<DI, HS><<<grid, 256, 0, st>>>(                             \
         q, k, c.block_table, b.units, c.max_blocks_per_seq, g.nsel, scores);             \
     break;
-    MSA_CASE(1) MSA_CASE(2) MSA_CASE(4) MSA_CASE(8)
+    MSA_CASE(2) MSA_CASE(4) MSA_CASE(8)
 #undef MSA_CASE
     default: return hipErrorInvalidValue;
   }
