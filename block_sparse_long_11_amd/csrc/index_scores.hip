@@ -192,22 +192,27 @@ __global__ __launch_bounds__(256) void index_prefill_wide_kernel(
 // prefill, bf16, group width <= 128: MFMA 32x32x16 on LDS-staged keys
 // ---------------------------------------------------------------------------
 //
-// A work-group handles two adjacent query tiles of one request (128 query rows
-// each) and one selection group, over a chunk of kChunk2 candidate blocks. Tiles
-// pair up inside a request: a unit with even tau leads and takes the next unit
-// when it belongs to the same request; a unit with odd tau that opens its request
-// leads alone; every other unit is taken by its leader. Each block's group keys
-// (128 keys x GD, the group's indexer heads side by side) are staged in LDS by
-// direct global->LDS loads, 16-byte chunks XOR-swizzled by key, double-buffered so
-// the next block is in flight while this one is scored. Wave w owns 64 rows (two
-// 32-row MFMA tiles) of tile w/2: every key fragment read from LDS feeds two
-// MFMAs. A = query rows in registers, B = key rows from LDS; the accumulators are
-// max-pooled straight away (the layout of a max does not matter).
+// A work-group handles up to kTiles adjacent query tiles of one request (128
+// query rows each) and one selection group, over a chunk of kChunk2 candidate
+// blocks. Tiles are grouped inside a request: a unit whose tau is a multiple of
+// kTiles, or that opens its request, leads; it takes the following units of the
+// same request until the next leader. Each block's group keys (128 keys x GD, the
+// group's indexer heads side by side) are staged in LDS by direct global->LDS
+// loads, 16-byte chunks XOR-swizzled by key, double-buffered so the next block is
+// in flight while this one is scored; one staged block serves every query row of
+// the group. Wave w owns 64 rows (two 32-row MFMA tiles) of tile w/2: every key
+// fragment read from LDS feeds two MFMAs. A = query rows in registers, B = key
+// rows from LDS; the accumulators are max-pooled straight away (the layout of a
+// max does not matter).
 
 constexpr int kChunk2 = 16;   // blocks per work-group
+// Query tiles per work-group. Two (256 query rows, 4 waves, two work-groups per
+// CU) measured twice as fast on MI355X as four (512 rows, 8 waves, one per CU).
+constexpr int kTiles = 2;
+constexpr int kIdxThreads = kTiles * 2 * kWave;
 
 template <int DI, int HS>
-__global__ __launch_bounds__(256) void index_prefill_bf16_kernel(
+__global__ __launch_bounds__(kIdxThreads) void index_prefill_bf16_kernel(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const int32_t *__restrict__ block_table, const msa_unit_t *__restrict__ units,
     int num_units, int max_blocks, int nsel, float *__restrict__ scores) {
@@ -215,29 +220,31 @@ __global__ __launch_bounds__(256) void index_prefill_bf16_kernel(
   constexpr int KS = GD / 16;            // k steps
   constexpr int CHG = GD / 8;            // 16-byte chunks per staged key row
   constexpr int CPH = DI / 8;            // chunks per head
-  constexpr int NLD = kBlk * CHG / 256;  // direct loads per thread per block
-  static_assert(GD <= 128 && NLD >= 1, "group width");
+  constexpr int NW = kIdxThreads / kWave;
+  constexpr int NLD = (kBlk * CHG + kIdxThreads - 1) / kIdxThreads;
+  static_assert(GD <= 128, "group width");
   __shared__ u32x4 Kb0[kBlk * CHG], Kb1[kBlk * CHG];
-  __shared__ float red[4][kChunk2];
+  __shared__ float red[NW][kChunk2];
 
   const int u0 = blockIdx.x, g = blockIdx.z;
   const msa_unit_t un0 = units[u0];
   const bool first = (u0 == 0) || (units[u0 - 1].r != un0.r);
-  if ((un0.tau & 1) && !first) return;           // taken by its leader
-  const bool pair = !(un0.tau & 1) && (u0 + 1 < num_units) && (units[u0 + 1].r == un0.r);
-  const msa_unit_t un1 = pair ? units[u0 + 1] : un0;
+  if ((un0.tau % kTiles) != 0 && !first) return;          // taken by its leader
+  int ntile = 1;
+  while (ntile < kTiles && u0 + ntile < num_units && units[u0 + ntile].r == un0.r &&
+         (units[u0 + ntile].tau % kTiles) != 0)
+    ++ntile;
   const int Hi = nsel * HS;
-  const int tau_max = pair ? un1.tau : un0.tau;
+  const int tau_max = units[u0 + ntile - 1].tau;
   const int b0 = blockIdx.y * kChunk2;
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
 
-  // the +inf / -inf entries of both tiles inside this chunk
-  for (int e = t; e < 2 * kChunk2; e += 256) {
+  // the +inf / -inf entries of every tile inside this chunk
+  for (int e = t; e < ntile * kChunk2; e += kIdxThreads) {
     const int tt = e / kChunk2, b = b0 + e % kChunk2;
-    if (tt == 1 && !pair) continue;
-    const int tau = tt ? un1.tau : un0.tau;
+    const int tau = units[u0 + tt].tau;
     if (b >= tau && b < max_blocks)
-      scores[(static_cast<size_t>(tt ? u0 + 1 : u0) * nsel + g) * max_blocks + b] =
+      scores[(static_cast<size_t>(u0 + tt) * nsel + g) * max_blocks + b] =
           (b == tau) ? pos_inf() : neg_inf();
   }
   if (b0 >= tau_max) return;
@@ -245,16 +252,15 @@ __global__ __launch_bounds__(256) void index_prefill_bf16_kernel(
 
   // this wave's tile and its two 32-row MFMA tiles
   const int tt = wave / 2;
-  const int my_rows = tt ? un1.num_rows : un0.num_rows;
-  const int my_row0 = tt ? un1.row0 : un0.row0;
-  const int my_tau = tt ? un1.tau : un0.tau;
-  const bool wave_live = (tt == 0 || pair) && (wave % 2) * 64 < my_rows;
+  const bool tile_live = tt < ntile;
+  const msa_unit_t mine = units[u0 + (tile_live ? tt : 0)];
+  const bool wave_live = tile_live && (wave % 2) * 64 < mine.num_rows;
   bf16x8 qa[KS], qb[KS];
   uint32_t valid = 0;                    // bit i: accumulator row of register i is real
   {
     const int r0 = (wave % 2) * 64 + (lane % 32), r1 = r0 + 32;
-    const int q0 = my_row0 + min(r0, my_rows - 1);
-    const int q1 = my_row0 + min(r1, my_rows - 1);
+    const int q0 = mine.row0 + min(r0, mine.num_rows - 1);
+    const int q1 = mine.row0 + min(r1, mine.num_rows - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int kk = ks * 16 + (lane / 32) * 8;
@@ -267,38 +273,44 @@ __global__ __launch_bounds__(256) void index_prefill_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = (i / 4) * 8 + (lane / 32) * 4 + (i % 4);
-      valid |= ((wave % 2) * 64 + row < my_rows ? 1u : 0u) << i;
-      valid |= ((wave % 2) * 64 + 32 + row < my_rows ? 1u : 0u) << (16 + i);
+      valid |= ((wave % 2) * 64 + row < mine.num_rows ? 1u : 0u) << i;
+      valid |= ((wave % 2) * 64 + 32 + row < mine.num_rows ? 1u : 0u) << (16 + i);
     }
   }
 
   const int32_t *bt = block_table + static_cast<size_t>(un0.r) * max_blocks;
-  auto issue = [&](int b, u32x4 *dst) {
+  auto issue = [&](int b, u32x4 *dst) __attribute__((always_inline)) {
     const uint16_t *kb = k_idx + static_cast<size_t>(bt[b]) * Hi * kBlk * DI;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int base = (4 * i + wave) * 64;
-      const int p = base + lane, key = p / CHG, c = (p % CHG) ^ (key % CHG);
-      const int h = g * HS + c / CPH, d = (c % CPH) * 8;
-      __builtin_amdgcn_global_load_lds(
-          kb + (static_cast<size_t>(h) * kBlk + key) * DI + d,
-          (__attribute__((address_space(3))) void *)(dst + base), 16, 0, 0);
+      const int base = (NW * i + wave) * 64;
+      if (base < kBlk * CHG) {
+        const int p = base + lane, key = p / CHG, c = (p % CHG) ^ (key % CHG);
+        const int h = g * HS + c / CPH, d = (c % CPH) * 8;
+        __builtin_amdgcn_global_load_lds(
+            kb + (static_cast<size_t>(h) * kBlk + key) * DI + d,
+            (__attribute__((address_space(3))) void *)(dst + base), 16, 0, 0);
+      }
     }
   };
-  auto score = [&](int bi, const u32x4 *src) {
+  auto score = [&](int bi, const u32x4 *src) __attribute__((always_inline)) {
     const int b = b0 + bi;
     float m = neg_inf();
-    if (wave_live && b < my_tau) {
+    if (wave_live && b < mine.tau) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int key = nt * 32 + lane % 32;
+        bf16x8 kf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kf[ks] = __builtin_bit_cast(bf16x8,
+                                      src[key * CHG + ((2 * ks + lane / 32) ^ (key % CHG))]);
+        __builtin_amdgcn_sched_barrier(0);  // all fragment reads in flight before the MFMAs
         f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const int c = 2 * ks + lane / 32;
-          const bf16x8 kf = __builtin_bit_cast(bf16x8, src[key * CHG + (c ^ (key % CHG))]);
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], kf, acc1, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], kf[ks], acc1, 0, 0, 0);
         }
         if (valid == 0xffffffffu) {
 #pragma unroll
@@ -331,12 +343,11 @@ __global__ __launch_bounds__(256) void index_prefill_bf16_kernel(
     if (++bi >= nblk) break;
   }
   __syncthreads();
-  // finished rows: tile 0 owns blocks b < tau0, tile 1 blocks b < tau1
-  for (int e = t; e < 2 * nblk; e += 256) {
+  // finished rows: tile t owns blocks b < tau_t
+  for (int e = t; e < ntile * nblk; e += kIdxThreads) {
     const int tile = e / nblk, bi = e % nblk, b = b0 + bi;
-    if (tile == 1 && !pair) continue;
-    if (b >= (tile ? un1.tau : un0.tau)) continue;
-    scores[(static_cast<size_t>(tile ? u0 + 1 : u0) * nsel + g) * max_blocks + b] =
+    if (b >= units[u0 + tile].tau) continue;
+    scores[(static_cast<size_t>(u0 + tile) * nsel + g) * max_blocks + b] =
         fmaxf(red[2 * tile][bi], red[2 * tile + 1][bi]);
   }
 }
@@ -407,7 +418,7 @@ hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_
 #define MSA_CASE(HS)                                                                     \
   case HS:                                                                               \
     if constexpr (HS * DI <= 128)                                                        \
-      index_prefill_bf16_kernel<DI, HS><<<grid, 256, 0, st>>>(                           \
+      index_prefill_bf16_kernel<DI, HS><<<grid, kIdxThreads, 0, st>>>(                   \
           q, k, c.block_table, b.units, b.total_units, c.max_blocks_per_seq, g.nsel,     \
           scores);                                                                       \
     break;

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <string>
 
 #include "msa.h"
@@ -104,6 +105,14 @@ msa_status_t check_batch(const msa_batch_t *b) {
 
 float resolve_scale(float s, int D) { return s > 0.f ? s : 1.0f / std::sqrt(float(D)); }
 
+// Bit-level NaN test: the library is built with -fno-honor-nans, under which
+// `x != x` may be folded away.
+bool is_nan_bits(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, sizeof(u));
+  return (u & 0x7fffffffu) > 0x7f800000u;
+}
+
 }  // namespace
 
 extern "C" {
@@ -186,7 +195,7 @@ msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *
   if (batch->total_units == 0) return ok();     // no queries
   MSA_REQUIRE(q != nullptr && ids != nullptr && out != nullptr, MSA_ERR_INVALID_ARG,
               "q / ids / out is NULL");
-  MSA_REQUIRE(!(softmax_scale != softmax_scale), MSA_ERR_INVALID_ARG, "softmax_scale is NaN");
+  MSA_REQUIRE(!is_nan_bits(softmax_scale), MSA_ERR_INVALID_ARG, "softmax_scale is NaN");
   return hip_status(msa::launch_attn_prefill(g, *cache, *batch, q, ids, topk,
                                              resolve_scale(softmax_scale, g.D), out, lse,
                                              static_cast<hipStream_t>(stream)),
@@ -214,7 +223,7 @@ msa_status_t msa_sparse_attn_decode(const msa_geom_t *geom, const msa_cache_t *c
   MSA_REQUIRE(q != nullptr && ids != nullptr && out != nullptr, MSA_ERR_INVALID_ARG,
               "q / ids / out is NULL");
   MSA_REQUIRE(topk >= 1, MSA_ERR_INVALID_ARG, "topk must be positive");
-  MSA_REQUIRE(!(softmax_scale != softmax_scale), MSA_ERR_INVALID_ARG, "softmax_scale is NaN");
+  MSA_REQUIRE(!is_nan_bits(softmax_scale), MSA_ERR_INVALID_ARG, "softmax_scale is NaN");
   const int s = num_splits > 0 ? (num_splits < topk ? num_splits : topk)
                                : msa::decode_auto_splits(g, cache->num_seqs, topk);
   if (g.bf16) {
