@@ -15,6 +15,7 @@ timed region. `cpu_baseline` times the CPU oracle on a bounded sample of units.
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -31,6 +32,8 @@ import block_sparse_long_11_amd as msa            # noqa: E402
 from block_sparse_long_11_amd import synth         # noqa: E402
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+CSRC = os.path.join(ROOT, "block_sparse_long_11_amd", "csrc")
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 BLK = 128
 
@@ -152,6 +155,23 @@ class Runner:
         return total_ms / steps, per, wall
 
 
+def measured_traffic(kernel_key, source_file):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a plain copy), or
+    None when there is no entry or the kernel's source changed since it was taken."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            summ = json.load(f)
+        e = summ["kernels"][kernel_key]
+        with open(os.path.join(CSRC, source_file), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if sha != e["source_sha256"]:
+            return None
+        return e["hbm_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def measure(w, dev, steps, warmup):
     r = Runner(w, dev)
     ms, per, wall = r.timed(steps, warmup)
@@ -166,7 +186,9 @@ def measure(w, dev, steps, warmup):
         t = per["index_scores"] * 1e-3
         res["roofline"] = dict(kernel="index_scores (decode)", bound="hbm",
                                achieved=nbytes / t / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
-                               frac=nbytes / t / 1e9 / HBM_PEAK_GBS, traffic=None,
+                               frac=nbytes / t / 1e9 / HBM_PEAK_GBS,
+                               traffic=measured_traffic(f"{w.name}:index_decode",
+                                                        "index_scores.hip"),
                                algorithmic_bytes=nbytes)
         # whole decode step against HBM: the algorithmic bytes of all four launches
         kv = tokens * w.head_dim * 2 * 2            # K and V rows of the selected keys
@@ -179,7 +201,9 @@ def measure(w, dev, steps, warmup):
         res["roofline"] = dict(kernel="sparse_attn_prefill", bound="mfma",
                                achieved=flops / t / 1e12, peak=MFMA_BF16_PEAK_TFLOPS,
                                unit="TFLOP/s", frac=flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                               traffic=None, algorithmic_flops=flops)
+                               traffic=measured_traffic(f"{w.name}:attn_prefill",
+                                                        "attn_prefill.hip"),
+                               algorithmic_flops=flops)
     res["_runner"] = r
     return res
 
