@@ -12,18 +12,28 @@
 // s <= pos(t). Only the diagonal block needs the causal test: every other kept
 // block lies entirely before the unit's first query.
 //
-// bf16 path (MFMA 32x32x16, fp32 accumulate). A work-group of 8 waves (two per
-// SIMD, so one wave's softmax arithmetic overlaps the other's MFMAs) owns (unit,
+// bf16 path (MFMA 32x32x16, fp32 accumulate). A work-group of 8 waves owns (unit,
 // KV head j, 2 query heads): 128 token rows x 2 heads, one wave per (head, 32
-// tokens). Per kept block the group stages K ([key][d]) and V ([d][key], the
-// cache's d-major blocks) in LDS by direct global->LDS loads, 16-byte chunks
-// XOR-swizzled by row, into one of two buffers while the other is being read.
-// Per 32-key tile each wave computes
+// tokens); waves w and w + 4 share a SIMD. Per 32-key tile each wave computes
 //   S^T = K . Q^T           (A = K rows from LDS, B = Q held in registers)
 //   O^T += V^T . P^T        (A = V^T rows from LDS, B = P from S^T's registers)
 // The S^T row m of a tile is fed key (m with bits 2 and 3 swapped): then lane
 // half a, register 8h+jj holds key 16h + 8a + jj, which is exactly the k-index
 // the P^T operand needs, so V^T is read in natural key order.
+//
+// Ping-pong: every tile T is split into an MFMA phase M(T) (S^T of tile T and
+// O^T += V^T P^T of tile T-1) and a softmax phase S(T) (mask, row maximum,
+// exponentials, P, and the LDS reads of the operands of M(T+1)). Phases end at
+// work-group barriers, and waves 4..7 run one phase behind waves 0..3, so on
+// every SIMD one wave issues MFMAs while the other does the softmax.
+//
+// K/V staging: half-blocks of 64 keys (K as [key][d], V as the cache's d-major
+// [d][key]) go through a ring of 4 LDS slots by direct global->LDS loads,
+// 16-byte chunks XOR-swizzled by row. Half-block h+3 is requested in S(2h+1),
+// after the last read of the slot it overwrites (half-block h-1, read up to
+// S(2h-1) by the trailing waves); every wave waits for its loads of half-block
+// h+1 at the end of S(2h), two barriers before the first read of it in S(2h+1).
+//
 // Online softmax in log2 units with a lazy reference maximum: O and the row sum
 // are rescaled only when a row's maximum grows by more than 8 (probabilities
 // stay <= 2^8); the result is exact after the final division by the row sum.
@@ -39,8 +49,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// 8 waves of 32 query rows (two per SIMD): measured faster on MI355X than 4 waves
-// (one per SIMD), with or without two 32-row tiles per wave.
 constexpr int kPrefWaves = 8;
 constexpr float kSlack = 8.f;
 
@@ -54,27 +62,72 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, bf16x2));
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+// Work-group barrier between phases. It does not wait for outstanding memory
+// operations (the direct loads are waited for explicitly), and neither the
+// compiler's memory-operation order nor its instruction schedule crosses it.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt vmcnt(n) (n < 16), other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
+
+// Direct global->LDS load of 16 bytes per lane: lane i reads gbase + voff (its
+// own offset) and writes LDS byte address lds + 16 i. Issued as one instruction
+// so that the compiler does not add waits of its own before later LDS reads;
+// completion is waited for explicitly (wait_vm) before a barrier.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(uint32_t lds, const void *gbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+template <int D>
+__global__ __launch_bounds__(kPrefWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vtc, const int32_t *__restrict__ block_table,
     const msa_unit_t *__restrict__ units, const int32_t *__restrict__ ids, int topk,
     int max_blocks, int Hq, int Hkv, int nsel, int num_uj, int pairs, float c,
     uint16_t *__restrict__ out, float *__restrict__ lse) {
+  constexpr int NW = kPrefWaves;
   constexpr int KS = D / 16;              // 16-wide d steps of S^T
   constexpr int DT = D / 32;              // 32-row d tiles of O^T
   constexpr int CH = D / 8;               // 16-byte chunks per K row
   constexpr int NT = NW * kWave;          // threads
-  constexpr int HPW = NW / 4;             // query heads per work-group
-  constexpr int KCH = kBlk * CH / NT;
-  constexpr int VCH = D * 16 / NT;
-  // Two LDS buffers per operand, filled by direct global->LDS loads while the
-  // other one is being read. K: chunk c of row r at c ^ kswz(r), keyed on the
-  // lane that reads row r; V^T: chunk c of row d at c ^ (d % 16).
-  auto kswz = [](int r) { return srow_key(r % 32) % CH; };
-  __shared__ u32x4 Ks0[kBlk * CH], Ks1[kBlk * CH];
-  __shared__ u32x4 Vs0[D * 16], Vs1[D * 16];
+  constexpr int HB = kBlk / 2;            // keys per half-block
+  constexpr int VC = HB / 8;              // 16-byte chunks per V^T row of a half-block
+  constexpr int KCH = HB * CH / NT;       // direct loads per wave per half-block: K
+  constexpr int VCH = D * VC / NT;        //   and V^T
+  constexpr int LPH = KCH + VCH;
+  constexpr int KSLOT = HB * CH * 16;     // bytes of one ring slot: K
+  constexpr int VSLOT = D * VC * 16;      //   and V^T
+  constexpr int VBASE = 4 * KSLOT;        // V^T slots follow the 4 K slots
+  static_assert(HB * CH % NT == 0 && D * VC % NT == 0, "staging split");
+  static_assert(4 * KSLOT <= 65536 && 4 * VSLOT <= 65536, "ds offsets");
+  // Ring of 4 half-block slots. K: chunk c of row r at c ^ (srow_key(r % 32) % CH),
+  // keyed on the lane that reads row r; V^T (rows of 8 chunks): chunk c of row d at
+  // c ^ ((d / 2) % 8), so that the 16 lanes of one LDS pass (16 rows, two per
+  // 256-byte bank line) hit 16 distinct bank groups.
+  __shared__ u32x4 smem[4 * (HB * CH + D * VC)];
+  const char *lds = reinterpret_cast<const char *>(smem);
+  const uint32_t lds_addr = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void *)smem));
 
   // XCD-aware order: the `pairs` work-groups of one (unit, KV head) get ids that
   // are equal mod 8 (same XCD, same L2) and adjacent in that XCD's dispatch order;
@@ -91,16 +144,39 @@ void attn_prefill_bf16_kernel(
   const int32_t *sel = ids + (static_cast<size_t>(u) * nsel + g) * topk;
   const int32_t *bt = block_table + static_cast<size_t>(un.r) * max_blocks;
 
-  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+  const int t = threadIdx.x, lane = t % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
   const int a = lane / 32, n = lane % 32;
-  const int hl = HPW * hp + wave / 4;     // head inside the group
+  const int grp = wave / 4;               // 0 leads, 1 trails by one phase
+  const int hl = 2 * hp + grp;            // head inside the group
   const int slab = wave % 4;              // 32-token slab of the tile
+  // Waves past the group's heads or the unit's rows compute on clamped (valid)
+  // rows like the others and store nothing.
   const bool active = hl < G && slab * 32 < un.num_rows;
   const int head = j * G + min(hl, G - 1);
   const int row_in_tile = slab * 32 + n;
   const bool row_ok = row_in_tile < un.num_rows;
   const int qrow = un.row0 + min(row_in_tile, un.num_rows - 1);
   const int qpos = row_ok ? un.pos0 + row_in_tile : 0x7fffffff;
+
+  // Kept blocks, attended in the order: diagonal block (the last kept id) first,
+  // then the others in id order. Lane p of phys holds the physical block of
+  // position 64 * phys_chunk + p.
+  int nk = 0;
+  while (nk < topk && sel[nk] >= 0) ++nk;
+  if (nk == 0) return;                    // nothing kept (never produced by the selection)
+  const int diag_b = sel[nk - 1];
+  const int NH = 2 * nk;                  // half-blocks
+  int phys_chunk = -1, phys = 0;
+  auto phys_at = [&](int p) __attribute__((always_inline)) {
+    if ((p >> 6) != phys_chunk) {
+      phys_chunk = p >> 6;
+      const int pl = 64 * phys_chunk + lane;
+      phys = pl < nk ? bt[sel[pl == 0 ? nk - 1 : pl - 1]] : 0;
+      wait_vm<0>();   // completes here, so no wait is needed where phys is read
+    }
+    return __builtin_amdgcn_readlane(phys, p & 63);
+  };
 
   bf16x8 qf[KS];
   {
@@ -110,135 +186,180 @@ void attn_prefill_bf16_kernel(
       qf[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(pq + ks * 16));
   }
 
-  // Enqueue the direct loads of block b into (Kd, Vd). Instruction i of wave w
-  // fills LDS chunks (NW i + w) * 64 + lane; each lane fetches the global chunk
-  // that the swizzle places there.
-  auto issue = [&](int b, u32x4 *Kd, u32x4 *Vd) __attribute__((always_inline)) {
-    const size_t off = (static_cast<size_t>(bt[b]) * Hkv + j) * kBlk * D;
+  // Direct loads: instruction i of wave w fills the slot's chunks
+  // (NW i + w) * 64 + lane; each lane fetches the global chunk that the swizzle
+  // places there (byte offsets from the half-block's first K row / V^T column).
+  uint32_t kgo[KCH], vgo[VCH];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int base = (NW * i + wave) * 64;
-      const int p = base + lane, r = p / CH, ch = (p % CH) ^ kswz(r);
-      __builtin_amdgcn_global_load_lds(
-          kc + off + r * D + ch * 8,
-          (__attribute__((address_space(3))) void *)(Kd + base), 16, 0, 0);
-    }
+  for (int i = 0; i < KCH; ++i) {
+    const int p = (NW * i + wave) * 64 + lane, rr = p / CH;
+    kgo[i] = (rr * D + ((p % CH) ^ (srow_key(rr % 32) % CH)) * 8) * 2;
+  }
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int base = (NW * i + wave) * 64;
-      const int p = base + lane, r = p / 16, ch = (p % 16) ^ (r % 16);
-      __builtin_amdgcn_global_load_lds(
-          vtc + off + r * kBlk + ch * 8,
-          (__attribute__((address_space(3))) void *)(Vd + base), 16, 0, 0);
-    }
+  for (int i = 0; i < VCH; ++i) {
+    const int p = (NW * i + wave) * 64 + lane, rr = p / VC;
+    vgo[i] = (rr * kBlk + ((p % VC) ^ ((rr >> 1) % VC)) * 8) * 2;
+  }
+  auto issue = [&](int hb, auto r) __attribute__((always_inline)) {
+    constexpr int R = decltype(r)::value % 4;
+    const size_t off = (static_cast<size_t>(phys_at(hb >> 1)) * Hkv + j) * kBlk * D;
+    const uint16_t *kg = kc + off + (hb & 1) * HB * D;
+    const uint16_t *vg = vtc + off + (hb & 1) * HB;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i)
+      load_lds16(lds_addr + R * KSLOT + (NW * i + wave) * 1024, kg, kgo[i]);
+#pragma unroll
+    for (int i = 0; i < VCH; ++i)
+      load_lds16(lds_addr + VBASE + R * VSLOT + (NW * i + wave) * 1024, vg, vgo[i]);
   };
+
+  // Per-lane LDS byte offsets of the operand fragments inside a slot: K fragment
+  // ks of tile row srow_key(n), and V^T fragment (tile kt2 of the half-block,
+  // 16-key half h) of row n of each 32-row d tile.
+  int koff[KS], voff[4];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = (srow_key(n) * CH + ((2 * ks + a) ^ (n % CH))) * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = VBASE + (n * VC + ((2 * i + a) ^ ((n >> 1) % VC))) * 16;
 
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+  f32x16 s = f32x16{};
+  bf16x8 kf[KS], vf[2 * DT], pf[2];
   float m_ref = neg_inf();                // reference maximum, log2 units
   float l_run = 0.f;                      // this lane's share of the row sum
 
-  // Per 32-key tile: the 8 K fragments and the 8 V^T fragments are read from LDS
-  // into registers first (batched reads, one wait), then S^T = K Q^T, the online
-  // softmax and O^T += V^T P^T.
-  // MASK is true only for the diagonal block: it gets its own copy of the code so
-  // that the other blocks carry no masking work.
-  auto compute = [&](auto mask_tag, int b, const u32x4 *Kb, const u32x4 *Vb)
-                     __attribute__((always_inline)) {
-    constexpr bool diag = decltype(mask_tag)::value;
-    const int lim = qpos - b * kBlk;      // keys with offset > lim are masked
+  auto read_k = [&](auto r, int kt2) __attribute__((always_inline)) {
+    constexpr int R = decltype(r)::value % 4;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int krow = kt * 32 + srow_key(n);
-      const int sw = kswz(krow);          // = n % CH: 8 consecutive lanes hit 8 chunks
-      bf16x8 kf[KS], vf[2 * DT];
+    for (int ks = 0; ks < KS; ++ks)
+      kf[ks] = *reinterpret_cast<const bf16x8 *>(lds + koff[ks] + R * KSLOT + kt2 * 32 * CH * 16);
+  };
+  auto read_v = [&](auto r, int kt2) __attribute__((always_inline)) {
+    constexpr int R = decltype(r)::value % 4;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[ks] = __builtin_bit_cast(bf16x8, Kb[krow * CH + ((2 * ks + a) ^ sw)]);
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int h = 0; h < 2; ++h)
+        vf[2 * dt + h] = *reinterpret_cast<const bf16x8 *>(lds + voff[2 * kt2 + h] + R * VSLOT +
+                                                           dt * 32 * VC * 16);
+  };
+
+  // M phase: S^T = K Q^T of the current tile and O^T += V^T P^T of the previous
+  // one, interleaved so that neither accumulation chain waits on itself.
+  auto mphase = [&](auto pv_tag, auto qk_tag) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
+    if constexpr (QK) s = f32x16{};
+    constexpr int NI = KS > 2 * DT ? KS : 2 * DT;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int d = dt * 32 + n, ch = 4 * kt + 2 * h + a;
-          vf[2 * dt + h] = __builtin_bit_cast(bf16x8, Vb[d * 16 + (ch ^ (d % 16))]);
-        }
-      f32x16 s = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
-      if constexpr (diag) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kt * 32 + 16 * (i / 8) + 8 * a + (i % 8);
-          if (key > lim) s[i] = neg_inf();
-        }
-      }
-      float x = fmaxf(fmaxf(s[0], s[1]), s[2]);
-#pragma unroll
-      for (int i = 3; i < 15; i += 2) x = fmaxf(fmaxf(x, s[i]), s[i + 1]);
-      x = fmaxf(x, s[15]);
-      {   // max with the other half of the wave (same query column)
-        const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
-                                                          __float_as_uint(x), false, false);
-        x = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * c;
-      }
-      const bool need = x > m_ref + kSlack;
-      if (__any(need)) {
-        const float nm = need ? x : m_ref;
-        const float al = __builtin_amdgcn_exp2f(m_ref - nm);
-        m_ref = nm;
-        l_run *= al;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
-      }
-      bf16x8 pf[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t w[4];
-#pragma unroll
-        for (int jj = 0; jj < 8; jj += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj], c, -m_ref));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj + 1], c, -m_ref));
-          w[jj / 2] = cvt_pk_bf16(p0, p1);
-          l_run += p0 + p1;
-        }
-        pf[h] = as_bf16x8(uint4{w[0], w[1], w[2], w[3]});
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[2 * dt + h], pf[h], o[dt], 0, 0, 0);
+    for (int i = 0; i < NI; ++i) {
+      if constexpr (QK)
+        if (i < KS) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i], s, 0, 0, 0);
+      if constexpr (PV)
+        if (i < 2 * DT)
+          o[i / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i % 2], o[i / 2], 0, 0, 0);
     }
   };
 
-  // The diagonal block (the last kept id) is attended first, from buffer 0, with
-  // the causal mask; the other kept blocks then alternate between the buffers.
-  // At the top of each step only that block's loads are outstanding; after the
-  // barrier every wave has finished with the other buffer, which then receives
-  // the next block. The softmax is order-independent, so the order is free.
-  int nk = 0;
-  while (nk < topk && sel[nk] >= 0) ++nk;
-  const std::true_type masked{};
-  const std::false_type plain{};
-  issue(sel[nk - 1], Ks0, Vs0);
-  __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0)
-  __syncthreads();
-  if (nk > 1) issue(sel[0], Ks1, Vs1);
-  if (active) compute(masked, sel[nk - 1], Ks0, Vs0);
-  for (int slot = 0; slot + 1 < nk;) {
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    __syncthreads();
-    if (slot + 2 < nk) issue(sel[slot + 1], Ks0, Vs0);
-    if (active) compute(plain, sel[slot], Ks1, Vs1);
-    if (++slot + 1 >= nk) break;
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    __syncthreads();
-    if (slot + 2 < nk) issue(sel[slot + 1], Ks1, Vs1);
-    if (active) compute(plain, sel[slot], Ks0, Vs0);
-    ++slot;
+  // Softmax of tile kt (0..3) of a block; masked for the diagonal block.
+  auto softmax = [&](auto mask_tag, int kt) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if constexpr (MASK) {
+      const int lim = qpos - diag_b * kBlk - kt * 32;   // tile keys with offset > lim are masked
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (16 * (i / 8) + 8 * a + (i % 8) > lim) s[i] = neg_inf();
+    }
+    float x = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) x = fmaxf(fmaxf(x, s[i]), s[i + 1]);
+    x = fmaxf(x, s[15]);
+    {   // max with the other half of the wave (same query column)
+      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+      x = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * c;
+    }
+    const bool need = x > m_ref + kSlack;
+    if (__any(need)) {
+      const float nm = need ? x : m_ref;
+      const float al = __builtin_amdgcn_exp2f(m_ref - nm);
+      m_ref = nm;
+      l_run *= al;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w[4];
+#pragma unroll
+      for (int jj = 0; jj < 8; jj += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj], c, -m_ref));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj + 1], c, -m_ref));
+        w[jj / 2] = cvt_pk_bf16(p0, p1);
+        l_run += p0 + p1;
+      }
+      pf[h] = as_bf16x8(uint4{w[0], w[1], w[2], w[3]});
+    }
+  };
+
+  // Tiles 4 bp .. 4 bp + 3 of block position bp, whose half-blocks sit in ring
+  // slots R0 and R0 + 1; the next block's are R0 + 2 and R0 + 3.
+  auto block_step = [&](auto mask_tag, auto r0, int bp) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int R0 = decltype(r0)::value;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int T = 4 * bp + kt;
+      if (MASK && kt == 0)
+        mphase(std::false_type{}, std::true_type{});     // first tile: no previous P
+      else
+        mphase(std::true_type{}, std::true_type{});
+      phase_barrier();
+      if (kt == 0) read_k(ic<R0>{}, 1);
+      else if (kt == 1) read_k(ic<R0 + 1>{}, 0);
+      else if (kt == 2) read_k(ic<R0 + 1>{}, 1);
+      else if (T + 1 < 4 * nk) read_k(ic<R0 + 2>{}, 0);
+      if (kt < 2) read_v(ic<R0>{}, kt);
+      else read_v(ic<R0 + 1>{}, kt - 2);
+      softmax(mask_tag, kt);
+      if (kt == 1) {
+        if (2 * bp + 3 < NH) issue(2 * bp + 3, ic<R0 + 3>{});
+      } else if (kt == 3) {
+        if (2 * bp + 4 < NH) issue(2 * bp + 4, ic<R0 + 4>{});
+      } else {
+        const int hb = 2 * bp + kt / 2 + 1;   // first read in S(T + 1)
+        if (hb < NH) {
+          if (hb + 1 < NH) wait_vm<LPH>();    // half-block hb + 1 may stay in flight
+          else wait_vm<0>();
+        }
+      }
+      phase_barrier();
+    }
+  };
+
+  // Prologue: half-blocks 0..2 requested, 0 waited for, K of tile 0 read.
+  issue(0, ic<0>{});
+  issue(1, ic<1>{});
+  if (NH > 2) {
+    issue(2, ic<2>{});
+    wait_vm<2 * LPH>();
+  } else {
+    wait_vm<LPH>();
   }
+  phase_barrier();
+  read_k(ic<0>{}, 0);
+  if (grp == 1) phase_barrier();
+
+  block_step(std::true_type{}, ic<0>{}, 0);
+  for (int bp = 1; bp < nk; bp += 2) {
+    block_step(std::false_type{}, ic<2>{}, bp);
+    if (bp + 1 >= nk) break;
+    block_step(std::false_type{}, ic<0>{}, bp + 1);
+  }
+  mphase(std::true_type{}, std::false_type{});          // O^T += V^T P^T of the last tile
+  if (grp == 0) phase_barrier();
+
   if (!active) return;
   float sum;
   {
@@ -354,11 +475,11 @@ hipError_t launch_attn_prefill(const Geom &g, const msa_cache_t &c, const msa_ba
   uint16_t *ob = static_cast<uint16_t *>(out);
   const float sl2 = scale * kLog2e;
   if (g.D == 64)
-    attn_prefill_bf16_kernel<64, NW><<<grid, NW * 64, 0, st>>>(
+    attn_prefill_bf16_kernel<64><<<grid, NW * 64, 0, st>>>(
         qb, kb, vb, c.block_table, b.units, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
         g.nsel, num_uj, pairs, sl2, ob, lse);
   else
-    attn_prefill_bf16_kernel<128, NW><<<grid, NW * 64, 0, st>>>(
+    attn_prefill_bf16_kernel<128><<<grid, NW * 64, 0, st>>>(
         qb, kb, vb, c.block_table, b.units, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
         g.nsel, num_uj, pairs, sl2, ob, lse);
   return hipGetLastError();
