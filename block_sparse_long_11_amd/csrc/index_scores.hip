@@ -196,23 +196,27 @@ __global__ __launch_bounds__(256) void index_prefill_wide_kernel(
 // query rows each) and one selection group, over a chunk of kChunk2 candidate
 // blocks. Tiles are grouped inside a request: a unit whose tau is a multiple of
 // kTiles, or that opens its request, leads; it takes the following units of the
-// same request until the next leader. Each block's group keys (128 keys x GD, the
-// group's indexer heads side by side) are staged in LDS by direct global->LDS
-// loads, 16-byte chunks XOR-swizzled by key, double-buffered so the next block is
-// in flight while this one is scored; one staged block serves every query row of
-// the group. Wave w owns 64 rows (two 32-row MFMA tiles) of tile w/2: every key
-// fragment read from LDS feeds two MFMAs. A = query rows in registers, B = key
-// rows from LDS; the accumulators are max-pooled straight away (the layout of a
-// max does not matter).
+// same request until the next leader. Work-group ids visit the even units first
+// (block ids are spread over the XCDs round-robin, and the leaders are normally
+// the even units, so this keeps every XCD busy). Each block's group keys (128
+// keys x GD, the group's indexer heads side by side) are staged in LDS by direct
+// global->LDS loads, 16-byte chunks XOR-swizzled by key, double-buffered so the
+// next block is in flight while this one is scored; one staged block serves every
+// query row of the group. Wave w owns 64 rows (two 32-row MFMA tiles) of tile
+// w/2: every key fragment read from LDS feeds two MFMAs. A = query rows in
+// registers, B = key rows from LDS. Per 32-key sub-tile the two MFMA chains run
+// one after the other, each accumulator max-pooled while the other chain runs,
+// and the next sub-tile's fragments are read meanwhile. Rows past a unit's end
+// repeat its last row, so they never change a maximum.
 
 constexpr int kChunk2 = 16;   // blocks per work-group
-// Query tiles per work-group. Two (256 query rows, 4 waves, two work-groups per
-// CU) measured twice as fast on MI355X as four (512 rows, 8 waves, one per CU).
+// Query tiles per work-group: two (256 query rows, 4 waves, two work-groups per CU).
 constexpr int kTiles = 2;
 constexpr int kIdxThreads = kTiles * 2 * kWave;
 
 template <int DI, int HS>
-__global__ __launch_bounds__(kIdxThreads) void index_prefill_bf16_kernel(
+__global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void index_prefill_bf16_kernel(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const int32_t *__restrict__ block_table, const msa_unit_t *__restrict__ units,
     int num_units, int max_blocks, int nsel, float *__restrict__ scores) {
@@ -226,7 +230,10 @@ __global__ __launch_bounds__(kIdxThreads) void index_prefill_bf16_kernel(
   __shared__ u32x4 Kb0[kBlk * CHG], Kb1[kBlk * CHG];
   __shared__ float red[NW][kChunk2];
 
-  const int u0 = blockIdx.x, g = blockIdx.z;
+  const int half = (num_units + 1) / 2;
+  const int u0 = 2 * (static_cast<int>(blockIdx.x) % half) + static_cast<int>(blockIdx.x) / half;
+  if (u0 >= num_units) return;
+  const int g = blockIdx.z;
   const msa_unit_t un0 = units[u0];
   const bool first = (u0 == 0) || (units[u0 - 1].r != un0.r);
   if ((un0.tau % kTiles) != 0 && !first) return;          // taken by its leader
@@ -256,7 +263,6 @@ __global__ __launch_bounds__(kIdxThreads) void index_prefill_bf16_kernel(
   const msa_unit_t mine = units[u0 + (tile_live ? tt : 0)];
   const bool wave_live = tile_live && (wave % 2) * 64 < mine.num_rows;
   bf16x8 qa[KS], qb[KS];
-  uint32_t valid = 0;                    // bit i: accumulator row of register i is real
   {
     const int r0 = (wave % 2) * 64 + (lane % 32), r1 = r0 + 32;
     const int q0 = mine.row0 + min(r0, mine.num_rows - 1);
@@ -269,12 +275,6 @@ __global__ __launch_bounds__(kIdxThreads) void index_prefill_bf16_kernel(
           q_idx + (static_cast<size_t>(q0) * Hi + h) * DI + d));
       qb[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(
           q_idx + (static_cast<size_t>(q1) * Hi + h) * DI + d));
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = (i / 4) * 8 + (lane / 32) * 4 + (i % 4);
-      valid |= ((wave % 2) * 64 + row < mine.num_rows ? 1u : 0u) << i;
-      valid |= ((wave % 2) * 64 + 32 + row < mine.num_rows ? 1u : 0u) << (16 + i);
     }
   }
 
@@ -297,33 +297,36 @@ __global__ __launch_bounds__(kIdxThreads) void index_prefill_bf16_kernel(
     const int b = b0 + bi;
     float m = neg_inf();
     if (wave_live && b < mine.tau) {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      bf16x8 kf[2][KS];
+      f32x16 acc0, acc1;
+      auto rd = [&](int nt, bf16x8 *dst) __attribute__((always_inline)) {
         const int key = nt * 32 + lane % 32;
-        bf16x8 kf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          kf[ks] = __builtin_bit_cast(bf16x8,
-                                      src[key * CHG + ((2 * ks + lane / 32) ^ (key % CHG))]);
-        __builtin_amdgcn_sched_barrier(0);  // all fragment reads in flight before the MFMAs
-        f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+          dst[ks] = __builtin_bit_cast(bf16x8,
+                                       src[key * CHG + ((2 * ks + lane / 32) ^ (key % CHG))]);
+      };
+      auto pool = [&](const f32x16 &v) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], kf[ks], acc1, 0, 0, 0);
-        }
-        if (valid == 0xffffffffu) {
+        for (int i = 0; i < 16; i += 2) m = fmaxf(m, fmaxf(v[i], v[i + 1]));
+      };
+      rd(0, kf[0]);
 #pragma unroll
-          for (int i = 0; i < 16; i += 2)
-            m = fmaxf(fmaxf(m, fmaxf(acc0[i], acc0[i + 1])), fmaxf(acc1[i], acc1[i + 1]));
-        } else {
+      for (int nt = 0; nt < 4; ++nt) {
+        const int cb = nt & 1;
+        if (nt < 3) rd(nt + 1, kf[cb ^ 1]);
+        acc0 = f32x16{};
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            if (valid & (1u << i)) m = fmaxf(m, acc0[i]);
-            if (valid & (1u << (16 + i))) m = fmaxf(m, acc1[i]);
-          }
-        }
+        for (int ks = 0; ks < KS; ++ks)
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[cb][ks], acc0, 0, 0, 0);
+        if (nt > 0) pool(acc1);
+        acc1 = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], kf[cb][ks], acc1, 0, 0, 0);
+        pool(acc0);
       }
+      pool(acc1);
     }
     m = group_max<kWave>(m);
     if (lane == 0) red[wave][bi] = m;

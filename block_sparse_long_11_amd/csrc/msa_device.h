@@ -38,18 +38,43 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-template <int W>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < W; o <<= 1) v += __shfl_xor(v, o, kWave);
+// Reductions over aligned groups of W consecutive lanes (W a power of two up to 64),
+// without LDS round trips: DPP moves inside rows of 16 lanes (quad permutations,
+// then the half-row and row mirrors, which pair the already reduced quads and
+// halves), then the row swaps of v_permlane16_swap / v_permlane32_swap.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+template <int W, typename Op>
+__device__ __forceinline__ float group_reduce(float v, Op op) {
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "group width");
+  if constexpr (W >= 2) v = op(v, dpp_move<0xB1>(v));    // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) v = op(v, dpp_move<0x4E>(v));    // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) v = op(v, dpp_move<0x141>(v));   // row_half_mirror
+  if constexpr (W >= 16) v = op(v, dpp_move<0x140>(v));  // row_mirror
+  if constexpr (W >= 32) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                     false, false);
+    v = op(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+  if constexpr (W >= 64) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                     false, false);
+    v = op(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
   return v;
 }
 
 template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  return group_reduce<W>(v, [](float x, float y) { return x + y; });
+}
+
+template <int W>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = 1; o < W; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return group_reduce<W>(v, [](float x, float y) { return fmaxf(x, y); });
 }
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
