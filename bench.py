@@ -263,7 +263,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="prefill_32k", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--second", default="decode_1m_b8",
                     help="second workload measured in the same run ('none' to skip)")
