@@ -37,6 +37,18 @@ Where the pages leave a step open this module takes these readings:
 Cache layout (block-major, paged): cache[phys_block][head][token_in_block][dim],
 block_table[r][logical_block] = phys_block, seq_lens[r] = tokens of request r
 including its new ones.
+
+New tokens before the steps above (qk_norm_rope_insert), from [feat] rows "QK
+normalization" (queries and keys each go through a per-head RMSNorm before the
+rotary embedding) and "Partial RoPE" (partial_rotary_factor 0.5, rotary_dim 64:
+only the first rotary_dim channels of each head are rotated, the rest pass
+through) and [dd] "Serving options" (fused QK-norm + RoPE + KV insert). Readings:
+  * RMSNorm of a head vector x (its head_dim channels): x / sqrt(mean(x^2) + eps)
+    times a weight vector of length head_dim shared by all heads; eps is given;
+  * rotation of position p: channel i < rotary_dim/2 pairs with i + rotary_dim/2
+    (the rotate-half form), angle p * theta**(-2 i / rotary_dim), theta given;
+  * K is normalized and rotated before it is written to the cache, V and the
+    indexer keys are written as given; q_idx is not touched.
 """
 
 import math
@@ -272,3 +284,72 @@ def run_decode(q, q_idx, k_cache, v_cache, k_idx_cache, block_table, seq_lens, n
     out, lse = attention(units, ids, q, k_cache, v_cache, block_table, seq_lens, n_sel,
                          scale)
     return dict(units=units, scores=scores, ids=ids, out=out, lse=lse)
+
+
+# ----------------------------------------------------------------------------
+# new tokens: QK-norm, partial RoPE and cache insert
+# ----------------------------------------------------------------------------
+
+def rms_norm(x, w, eps):
+    """RMSNorm over the last axis ([feat] "QK normalization": per head)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(w, dtype=np.float64)
+
+
+def rope(x, pos, theta, rotary_dim):
+    """Rotary embedding of the first rotary_dim channels of x[..., T, H, D]-like
+    arrays whose leading axis is the token axis; pos[T] are the token positions
+    ([feat] "Partial RoPE": channel i pairs with i + rotary_dim/2)."""
+    x = np.asarray(x, dtype=np.float64)
+    half = rotary_dim // 2
+    inv = float(theta) ** (-2.0 * np.arange(half, dtype=np.float64) / rotary_dim)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv[None, :]        # [T][half]
+    shape = (ang.shape[0],) + (1,) * (x.ndim - 2) + (half,)
+    c, s = np.cos(ang).reshape(shape), np.sin(ang).reshape(shape)
+    out = x.copy()
+    x1, x2 = x[..., :half], x[..., half:rotary_dim]
+    out[..., :half] = x1 * c - x2 * s
+    out[..., half:rotary_dim] = x2 * c + x1 * s
+    return out
+
+
+def token_positions(units):
+    """(row, request, position) of every new token of the units, in row order."""
+    rows = []
+    for u in units:
+        for i in range(u["row1"] - u["row0"]):
+            rows.append((u["row0"] + i, u["r"], u["pos0"] + i))
+    rows.sort()
+    return rows
+
+
+def qk_norm_rope_insert(units, q, k, v, k_idx, q_norm_w, k_norm_w, eps, theta, rotary_dim,
+                        k_cache, v_cache, k_idx_cache, block_table):
+    """Normalize and rotate the new queries and keys; write K, V and the indexer
+    keys of every new token into copies of the caches (token-major layout
+    cache[phys][head][row][dim]). Token at row t, request r, position p goes to
+    physical block block_table[r][p // 128], row p % 128.
+
+    Returns (q_out [T][H_q][D], k_cache, v_cache, k_idx_cache), all float64."""
+    toks = token_positions(units)
+    rows = np.array([t[0] for t in toks], dtype=np.int64)
+    pos = np.array([t[2] for t in toks], dtype=np.float64)
+    q_out = rope(rms_norm(np.asarray(q, np.float64)[rows], q_norm_w, eps), pos, theta,
+                 rotary_dim)
+    k_new = rope(rms_norm(np.asarray(k, np.float64)[rows], k_norm_w, eps), pos, theta,
+                 rotary_dim)
+    kc = np.array(k_cache, dtype=np.float64)
+    vc = np.array(v_cache, dtype=np.float64)
+    ic = np.array(k_idx_cache, dtype=np.float64)
+    v64 = np.asarray(v, np.float64)
+    i64 = np.asarray(k_idx, np.float64)
+    for n, (row, r, p) in enumerate(toks):
+        phys = int(block_table[r][p // BLOCK])
+        kc[phys, :, p % BLOCK, :] = k_new[n]
+        vc[phys, :, p % BLOCK, :] = v64[row]
+        ic[phys, :, p % BLOCK, :] = i64[row]
+    q_full = np.zeros(np.asarray(q).shape, dtype=np.float64)
+    q_full[rows] = q_out
+    return q_full, kc, vc, ic
+

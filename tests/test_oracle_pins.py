@@ -446,3 +446,131 @@ def test_planted_pins_would_catch_a_transposed_group():
     wrong = max(float(np.max(qi[t, 0::2].reshape(-1) @ O.logical_block(ki, bt[0], 0, slice(0, 4, 2))
                              .reshape(BLK, -1).T)) for t in range(un["row0"], un["row1"]))
     assert wrong != 0.0
+
+
+# ---------------------------------------------------------------------------
+# QK-norm, partial RoPE and cache insert (the new-token step before the path)
+# ---------------------------------------------------------------------------
+
+def _golden_qk():
+    with open(os.path.join(GOLDEN, "qk_norm_rope.json")) as f:
+        return json.load(f)
+
+
+def test_rms_norm_golden():
+    for case in _golden_qk()["rms_norm"]:
+        got = O.rms_norm(np.array(case["x"]), np.array(case["w"]), case["eps"])
+        np.testing.assert_allclose(got, case["out"], rtol=1e-15, atol=1e-15)
+
+
+def test_rope_golden():
+    for case in _golden_qk()["rope"]:
+        x = np.array(case["x"], dtype=np.float64)[None, None, :]
+        got = O.rope(x, np.array([case["pos"]]), case["theta"], case["rotary_dim"])[0, 0]
+        np.testing.assert_allclose(got, case["out"], rtol=1e-15, atol=1e-15)
+
+
+def test_rms_norm_unit_rms_and_scale_invariance():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((5, 3, 64))
+    y = O.rms_norm(x, np.ones(64), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(O.rms_norm(7.5 * x, np.ones(64), 0.0), y, rtol=1e-13)
+    # a large eps shrinks every output towards zero
+    assert np.max(np.abs(O.rms_norm(x, np.ones(64), 1e12))) < 1e-4
+
+
+def test_rope_matches_complex_rotation():
+    """Independent formulation: channels (i, i + r/2) as the complex number
+    x_i + 1j * x_{i + r/2}, multiplied by exp(1j * p * theta^(-2i/r))."""
+    rng = np.random.default_rng(12)
+    T, H, D, r, theta = 6, 3, 16, 8, 777.0
+    x = rng.standard_normal((T, H, D))
+    pos = rng.integers(0, 10 ** 6, T)
+    got = O.rope(x, pos, theta, r)
+    for t in range(T):
+        for i in range(r // 2):
+            z = complex(x[t, 0, i], x[t, 0, i + r // 2]) * np.exp(
+                1j * pos[t] * theta ** (-2.0 * i / r))
+            assert abs(got[t, 0, i] - z.real) < 1e-9 * max(1.0, abs(z))
+            assert abs(got[t, 0, i + r // 2] - z.imag) < 1e-9 * max(1.0, abs(z))
+    np.testing.assert_array_equal(got[..., r:], x[..., r:])   # pass-through channels
+
+
+def test_rope_rotation_invariants():
+    rng = np.random.default_rng(13)
+    T, D, r, theta = 5, 32, 16, 10000.0
+    q = rng.standard_normal((T, 1, D))
+    k = rng.standard_normal((T, 1, D))
+    m = rng.integers(0, 5000, T).astype(np.float64)
+    n = rng.integers(0, 5000, T).astype(np.float64)
+    zero = np.zeros(T)
+    np.testing.assert_allclose(O.rope(q, zero, theta, r), q, rtol=0, atol=0)
+    back = O.rope(O.rope(q, m, theta, r), -m, theta, r)
+    np.testing.assert_allclose(back, q, atol=1e-10)
+    np.testing.assert_allclose(O.rope(O.rope(q, m, theta, r), n, theta, r),
+                               O.rope(q, m + n, theta, r), atol=1e-9)
+    # the rotary part makes dot products depend on the position difference only
+    lhs = np.sum(O.rope(q, m, theta, r) * O.rope(k, n, theta, r), axis=-1)
+    rhs = np.sum(O.rope(q, m - n, theta, r) * k, axis=-1)
+    np.testing.assert_allclose(lhs, rhs, atol=1e-9)
+    # each rotated pair keeps its length
+    y = O.rope(q, m, theta, r)
+    np.testing.assert_allclose(y[..., :r // 2] ** 2 + y[..., r // 2:r] ** 2,
+                               q[..., :r // 2] ** 2 + q[..., r // 2:r] ** 2, rtol=1e-12)
+
+
+def _insert_case(permute):
+    rng = np.random.default_rng(14)
+    seq_lens, q_lens = [300, 129], [300, 2]
+    Hq, Hkv, D, Hi, Di = 4, 2, 16, 2, 8
+    units = O.prefill_units(seq_lens, q_lens)
+    T = sum(q_lens)
+    nb = [(L + 127) // 128 for L in seq_lens]
+    P = sum(nb)
+    perm = rng.permutation(P)
+    phys = perm if permute else np.arange(P)
+    bt = np.zeros((2, max(nb)), dtype=np.int64)
+    bt[0, :nb[0]] = phys[:nb[0]]
+    bt[1, :nb[1]] = phys[nb[0]:]
+    arrs = dict(q=rng.standard_normal((T, Hq, D)), k=rng.standard_normal((T, Hkv, D)),
+                v=rng.standard_normal((T, Hkv, D)), ki=rng.standard_normal((T, Hi, Di)))
+    caches = [np.full((P, Hkv, 128, D), 9.0), np.full((P, Hkv, 128, D), 8.0),
+              np.full((P, Hi, 128, Di), 7.0)]
+    wq, wk = rng.uniform(0.5, 1.5, D), rng.uniform(0.5, 1.5, D)
+    res = O.qk_norm_rope_insert(units, arrs["q"], arrs["k"], arrs["v"], arrs["ki"], wq, wk,
+                                1e-6, 5e5, 8, caches[0], caches[1], caches[2], bt)
+    return units, arrs, caches, (wq, wk), bt, res
+
+
+def test_insert_places_rows_and_leaves_the_rest():
+    units, arrs, caches, (wq, wk), bt, (q_out, kc, vc, ic) = _insert_case(False)
+    toks = O.token_positions(units)
+    touched = set()
+    for row, r, p in toks:
+        phys, slot = int(bt[r][p // 128]), p % 128
+        touched.add((phys, slot))
+        np.testing.assert_array_equal(vc[phys, :, slot], arrs["v"][row])
+        np.testing.assert_array_equal(ic[phys, :, slot], arrs["ki"][row])
+        kn = O.rope(O.rms_norm(arrs["k"][row][None], wk, 1e-6), np.array([p]), 5e5, 8)[0]
+        np.testing.assert_allclose(kc[phys, :, slot], kn, rtol=1e-14)
+        qn = O.rope(O.rms_norm(arrs["q"][row][None], wq, 1e-6), np.array([p]), 5e5, 8)[0]
+        np.testing.assert_allclose(q_out[row], qn, rtol=1e-14)
+    for phys in range(kc.shape[0]):
+        for slot in range(128):
+            if (phys, slot) not in touched:
+                assert np.all(kc[phys, :, slot] == 9.0) and np.all(vc[phys, :, slot] == 8.0)
+                assert np.all(ic[phys, :, slot] == 7.0)
+
+
+def test_insert_is_independent_of_physical_placement():
+    u0, _, _, _, bt0, (q0, k0, v0, i0) = _insert_case(False)
+    u1, _, _, _, bt1, (q1, k1, v1, i1) = _insert_case(True)
+    np.testing.assert_array_equal(q0, q1)
+    for r in range(bt0.shape[0]):
+        for b in range(bt0.shape[1]):
+            if r == 1 and b >= 2:
+                continue
+            np.testing.assert_array_equal(k0[bt0[r, b]], k1[bt1[r, b]])
+            np.testing.assert_array_equal(v0[bt0[r, b]], v1[bt1[r, b]])
+            np.testing.assert_array_equal(i0[bt0[r, b]], i1[bt1[r, b]])
