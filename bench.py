@@ -12,6 +12,9 @@ Prints ONE JSON line. `value` is selected-KV tokens per second: the sum over
 `roofline` is for the step's dominant kernel, with its average launch duration
 measured by HIP events recorded on the launch stream around every launch in the
 timed region. `cpu_baseline` times the CPU oracle on a bounded sample of units.
+`qk_norm_rope_insert` times the step that precedes the path (QK-norm, partial
+RoPE and the insert of the new tokens' K, V and indexer keys) on each workload's
+new tokens, per launch, against the HBM peak; it is not part of the step.
 """
 
 import argparse
@@ -208,6 +211,47 @@ def measure(w, dev, steps, warmup):
     return res
 
 
+def insert_bytes(w):
+    """Algorithmic HBM bytes of one msa_qk_norm_rope_insert launch over all new
+    tokens: q, k, v and k_idx read once; q_out, the K and V cache rows and the
+    indexer-key rows written once (the norm weights and the plan are negligible)."""
+    sz = 2 if w.dtype == "bf16" else 4
+    per_token = (w.num_q_heads * w.head_dim + 2 * w.num_kv_heads * w.head_dim
+                 + w.num_idx_heads * w.idx_head_dim)
+    return 2 * w.total_q * per_token * sz
+
+
+def measure_insert(runner, launches=20, warmup=10):
+    """Times msa_qk_norm_rope_insert on the workload's new tokens (partial RoPE over
+    64 of 128 channels): HIP events on the launch stream around every launch."""
+    w, dev = runner.w, runner.dev
+    new = synth.make_new_tokens(w, dev)
+    rope = synth.ROPE
+
+    def launch():
+        msa.msa_qk_norm_rope_insert(runner.geom, runner.cache, runner.batch, new["q"], new["k"],
+                                    new["v"], new["k_idx"], new["q_norm_w"], new["k_norm_w"],
+                                    rope["eps"], rope["theta"], rope["rotary_dim"], runner.out)
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    for a, b in evs:
+        a.record()
+        launch()
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    nbytes = insert_bytes(w)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del new
+    return dict(workload=w.name, new_tokens=w.total_q, rotary_dim=rope["rotary_dim"],
+                us_per_launch=us, algorithmic_bytes=nbytes, achieved=gbs, unit="GB/s",
+                peak=HBM_PEAK_GBS, frac=gbs / HBM_PEAK_GBS)
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of units
 # ----------------------------------------------------------------------------
@@ -299,6 +343,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         cpu = cpu_baseline(w, main_res["_runner"], args.cpu_budget)
+    inserts = [measure_insert(main_res["_runner"])]
+    log(f"{w.name}: insert {inserts[-1]['us_per_launch']:.1f} us")
     del main_res["_runner"]
     torch.cuda.empty_cache()
 
@@ -307,6 +353,8 @@ def main():
         w2 = synth.WORKLOADS[args.second]
         second = measure(w2, dev, args.steps, args.warmup)
         log(f"{w2.name}: {second['ms_per_step']:.3f} ms/step, kernels {second['kernel_ms']}")
+        inserts.append(measure_insert(second["_runner"]))
+        log(f"{w2.name}: insert {inserts[-1]['us_per_launch']:.1f} us")
         del second["_runner"]
         torch.cuda.empty_cache()
 
@@ -338,6 +386,9 @@ def main():
         line["second_workload"] = {k: second[k] for k in (
             "workload", "value", "ms_per_step", "kernel_ms", "roofline", "step_hbm_frac")
             if k in second}
+    # the new-token step before the path (QK-norm + partial RoPE + cache insert),
+    # timed on its own: not part of the step above
+    line["qk_norm_rope_insert"] = inserts
     print(json.dumps(line), flush=True)
 
 

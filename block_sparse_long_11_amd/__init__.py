@@ -76,6 +76,13 @@ EXPORTS = {
                                               ctypes.c_float, ctypes.c_int32, ctypes.c_void_p,
                                               ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p]),
+    "msa_qk_norm_rope_insert": (ctypes.c_int, [ctypes.POINTER(_Geom), ctypes.POINTER(_Cache),
+                                               ctypes.POINTER(_Batch), ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
+                                               ctypes.c_int32, ctypes.c_void_p,
+                                               ctypes.c_void_p]),
     "msa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "msa_last_error": (ctypes.c_char_p, []),
     "msa_version": (ctypes.c_int32, []),
@@ -319,6 +326,36 @@ def msa_sparse_attn_decode(geom: Geometry, cache: Cache, q, ids, topk, out, work
                                         topk, float(softmax_scale), num_splits, _ptr(workspace),
                                         workspace.numel(), _ptr(out), _ptr(lse),
                                         _stream(stream)))
+
+
+def msa_qk_norm_rope_insert(geom: Geometry, cache: Cache, batch, q, k, v, k_idx, q_norm_w,
+                            k_norm_w, eps, rope_theta, rotary_dim, q_out=None, stream=None):
+    """Step 0: QK-norm + partial RoPE of the new tokens; K, V and k_idx go into the
+    caches. batch=None is decode (row r = sequence r at position seq_lens[r]-1).
+    q/q_out [rows][H_q][D] (q_out=None: in place), k/v [rows][H_kv][D],
+    k_idx [rows][H_i][D_i], q_norm_w/k_norm_w [D]."""
+    cache.check(geom)
+    dev, dt = cache.block_table.device, geom.torch_dtype
+    rows = cache.num_seqs if batch is None else batch.total_q
+    if q_out is None:
+        q_out = q
+    for t, name, shape in ((q, "q", (rows, geom.num_q_heads, geom.head_dim)),
+                           (q_out, "q_out", (rows, geom.num_q_heads, geom.head_dim)),
+                           (k, "k", (rows, geom.num_kv_heads, geom.head_dim)),
+                           (v, "v", (rows, geom.num_kv_heads, geom.head_dim)),
+                           (k_idx, "k_idx", (rows, geom.num_idx_heads, geom.idx_head_dim)),
+                           (q_norm_w, "q_norm_w", (geom.head_dim,)),
+                           (k_norm_w, "k_norm_w", (geom.head_dim,))):
+        _need(t, name, dt, len(shape), dev)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+    g, c = geom.c(), cache.c()
+    b = None if batch is None else ctypes.pointer(batch.c())
+    _check(lib().msa_qk_norm_rope_insert(ctypes.byref(g), ctypes.byref(c), b, _ptr(q), _ptr(k),
+                                         _ptr(v), _ptr(k_idx), _ptr(q_norm_w), _ptr(k_norm_w),
+                                         float(eps), float(rope_theta), int(rotary_dim),
+                                         _ptr(q_out), _stream(stream)))
+    return q_out
 
 
 def workspace(nbytes, device):

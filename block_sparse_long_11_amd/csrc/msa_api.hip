@@ -255,4 +255,38 @@ const char *msa_last_error(void) { return g_last_error.c_str(); }
 
 int32_t msa_version(void) { return 1; }
 
+msa_status_t msa_qk_norm_rope_insert(const msa_geom_t *geom, const msa_cache_t *cache,
+                                     const msa_batch_t *batch, const void *q, const void *k,
+                                     const void *v, const void *k_idx, const void *q_norm_w,
+                                     const void *k_norm_w, float eps, float rope_theta,
+                                     int32_t rotary_dim, void *q_out, void *stream) {
+  msa::Geom g;
+  msa_status_t st = check_geom(geom, &g);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache(cache, true, true)) != MSA_OK) return st;
+  if (batch != nullptr) {
+    if ((st = check_batch(batch)) != MSA_OK) return st;
+    if (batch->total_units == 0) return ok();
+  }
+  MSA_REQUIRE(q != nullptr && k != nullptr && v != nullptr && k_idx != nullptr &&
+                  q_out != nullptr,
+              MSA_ERR_INVALID_ARG, "q / k / v / k_idx / q_out is NULL");
+  MSA_REQUIRE(q_norm_w != nullptr && k_norm_w != nullptr, MSA_ERR_INVALID_ARG,
+              "q_norm_w / k_norm_w is NULL");
+  MSA_REQUIRE(!is_nan_bits(eps) && eps >= 0.f && std::isfinite(eps), MSA_ERR_INVALID_ARG,
+              "eps must be finite and >= 0");
+  MSA_REQUIRE(!is_nan_bits(rope_theta) && rope_theta > 0.f && std::isfinite(rope_theta),
+              MSA_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+  const int min_rd = g.bf16 ? 16 : 8;   // two 16-byte lane chunks
+  MSA_REQUIRE(rotary_dim == 0 || (rotary_dim >= min_rd && rotary_dim <= g.D &&
+                                  (rotary_dim & (rotary_dim - 1)) == 0),
+              MSA_ERR_UNSUPPORTED,
+              "rotary_dim %d unsupported (0, or a power of two in [%d, head_dim])", rotary_dim,
+              min_rd);
+  return hip_status(msa::launch_qk_norm_rope_insert(g, *cache, batch, q, k, v, k_idx, q_norm_w,
+                                                    k_norm_w, eps, rope_theta, rotary_dim,
+                                                    q_out, static_cast<hipStream_t>(stream)),
+                    "qk_norm_rope_insert");
+}
+
 }  // extern "C"

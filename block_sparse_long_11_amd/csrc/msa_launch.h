@@ -32,4 +32,10 @@ hipError_t launch_attn_decode(const Geom &g, const msa_cache_t &c, const void *q
                               const int32_t *ids, int topk, float scale, int num_splits,
                               void *workspace, void *out, float *lse, hipStream_t st);
 
+hipError_t launch_qk_norm_rope_insert(const Geom &g, const msa_cache_t &c, const msa_batch_t *b,
+                                      const void *q, const void *k, const void *v,
+                                      const void *k_idx, const void *q_norm_w,
+                                      const void *k_norm_w, float eps, float theta, int rd,
+                                      void *q_out, hipStream_t st);
+
 }  // namespace msa

@@ -41,6 +41,12 @@ BLOCK = 128
 
 # stream ids of the seeded draws
 _T_Q, _T_K, _T_V, _T_QIDX, _T_KIDX, _T_PLANT_POS, _T_PLANT_DIR, _T_PERM = range(8)
+_T_NEW_Q, _T_NEW_K, _T_NEW_V, _T_NEW_KIDX, _T_NORM_W, _T_ROW_SCALE = range(8, 14)
+
+# Rotary settings of the new-token step: rotary_dim 64 of head_dim 128 (partial
+# rotary factor 0.5); eps and theta are not given by the pages, these are the
+# usual RMSNorm epsilon and the original rotary base.
+ROPE = dict(rotary_dim=64, eps=1e-6, theta=10000.0)
 
 
 @dataclasses.dataclass
@@ -250,6 +256,34 @@ def make_inputs(w: Workload, device="cpu", permute=False, chunk_blocks=2048):
     out["q_lens"] = torch.tensor(q_lens, dtype=torch.int32, device=device)
     out["cu_q_lens"] = torch.from_numpy(cu).to(device)
     return out
+
+
+def make_new_tokens(w: Workload, device="cpu", rows=None):
+    """Raw inputs of the new tokens before QK-norm and RoPE, as torch tensors in
+    the workload dtype: q [T][H_q][D], k and v [T][H_kv][D], k_idx [T][H_i][D_i]
+    (T = rows, default the workload's new-token count) and the norm weights
+    q_norm_w, k_norm_w [D].
+
+    Entries are N(0,1); every (token, head) row of q and k is multiplied by
+    exp(N(0, 1/2)) so that rows reach the norm with varied magnitudes. The
+    weights are 1 + N(0, 1/5^2)."""
+    dt = _torch_dtype(w)
+    T = w.total_q if rows is None else rows
+    H_q, H_kv, D = w.num_q_heads, w.num_kv_heads, w.head_dim
+    sc = _gen(w, _T_ROW_SCALE, device)
+
+    def scaled(stream, heads):
+        x = _randn(_gen(w, stream, device), (T, heads, D), device)
+        return (x * torch.exp(0.5 * _randn(sc, (T, heads, 1), device))).to(dt)
+
+    wg = _gen(w, _T_NORM_W, device)
+    return dict(
+        q=scaled(_T_NEW_Q, H_q), k=scaled(_T_NEW_K, H_kv),
+        v=_randn(_gen(w, _T_NEW_V, device), (T, H_kv, D), device).to(dt),
+        k_idx=_randn(_gen(w, _T_NEW_KIDX, device), (T, w.num_idx_heads, w.idx_head_dim),
+                     device).to(dt),
+        q_norm_w=(1.0 + 0.2 * _randn(wg, (D,), device)).to(dt),
+        k_norm_w=(1.0 + 0.2 * _randn(wg, (D,), device)).to(dt))
 
 
 def v_token_major(v_cache: torch.Tensor) -> torch.Tensor:

@@ -85,10 +85,12 @@ typedef struct {
   int32_t dtype;                    /* msa_dtype_t */
 } msa_geom_t;
 
+/* The three caches are written only by msa_qk_norm_rope_insert; every other
+ * call reads them. */
 typedef struct {
-  const void *k_cache;
-  const void *v_cache;
-  const void *k_idx_cache;
+  void *k_cache;
+  void *v_cache;
+  void *k_idx_cache;
   int64_t num_phys_blocks;
   const int32_t *block_table;       /* [num_seqs][max_blocks_per_seq] */
   int32_t max_blocks_per_seq;
@@ -192,6 +194,39 @@ msa_status_t msa_sparse_attn_decode(const msa_geom_t *geom, const msa_cache_t *c
                                     float softmax_scale, int32_t num_splits,
                                     void *workspace, size_t workspace_bytes, void *out,
                                     float *lse, void *stream);
+
+/* Step 0, the new tokens before step 1: per-head RMSNorm of queries and keys,
+ * partial rotary embedding, and the insert of K, V and the indexer keys into the
+ * caches ([feat] table "Checked in its code", rows "QK normalization" and
+ * "Partial RoPE" (partial_rotary_factor 0.5, rotary_dim 64); [dd] "Serving
+ * options": fused QK-norm + RoPE + KV insert). For a new token at position p and
+ * a head vector x (D channels), with R = rotary_dim:
+ *   n[c] = x[c] / sqrt(mean(x^2) + eps) * w[c]        (w = q_norm_w or k_norm_w)
+ *   c < R/2, a = p * rope_theta^(-2c/R):
+ *     y[c] = n[c] cos a - n[c+R/2] sin a;  y[c+R/2] = n[c+R/2] cos a + n[c] sin a
+ *   c >= R: y[c] = n[c]
+ * Angles are formed in fp64; the rest runs in fp32 and is rounded to dtype
+ * (nearest even) once.
+ *   batch    prefill: the planned batch (msa_prefill_plan), token t of unit u is
+ *            row u.row0 + t at position u.pos0 + t; NULL: decode, the one new
+ *            token of sequence r is row r at position seq_lens[r] - 1
+ *   q        [rows][H_q][D]        -> q_out [rows][H_q][D] (may equal q: in place)
+ *   k        [rows][H_kv][D]       -> k_cache rows, normalized and rotated
+ *   v        [rows][H_kv][D]       -> v_cache (d-major blocks), unchanged bits
+ *   k_idx    [rows][H_i][D_i]      -> k_idx_cache rows, unchanged bits
+ *   q_norm_w, k_norm_w  [D] (dtype), shared by all heads
+ *   eps >= 0, rope_theta > 0, rotary_dim 0 (no rotation) or a power of two with
+ *   16 <= rotary_dim <= D (bf16; 8 <= rotary_dim for fp32).
+ * rows = batch->total_q or num_seqs. A new token at position p of request r goes
+ * to physical block block_table[r][p / 128], row p % 128; nothing else in the
+ * caches is written, and q_idx is not an input (the indexer query is used as
+ * given). Non-finite results (eps == 0 with an all-zero head) are undefined.
+ * A prefill batch with no units enqueues nothing. */
+msa_status_t msa_qk_norm_rope_insert(const msa_geom_t *geom, const msa_cache_t *cache,
+                                     const msa_batch_t *batch, const void *q, const void *k,
+                                     const void *v, const void *k_idx, const void *q_norm_w,
+                                     const void *k_norm_w, float eps, float rope_theta,
+                                     int32_t rotary_dim, void *q_out, void *stream);
 
 const char *msa_status_string(msa_status_t status);
 const char *msa_last_error(void);

@@ -171,3 +171,49 @@ def test_binding_checks_tensors_before_calling(lib):
     with pytest.raises(ValueError):
         msa.msa_index_scores(geom, cache, None, torch.zeros(1, 4, 64, dtype=torch.bfloat16),
                              torch.zeros(1, 2, 4))
+
+
+def _insert(lib, g, c, b, eps=1e-6, theta=1e6, rd=64, q=FAKE, k=FAKE, v=FAKE, ki=FAKE,
+            qw=FAKE, kw=FAKE, qo=FAKE):
+    return lib.msa_qk_norm_rope_insert(ctypes.byref(g), ctypes.byref(c),
+                                       None if b is None else ctypes.byref(b), q, k, v, ki, qw,
+                                       kw, eps, theta, rd, qo, None)
+
+
+def test_insert_argument_checks(lib):
+    g, c, b = _geom(), _cache(), msa._Batch(FAKE, 3, 300)
+    assert _insert(lib, g, c, msa._Batch(None, 0, 0)) == OK      # empty batch: nothing to do
+    assert _insert(lib, g, c, b, eps=-1.0) == INVALID
+    assert _insert(lib, g, c, b, eps=float("nan")) == INVALID
+    assert _insert(lib, g, c, b, eps=float("inf")) == INVALID
+    assert _insert(lib, g, c, b, theta=0.0) == INVALID
+    assert _insert(lib, g, c, b, theta=float("nan")) == INVALID
+    for rd in (8, 48, 256, -64):            # bf16 needs a power of two in [16, D]
+        assert _insert(lib, g, c, b, rd=rd) == UNSUPPORTED, rd
+    assert _insert(lib, _geom(dtype=msa.MSA_F32), c, b, rd=4) == UNSUPPORTED
+    for kw in ("q", "k", "v", "ki", "qw", "kw", "qo"):
+        assert _insert(lib, g, c, b, **{kw: None}) == INVALID, kw
+    assert _insert(lib, g, _cache(k_idx_cache=None), b) == INVALID
+    assert _insert(lib, g, _cache(v_cache=None), None) == INVALID
+    assert _insert(lib, _geom(head_dim=96), c, b) == UNSUPPORTED
+    assert lib.msa_last_error()
+
+
+def test_insert_binding_checks_shapes(lib):
+    geom = msa.Geometry(8, 2, 128, 4, 64, 2, "bf16")
+    P, bf = 4, torch.bfloat16
+    cache = msa.Cache(torch.zeros(P, 2, 128, 128, dtype=bf), torch.zeros(P, 2, 128, 128, dtype=bf),
+                      torch.zeros(P, 4, 128, 64, dtype=bf), torch.zeros(1, 4, dtype=torch.int32),
+                      torch.tensor([500], dtype=torch.int32))
+    q = torch.zeros(1, 8, 128, dtype=bf)
+    kv = torch.zeros(1, 2, 128, dtype=bf)
+    ki = torch.zeros(1, 4, 64, dtype=bf)
+    w = torch.ones(128, dtype=bf)
+    with pytest.raises(ValueError):
+        msa.msa_qk_norm_rope_insert(geom, cache, None, q, kv, kv, ki, w, torch.ones(64, dtype=bf),
+                                    1e-6, 1e6, 64)
+    with pytest.raises(ValueError):
+        msa.msa_qk_norm_rope_insert(geom, cache, None, q, kv, torch.zeros(1, 2, 64, dtype=bf), ki,
+                                    w, w, 1e-6, 1e6, 64)
+    with pytest.raises(TypeError):
+        msa.msa_qk_norm_rope_insert(geom, cache, None, q.float(), kv, kv, ki, w, w, 1e-6, 1e6, 64)
