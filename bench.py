@@ -248,8 +248,9 @@ def measure_insert(runner, launches=20, warmup=10):
     gbs = nbytes / (us * 1e-6) / 1e9
     del new
     return dict(workload=w.name, new_tokens=w.total_q, rotary_dim=rope["rotary_dim"],
-                us_per_launch=us, algorithmic_bytes=nbytes, achieved=gbs, unit="GB/s",
-                peak=HBM_PEAK_GBS, frac=gbs / HBM_PEAK_GBS)
+                us_per_launch=us, bound="hbm", algorithmic_bytes=nbytes, achieved=gbs,
+                unit="GB/s", peak=HBM_PEAK_GBS, frac=gbs / HBM_PEAK_GBS,
+                traffic=measured_traffic(f"{w.name}:insert", "qk_insert.hip"))
 
 
 # ----------------------------------------------------------------------------
