@@ -353,3 +353,108 @@ def qk_norm_rope_insert(units, q, k, v, k_idx, q_norm_w, k_norm_w, eps, theta, r
     q_full[rows] = q_out
     return q_full, kc, vc, ic
 
+
+
+# ----------------------------------------------------------------------------
+# FP8 caches: E4M3 codes with one power-of-two scale per 32 channels of a row
+# ----------------------------------------------------------------------------
+# [dd] "What's coming" lists FP8 KV-cache paths; the pages give no format. Read
+# here as the OCP 8-bit floating-point E4M3 encoding (1 sign bit, 4 exponent bits
+# with bias 7, 3 mantissa bits; exponent field 15 with mantissa 7 is NaN, so the
+# largest finite magnitude is 1.75 * 2^8 = 448; exponent field 0 holds the
+# subnormals m/8 * 2^-6) with one scale per block of 32 consecutive channels of
+# one token's head vector. The scale is a power of two 2^e, stored as the byte
+# e + 127 (the OCP E8M0 scale encoding), e the smallest integer with
+# max|x| / 2^e <= 448; each channel stores the E4M3 code nearest to x / 2^e
+# (ties to the even code). The value a code stands for is decode(code) * 2^e.
+
+E4M3_MAX = 448.0
+SCALE_BLOCK = 32
+SCALE_BIAS = 127
+
+
+def e4m3_decode(codes):
+    """Values (float64) of E4M3 codes; NaN for the two NaN codes."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = m / 8.0 * 2.0 ** -6
+    v = sign * np.where(e == 0, sub, normal)
+    return np.where((e == 15) & ((c & 0x7) == 7), np.nan, v)
+
+
+_E4M3_POS = e4m3_decode(np.arange(0x7F))          # codes 0x00..0x7E, increasing
+
+
+def e4m3_encode(y):
+    """E4M3 code (uint8) of the value nearest to each y, ties to the even code.
+    Requires |y| <= 448. The sign is kept, also when the result is zero."""
+    y = np.asarray(y, dtype=np.float64)
+    mag = np.abs(y)
+    assert np.all(mag <= E4M3_MAX), "value outside the E4M3 range"
+    hi = np.clip(np.searchsorted(_E4M3_POS, mag, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_hi, d_lo = _E4M3_POS[hi] - mag, mag - _E4M3_POS[lo]
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    code = np.where(pick_lo, lo, hi)
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def mx_exponent(amax):
+    """Smallest integer e with amax / 2^e <= 448 (amax >= 0), within [-127, 127];
+    amax == 0 gives -127."""
+    a = np.asarray(amax, dtype=np.float64)
+    frac, k = np.frexp(a)                    # a = frac * 2^k, frac in [0.5, 1)
+    e = (k - 1) - 8 + (2.0 * frac > 1.75)   # a = (2 frac) * 2^(k-1)
+    e = np.where(a == 0, -127, e)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def mx_quantize(x):
+    """x [..., C] (C a multiple of 32) -> (codes uint8 [..., C], scale bytes uint8
+    [..., C/32]): one scale per 32 consecutive channels of the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    blk = x.reshape(x.shape[:-1] + (x.shape[-1] // SCALE_BLOCK, SCALE_BLOCK))
+    e = mx_exponent(np.abs(blk).max(axis=-1))
+    codes = e4m3_encode(blk / np.exp2(e.astype(np.float64))[..., None])
+    return codes.reshape(x.shape), (e + SCALE_BIAS).astype(np.uint8)
+
+
+def mx_dequantize(codes, scales):
+    """Values (float64 [..., C]) of codes [..., C] with scale bytes [..., C/32]."""
+    codes = np.asarray(codes)
+    v = e4m3_decode(codes).reshape(codes.shape[:-1] + (-1, SCALE_BLOCK))
+    e = np.asarray(scales, dtype=np.float64) - SCALE_BIAS
+    return (v * np.exp2(e)[..., None]).reshape(codes.shape)
+
+
+def qk_norm_rope_insert_fp8(units, q, k, v, k_idx, q_norm_w, k_norm_w, eps, theta,
+                            rotary_dim, caches, block_table):
+    """The new-token step into FP8 caches. caches is a dict of token-major code and
+    scale arrays: k, v [P][H_kv][128][D] with k_s, v_s [P][H_kv][128][D/32], and
+    i [P][H_i][128][D_i] with i_s [P][H_i][128][D_i/32]. Each new token's K (after
+    norm and rotation), V and indexer-key rows are quantized row by row and
+    replace that token's codes and scales; nothing else changes.
+
+    Returns (q_out float64, new caches dict)."""
+    toks = token_positions(units)
+    rows = np.array([t[0] for t in toks], dtype=np.int64)
+    pos = np.array([t[2] for t in toks], dtype=np.float64)
+    q_out = rope(rms_norm(np.asarray(q, np.float64)[rows], q_norm_w, eps), pos, theta,
+                 rotary_dim)
+    k_new = rope(rms_norm(np.asarray(k, np.float64)[rows], k_norm_w, eps), pos, theta,
+                 rotary_dim)
+    out = {name: np.array(a) for name, a in caches.items()}
+    kq, ks = mx_quantize(k_new)
+    vq, vs = mx_quantize(np.asarray(v, np.float64)[rows])
+    iq, is_ = mx_quantize(np.asarray(k_idx, np.float64)[rows])
+    for n, (row, r, p) in enumerate(toks):
+        phys, slot = int(block_table[r][p // BLOCK]), p % BLOCK
+        out["k"][phys, :, slot], out["k_s"][phys, :, slot] = kq[n], ks[n]
+        out["v"][phys, :, slot], out["v_s"][phys, :, slot] = vq[n], vs[n]
+        out["i"][phys, :, slot], out["i_s"][phys, :, slot] = iq[n], is_[n]
+    q_full = np.zeros(np.asarray(q).shape, dtype=np.float64)
+    q_full[rows] = q_out
+    return q_full, out

@@ -574,3 +574,145 @@ def test_insert_is_independent_of_physical_placement():
             np.testing.assert_array_equal(k0[bt0[r, b]], k1[bt1[r, b]])
             np.testing.assert_array_equal(v0[bt0[r, b]], v1[bt1[r, b]])
             np.testing.assert_array_equal(i0[bt0[r, b]], i1[bt1[r, b]])
+
+
+# ----------------------------------------------------------------------------
+# FP8 cache format: E4M3 codes, power-of-two scale per 32 channels
+# ----------------------------------------------------------------------------
+
+def _golden_fp8():
+    with open(os.path.join(GOLDEN, "fp8_e4m3.json")) as f:
+        return json.load(f)
+
+
+def _torch_e4m3_values():
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_e4m3_golden():
+    g = _golden_fp8()
+    for e in g["decode"]:
+        v = float(O.e4m3_decode(int(e["code"], 16)))
+        assert v == e["value"] and math.copysign(1, v) == math.copysign(1, e["value"]), e
+    for e in g["encode"]:
+        assert int(O.e4m3_encode(e["value"])) == int(e["code"], 16), e
+    for e in g["exponent"]:
+        assert int(O.mx_exponent(e["amax"])) == e["e"], e
+
+
+def test_e4m3_decode_matches_torch_float8():
+    ref = _torch_e4m3_values()
+    got = O.e4m3_decode(np.arange(256))
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isnan(got), ~fin)            # exactly the two NaN codes
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+
+
+def test_e4m3_encode_matches_torch_cast_on_a_dense_sweep():
+    vals = np.unique(_torch_e4m3_values()[np.isfinite(_torch_e4m3_values())])
+    mids = (vals[1:] + vals[:-1]) / 2
+    rng = np.random.default_rng(3)
+    x = np.concatenate([vals, mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf),
+                        rng.uniform(-448, 448, 20000), rng.normal(size=20000) * 3,
+                        rng.normal(size=5000) * 1e-3])
+    x = np.clip(x, -448, 448).astype(np.float32)          # exactly representable inputs
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(x.astype(np.float64)), ref)
+
+
+def test_e4m3_encode_is_nearest_and_monotone():
+    rng = np.random.default_rng(4)
+    x = np.sort(rng.uniform(-448, 448, 5000))
+    c = O.e4m3_encode(x)
+    v = O.e4m3_decode(c)
+    assert np.all(np.diff(v) >= 0)
+    grid = np.unique(O.e4m3_decode(np.arange(256))[np.isfinite(O.e4m3_decode(np.arange(256)))])
+    best = np.abs(grid[None, :] - x[:, None]).min(axis=1)
+    assert np.allclose(np.abs(v - x), best, rtol=0, atol=0)
+
+
+def test_mx_exponent_is_the_smallest_that_fits():
+    rng = np.random.default_rng(5)
+    a = np.concatenate([np.exp2(rng.uniform(-40, 40, 4000)), 448 * np.exp2(np.arange(-20, 20)),
+                        1.75 * np.exp2(np.arange(-20, 20)),
+                        np.nextafter(1.75 * np.exp2(np.arange(-20, 20)), np.inf)])
+    e = O.mx_exponent(a).astype(np.float64)
+    assert np.all(a / np.exp2(e) <= 448.0)
+    assert np.all(a / np.exp2(e - 1) > 448.0)
+
+
+def test_mx_quantize_error_bound_and_top_binade():
+    rng = np.random.default_rng(6)
+    x = rng.normal(size=(50, 4, 128)) * np.exp2(rng.integers(-6, 6, size=(50, 4, 1)))
+    codes, scales = O.mx_quantize(x)
+    assert codes.dtype == np.uint8 and scales.shape == (50, 4, 4)
+    y = O.mx_dequantize(codes, scales)
+    e = (scales.astype(np.float64) - O.SCALE_BIAS).repeat(O.SCALE_BLOCK, axis=-1)
+    half_ulp = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * np.exp2(e))
+    assert np.all(np.abs(y - x) <= half_ulp)
+    # the largest magnitude of each block lands in the top binade [224, 448]
+    top = np.abs(O.e4m3_decode(codes)).reshape(50, 4, 4, 32).max(axis=-1)
+    assert np.all((top >= 224) & (top <= 448))
+
+
+def test_mx_round_trip_of_representable_blocks_and_scaling():
+    rng = np.random.default_rng(7)
+    x = rng.normal(size=(20, 64)) * 10
+    c, s = O.mx_quantize(x)
+    y = O.mx_dequantize(c, s)
+    c2, s2 = O.mx_quantize(y)                  # values already on the grid come back
+    assert np.array_equal(O.mx_dequantize(c2, s2), y)
+    # codes too, unless a block's largest code is exactly 224 (then the smaller
+    # exponent fits as well and is the one chosen)
+    top = np.abs(O.e4m3_decode(c)).reshape(20, 2, 32).max(axis=-1)
+    same = (top > 224).repeat(32, axis=-1).reshape(20, 64)
+    assert np.array_equal(c[same], c2[same]) and np.array_equal(s[top > 224], s2[top > 224])
+    for k in (-5, 1, 9):                       # a power-of-two factor moves only the scales
+        c3, s3 = O.mx_quantize(x * 2.0 ** k)
+        assert np.array_equal(c, c3) and np.array_equal(s3.astype(int), s.astype(int) + k)
+
+
+def test_mx_blocks_are_independent():
+    rng = np.random.default_rng(8)
+    x = rng.normal(size=(3, 128))
+    c, s = O.mx_quantize(x)
+    x2 = x.copy()
+    x2[:, 32:64] *= 1000.0
+    c2, s2 = O.mx_quantize(x2)
+    keep = np.r_[0:32, 64:128]
+    assert np.array_equal(c[:, keep], c2[:, keep]) and np.array_equal(s[:, [0, 2, 3]],
+                                                                      s2[:, [0, 2, 3]])
+    assert np.all(s2[:, 1].astype(int) == s[:, 1].astype(int) + 10)   # 1000 ~ 2^10 lift
+
+
+def test_insert_fp8_is_quantized_insert():
+    rng = np.random.default_rng(9)
+    Hq, Hkv, D, Hi, Di, P = 4, 2, 64, 2, 32, 3
+    units = O.prefill_units([200], [150])
+    T = 150
+    q, k, v = (rng.normal(size=(T, h, D)) for h in (Hq, Hkv, Hkv))
+    ki = rng.normal(size=(T, Hi, Di))
+    wq, wk = 1 + 0.1 * rng.normal(size=D), 1 + 0.1 * rng.normal(size=D)
+    bt = np.array([[2, 0]])
+    caches = dict(k=rng.integers(0, 0x7E, (P, Hkv, 128, D)).astype(np.uint8),
+                  v=rng.integers(0, 0x7E, (P, Hkv, 128, D)).astype(np.uint8),
+                  i=rng.integers(0, 0x7E, (P, Hi, 128, Di)).astype(np.uint8),
+                  k_s=rng.integers(100, 140, (P, Hkv, 128, D // 32)).astype(np.uint8),
+                  v_s=rng.integers(100, 140, (P, Hkv, 128, D // 32)).astype(np.uint8),
+                  i_s=rng.integers(100, 140, (P, Hi, 128, Di // 32)).astype(np.uint8))
+    q8, out = O.qk_norm_rope_insert_fp8(units, q, k, v, ki, wq, wk, 1e-6, 1e4, 32, caches, bt)
+    z = np.zeros((P, Hkv, 128, D))
+    q64, kc, vc, ic = O.qk_norm_rope_insert(units, q, k, v, ki, wq, wk, 1e-6, 1e4, 32, z, z,
+                                            np.zeros((P, Hi, 128, Di)), bt)
+    assert np.array_equal(q8, q64)
+    new = np.zeros((P, 128), dtype=bool)
+    new[2, 50:128] = True                       # positions 50..199 of the request
+    new[0, 0:72] = True
+    for name in ("k", "v", "i", "k_s", "v_s", "i_s"):
+        a, b = out[name].transpose(0, 2, 1, 3), caches[name].transpose(0, 2, 1, 3)
+        assert np.array_equal(a[~new], b[~new]), name
+    for codes, sc, ref in (("k", "k_s", kc), ("v", "v_s", vc), ("i", "i_s", ic)):
+        c_ref, s_ref = O.mx_quantize(ref.transpose(0, 2, 1, 3)[new])
+        assert np.array_equal(out[codes].transpose(0, 2, 1, 3)[new], c_ref), codes
+        assert np.array_equal(out[sc].transpose(0, 2, 1, 3)[new], s_ref), sc
