@@ -47,7 +47,15 @@ def log(msg):
 
 def geometry(w):
     return msa.Geometry(w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_idx_heads,
-                        w.idx_head_dim, w.num_sel_groups, w.dtype)
+                        w.idx_head_dim, w.num_sel_groups, w.dtype, w.cache_format)
+
+
+def cache_row_bytes(w, dim):
+    """Bytes of one token's head row in a cache: bf16, or FP8 codes plus one
+    scale byte per 32 channels."""
+    if w.cache_format == "fp8":
+        return dim + dim // 32
+    return dim * (2 if w.dtype == "bf16" else 4)
 
 
 # ----------------------------------------------------------------------------
@@ -82,7 +90,7 @@ def plan_units(w):
 
 def index_decode_bytes(w):
     """Indexer keys every non-diagonal block must stream, plus q_idx and scores."""
-    per_block = w.num_idx_heads * BLK * w.idx_head_dim * 2
+    per_block = w.num_idx_heads * BLK * cache_row_bytes(w, w.idx_head_dim)
     blocks = sum(w.blocks(r) - 1 for r in range(w.num_seqs))
     q = w.num_seqs * w.num_idx_heads * w.idx_head_dim * 2
     scores = w.num_seqs * w.num_sel_groups * w.max_blocks * 4
@@ -104,7 +112,8 @@ class Runner:
         self.geom = geometry(w)
         self.cache = msa.Cache(self.inp["k_cache"], self.inp["v_cache"],
                                self.inp["k_idx_cache"], self.inp["block_table"],
-                               self.inp["seq_lens"])
+                               self.inp["seq_lens"], self.inp.get("k_scale"),
+                               self.inp.get("v_scale"), self.inp.get("k_idx_scale"))
         U = w.num_seqs if w.is_decode else len(msa.msa_prefill_plan(w.seq_lens, w.q_lens))
         self.batch = None if w.is_decode else msa.make_batch(w.seq_lens, w.q_lens, dev)
         self.scores = torch.empty((U, w.num_sel_groups, self.cache.max_blocks),
@@ -194,7 +203,7 @@ def measure(w, dev, steps, warmup):
                                                         "index_scores.hip"),
                                algorithmic_bytes=nbytes)
         # whole decode step against HBM: the algorithmic bytes of all four launches
-        kv = tokens * w.head_dim * 2 * 2            # K and V rows of the selected keys
+        kv = tokens * cache_row_bytes(w, w.head_dim) * 2   # K and V rows of the selected keys
         step_bytes = nbytes + kv + 2 * w.num_seqs * w.num_q_heads * w.head_dim * 2
         res["step_hbm_frac"] = step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
         res["step_algorithmic_bytes"] = step_bytes
@@ -216,9 +225,13 @@ def insert_bytes(w):
     tokens: q, k, v and k_idx read once; q_out, the K and V cache rows and the
     indexer-key rows written once (the norm weights and the plan are negligible)."""
     sz = 2 if w.dtype == "bf16" else 4
-    per_token = (w.num_q_heads * w.head_dim + 2 * w.num_kv_heads * w.head_dim
-                 + w.num_idx_heads * w.idx_head_dim)
-    return 2 * w.total_q * per_token * sz
+    T = w.total_q
+    read = T * (w.num_q_heads * w.head_dim + 2 * w.num_kv_heads * w.head_dim
+                + w.num_idx_heads * w.idx_head_dim) * sz
+    written = T * (w.num_q_heads * w.head_dim * sz + 2 * w.num_kv_heads *
+                   cache_row_bytes(w, w.head_dim) +
+                   w.num_idx_heads * cache_row_bytes(w, w.idx_head_dim))
+    return read + written
 
 
 def measure_insert(runner, launches=20, warmup=10):
@@ -312,6 +325,8 @@ def main():
     ap.add_argument("--workload", default="prefill_32k", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--second", default="decode_1m_b8",
                     help="second workload measured in the same run ('none' to skip)")
+    ap.add_argument("--fp8", default="decode_1m_b8_fp8",
+                    help="FP8-cache workload measured in the same run ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -359,6 +374,16 @@ def main():
         del second["_runner"]
         torch.cuda.empty_cache()
 
+    fp8 = None
+    if args.fp8 != "none" and args.fp8 not in (args.workload, args.second):
+        w3 = synth.WORKLOADS[args.fp8]
+        fp8 = measure(w3, dev, args.steps, args.warmup)
+        log(f"{w3.name}: {fp8['ms_per_step']:.3f} ms/step, kernels {fp8['kernel_ms']}")
+        inserts.append(measure_insert(fp8["_runner"]))
+        log(f"{w3.name}: insert {inserts[-1]['us_per_launch']:.1f} us")
+        del fp8["_runner"]
+        torch.cuda.empty_cache()
+
     config = dict(workload=w.name, batch=w.num_seqs,
                   seq_lens=w.seq_lens if len(set(w.seq_lens)) > 1 else w.seq_lens[0],
                   q_per_seq=(w.q_lens[0] if w.q_lens else 1), q_heads=w.num_q_heads,
@@ -387,6 +412,12 @@ def main():
         line["second_workload"] = {k: second[k] for k in (
             "workload", "value", "ms_per_step", "kernel_ms", "roofline", "step_hbm_frac")
             if k in second}
+    if fp8 is not None:
+        # the same decode on FP8 caches (E4M3 codes, power-of-two scale per 32
+        # channels): fewer bytes for the same selections
+        line["fp8_cache_workload"] = {k: fp8[k] for k in (
+            "workload", "value", "ms_per_step", "kernel_ms", "roofline", "step_hbm_frac")
+            if k in fp8}
     # the new-token step before the path (QK-norm + partial RoPE + cache insert),
     # timed on its own: not part of the step above
     line["qk_norm_rope_insert"] = inserts

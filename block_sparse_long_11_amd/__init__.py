@@ -14,6 +14,7 @@ plus two helpers that allocate outputs and run the whole path:
 import ctypes
 import dataclasses
 import pathlib
+from typing import Optional
 
 import numpy as np
 import torch
@@ -22,7 +23,9 @@ _LIB_PATH = pathlib.Path(__file__).resolve().parent / "libmsa.so"
 _lib = None
 
 MSA_F32, MSA_BF16 = 0, 1
+MSA_CACHE_PLAIN, MSA_CACHE_FP8_E4M3 = 0, 1
 BLOCK = 128
+SCALE_BLOCK = 32      # channels per FP8 scale
 
 
 class MsaError(RuntimeError):
@@ -36,14 +39,16 @@ class MsaError(RuntimeError):
 class _Geom(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_q_heads", "num_kv_heads", "head_dim", "num_idx_heads", "idx_head_dim",
-        "num_sel_groups", "block_size", "dtype")]
+        "num_sel_groups", "block_size", "dtype", "cache_format")]
 
 
 class _Cache(ctypes.Structure):
     _fields_ = [("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
                 ("k_idx_cache", ctypes.c_void_p), ("num_phys_blocks", ctypes.c_int64),
                 ("block_table", ctypes.c_void_p), ("max_blocks_per_seq", ctypes.c_int32),
-                ("seq_lens", ctypes.c_void_p), ("num_seqs", ctypes.c_int32)]
+                ("seq_lens", ctypes.c_void_p), ("num_seqs", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("k_idx_scale", ctypes.c_void_p)]
 
 
 class _Unit(ctypes.Structure):
@@ -153,28 +158,42 @@ class Geometry:
     idx_head_dim: int
     num_sel_groups: int
     dtype: str = "bf16"          # "bf16" or "f32"
+    cache_format: str = "plain"  # "plain" (caches in dtype) or "fp8" (E4M3 + scales)
 
     @property
     def torch_dtype(self):
         return torch.bfloat16 if self.dtype == "bf16" else torch.float32
 
+    @property
+    def fp8(self):
+        return self.cache_format == "fp8"
+
+    @property
+    def cache_torch_dtype(self):
+        return torch.uint8 if self.fp8 else self.torch_dtype
+
     def c(self):
         return _Geom(self.num_q_heads, self.num_kv_heads, self.head_dim, self.num_idx_heads,
                      self.idx_head_dim, self.num_sel_groups, BLOCK,
-                     MSA_BF16 if self.dtype == "bf16" else MSA_F32)
+                     MSA_BF16 if self.dtype == "bf16" else MSA_F32,
+                     MSA_CACHE_FP8_E4M3 if self.fp8 else MSA_CACHE_PLAIN)
 
 
 @dataclasses.dataclass
 class Cache:
-    """Block-major paged caches on one device (see include/msa.h)."""
+    """Block-major paged caches on one device (see include/msa.h). With FP8 caches
+    the three caches are uint8 E4M3 codes and the scale tensors are set."""
     k_cache: torch.Tensor        # [P][H_kv][128][D]
     v_cache: torch.Tensor        # [P][H_kv][D][128] (each block d-major)
     k_idx_cache: torch.Tensor    # [P][H_i][128][D_i]
     block_table: torch.Tensor    # int32 [B][max_blocks]
     seq_lens: torch.Tensor       # int32 [B]
+    k_scale: Optional[torch.Tensor] = None       # uint8 [P][H_kv][128][D/32]
+    v_scale: Optional[torch.Tensor] = None       # uint8 [P][H_kv][D/32][128]
+    k_idx_scale: Optional[torch.Tensor] = None   # uint8 [P][H_i][128][D_i/32]
 
     def check(self, geom: Geometry):
-        dt, dev = geom.torch_dtype, self.block_table.device
+        dt, dev = geom.cache_torch_dtype, self.block_table.device
         _need(self.k_cache, "k_cache", dt, 4, dev)
         _need(self.v_cache, "v_cache", dt, 4, dev)
         _need(self.k_idx_cache, "k_idx_cache", dt, 4, dev)
@@ -189,6 +208,15 @@ class Cache:
             raise ValueError("k_idx_cache must be [P][H_i][128][D_i]")
         if self.seq_lens.shape[0] != self.block_table.shape[0]:
             raise ValueError("seq_lens and block_table disagree on the number of sequences")
+        if geom.fp8:
+            H, D, Hi, Di = geom.num_kv_heads, geom.head_dim, geom.num_idx_heads, geom.idx_head_dim
+            for t, name, shape in ((self.k_scale, "k_scale", (P, H, BLOCK, D // SCALE_BLOCK)),
+                                   (self.v_scale, "v_scale", (P, H, D // SCALE_BLOCK, BLOCK)),
+                                   (self.k_idx_scale, "k_idx_scale",
+                                    (P, Hi, BLOCK, Di // SCALE_BLOCK))):
+                _need(t, name, torch.uint8, 4, dev)
+                if tuple(t.shape) != shape:
+                    raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
 
     @property
     def num_seqs(self):
@@ -199,10 +227,12 @@ class Cache:
         return self.block_table.shape[1]
 
     def c(self):
+        sp = lambda t: None if t is None else t.data_ptr()
         return _Cache(self.k_cache.data_ptr(), self.v_cache.data_ptr(),
                       self.k_idx_cache.data_ptr(), self.k_cache.shape[0],
                       self.block_table.data_ptr(), self.block_table.shape[1],
-                      self.seq_lens.data_ptr(), self.block_table.shape[0])
+                      self.seq_lens.data_ptr(), self.block_table.shape[0],
+                      sp(self.k_scale), sp(self.v_scale), sp(self.k_idx_scale))
 
 
 @dataclasses.dataclass

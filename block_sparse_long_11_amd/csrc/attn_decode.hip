@@ -21,6 +21,15 @@
 // their natural-log lse, to the workspace.
 // Phase 2: per (sequence, query head) the parts are merged:
 //   lse = log sum_s exp(lse_s),  out = sum_s exp(lse_s - lse) o_s.
+//
+// FP8 caches (E4M3 codes, a power-of-two scale per 32 channels of a token's head
+// row): a K operand row of 8 channels lies in one scale block, so its 8 codes
+// become bf16 with the scale applied in the conversion (exact: every E4M3 value
+// times a power of two is a bf16 value). The 8 keys of a V^T operand row each
+// carry their own scale, so the scale moves to the other operand: for the
+// 32-channel block c the probabilities are multiplied by 2^e(c, key) before
+// their bf16 rounding (exact, a power of two commutes with the rounding) and the
+// V codes convert unscaled.
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -42,15 +51,35 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, bf16x2));
 }
 
-template <int D>
+// 8 E4M3 codes (two words) as a bf16x8 MFMA operand, each times `scale`
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 w, float scale) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, scale, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, scale, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, scale, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, scale, true);
+  return as_bf16x8(uint4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                         __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)});
+}
+
+__device__ __forceinline__ float scale_of(uint32_t byte) {
+  return ldexpf(1.0f, static_cast<int>(byte) - 127);
+}
+
+template <int D, bool FP8>
 __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
-    const uint16_t *__restrict__ vtc, const int32_t *__restrict__ block_table,
+    const uint16_t *__restrict__ q, const void *__restrict__ kc_,
+    const void *__restrict__ vtc_, const uint8_t *__restrict__ ksc,
+    const uint8_t *__restrict__ vsc, const int32_t *__restrict__ block_table,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ ids, int topk,
     int max_blocks, int Hq, int Hkv, int nsel, int num_splits, int per_split, float c,
     float *__restrict__ o_part, float *__restrict__ lse_part) {
-  constexpr int KS = D / 32;   // k steps of S^T
+  constexpr int KS = D / 32;   // k steps of S^T (one FP8 scale block each)
   constexpr int DT = D / 16;   // d tiles of O^T
+  constexpr int NC = D / 32;   // FP8 scale blocks per head row
+  const uint16_t *kc = static_cast<const uint16_t *>(kc_);
+  const uint16_t *vtc = static_cast<const uint16_t *>(vtc_);
+  const uint8_t *kc8 = static_cast<const uint8_t *>(kc_);
+  const uint8_t *vtc8 = static_cast<const uint8_t *>(vtc_);
   __shared__ float Ow[4][16][D + 1];
   __shared__ float Mw[4][16], Lw[4][16];
 
@@ -96,11 +125,25 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
     for (int tt = 0; tt < 2; ++tt) {
       s[tt] = f32x4{};
       const int key = wave * 32 + 8 * (n / 4) + 4 * tt + (n % 4);
-      const uint16_t *kr = kc + off + key * D + q4 * 8;
+      if constexpr (FP8) {
+        const uint8_t *kr = kc8 + off + key * D + q4 * 8;
+        const uint8_t *sr = ksc + (off / 32) + key * NC;      // the key's scale bytes
+        uint32_t sb[NC];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(kr + ks * 32));
-        s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], s[tt], 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) sb[ks] = sr[ks];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = fp8x8_to_bf16(*reinterpret_cast<const uint2 *>(kr + ks * 32),
+                                         scale_of(sb[ks]));
+          s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], s[tt], 0, 0, 0);
+        }
+      } else {
+        const uint16_t *kr = kc + off + key * D + q4 * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(kr + ks * 32));
+          s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], s[tt], 0, 0, 0);
+        }
       }
     }
     // register i of tile tt holds key wave*32 + 8*q4 + 4*tt + i
@@ -133,13 +176,40 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
                         : __builtin_amdgcn_exp2f(fmaf(s[tt][i], c, -m_ref));
         l_run += p[tt * 4 + i];
       }
-    const bf16x8 pb = as_bf16x8(uint4{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]),
-                                      cvt_pk_bf16(p[4], p[5]), cvt_pk_bf16(p[6], p[7])});
-    const uint16_t *vr = vtc + off + n * kBlk + wave * 32 + q4 * 8;
+    if constexpr (FP8) {
+      // scales of this lane's 8 keys in each 32-channel block: v_scale[c][key]
+      const uint8_t *sr = vsc + (off / 32) + wave * 32 + q4 * 8;
+      uint2 sw[NC];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(vr + dt * 16 * kBlk));
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
+      for (int c = 0; c < NC; ++c) sw[c] = *reinterpret_cast<const uint2 *>(sr + c * kBlk);
+      const uint8_t *vr = vtc8 + off + n * kBlk + wave * 32 + q4 * 8;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        float ps[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t w = i < 4 ? sw[c].x : sw[c].y;
+          ps[i] = ldexpf(p[i], static_cast<int>((w >> (8 * (i % 4))) & 0xffu) - 127);
+        }
+        const bf16x8 pb = as_bf16x8(uint4{cvt_pk_bf16(ps[0], ps[1]), cvt_pk_bf16(ps[2], ps[3]),
+                                          cvt_pk_bf16(ps[4], ps[5]), cvt_pk_bf16(ps[6], ps[7])});
+#pragma unroll
+        for (int dd = 0; dd < 2; ++dd) {                // the two 16-row tiles of block c
+          const int dt = 2 * c + dd;
+          const bf16x8 a =
+              fp8x8_to_bf16(*reinterpret_cast<const uint2 *>(vr + dt * 16 * kBlk), 1.0f);
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
+        }
+      }
+    } else {
+      const bf16x8 pb = as_bf16x8(uint4{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]),
+                                        cvt_pk_bf16(p[4], p[5]), cvt_pk_bf16(p[6], p[7])});
+      const uint16_t *vr = vtc + off + n * kBlk + wave * 32 + q4 * 8;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(vr + dt * 16 * kBlk));
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
+      }
     }
   }
 
@@ -233,22 +303,22 @@ hipError_t launch_attn_decode(const Geom &g, const msa_cache_t &c, const void *q
       ((parts * g.D * sizeof(float) + 255) & ~static_cast<size_t>(255)));
   const dim3 grid(c.num_seqs * g.Hkv, num_splits);
   const uint16_t *qb = static_cast<const uint16_t *>(q);
-  const uint16_t *kb = static_cast<const uint16_t *>(c.k_cache);
-  const uint16_t *vb = static_cast<const uint16_t *>(c.v_cache);
   const float sl2 = scale * kLog2e;
+#define MSA_DEC(DD, F8)                                                                    \
+  attn_decode_bf16_kernel<DD, F8><<<grid, kDecThreads, 0, st>>>(                           \
+      qb, c.k_cache, c.v_cache, c.k_scale, c.v_scale, c.block_table, c.seq_lens, ids,     \
+      topk, c.max_blocks_per_seq, g.Hq, g.Hkv, g.nsel, num_splits, per, sl2, o_part,       \
+      lse_part)
   if (g.D == 64) {
-    attn_decode_bf16_kernel<64><<<grid, kDecThreads, 0, st>>>(
-        qb, kb, vb, c.block_table, c.seq_lens, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
-        g.nsel, num_splits, per, sl2, o_part, lse_part);
+    if (g.fp8) MSA_DEC(64, true); else MSA_DEC(64, false);
     combine_kernel<64, true><<<c.num_seqs * g.Hq, 64, 0, st>>>(o_part, lse_part, num_splits,
                                                                 out, lse);
   } else {
-    attn_decode_bf16_kernel<128><<<grid, kDecThreads, 0, st>>>(
-        qb, kb, vb, c.block_table, c.seq_lens, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
-        g.nsel, num_splits, per, sl2, o_part, lse_part);
+    if (g.fp8) MSA_DEC(128, true); else MSA_DEC(128, false);
     combine_kernel<128, true><<<c.num_seqs * g.Hq, 128, 0, st>>>(o_part, lse_part,
                                                                   num_splits, out, lse);
   }
+#undef MSA_DEC
   return hipGetLastError();
 }
 

@@ -104,6 +104,100 @@ __global__ __launch_bounds__(256) void index_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// decode over FP8 indexer keys (E4M3 codes, one power-of-two scale per 32
+// channels of a token's head row): same work-group layout as above, a token row
+// of one head is D_i bytes of codes, 16 per lane. The codes become bf16 exactly
+// (every E4M3 value is a bf16 value) and meet the bf16 query in
+// v_dot2c_f32_bf16; a lane's 16 channels lie in one scale block, so its partial
+// dot product is multiplied by that block's 2^e (exact) before the lanes of the
+// row are summed. The result is the dot product with the decoded keys up to the
+// order of the fp32 sums. A block's bytes: codes H_i*128*D_i plus scales
+// H_i*128*D_i/32, about half of the bf16 block.
+// ---------------------------------------------------------------------------
+
+template <int DI, int HS>
+__global__ __launch_bounds__(256) void index_decode_fp8_kernel(
+    const uint16_t *__restrict__ q_idx, const uint8_t *__restrict__ k_idx,
+    const uint8_t *__restrict__ k_scale, const int32_t *__restrict__ block_table,
+    const int32_t *__restrict__ seq_lens, int max_blocks, int nsel,
+    float *__restrict__ scores) {
+  constexpr int LPR = DI / 16;           // lanes per token row of one head
+  constexpr int ROWS = 256 / LPR;        // token rows per pass
+  constexpr int PASSES = kBlk / ROWS;
+  constexpr int SPR = DI / 32;           // scale bytes per token row
+  __shared__ float red[4][16];
+
+  const int Hi = nsel * HS;
+  const int r = blockIdx.x / max_blocks;
+  const int b = blockIdx.x - r * max_blocks;
+  const int L = seq_lens[r];
+  const int tau = (L - 1) / kBlk;
+  float *out = scores + static_cast<size_t>(r) * nsel * max_blocks + b;
+  if (b >= tau) {
+    if (threadIdx.x < nsel) out[static_cast<size_t>(threadIdx.x) * max_blocks] =
+        (b == tau) ? pos_inf() : neg_inf();
+    return;
+  }
+  const int64_t phys = block_table[static_cast<size_t>(r) * max_blocks + b];
+  const int t = threadIdx.x;
+  const int piece = t % LPR;
+  const int row = t / LPR;
+  const int chunk = piece / 2;           // 32-channel scale block of this lane
+  const uint8_t *kblk = k_idx + static_cast<size_t>(phys) * Hi * kBlk * DI;
+  const uint8_t *sblk = k_scale + static_cast<size_t>(phys) * Hi * kBlk * SPR;
+  const uint16_t *qrow = q_idx + static_cast<size_t>(r) * Hi * DI;
+  const int wave = t / kWave, lane = t % kWave;
+
+  for (int g = 0; g < nsel; ++g) {
+    uint32_t qw[HS][8];                  // this lane's 16 query channels, bf16 pairs
+#pragma unroll
+    for (int hh = 0; hh < HS; ++hh) {
+      const uint16_t *qp = qrow + (g * HS + hh) * DI + piece * 16;
+      const uint4 a = *reinterpret_cast<const uint4 *>(qp);
+      const uint4 c = *reinterpret_cast<const uint4 *>(qp + 8);
+      qw[hh][0] = a.x; qw[hh][1] = a.y; qw[hh][2] = a.z; qw[hh][3] = a.w;
+      qw[hh][4] = c.x; qw[hh][5] = c.y; qw[hh][6] = c.z; qw[hh][7] = c.w;
+    }
+    uint4 kv[PASSES][HS];
+    uint32_t sc[PASSES][HS];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+      for (int hh = 0; hh < HS; ++hh) {
+        const size_t tok = static_cast<size_t>(g * HS + hh) * kBlk + p * ROWS + row;
+        kv[p][hh] = load_stream16(kblk + tok * DI + piece * 16);
+        sc[p][hh] = sblk[tok * SPR + chunk];
+      }
+    float m = neg_inf();
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      float acc = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < HS; ++hh) {
+        const uint32_t w[4] = {kv[p][hh].x, kv[p][hh].y, kv[p][hh].z, kv[p][hh].w};
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
+          const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+          part = dot2_bf16(qw[hh][2 * i], __builtin_bit_cast(uint32_t, lo), part);
+          part = dot2_bf16(qw[hh][2 * i + 1], __builtin_bit_cast(uint32_t, hi), part);
+        }
+        acc = fmaf(part, ldexpf(1.0f, static_cast<int>(sc[p][hh]) - 127), acc);
+      }
+      acc = group_sum<LPR>(acc);   // full group score of token row p*ROWS+row
+      m = fmaxf(m, acc);
+    }
+    m = group_max<kWave>(m);
+    if (lane == 0) red[wave][g] = m;
+  }
+  __syncthreads();
+  if (t < nsel)
+    out[static_cast<size_t>(t) * max_blocks] =
+        fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+}
+
+// ---------------------------------------------------------------------------
 // prefill, bf16, group width above 128: MFMA 32x32x16, one work-group per
 // (unit, group, block chunk), keys read straight from L2
 // ---------------------------------------------------------------------------
@@ -410,6 +504,26 @@ hipError_t dispatch_decode_hs(const Geom &g, const msa_cache_t &c, const void *q
 }
 
 template <int DI>
+hipError_t dispatch_decode_fp8(const Geom &g, const msa_cache_t &c, const void *q_idx,
+                               float *scores, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(c.num_seqs) * c.max_blocks_per_seq);
+  const uint16_t *q = static_cast<const uint16_t *>(q_idx);
+  const uint8_t *k = static_cast<const uint8_t *>(c.k_idx_cache);
+  switch (g.Hs()) {
+#define MSA_CASE(HS)                                                                     \
+  case HS:                                                                               \
+    index_decode_fp8_kernel<DI, HS><<<grid, 256, 0, st>>>(                               \
+        q, k, c.k_idx_scale, c.block_table, c.seq_lens, c.max_blocks_per_seq, g.nsel,    \
+        scores);                                                                         \
+    break;
+    MSA_CASE(1) MSA_CASE(2) MSA_CASE(4) MSA_CASE(8)
+#undef MSA_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int DI>
 hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                  const void *q_idx, float *scores, hipStream_t st) {
   const uint16_t *q = static_cast<const uint16_t *>(q_idx);
@@ -449,6 +563,10 @@ hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_
 
 hipError_t launch_index_decode(const Geom &g, const msa_cache_t &c, const void *q_idx,
                                float *scores, hipStream_t st) {
+  if (g.fp8) {
+    return g.Di == 64 ? dispatch_decode_fp8<64>(g, c, q_idx, scores, st)
+                      : dispatch_decode_fp8<32>(g, c, q_idx, scores, st);
+  }
   if (g.bf16) {
     return g.Di == 64 ? dispatch_decode_hs<true, 64>(g, c, q_idx, scores, st)
                       : dispatch_decode_hs<true, 32>(g, c, q_idx, scores, st);
@@ -460,6 +578,7 @@ hipError_t launch_index_decode(const Geom &g, const msa_cache_t &c, const void *
 hipError_t launch_index_prefill(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                 const void *q_idx, float *scores, hipStream_t st) {
   if (b.total_units == 0) return hipSuccess;
+  if (g.fp8) return hipErrorInvalidValue;   // rejected by the entry point already
   if (g.bf16) {
     return g.Di == 64 ? dispatch_prefill_bf16<64>(g, c, b, q_idx, scores, st)
                       : dispatch_prefill_bf16<32>(g, c, b, q_idx, scores, st);

@@ -71,6 +71,10 @@ msa_status_t check_geom(const msa_geom_t *g, msa::Geom *out) {
   MSA_REQUIRE(g->num_sel_groups <= 16, MSA_ERR_UNSUPPORTED, "more than 16 selection groups");
   MSA_REQUIRE(g->dtype != MSA_BF16 || g->num_q_heads / g->num_kv_heads <= 16,
               MSA_ERR_UNSUPPORTED, "bf16 needs at most 16 query heads per KV head");
+  MSA_REQUIRE(g->cache_format == MSA_CACHE_PLAIN || g->cache_format == MSA_CACHE_FP8_E4M3,
+              MSA_ERR_UNSUPPORTED, "cache_format %d unsupported", g->cache_format);
+  MSA_REQUIRE(g->cache_format != MSA_CACHE_FP8_E4M3 || g->dtype == MSA_BF16,
+              MSA_ERR_UNSUPPORTED, "FP8 caches need dtype bf16");
   out->Hq = g->num_q_heads;
   out->Hkv = g->num_kv_heads;
   out->D = g->head_dim;
@@ -78,15 +82,20 @@ msa_status_t check_geom(const msa_geom_t *g, msa::Geom *out) {
   out->Di = g->idx_head_dim;
   out->nsel = g->num_sel_groups;
   out->bf16 = g->dtype == MSA_BF16;
+  out->fp8 = g->cache_format == MSA_CACHE_FP8_E4M3;
   return ok();
 }
 
-msa_status_t check_cache(const msa_cache_t *c, bool need_kv, bool need_kidx) {
+msa_status_t check_cache(const msa_cache_t *c, bool need_kv, bool need_kidx, bool fp8) {
   MSA_REQUIRE(c != nullptr, MSA_ERR_INVALID_ARG, "cache is NULL");
   MSA_REQUIRE(!need_kv || (c->k_cache != nullptr && c->v_cache != nullptr),
               MSA_ERR_INVALID_ARG, "k_cache / v_cache is NULL");
   MSA_REQUIRE(!need_kidx || c->k_idx_cache != nullptr, MSA_ERR_INVALID_ARG,
               "k_idx_cache is NULL");
+  MSA_REQUIRE(!fp8 || !need_kv || (c->k_scale != nullptr && c->v_scale != nullptr),
+              MSA_ERR_INVALID_ARG, "FP8 caches: k_scale / v_scale is NULL");
+  MSA_REQUIRE(!fp8 || !need_kidx || c->k_idx_scale != nullptr, MSA_ERR_INVALID_ARG,
+              "FP8 caches: k_idx_scale is NULL");
   MSA_REQUIRE(c->block_table != nullptr && c->seq_lens != nullptr, MSA_ERR_INVALID_ARG,
               "block_table / seq_lens is NULL");
   MSA_REQUIRE(c->num_phys_blocks > 0 && c->max_blocks_per_seq > 0 && c->num_seqs > 0,
@@ -156,9 +165,10 @@ msa_status_t msa_index_scores(const msa_geom_t *geom, const msa_cache_t *cache,
   msa::Geom g;
   msa_status_t st = check_geom(geom, &g);
   if (st != MSA_OK) return st;
-  if ((st = check_cache(cache, false, true)) != MSA_OK) return st;
+  if ((st = check_cache(cache, false, true, g.fp8)) != MSA_OK) return st;
   if (batch != nullptr) {
     if ((st = check_batch(batch)) != MSA_OK) return st;
+    MSA_REQUIRE(!g.fp8, MSA_ERR_UNSUPPORTED, "the prefill indexer does not read FP8 caches");
     if (batch->total_units == 0) return ok();   // nothing to score
   }
   MSA_REQUIRE(q_idx != nullptr && scores != nullptr, MSA_ERR_INVALID_ARG,
@@ -189,8 +199,9 @@ msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *
   msa::Geom g;
   msa_status_t st = check_geom(geom, &g);
   if (st != MSA_OK) return st;
-  if ((st = check_cache(cache, true, false)) != MSA_OK) return st;
+  if ((st = check_cache(cache, true, false, g.fp8)) != MSA_OK) return st;
   if ((st = check_batch(batch)) != MSA_OK) return st;
+  MSA_REQUIRE(!g.fp8, MSA_ERR_UNSUPPORTED, "prefill attention does not read FP8 caches");
   MSA_REQUIRE(topk >= 1, MSA_ERR_INVALID_ARG, "topk must be positive");
   if (batch->total_units == 0) return ok();     // no queries
   MSA_REQUIRE(q != nullptr && ids != nullptr && out != nullptr, MSA_ERR_INVALID_ARG,
@@ -219,7 +230,7 @@ msa_status_t msa_sparse_attn_decode(const msa_geom_t *geom, const msa_cache_t *c
   msa::Geom g;
   msa_status_t st = check_geom(geom, &g);
   if (st != MSA_OK) return st;
-  if ((st = check_cache(cache, true, false)) != MSA_OK) return st;
+  if ((st = check_cache(cache, true, false, g.fp8)) != MSA_OK) return st;
   MSA_REQUIRE(q != nullptr && ids != nullptr && out != nullptr, MSA_ERR_INVALID_ARG,
               "q / ids / out is NULL");
   MSA_REQUIRE(topk >= 1, MSA_ERR_INVALID_ARG, "topk must be positive");
@@ -253,7 +264,7 @@ const char *msa_status_string(msa_status_t status) {
 
 const char *msa_last_error(void) { return g_last_error.c_str(); }
 
-int32_t msa_version(void) { return 1; }
+int32_t msa_version(void) { return 2; }
 
 msa_status_t msa_qk_norm_rope_insert(const msa_geom_t *geom, const msa_cache_t *cache,
                                      const msa_batch_t *batch, const void *q, const void *k,
@@ -263,7 +274,7 @@ msa_status_t msa_qk_norm_rope_insert(const msa_geom_t *geom, const msa_cache_t *
   msa::Geom g;
   msa_status_t st = check_geom(geom, &g);
   if (st != MSA_OK) return st;
-  if ((st = check_cache(cache, true, true)) != MSA_OK) return st;
+  if ((st = check_cache(cache, true, true, g.fp8)) != MSA_OK) return st;
   if (batch != nullptr) {
     if ((st = check_batch(batch)) != MSA_OK) return st;
     if (batch->total_units == 0) return ok();

@@ -12,6 +12,7 @@ namespace msa {
 struct Geom {
   int Hq, Hkv, D, Hi, Di, nsel;
   bool bf16;
+  bool fp8;   // FP8 E4M3 caches with power-of-two scales per 32 channels
   int G() const { return Hq / Hkv; }
   int Hs() const { return Hi / nsel; }
 };

@@ -35,6 +35,14 @@
 //      one xor lane shuffle per channel. Four rows per lane are in flight at once.
 // Everything is HBM streaming: each input byte is read once and each output byte
 // written once.
+//
+// FP8 caches: K, V and the indexer keys are stored as E4M3 codes with one
+// power-of-two scale 2^e per 32 channels of a token's head row (e the smallest
+// with max|x| / 2^e <= 448, stored as e + 127; codes round x / 2^e to nearest
+// even). Four lanes (8 channels each) share a 32-channel block: they take its
+// maximum with DPP, and each converts its channels with v_cvt_pk_fp8_f32. V's
+// scales, one per (token, block), are found from the staged tile before the
+// transposed codes are written.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -56,6 +64,7 @@ struct InsertArgs {
   int mbps;                  // max blocks per sequence
   const char *q, *k, *v, *kidx, *qw, *kw;
   char *q_out, *kc, *vc, *ic;
+  uint8_t *ks, *vs, *is;     // FP8 caches: scale bytes of K, V, indexer keys
   int Hq, Hkv, Hi, Di, rd;
   float eps, theta;
 };
@@ -95,11 +104,45 @@ struct Bits {
   E e[EPL];
 };
 
+// Exponent of the power-of-two scale of a 32-channel block whose largest
+// magnitude is amax: the smallest e with amax / 2^e <= 448 (448 = 0.875 * 2^9, the
+// largest E4M3 value), clamped to the scale byte's range [-127, 127].
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (amax == 0.f) return -127;
+  int k;
+  const float fr = frexpf(amax, &k);   // amax = fr * 2^k, fr in [0.5, 1)
+  const int e = k - 9 + (fr > 0.875f ? 1 : 0);
+  return min(max(e, -127), 127);
+}
+
+// E4M3 codes (nearest, ties to even) of four values within [-448, 448], byte i
+// holding the i-th value.
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+
+// Codes of 8 channels scaled by 2^-e.
+__device__ __forceinline__ uint2 fp8x8(const float *x, int e) {
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = ldexpf(x[i], -e);
+  return uint2{fp8x4(y[0], y[1], y[2], y[3]), fp8x4(y[4], y[5], y[6], y[7])};
+}
+
+__device__ __forceinline__ float absmax8(const float *x) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+  return m;
+}
+
 __device__ __forceinline__ uint4 ld16(const char *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void st16(char *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
 
-template <bool BF, int D>
+template <bool BF, int D, bool FP8>
 __global__ __launch_bounds__(kThreads) void qk_norm_rope_insert_kernel(InsertArgs a) {
+  static_assert(!FP8 || BF, "FP8 caches come with bf16 inputs");
   constexpr int SZ = BF ? 2 : 4;      // bytes per element
   constexpr int EPL = 16 / SZ;        // elements per lane (16 bytes)
   constexpr int LPH = D / EPL;        // lanes per head row
@@ -142,34 +185,104 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_insert_kernel(InsertArg
 
     const int nh = (a.Hi - j + a.Hkv - 1) / a.Hkv;           // indexer heads j, j+H_kv, ...
     const int IB = a.Di * SZ, CPI = IB / 16;
-    for (int c = tid; c < n * nh * CPI; c += kThreads) {
-      const int ch = c % CPI, rest = c / CPI;
-      const int m = rest % nh, t = rest / nh;
-      const int h = j + m * a.Hkv;
-      const uint4 x = ld16(a.kidx + (static_cast<int64_t>(row0 + t) * a.Hi + h) * IB + ch * 16);
-      st16(a.ic + ((phys * a.Hi + h) * kBlk + rbase + t) * IB + ch * 16, x);
+    if constexpr (FP8) {
+      // (token, head, 32-channel block) per group of 4 lanes, 8 channels a lane
+      const int NCI = a.Di / 32;
+      const int items = n * nh * NCI;
+      const int q4 = tid % 4, grp4 = tid / 4;
+      for (int base = 0; base < items; base += kThreads / 4) {
+        const int it = base + grp4;
+        const bool ok = it < items;
+        const int itc = ok ? it : items - 1;
+        const int cb = itc % NCI, rest = itc / NCI;
+        const int m = rest % nh, t = rest / nh;
+        const int h = j + m * a.Hkv;
+        float x[8];
+        unpack16<true>(ld16(a.kidx + (static_cast<int64_t>(row0 + t) * a.Hi + h) * IB +
+                            cb * 64 + q4 * 16), x);
+        const int ex = mx_exponent(group_max<4>(absmax8(x)));
+        const uint2 w = fp8x8(x, ex);
+        if (ok) {
+          const int64_t rowb = (phys * a.Hi + h) * kBlk + rbase + t;   // cache row
+          *reinterpret_cast<uint2 *>(a.ic + rowb * a.Di + cb * 32 + q4 * 8) = w;
+          if (q4 == 0) a.is[rowb * NCI + cb] = static_cast<uint8_t>(ex + 127);
+        }
+      }
+    } else {
+      for (int c = tid; c < n * nh * CPI; c += kThreads) {
+        const int ch = c % CPI, rest = c / CPI;
+        const int m = rest % nh, t = rest / nh;
+        const int h = j + m * a.Hkv;
+        const uint4 x =
+            ld16(a.kidx + (static_cast<int64_t>(row0 + t) * a.Hi + h) * IB + ch * 16);
+        st16(a.ic + ((phys * a.Hi + h) * kBlk + rbase + t) * IB + ch * 16, x);
+      }
     }
     __syncthreads();
 
-    char *vdst = a.vc + (phys * a.Hkv + j) * static_cast<int64_t>(D) * kBlk * SZ;
-    if (rbase % EPL == 0 && n % EPL == 0) {
-      // lane -> (channel d, EPL consecutive tokens): 16-byte stores along a d-row
-      for (int c = tid; c < D * (n / EPL); c += kThreads) {
-        const int d = c % D, tc = c / D;
-        Bits<SZ, EPL> x;
+    if constexpr (FP8) {
+      constexpr int NC = D / 32;
+      int *es = reinterpret_cast<int *>(lds + n * RB);         // exponents [n][NC]
+      uint8_t *vsd = a.vs + (phys * a.Hkv + j) * NC * kBlk;   // scales [NC][128]
+      const int q4 = tid % 4, grp4 = tid / 4;
+      for (int base = 0; base < n * NC; base += kThreads / 4) {
+        const int it = base + grp4;
+        const bool ok = it < n * NC;
+        const int itc = ok ? it : n * NC - 1;
+        const int t = itc / NC, cb = itc % NC;
+        float x[8];
+        unpack16<true>(*reinterpret_cast<const uint4 *>(lds + t * RB + cb * 64 + q4 * 16), x);
+        const int ex = mx_exponent(group_max<4>(absmax8(x)));
+        if (ok && q4 == 0) {
+          es[t * NC + cb] = ex;
+          vsd[cb * kBlk + rbase + t] = static_cast<uint8_t>(ex + 127);
+        }
+      }
+      __syncthreads();
+      uint8_t *vdst8 = reinterpret_cast<uint8_t *>(a.vc) + (phys * a.Hkv + j) * D * kBlk;
+      auto val = [&](int t, int d) {
+        return ldexpf(bf16_to_f32(*reinterpret_cast<const uint16_t *>(lds + t * RB + d * 2)),
+                      -es[t * NC + d / 32]);
+      };
+      if (rbase % 16 == 0 && n % 16 == 0) {
+        // lane -> (channel d, 16 consecutive tokens): 16-byte stores along a d-row
+        for (int c = tid; c < D * (n / 16); c += kThreads) {
+          const int d = c % D, t0 = (c / D) * 16;
+          uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e)
-          x.e[e] = *reinterpret_cast<const typename Bits<SZ, EPL>::E *>(
-              lds + (tc * EPL + e) * RB + d * SZ);
-        st16(vdst + (static_cast<int64_t>(d) * kBlk + rbase + tc * EPL) * SZ,
-             __builtin_bit_cast(uint4, x));
+          for (int i = 0; i < 4; ++i)
+            w[i] = fp8x4(val(t0 + 4 * i, d), val(t0 + 4 * i + 1, d), val(t0 + 4 * i + 2, d),
+                         val(t0 + 4 * i + 3, d));
+          st16(reinterpret_cast<char *>(vdst8 + d * kBlk + rbase + t0),
+               uint4{w[0], w[1], w[2], w[3]});
+        }
+      } else {
+        for (int c = tid; c < D * n; c += kThreads) {
+          const int t = c % n, d = c / n;
+          vdst8[d * kBlk + rbase + t] = static_cast<uint8_t>(fp8x4(val(t, d), 0.f, 0.f, 0.f));
+        }
       }
     } else {
-      for (int c = tid; c < D * n; c += kThreads) {
-        const int t = c % n, d = c / n;
-        using E = typename Bits<SZ, EPL>::E;
-        *reinterpret_cast<E *>(vdst + (static_cast<int64_t>(d) * kBlk + rbase + t) * SZ) =
-            *reinterpret_cast<const E *>(lds + t * RB + d * SZ);
+      char *vdst = a.vc + (phys * a.Hkv + j) * static_cast<int64_t>(D) * kBlk * SZ;
+      if (rbase % EPL == 0 && n % EPL == 0) {
+        // lane -> (channel d, EPL consecutive tokens): 16-byte stores along a d-row
+        for (int c = tid; c < D * (n / EPL); c += kThreads) {
+          const int d = c % D, tc = c / D;
+          Bits<SZ, EPL> x;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e)
+            x.e[e] = *reinterpret_cast<const typename Bits<SZ, EPL>::E *>(
+                lds + (tc * EPL + e) * RB + d * SZ);
+          st16(vdst + (static_cast<int64_t>(d) * kBlk + rbase + tc * EPL) * SZ,
+               __builtin_bit_cast(uint4, x));
+        }
+      } else {
+        for (int c = tid; c < D * n; c += kThreads) {
+          const int t = c % n, d = c / n;
+          using E = typename Bits<SZ, EPL>::E;
+          *reinterpret_cast<E *>(vdst + (static_cast<int64_t>(d) * kBlk + rbase + t) * SZ) =
+              *reinterpret_cast<const E *>(lds + t * RB + d * SZ);
+        }
       }
     }
     __syncthreads();   // the LDS tile is reused below
@@ -263,14 +376,27 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_insert_kernel(InsertArg
           }
         }
       }
-      if (ok[u]) st16(dst[u] + c0 * SZ, pack16<BF>(x));
+      if constexpr (FP8) {
+        // keys: codes and a scale per 32 channels (4 lanes); queries stay bf16
+        const int ex = mx_exponent(group_max<4>(absmax8(x)));
+        if (ok[u] && isk[u]) {
+          const int64_t rowk = (phys * a.Hkv + j) * kBlk + rbase + tt[u];   // cache row
+          *reinterpret_cast<uint2 *>(a.kc + rowk * D + c0) = fp8x8(x, ex);
+          if (lane % 4 == 0) a.ks[rowk * (D / 32) + c0 / 32] = static_cast<uint8_t>(ex + 127);
+        } else if (ok[u]) {
+          st16(dst[u] + c0 * SZ, pack16<BF>(x));
+        }
+      } else {
+        if (ok[u]) st16(dst[u] + c0 * SZ, pack16<BF>(x));
+      }
     }
   }
 }
 
-template <bool BF, int D>
+template <bool BF, int D, bool FP8 = false>
 hipError_t launch_one(const InsertArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((qk_norm_rope_insert_kernel<BF, D>), grid, dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((qk_norm_rope_insert_kernel<BF, D, FP8>), grid, dim3(kThreads), lds, st,
+                     a);
   return hipGetLastError();
 }
 
@@ -296,6 +422,9 @@ hipError_t launch_qk_norm_rope_insert(const Geom &g, const msa_cache_t &c, const
   a.kc = static_cast<char *>(c.k_cache);
   a.vc = static_cast<char *>(c.v_cache);
   a.ic = static_cast<char *>(c.k_idx_cache);
+  a.ks = c.k_scale;
+  a.vs = c.v_scale;
+  a.is = c.k_idx_scale;
   a.Hq = g.Hq;
   a.Hkv = g.Hkv;
   a.Hi = g.Hi;
@@ -306,9 +435,14 @@ hipError_t launch_qk_norm_rope_insert(const Geom &g, const msa_cache_t &c, const
 
   const int rows = b != nullptr ? kBlk : 1;            // tokens per work-group at most
   const int sz = g.bf16 ? 2 : 4;
+  // the V tile (+ FP8 block exponents) in phase 1, the cos/sin table after it
   const size_t lds = std::max<size_t>(size_t(rows) * (rd / 2) * sizeof(float2),
-                                      size_t(rows) * g.D * sz);
+                                      size_t(rows) * g.D * sz +
+                                          (g.fp8 ? size_t(rows) * (g.D / 32) * sizeof(int) : 0));
   const dim3 grid(b != nullptr ? b->total_units : c.num_seqs, g.Hkv);
+  if (g.fp8)
+    return g.D == 64 ? launch_one<true, 64, true>(a, grid, lds, st)
+                     : launch_one<true, 128, true>(a, grid, lds, st);
   if (g.bf16)
     return g.D == 64 ? launch_one<true, 64>(a, grid, lds, st)
                      : launch_one<true, 128>(a, grid, lds, st);

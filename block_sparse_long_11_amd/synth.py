@@ -42,6 +42,8 @@ BLOCK = 128
 # stream ids of the seeded draws
 _T_Q, _T_K, _T_V, _T_QIDX, _T_KIDX, _T_PLANT_POS, _T_PLANT_DIR, _T_PERM = range(8)
 _T_NEW_Q, _T_NEW_K, _T_NEW_V, _T_NEW_KIDX, _T_NORM_W, _T_ROW_SCALE = range(8, 14)
+_T_SCALE_K, _T_SCALE_V, _T_SCALE_KIDX = range(14, 17)
+SCALE_BLOCK = 32
 
 # Rotary settings of the new-token step: rotary_dim 64 of head_dim 128 (partial
 # rotary factor 0.5); eps and theta are not given by the pages, these are the
@@ -65,6 +67,7 @@ class Workload:
     plant_count: int = 8            # planted blocks per span per (seq, group)
     plant_span: Optional[int] = 32  # span in blocks; None = whole context
     seed: int = 0
+    cache_format: str = "plain"     # "plain" or "fp8" (E4M3 codes + power-of-two scales)
 
     @property
     def is_decode(self):
@@ -111,6 +114,9 @@ WORKLOADS = {
         "chunked_prefill", "bf16",
         [1048576 + 8192, 524288 + 8192, 131072 + 8192, 32768 + 8192], [8192] * 4,
         topk=64, plant_count=8, plant_span=32, seed=1005),
+    "decode_1m_b8_fp8": Workload(
+        "decode_1m_b8_fp8", "bf16", [1048576] * 8, None, topk=64, plant_count=63,
+        plant_span=None, seed=1004, cache_format="fp8"),
 }
 
 
@@ -196,7 +202,13 @@ def make_inputs(w: Workload, device="cpu", permute=False, chunk_blocks=2048):
     d-major), k_idx_cache [P][H_i][128][D_i] (all in the workload dtype),
     block_table int32 [B][max_blocks], seq_lens int32 [B], q_lens int32 [B]
     (decode: ones) and cu_q_lens int32 [B+1]. The caches are drawn chunk by chunk
-    of physical blocks so that only one fp32 chunk is alive at a time."""
+    of physical blocks so that only one fp32 chunk is alive at a time.
+
+    With w.cache_format == "fp8" the caches are uint8 E4M3 codes and the dict also
+    holds k_scale [P][H_kv][128][D/32], v_scale [P][H_kv][D/32][128] and
+    k_idx_scale [P][H_i][128][D_i/32] (bytes e + 127): each 32-channel block of a
+    token row gets a seeded exponent e from {-1, 0, 1}, and its codes are torch's
+    float8_e4m3fn cast of the drawn values times 2^-e."""
     dt = _torch_dtype(w)
     B, P = w.num_seqs, w.num_phys_blocks
     T = w.total_q
@@ -226,12 +238,19 @@ def make_inputs(w: Workload, device="cpu", permute=False, chunk_blocks=2048):
             qi[cu[r]:cu[r + 1], g * hs:(g + 1) * hs, :] += a * u
     out["q_idx"] = qi.to(dt)
 
-    def cache(stream, heads, dim, plant, d_major=False):
+    fp8 = w.cache_format == "fp8"
+
+    def cache(stream, heads, dim, plant, d_major=False, scale_stream=None):
         # drawn in packed order, chunk by chunk, then scattered to physical blocks;
         # d_major stores each block's [128][dim] rows transposed as [dim][128]
         gen = _gen(w, stream, device)
         shape = (P, heads, dim, BLOCK) if d_major else (P, heads, BLOCK, dim)
-        res = torch.empty(shape, dtype=dt, device=device)
+        res = torch.empty(shape, dtype=torch.uint8 if fp8 else dt, device=device)
+        if fp8:
+            sgen = _gen(w, scale_stream, device)
+            nb = dim // SCALE_BLOCK
+            sshape = (P, heads, nb, BLOCK) if d_major else (P, heads, BLOCK, nb)
+            scales = torch.empty(sshape, dtype=torch.uint8, device=device)
         for c0 in range(0, P, chunk_blocks):
             c1 = min(P, c0 + chunk_blocks)
             x = _randn(gen, (c1 - c0, heads, BLOCK, dim), device)
@@ -244,13 +263,30 @@ def make_inputs(w: Workload, device="cpu", permute=False, chunk_blocks=2048):
                         ut = torch.from_numpy(u).to(device)[None, :, None, :]
                         x[idx, g * hs:(g + 1) * hs] += a * ut
             dst = torch.from_numpy(perm[c0:c1]).to(device)
-            res[dst] = (x.transpose(2, 3) if d_major else x).to(dt)
+            if fp8:
+                e = torch.randint(-1, 2, (c1 - c0, heads, BLOCK, dim // SCALE_BLOCK),
+                                  generator=sgen, device=device, dtype=torch.int32)
+                y = x * torch.exp2(-e.float()).repeat_interleave(SCALE_BLOCK, dim=3)
+                codes = y.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+                sc = (e + 127).to(torch.uint8)
+                res[dst] = codes.transpose(2, 3).contiguous() if d_major else codes
+                scales[dst] = sc.transpose(2, 3).contiguous() if d_major else sc
+                del y, codes, e
+            else:
+                res[dst] = (x.transpose(2, 3) if d_major else x).to(dt)
             del x
-        return res
+        return (res, scales) if fp8 else res
 
-    out["k_cache"] = cache(_T_K, H_kv, D, False)
-    out["v_cache"] = cache(_T_V, H_kv, D, False, d_major=True)
-    out["k_idx_cache"] = cache(_T_KIDX, H_i, D_i, True)
+    if fp8:
+        out["k_cache"], out["k_scale"] = cache(_T_K, H_kv, D, False, scale_stream=_T_SCALE_K)
+        out["v_cache"], out["v_scale"] = cache(_T_V, H_kv, D, False, d_major=True,
+                                               scale_stream=_T_SCALE_V)
+        out["k_idx_cache"], out["k_idx_scale"] = cache(_T_KIDX, H_i, D_i, True,
+                                                       scale_stream=_T_SCALE_KIDX)
+    else:
+        out["k_cache"] = cache(_T_K, H_kv, D, False)
+        out["v_cache"] = cache(_T_V, H_kv, D, False, d_major=True)
+        out["k_idx_cache"] = cache(_T_KIDX, H_i, D_i, True)
     out["block_table"] = torch.from_numpy(bt).to(device)
     out["seq_lens"] = torch.tensor(w.seq_lens, dtype=torch.int32, device=device)
     out["q_lens"] = torch.tensor(q_lens, dtype=torch.int32, device=device)

@@ -41,6 +41,21 @@
  *                      queries (their K/V/k_idx are inserted before these calls)
  *   Token s of sequence r lives in physical block block_table[r][s / 128], row
  *   s % 128. Byte offsets are 64-bit.
+ *
+ * FP8 caches (geom->cache_format == MSA_CACHE_FP8_E4M3; [dd] "What's coming" lists
+ * FP8 KV-cache paths, the format is this library's): the three caches hold one
+ * byte per element, an OCP E4M3 code (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, largest finite 448, S.1111.111 = NaN), same shapes as above.
+ * Every 32 consecutive channels of one token's head vector share a scale 2^e,
+ * stored as the byte e + 127 (OCP E8M0); the element's value is code * 2^e.
+ *   k_scale            uint8 [num_phys_blocks][H_kv][128][D/32]
+ *   v_scale            uint8 [num_phys_blocks][H_kv][D/32][128]  (token fastest,
+ *                      like the d-major V codes)
+ *   k_idx_scale        uint8 [num_phys_blocks][H_i][128][D_i/32]
+ * A writer picks e as the smallest integer with max|x| / 2^e <= 448 over the 32
+ * channels and stores the nearest code of x / 2^e (ties to even), as
+ * msa_qk_norm_rope_insert does. Scales never span tokens, so inserting a token
+ * touches only that token's bytes.
  */
 #ifndef MSA_H_
 #define MSA_H_
@@ -64,6 +79,11 @@ typedef enum {
 
 typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype_t;
 
+typedef enum {
+  MSA_CACHE_PLAIN = 0,      /* caches in geom->dtype */
+  MSA_CACHE_FP8_E4M3 = 1    /* E4M3 codes + a power-of-two scale per 32 channels */
+} msa_cache_format_t;
+
 /* Head geometry ([feat] "Grouped-query attention": 64 query heads share 4 KV heads;
  * query head i reads KV head i / (num_q_heads / num_kv_heads)).
  *   num_q_heads % num_kv_heads == 0, (num_q_heads / num_kv_heads) <= 16 for bf16
@@ -73,7 +93,11 @@ typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype_t;
  *     blocks of KV head g) or 1 (the sum over all indexer heads selects for every
  *     KV head); num_idx_heads % num_sel_groups == 0, H_s * idx_head_dim <= 512
  *   block_size must be 128.
- *   dtype applies to q, q_idx, the three caches and out. */
+ *   dtype applies to q, q_idx, out and (cache_format PLAIN) the three caches.
+ *   cache_format MSA_CACHE_FP8_E4M3 needs dtype MSA_BF16; it is read by the decode
+ *     calls (msa_index_scores with batch == NULL, msa_sparse_attn_decode) and
+ *     written by msa_qk_norm_rope_insert; the prefill indexer and attention return
+ *     MSA_ERR_UNSUPPORTED for it. */
 typedef struct {
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -83,6 +107,7 @@ typedef struct {
   int32_t num_sel_groups;
   int32_t block_size;
   int32_t dtype;                    /* msa_dtype_t */
+  int32_t cache_format;             /* msa_cache_format_t */
 } msa_geom_t;
 
 /* The three caches are written only by msa_qk_norm_rope_insert; every other
@@ -96,6 +121,9 @@ typedef struct {
   int32_t max_blocks_per_seq;
   const int32_t *seq_lens;          /* [num_seqs] */
   int32_t num_seqs;
+  uint8_t *k_scale;                 /* FP8 caches only (else ignored), see above */
+  uint8_t *v_scale;
+  uint8_t *k_idx_scale;
 } msa_cache_t;
 
 /* One prefill unit: the new queries of request r whose positions fall in the

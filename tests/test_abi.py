@@ -40,14 +40,15 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.msa_version() >= 1
+    assert lib.msa_version() >= 2
     assert lib.msa_status_string(0) == b"MSA_OK"
     assert lib.msa_status_string(3) == b"MSA_ERR_WORKSPACE_TOO_SMALL"
 
 
 def _geom(**kw):
     base = dict(num_q_heads=64, num_kv_heads=4, head_dim=128, num_idx_heads=8,
-                idx_head_dim=64, num_sel_groups=4, block_size=128, dtype=msa.MSA_BF16)
+                idx_head_dim=64, num_sel_groups=4, block_size=128, dtype=msa.MSA_BF16,
+                cache_format=msa.MSA_CACHE_PLAIN)
     base.update(kw)
     return msa._Geom(*[base[f] for f, _ in msa._Geom._fields_])
 
@@ -57,7 +58,8 @@ FAKE = 0x1000    # never dereferenced: validation fails before any launch
 
 def _cache(**kw):
     base = dict(k_cache=FAKE, v_cache=FAKE, k_idx_cache=FAKE, num_phys_blocks=10,
-                block_table=FAKE, max_blocks_per_seq=4, seq_lens=FAKE, num_seqs=2)
+                block_table=FAKE, max_blocks_per_seq=4, seq_lens=FAKE, num_seqs=2,
+                k_scale=FAKE, v_scale=FAKE, k_idx_scale=FAKE)
     base.update(kw)
     return msa._Cache(*[base[f] for f, _ in msa._Cache._fields_])
 
@@ -73,6 +75,8 @@ BAD_GEOMS = [
     (dict(idx_head_dim=48), UNSUPPORTED),
     (dict(num_q_heads=128, num_kv_heads=4), UNSUPPORTED),     # G = 32 on bf16
     (dict(num_idx_heads=12, num_sel_groups=4), UNSUPPORTED),  # 3 heads per group
+    (dict(cache_format=2), UNSUPPORTED),
+    (dict(cache_format=msa.MSA_CACHE_FP8_E4M3, dtype=msa.MSA_F32), UNSUPPORTED),
 ]
 
 
@@ -217,3 +221,26 @@ def test_insert_binding_checks_shapes(lib):
                                     w, w, 1e-6, 1e6, 64)
     with pytest.raises(TypeError):
         msa.msa_qk_norm_rope_insert(geom, cache, None, q.float(), kv, kv, ki, w, w, 1e-6, 1e6, 64)
+
+
+def test_fp8_cache_checks(lib):
+    g = _geom(cache_format=msa.MSA_CACHE_FP8_E4M3)
+    c = _cache()
+    b = msa._Batch(FAKE, 3, 300)
+    # the prefill indexer and prefill attention do not read FP8 caches
+    assert lib.msa_index_scores(ctypes.byref(g), ctypes.byref(c), ctypes.byref(b), FAKE, FAKE,
+                                None) == UNSUPPORTED
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(g), ctypes.byref(c), ctypes.byref(b), FAKE,
+                                       FAKE, 4, 0.0, FAKE, None, None) == UNSUPPORTED
+    # scale arrays are required where a call reads or writes that cache
+    c = _cache(k_idx_scale=None)
+    assert lib.msa_index_scores(ctypes.byref(g), ctypes.byref(c), None, FAKE, FAKE,
+                                None) == INVALID
+    c = _cache(v_scale=None)
+    assert lib.msa_sparse_attn_decode(ctypes.byref(g), ctypes.byref(c), FAKE, FAKE, 16, 0.0, 0,
+                                      FAKE, 1 << 30, FAKE, None, None) == INVALID
+    for kw in ("k_scale", "v_scale", "k_idx_scale"):
+        assert _insert(lib, g, _cache(**{kw: None}), b) == INVALID, kw
+    # plain caches ignore the scale pointers
+    g0, c0 = _geom(), _cache(k_scale=None, v_scale=None, k_idx_scale=None)
+    assert _insert(lib, g0, c0, msa._Batch(None, 0, 0)) == OK

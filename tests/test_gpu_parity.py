@@ -23,14 +23,18 @@ def say(msg):
 
 def geometry(w):
     return msa.Geometry(w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_idx_heads,
-                        w.idx_head_dim, w.num_sel_groups, w.dtype)
+                        w.idx_head_dim, w.num_sel_groups, w.dtype, w.cache_format)
+
+
+def cache_of(inp):
+    return msa.Cache(inp["k_cache"], inp["v_cache"], inp["k_idx_cache"], inp["block_table"],
+                     inp["seq_lens"], inp.get("k_scale"), inp.get("v_scale"),
+                     inp.get("k_idx_scale"))
 
 
 def setup(w, dev, permute=False):
     inp = synth.make_inputs(w, dev, permute=permute)
-    cache = msa.Cache(inp["k_cache"], inp["v_cache"], inp["k_idx_cache"],
-                      inp["block_table"], inp["seq_lens"])
-    return inp, geometry(w), cache
+    return inp, geometry(w), cache_of(inp)
 
 
 def run_gpu(w, inp, geom, cache, dev, num_splits=0):
