@@ -302,27 +302,45 @@ __global__ __launch_bounds__(256) void index_prefill_wide_kernel(
 // one after the other, each accumulator max-pooled while the other chain runs,
 // and the next sub-tile's fragments are read meanwhile. Rows past a unit's end
 // repeat its last row, so they never change a maximum.
+//
+// FP8 indexer keys: the staged rows are the group's E4M3 codes (GD bytes a key,
+// swizzled in 16-byte chunks by key / (16 / chunks per row) so a 16-lane read
+// pass covers distinct banks), and the blocks' scale bytes are staged beside
+// them. The contraction takes the group channels in the order
+// (ks / 2) * 32 + (lane / 32) * 16 + (ks % 2) * 8 for k step ks and lane half
+// lane / 32 (the query operand uses the same order), so one 16-byte LDS read
+// gives a lane its codes for two k steps, all in one 32-channel scale block; they
+// become bf16 with that block's power of two applied in the conversion (exact).
 
 constexpr int kChunk2 = 16;   // blocks per work-group
 // Query tiles per work-group: two (256 query rows, 4 waves, two work-groups per CU).
 constexpr int kTiles = 2;
 constexpr int kIdxThreads = kTiles * 2 * kWave;
 
-template <int DI, int HS>
+template <int DI, int HS, bool FP8>
 __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void index_prefill_bf16_kernel(
-    const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
-    const int32_t *__restrict__ block_table, const msa_unit_t *__restrict__ units,
-    int num_units, int max_blocks, int nsel, float *__restrict__ scores) {
+    const uint16_t *__restrict__ q_idx, const void *__restrict__ k_idx_,
+    const uint8_t *__restrict__ k_scale, const int32_t *__restrict__ block_table,
+    const msa_unit_t *__restrict__ units, int num_units, int max_blocks, int nsel,
+    float *__restrict__ scores) {
   constexpr int GD = HS * DI;            // group width
   constexpr int KS = GD / 16;            // k steps
-  constexpr int CHG = GD / 8;            // 16-byte chunks per staged key row
-  constexpr int CPH = DI / 8;            // chunks per head
+  constexpr int CHG = FP8 ? GD / 16 : GD / 8;   // 16-byte chunks per staged key row
+  constexpr int CPH = FP8 ? DI / 16 : DI / 8;   // chunks per head
   constexpr int NW = kIdxThreads / kWave;
   constexpr int NLD = (kBlk * CHG + kIdxThreads - 1) / kIdxThreads;
+  constexpr int NS = DI / 32;            // FP8 scale bytes per key and head
+  constexpr int SCH = FP8 ? HS * kBlk * NS / 16 : 1;   // 16-byte chunks of a block's scales
   static_assert(GD <= 128, "group width");
+  static_assert(!FP8 || SCH <= kWave, "one wave stages the scales");
   __shared__ u32x4 Kb0[kBlk * CHG], Kb1[kBlk * CHG];
+  __shared__ u32x4 Ks0[SCH], Ks1[SCH];
   __shared__ float red[NW][kChunk2];
+  const uint16_t *k_idx = static_cast<const uint16_t *>(k_idx_);
+  const uint8_t *k_idx8 = static_cast<const uint8_t *>(k_idx_);
+  // FP8 row swizzle: keys sharing a 256-byte bank row get distinct chunk slots
+  auto swz = [](int key) { return FP8 ? (key / (16 / CHG)) % CHG : key % CHG; };
 
   const int half = (num_units + 1) / 2;
   const int u0 = 2 * (static_cast<int>(blockIdx.x) % half) + static_cast<int>(blockIdx.x) / half;
@@ -363,7 +381,8 @@ void index_prefill_bf16_kernel(
     const int q1 = mine.row0 + min(r1, mine.num_rows - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int kk = ks * 16 + (lane / 32) * 8;
+      const int kk = FP8 ? (ks / 2) * 32 + (lane / 32) * 16 + (ks % 2) * 8
+                         : ks * 16 + (lane / 32) * 8;
       const int h = g * HS + kk / DI, d = kk % DI;
       qa[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(
           q_idx + (static_cast<size_t>(q0) * Hi + h) * DI + d));
@@ -373,21 +392,34 @@ void index_prefill_bf16_kernel(
   }
 
   const int32_t *bt = block_table + static_cast<size_t>(un0.r) * max_blocks;
-  auto issue = [&](int b, u32x4 *dst) __attribute__((always_inline)) {
-    const uint16_t *kb = k_idx + static_cast<size_t>(bt[b]) * Hi * kBlk * DI;
+  auto issue = [&](int b, u32x4 *dst, u32x4 *sdst) __attribute__((always_inline)) {
+    const size_t phys = static_cast<size_t>(bt[b]);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int base = (NW * i + wave) * 64;
       if (base < kBlk * CHG) {
-        const int p = base + lane, key = p / CHG, c = (p % CHG) ^ (key % CHG);
-        const int h = g * HS + c / CPH, d = (c % CPH) * 8;
+        const int p = base + lane, key = p / CHG, c = (p % CHG) ^ swz(key);
+        const int h = g * HS + c / CPH;
+        const void *src;
+        if constexpr (FP8)
+          src = k_idx8 + ((phys * Hi + h) * kBlk + key) * DI + (c % CPH) * 16;
+        else
+          src = k_idx + ((phys * Hi + h) * kBlk + key) * DI + (c % CPH) * 8;
         __builtin_amdgcn_global_load_lds(
-            kb + (static_cast<size_t>(h) * kBlk + key) * DI + d,
-            (__attribute__((address_space(3))) void *)(dst + base), 16, 0, 0);
+            src, (__attribute__((address_space(3))) void *)(dst + base), 16, 0, 0);
+      }
+    }
+    if constexpr (FP8) {
+      // the group's scale bytes: head hh's [128][NS] bytes are contiguous
+      if (wave == 0 && lane < SCH) {
+        const int hh = lane / (kBlk * NS / 16), off = (lane % (kBlk * NS / 16)) * 16;
+        __builtin_amdgcn_global_load_lds(
+            k_scale + (phys * Hi + g * HS + hh) * kBlk * NS + off,
+            (__attribute__((address_space(3))) void *)sdst, 16, 0, 0);
       }
     }
   };
-  auto score = [&](int bi, const u32x4 *src) __attribute__((always_inline)) {
+  auto score = [&](int bi, const u32x4 *src, const u32x4 *ssrc) __attribute__((always_inline)) {
     const int b = b0 + bi;
     float m = neg_inf();
     if (wave_live && b < mine.tau) {
@@ -395,10 +427,31 @@ void index_prefill_bf16_kernel(
       f32x16 acc0, acc1;
       auto rd = [&](int nt, bf16x8 *dst) __attribute__((always_inline)) {
         const int key = nt * 32 + lane % 32;
+        if constexpr (FP8) {
+          const uint8_t *sb = reinterpret_cast<const uint8_t *>(ssrc);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          dst[ks] = __builtin_bit_cast(bf16x8,
-                                       src[key * CHG + ((2 * ks + lane / 32) ^ (key % CHG))]);
+          for (int k2 = 0; k2 < KS / 2; ++k2) {
+            const u32x4 w = src[key * CHG + ((2 * k2 + lane / 32) ^ swz(key))];
+            const int hh = (k2 * 32) / DI, sub = (k2 * 32 % DI) / 32;
+            const float sc =
+                ldexpf(1.0f, static_cast<int>(sb[(hh * kBlk + key) * NS + sub]) - 127);
+            uint32_t o[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              o[2 * i] = __builtin_bit_cast(
+                  uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, false));
+              o[2 * i + 1] = __builtin_bit_cast(
+                  uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, true));
+            }
+            dst[2 * k2] = as_bf16x8(uint4{o[0], o[1], o[2], o[3]});
+            dst[2 * k2 + 1] = as_bf16x8(uint4{o[4], o[5], o[6], o[7]});
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            dst[ks] = __builtin_bit_cast(bf16x8,
+                                         src[key * CHG + ((2 * ks + lane / 32) ^ swz(key))]);
+        }
       };
       auto pool = [&](const f32x16 &v) __attribute__((always_inline)) {
 #pragma unroll
@@ -426,17 +479,17 @@ void index_prefill_bf16_kernel(
     if (lane == 0) red[wave][bi] = m;
   };
 
-  issue(b0, Kb0);
+  issue(b0, Kb0, Ks0);
   for (int bi = 0;;) {
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this block's keys landed
     __syncthreads();
-    if (bi + 1 < nblk) issue(b0 + bi + 1, Kb1);
-    score(bi, Kb0);
+    if (bi + 1 < nblk) issue(b0 + bi + 1, Kb1, Ks1);
+    score(bi, Kb0, Ks0);
     if (++bi >= nblk) break;
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
-    if (bi + 1 < nblk) issue(b0 + bi + 1, Kb0);
-    score(bi, Kb1);
+    if (bi + 1 < nblk) issue(b0 + bi + 1, Kb0, Ks0);
+    score(bi, Kb1, Ks1);
     if (++bi >= nblk) break;
   }
   __syncthreads();
@@ -523,7 +576,7 @@ hipError_t dispatch_decode_fp8(const Geom &g, const msa_cache_t &c, const void *
   return hipGetLastError();
 }
 
-template <int DI>
+template <int DI, bool FP8>
 hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                  const void *q_idx, float *scores, hipStream_t st) {
   const uint16_t *q = static_cast<const uint16_t *>(q_idx);
@@ -535,9 +588,9 @@ hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_
 #define MSA_CASE(HS)                                                                     \
   case HS:                                                                               \
     if constexpr (HS * DI <= 128)                                                        \
-      index_prefill_bf16_kernel<DI, HS><<<grid, kIdxThreads, 0, st>>>(                   \
-          q, k, c.block_table, b.units, b.total_units, c.max_blocks_per_seq, g.nsel,     \
-          scores);                                                                       \
+      index_prefill_bf16_kernel<DI, HS, FP8><<<grid, kIdxThreads, 0, st>>>(              \
+          q, c.k_idx_cache, c.k_idx_scale, c.block_table, b.units, b.total_units,        \
+          c.max_blocks_per_seq, g.nsel, scores);                                         \
     break;
       MSA_CASE(1) MSA_CASE(2) MSA_CASE(4)
 #undef MSA_CASE
@@ -545,6 +598,7 @@ hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_
     }
     return hipGetLastError();
   }
+  if (FP8) return hipErrorInvalidValue;   // wide groups read bf16 keys only
   const dim3 grid(b.total_units, (c.max_blocks_per_seq + kChunk - 1) / kChunk, g.nsel);
   switch (hs) {
 #define MSA_CASE(HS)                                                                     \
@@ -578,10 +632,13 @@ hipError_t launch_index_decode(const Geom &g, const msa_cache_t &c, const void *
 hipError_t launch_index_prefill(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                 const void *q_idx, float *scores, hipStream_t st) {
   if (b.total_units == 0) return hipSuccess;
-  if (g.fp8) return hipErrorInvalidValue;   // rejected by the entry point already
+  if (g.fp8) {
+    return g.Di == 64 ? dispatch_prefill_bf16<64, true>(g, c, b, q_idx, scores, st)
+                      : dispatch_prefill_bf16<32, true>(g, c, b, q_idx, scores, st);
+  }
   if (g.bf16) {
-    return g.Di == 64 ? dispatch_prefill_bf16<64>(g, c, b, q_idx, scores, st)
-                      : dispatch_prefill_bf16<32>(g, c, b, q_idx, scores, st);
+    return g.Di == 64 ? dispatch_prefill_bf16<64, false>(g, c, b, q_idx, scores, st)
+                      : dispatch_prefill_bf16<32, false>(g, c, b, q_idx, scores, st);
   }
   const dim3 grid(b.total_units, c.max_blocks_per_seq, g.nsel);
   index_prefill_f32_kernel<<<grid, 128, 0, st>>>(

@@ -94,10 +94,11 @@ typedef enum {
  *     KV head); num_idx_heads % num_sel_groups == 0, H_s * idx_head_dim <= 512
  *   block_size must be 128.
  *   dtype applies to q, q_idx, out and (cache_format PLAIN) the three caches.
- *   cache_format MSA_CACHE_FP8_E4M3 needs dtype MSA_BF16; it is read by the decode
- *     calls (msa_index_scores with batch == NULL, msa_sparse_attn_decode) and
- *     written by msa_qk_norm_rope_insert; the prefill indexer and attention return
- *     MSA_ERR_UNSUPPORTED for it. */
+ *   cache_format MSA_CACHE_FP8_E4M3 needs dtype MSA_BF16; it is read by
+ *     msa_index_scores (prefill: selection groups of at most 128 channels,
+ *     H_s * D_i <= 128) and msa_sparse_attn_decode, and written by
+ *     msa_qk_norm_rope_insert; msa_sparse_attn_prefill returns MSA_ERR_UNSUPPORTED
+ *     for it. */
 typedef struct {
   int32_t num_q_heads;
   int32_t num_kv_heads;

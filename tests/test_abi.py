@@ -227,9 +227,10 @@ def test_fp8_cache_checks(lib):
     g = _geom(cache_format=msa.MSA_CACHE_FP8_E4M3)
     c = _cache()
     b = msa._Batch(FAKE, 3, 300)
-    # the prefill indexer and prefill attention do not read FP8 caches
-    assert lib.msa_index_scores(ctypes.byref(g), ctypes.byref(c), ctypes.byref(b), FAKE, FAKE,
-                                None) == UNSUPPORTED
+    # the prefill indexer reads FP8 caches for groups up to 128 channels only
+    g_wide = _geom(cache_format=msa.MSA_CACHE_FP8_E4M3, num_sel_groups=1)   # 8 x 64 channels
+    assert lib.msa_index_scores(ctypes.byref(g_wide), ctypes.byref(c), ctypes.byref(b), FAKE,
+                                FAKE, None) == UNSUPPORTED
     assert lib.msa_sparse_attn_prefill(ctypes.byref(g), ctypes.byref(c), ctypes.byref(b), FAKE,
                                        FAKE, 4, 0.0, FAKE, None, None) == UNSUPPORTED
     # scale arrays are required where a call reads or writes that cache

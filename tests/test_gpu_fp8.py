@@ -276,3 +276,41 @@ def test_fp8_full_size_decode_1m_sampled(gpu_device):
     assert np.isposinf(sc[:, :, -1]).all() and np.isfinite(sc[:, :, :-1]).all()
     del inp, cache
     torch.cuda.empty_cache()
+
+
+def prefill_index_parity(w, inp, cache, scores, ids, where):
+    _, _, ki = decoded(fp8_host(cache))
+    qi = host(inp["q_idx"])
+    bt = inp["block_table"].cpu().numpy()
+    units = O.prefill_units(w.seq_lens, w.q_lens)
+    ref = O.index_scores(units, qi, ki, bt, w.num_sel_groups, bt.shape[1])
+    P.check_scores(scores, ref, P.score_tolerance(qi, ki, w.num_sel_groups), where)
+    P.check_ids(ids, ref, units, w.topk, where)
+
+
+PREFILL_INDEX = {
+    "m3_heads": dict(seq_lens=(1100,), q_lens=(600,), num_q_heads=64, num_kv_heads=4,
+                     num_idx_heads=8, num_sel_groups=4, topk=5),
+    "ragged_permuted": dict(seq_lens=(1000, 260, 129, 5), q_lens=(1000, 200, 1, 5), topk=4),
+    "one_head_groups_di32": dict(seq_lens=(1300,), q_lens=(700,), num_q_heads=16,
+                                 num_kv_heads=4, head_dim=64, num_idx_heads=4, idx_head_dim=32,
+                                 num_sel_groups=4, topk=3),
+    "four_heads_di32": dict(seq_lens=(900, 400), q_lens=(500, 400), num_idx_heads=4,
+                            idx_head_dim=32, num_sel_groups=1, topk=4),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL_INDEX))
+def test_fp8_prefill_indexer_parity(name, gpu_device):
+    w = synth.small_workload(cache_format="fp8", **PREFILL_INDEX[name])
+    say(f"fp8 prefill indexer {name}")
+    inp, geom, cache = T.setup(w, gpu_device, permute=True)
+    batch = msa.make_batch(w.seq_lens, w.q_lens, gpu_device)
+    scores = torch.empty((batch.total_units, w.num_sel_groups, cache.max_blocks),
+                         dtype=torch.float32, device=gpu_device)
+    ids = torch.empty((batch.total_units, w.num_sel_groups, w.topk), dtype=torch.int32,
+                      device=gpu_device)
+    msa.msa_index_scores(geom, cache, batch, inp["q_idx"], scores)
+    msa.msa_select_topk_blocks(scores, w.topk, ids)
+    torch.cuda.synchronize()
+    prefill_index_parity(w, inp, cache, scores.cpu().numpy(), ids.cpu().numpy(), name)
