@@ -325,8 +325,9 @@ def main():
     ap.add_argument("--workload", default="prefill_32k", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--second", default="decode_1m_b8",
                     help="second workload measured in the same run ('none' to skip)")
-    ap.add_argument("--fp8", default="decode_1m_b8_fp8",
-                    help="FP8-cache workload measured in the same run ('none' to skip)")
+    ap.add_argument("--fp8", default="decode_1m_b8_fp8,prefill_32k_fp8",
+                    help="FP8-cache workloads measured in the same run, comma-separated "
+                         "('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -374,15 +375,18 @@ def main():
         del second["_runner"]
         torch.cuda.empty_cache()
 
-    fp8 = None
-    if args.fp8 != "none" and args.fp8 not in (args.workload, args.second):
-        w3 = synth.WORKLOADS[args.fp8]
-        fp8 = measure(w3, dev, args.steps, args.warmup)
-        log(f"{w3.name}: {fp8['ms_per_step']:.3f} ms/step, kernels {fp8['kernel_ms']}")
-        inserts.append(measure_insert(fp8["_runner"]))
+    fp8 = []
+    for name in ([] if args.fp8 == "none" else args.fp8.split(",")):
+        if name in (args.workload, args.second):
+            continue
+        w3 = synth.WORKLOADS[name]
+        res = measure(w3, dev, args.steps, args.warmup)
+        log(f"{w3.name}: {res['ms_per_step']:.3f} ms/step, kernels {res['kernel_ms']}")
+        inserts.append(measure_insert(res["_runner"]))
         log(f"{w3.name}: insert {inserts[-1]['us_per_launch']:.1f} us")
-        del fp8["_runner"]
+        del res["_runner"]
         torch.cuda.empty_cache()
+        fp8.append(res)
 
     config = dict(workload=w.name, batch=w.num_seqs,
                   seq_lens=w.seq_lens if len(set(w.seq_lens)) > 1 else w.seq_lens[0],
@@ -412,12 +416,12 @@ def main():
         line["second_workload"] = {k: second[k] for k in (
             "workload", "value", "ms_per_step", "kernel_ms", "roofline", "step_hbm_frac")
             if k in second}
-    if fp8 is not None:
-        # the same decode on FP8 caches (E4M3 codes, power-of-two scale per 32
-        # channels): fewer bytes for the same selections
-        line["fp8_cache_workload"] = {k: fp8[k] for k in (
+    if fp8:
+        # the same workloads on FP8 caches (E4M3 codes, power-of-two scale per 32
+        # channels): fewer cache bytes for the same selections
+        line["fp8_cache_workloads"] = [{k: r[k] for k in (
             "workload", "value", "ms_per_step", "kernel_ms", "roofline", "step_hbm_frac")
-            if k in fp8}
+            if k in r} for r in fp8]
     # the new-token step before the path (QK-norm + partial RoPE + cache insert),
     # timed on its own: not part of the step above
     line["qk_norm_rope_insert"] = inserts

@@ -38,6 +38,15 @@
 // are rescaled only when a row's maximum grows by more than 8 (probabilities
 // stay <= 2^8); the result is exact after the final division by the row sum.
 //
+// FP8 caches (E4M3 codes, a power-of-two scale per 32 channels of a token's head
+// row): attn_prefill_fp8_kernel keeps the work-group layout, the LDS layout and
+// swizzles, the operand reads and the softmax of the bf16 kernel, but fills the
+// LDS tiles itself: each thread loads 16 codes of one K row (one scale) and 16
+// keys of one V^T row (16 scales) of a half-block, converts them to bf16 (exact:
+// E4M3 times a power of two is a bf16 value) and writes them; the next
+// half-block's codes are in flight while the current one is attended. Phases are
+// not ping-ponged (the staged registers leave no room for it).
+//
 // fp32 path: plain FMA, one thread per (query, head); for small exact checks.
 #include <type_traits>
 
@@ -384,6 +393,229 @@ void attn_prefill_bf16_kernel(
     lse[static_cast<size_t>(qrow) * Hq + head] = (m_ref + __builtin_log2f(sum)) * kLn2;
 }
 
+// FP8 K/V: same tiles as attn_prefill_bf16_kernel, staged through registers.
+template <int D>
+__global__ __launch_bounds__(kPrefWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_prefill_fp8_kernel(
+    const uint16_t *__restrict__ q, const uint8_t *__restrict__ kc8,
+    const uint8_t *__restrict__ vtc8, const uint8_t *__restrict__ ksc,
+    const uint8_t *__restrict__ vsc, const int32_t *__restrict__ block_table,
+    const msa_unit_t *__restrict__ units, const int32_t *__restrict__ ids, int topk,
+    int max_blocks, int Hq, int Hkv, int nsel, int num_uj, int pairs, float c,
+    uint16_t *__restrict__ out, float *__restrict__ lse) {
+  constexpr int NW = kPrefWaves;
+  constexpr int NT = NW * kWave;          // threads
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int CH = D / 8;               // 16-byte bf16 chunks per K row
+  constexpr int HB = kBlk / 2;            // keys per half-block
+  constexpr int VC = HB / 8;              // 16-byte bf16 chunks per V^T row of a half-block
+  constexpr int KSLOT = HB * CH * 16;
+  constexpr int VSLOT = D * VC * 16;
+  constexpr int VBASE = 2 * KSLOT;        // two K slots, then two V^T slots
+  constexpr int UK = HB * D / 16;         // 16-code staging units of a half-block: K
+  constexpr int UV = D * HB / 16;         //   and V^T
+  constexpr int NS = D / 32;              // scale bytes per K row
+  static_assert(UK <= NT && UV <= NT, "one staging unit per thread");
+  __shared__ u32x4 smem[2 * (HB * CH + D * VC)];
+  char *lds = reinterpret_cast<char *>(smem);
+
+  const int id = blockIdx.x;
+  const int uj_rev = 8 * (id / (8 * pairs)) + id % 8;
+  const int hp = (id / 8) % pairs;
+  if (uj_rev >= num_uj) return;
+  const int uj = num_uj - 1 - uj_rev;
+  const int u = uj / Hkv, j = uj % Hkv;
+  const msa_unit_t un = units[u];
+  const int G = Hq / Hkv;
+  const int g = (nsel == Hkv) ? j : 0;
+  const int32_t *sel = ids + (static_cast<size_t>(u) * nsel + g) * topk;
+  const int32_t *bt = block_table + static_cast<size_t>(un.r) * max_blocks;
+
+  const int t = threadIdx.x, lane = t % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+  const int a = lane / 32, n = lane % 32;
+  const int hl = 2 * hp + wave / 4;
+  const int slab = wave % 4;
+  const bool active = hl < G && slab * 32 < un.num_rows;
+  const int head = j * G + min(hl, G - 1);
+  const int row_in_tile = slab * 32 + n;
+  const bool row_ok = row_in_tile < un.num_rows;
+  const int qrow = un.row0 + min(row_in_tile, un.num_rows - 1);
+  const int qpos = row_ok ? un.pos0 + row_in_tile : 0x7fffffff;
+
+  int nk = 0;
+  while (nk < topk && sel[nk] >= 0) ++nk;
+  if (nk == 0) return;
+  const int diag_b = sel[nk - 1];
+  const int NH = 2 * nk;                  // half-blocks, the diagonal block's first
+  auto phys_of = [&](int p) { return bt[sel[p == 0 ? nk - 1 : p - 1]]; };
+
+  bf16x8 qf[KS];
+  {
+    const uint16_t *pq = q + (static_cast<size_t>(qrow) * Hq + head) * D + a * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(pq + ks * 16));
+  }
+
+  // staging: K unit t = (row t / (D/16), 16 channels t % (D/16)); V^T unit t =
+  // (d-row t / (HB/16), 16 keys t % (HB/16))
+  const int k_row = t / (D / 16), k_m = t % (D / 16);
+  const int v_row = t / (HB / 16), v_m = t % (HB / 16);
+  uint4 kcode = {}, vcode = {}, vscale = {};
+  uint32_t kscale = 0;
+  auto load = [&](int hb) __attribute__((always_inline)) {
+    const size_t blk = static_cast<size_t>(phys_of(hb >> 1)) * Hkv + j;   // (phys, j)
+    const int key0 = (hb & 1) * HB;
+    if (t < UK) {
+      const size_t row = blk * kBlk + key0 + k_row;
+      kcode = *reinterpret_cast<const uint4 *>(kc8 + row * D + k_m * 16);
+      kscale = ksc[row * NS + k_m / 2];
+    }
+    if (t < UV) {
+      vcode = *reinterpret_cast<const uint4 *>(vtc8 + (blk * D + v_row) * kBlk + key0 + v_m * 16);
+      vscale = *reinterpret_cast<const uint4 *>(vsc + (blk * NS + v_row / 32) * kBlk + key0 +
+                                                v_m * 16);
+    }
+  };
+  auto store = [&](int slot) __attribute__((always_inline)) {
+    if (t < UK) {
+      const float sc = ldexpf(1.0f, static_cast<int>(kscale) - 127);
+      const uint32_t w[4] = {kcode.x, kcode.y, kcode.z, kcode.w};
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __builtin_bit_cast(uint32_t,
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, false));
+        o[2 * i + 1] = __builtin_bit_cast(
+            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, true));
+      }
+      const int sw = srow_key(k_row % 32) % CH;
+      char *base = lds + slot * KSLOT + k_row * CH * 16;
+      *reinterpret_cast<uint4 *>(base + ((2 * k_m) ^ sw) * 16) = uint4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<uint4 *>(base + ((2 * k_m + 1) ^ sw) * 16) = uint4{o[4], o[5], o[6], o[7]};
+    }
+    if (t < UV) {
+      const uint32_t w[4] = {vcode.x, vcode.y, vcode.z, vcode.w};
+      const uint32_t e[4] = {vscale.x, vscale.y, vscale.z, vscale.w};
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+        const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+        auto ex = [&](int b) { return static_cast<int>((e[i] >> (8 * b)) & 0xffu) - 127; };
+        o[2 * i] = cvt_pk_bf16(ldexpf(lo.x, ex(0)), ldexpf(lo.y, ex(1)));
+        o[2 * i + 1] = cvt_pk_bf16(ldexpf(hi.x, ex(2)), ldexpf(hi.y, ex(3)));
+      }
+      const int sw = (v_row >> 1) % VC;
+      char *base = lds + VBASE + slot * VSLOT + v_row * VC * 16;
+      *reinterpret_cast<uint4 *>(base + ((2 * v_m) ^ sw) * 16) = uint4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<uint4 *>(base + ((2 * v_m + 1) ^ sw) * 16) = uint4{o[4], o[5], o[6], o[7]};
+    }
+  };
+
+  int koff[KS], voff[4];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = (srow_key(n) * CH + ((2 * ks + a) ^ (n % CH))) * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = VBASE + (n * VC + ((2 * i + a) ^ ((n >> 1) % VC))) * 16;
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+  float m_ref = neg_inf(), l_run = 0.f;
+
+  load(0);
+  for (int hb = 0; hb < NH; ++hb) {
+    const int slot = hb & 1;
+    store(slot);
+    __syncthreads();
+    if (hb + 1 < NH) load(hb + 1);
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2) {
+      bf16x8 kf[KS], vf[2 * DT], pf[2];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[ks] = *reinterpret_cast<const bf16x8 *>(lds + koff[ks] + slot * KSLOT +
+                                                   kt2 * 32 * CH * 16);
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+      if (hb < 2) {   // the diagonal block: keys past the query are masked
+        const int lim = qpos - diag_b * kBlk - (hb * 2 + kt2) * 32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (16 * (i / 8) + 8 * a + (i % 8) > lim) s[i] = neg_inf();
+      }
+      float x = s[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) x = fmaxf(x, s[i]);
+      {
+        const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                          false, false);
+        x = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * c;
+      }
+      const bool need = x > m_ref + kSlack;
+      if (__any(need)) {
+        const float nm = need ? x : m_ref;
+        const float al = __builtin_amdgcn_exp2f(m_ref - nm);
+        m_ref = nm;
+        l_run *= al;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t w[4];
+#pragma unroll
+        for (int jj = 0; jj < 8; jj += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj], c, -m_ref));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj + 1], c, -m_ref));
+          w[jj / 2] = cvt_pk_bf16(p0, p1);
+          l_run += p0 + p1;
+        }
+        pf[h] = as_bf16x8(uint4{w[0], w[1], w[2], w[3]});
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          vf[2 * dt + h] = *reinterpret_cast<const bf16x8 *>(
+              lds + voff[2 * kt2 + h] + slot * VSLOT + dt * 32 * VC * 16);
+#pragma unroll
+      for (int i = 0; i < 2 * DT; ++i)
+        o[i / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i % 2], o[i / 2], 0, 0, 0);
+    }
+    __syncthreads();   // every wave is done with this slot before it is refilled
+  }
+
+  if (!active) return;
+  float sum;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
+                                                     __float_as_uint(l_run), false, false);
+    sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  if (!row_ok) return;
+  const float inv = 1.f / sum;
+  uint16_t *op = out + (static_cast<size_t>(qrow) * Hq + head) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = dt * 32 + i4 * 8 + a * 4;
+      uint2 w;
+      w.x = cvt_pk_bf16(o[dt][i4 * 4 + 0] * inv, o[dt][i4 * 4 + 1] * inv);
+      w.y = cvt_pk_bf16(o[dt][i4 * 4 + 2] * inv, o[dt][i4 * 4 + 3] * inv);
+      *reinterpret_cast<uint2 *>(op + d) = w;
+    }
+  if (lse != nullptr && a == 0)
+    lse[static_cast<size_t>(qrow) * Hq + head] = (m_ref + __builtin_log2f(sum)) * kLn2;
+}
+
 }  // namespace
 
 // fp32 attention, shared by prefill (units from the plan) and decode (one query
@@ -474,6 +706,19 @@ hipError_t launch_attn_prefill(const Geom &g, const msa_cache_t &c, const msa_ba
   const uint16_t *vb = static_cast<const uint16_t *>(c.v_cache);
   uint16_t *ob = static_cast<uint16_t *>(out);
   const float sl2 = scale * kLog2e;
+  if (g.fp8) {
+    const uint8_t *k8 = static_cast<const uint8_t *>(c.k_cache);
+    const uint8_t *v8 = static_cast<const uint8_t *>(c.v_cache);
+    if (g.D == 64)
+      attn_prefill_fp8_kernel<64><<<grid, NW * 64, 0, st>>>(
+          qb, k8, v8, c.k_scale, c.v_scale, c.block_table, b.units, ids, topk,
+          c.max_blocks_per_seq, g.Hq, g.Hkv, g.nsel, num_uj, pairs, sl2, ob, lse);
+    else
+      attn_prefill_fp8_kernel<128><<<grid, NW * 64, 0, st>>>(
+          qb, k8, v8, c.k_scale, c.v_scale, c.block_table, b.units, ids, topk,
+          c.max_blocks_per_seq, g.Hq, g.Hkv, g.nsel, num_uj, pairs, sl2, ob, lse);
+    return hipGetLastError();
+  }
   if (g.D == 64)
     attn_prefill_bf16_kernel<64><<<grid, NW * 64, 0, st>>>(
         qb, kb, vb, c.block_table, b.units, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,

@@ -202,7 +202,6 @@ msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *
   if (st != MSA_OK) return st;
   if ((st = check_cache(cache, true, false, g.fp8)) != MSA_OK) return st;
   if ((st = check_batch(batch)) != MSA_OK) return st;
-  MSA_REQUIRE(!g.fp8, MSA_ERR_UNSUPPORTED, "prefill attention does not read FP8 caches");
   MSA_REQUIRE(topk >= 1, MSA_ERR_INVALID_ARG, "topk must be positive");
   if (batch->total_units == 0) return ok();     // no queries
   MSA_REQUIRE(q != nullptr && ids != nullptr && out != nullptr, MSA_ERR_INVALID_ARG,

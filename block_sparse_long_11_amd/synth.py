@@ -20,6 +20,8 @@ of context):
   chunked_prefill     bf16, 4 requests, each an 8192-token chunk after cached
                       prefixes of 1M / 512k / 128k / 32k tokens, top-k 64,
                       8 planted blocks per 32-block span
+  decode_1m_b8_fp8,   the 1M decode and the 32k prefill on FP8 caches (E4M3
+  prefill_32k_fp8     codes, a power-of-two scale per 32 channels of a row)
 
 Planting ("relevant blocks"): for every (sequence, selection group g) a seeded
 unit direction u_h is drawn per indexer head h of the group; a * u_h is added to
@@ -117,6 +119,9 @@ WORKLOADS = {
     "decode_1m_b8_fp8": Workload(
         "decode_1m_b8_fp8", "bf16", [1048576] * 8, None, topk=64, plant_count=63,
         plant_span=None, seed=1004, cache_format="fp8"),
+    "prefill_32k_fp8": Workload(
+        "prefill_32k_fp8", "bf16", [32768], [32768], topk=16, plant_count=8,
+        plant_span=32, seed=1002, cache_format="fp8"),
 }
 
 

@@ -314,3 +314,104 @@ def test_fp8_prefill_indexer_parity(name, gpu_device):
     msa.msa_select_topk_blocks(scores, w.topk, ids)
     torch.cuda.synchronize()
     prefill_index_parity(w, inp, cache, scores.cpu().numpy(), ids.cpu().numpy(), name)
+
+
+def prefill_parity(w, inp, cache, res, where):
+    kc, vc, ki = decoded(fp8_host(cache))
+    q, qi = host(inp["q"]), host(inp["q_idx"])
+    bt = inp["block_table"].cpu().numpy()
+    units = O.prefill_units(w.seq_lens, w.q_lens)
+    ref = O.index_scores(units, qi, ki, bt, w.num_sel_groups, bt.shape[1])
+    P.check_scores(res["scores"].numpy(), ref, P.score_tolerance(qi, ki, w.num_sel_groups),
+                   where)
+    ids = res["ids"].numpy()
+    P.check_ids(ids, ref, units, w.topk, where)
+    out, lse = O.attention(units, ids, q, kc, vc, bt, w.seq_lens, w.num_sel_groups)
+    return P.check_attention(host(res["out"]), res["lse"].numpy(), out, lse, w.dtype, where)
+
+
+PREFILL_FULL = {
+    "one_request": dict(seq_lens=(700,), q_lens=(300,)),
+    "ragged_permuted": dict(seq_lens=(1000, 260, 129, 5), q_lens=(1000, 200, 1, 5), topk=4),
+    "m3_heads": dict(seq_lens=(1100,), q_lens=(600,), num_q_heads=64, num_kv_heads=4,
+                     num_idx_heads=8, num_sel_groups=4, topk=5),
+    "g16_d64_di32": dict(seq_lens=(1300,), q_lens=(700,), num_q_heads=16, num_kv_heads=1,
+                         head_dim=64, num_idx_heads=2, idx_head_dim=32, num_sel_groups=1),
+    "topk_covers_all": dict(seq_lens=(1000,), q_lens=(1000,), topk=16),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL_FULL))
+def test_fp8_prefill_parity(name, gpu_device):
+    w = synth.small_workload(cache_format="fp8", **PREFILL_FULL[name])
+    say(f"fp8 prefill {name}")
+    inp, geom, cache = T.setup(w, gpu_device, permute=True)
+    res = T.run_gpu(w, inp, geom, cache, gpu_device)
+    prefill_parity(w, inp, cache, res, name)
+
+
+def test_fp8_insert_then_prefill_step(gpu_device):
+    """A chunked prefill on FP8 caches: the chunk's tokens are quantized into the
+    caches by the HIP path (after a cached prefix), then scored, selected and
+    attended from them."""
+    w = synth.small_workload(seq_lens=(1500, 700), q_lens=(600, 700), topk=4, cache_format="fp8",
+                             num_q_heads=64, num_kv_heads=4, num_idx_heads=8, num_sel_groups=4)
+    say("fp8 insert + prefill")
+    inp, geom, cache = T.setup(w, gpu_device, permute=True)
+    new = synth.make_new_tokens(w, gpu_device)
+    before = fp8_host(cache)
+    bt = inp["block_table"].cpu().numpy()
+    units = O.prefill_units(w.seq_lens, w.q_lens)
+    batch = msa.make_batch(w.seq_lens, w.q_lens, gpu_device)
+    q = I.run_insert(geom, cache, batch, new, synth.ROPE, torch.empty_like(new["q"]))
+    compare_fp8_insert(w, units, bt, before, fp8_host(cache), host(q), new, synth.ROPE,
+                       "insert")
+    inp = dict(inp, q=q)
+    res = T.run_gpu(w, inp, geom, cache, gpu_device)
+    prefill_parity(w, inp, cache, res, "prefill after insert")
+
+
+def test_fp8_full_size_prefill_32k_sampled(gpu_device):
+    """The 32k prefill on FP8 caches (the benchmark's launch): sampled units, every
+    group's scores and ids, attention of sampled rows for every KV head."""
+    w = synth.WORKLOADS["prefill_32k_fp8"]
+    say(f"{w.name} generate")
+    inp, geom, cache = T.setup(w, gpu_device)
+    say(f"{w.name} run")
+    res = T.run_gpu(w, inp, geom, cache, gpu_device)
+    units = O.prefill_units(w.seq_lens, w.q_lens)
+    bt_all = inp["block_table"].cpu().numpy()
+    Hs, G = w.num_idx_heads // w.num_sel_groups, w.num_q_heads // w.num_kv_heads
+    scores, ids = res["scores"].numpy(), res["ids"].numpy()
+    rng = np.random.default_rng(4)
+    for u in T._sample_units(units, 4, 1):
+        un = units[u]
+        r, tau = un["r"], un["tau"]
+        say(f"{w.name} unit {u} (tau={tau})")
+        rows = slice(un["row0"], un["row1"])
+        for g in range(w.num_sel_groups):
+            heads = slice(g * Hs, (g + 1) * Hs)
+            cand = list(range(tau)) if tau > 0 else [0]
+            ki, btm = _mini_fp8(inp["k_idx_cache"], inp["k_idx_scale"], bt_all[r], cand, heads)
+            qi = host(inp["q_idx"][rows, heads])
+            ref = O.unit_block_scores(qi, ki, btm, tau, 1, scores.shape[2])
+            P.check_scores(scores[u, g][None, None], ref[None], P.score_tolerance(qi, ki, 1),
+                           f"u{u} g{g}")
+            ok, _ = P.ids_acceptable(ids[u, g], ref[0], tau, w.topk)
+            assert ok, f"u{u} g{g}: ids {ids[u, g]}"
+        n = un["row1"] - un["row0"]
+        pick = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 8)]))
+        for j in range(w.num_kv_heads):
+            kept = [int(b) for b in ids[u, j] if b >= 0]
+            kc, btm = _mini_fp8(inp["k_cache"], inp["k_scale"], bt_all[r], kept, slice(j, j + 1))
+            vc, _ = _mini_fp8(inp["v_cache"], inp["v_scale"], bt_all[r], kept, slice(j, j + 1),
+                              d_major=True)
+            qh = host(inp["q"][rows, j * G:(j + 1) * G])
+            for t in pick:
+                o, l = O.unit_attention(qh[t:t + 1], un["pos0"] + t, ids[u, j][None], kc, vc,
+                                        btm, int(w.seq_lens[r]), 1)
+                P.check_attention(host(res["out"][un["row0"] + t, j * G:(j + 1) * G])[None],
+                                  res["lse"][un["row0"] + t, j * G:(j + 1) * G].numpy()[None],
+                                  o, l, w.dtype, f"u{u} row{t} kv{j}")
+    del inp, cache
+    torch.cuda.empty_cache()
