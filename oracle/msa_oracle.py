@@ -97,6 +97,24 @@ def decode_units(seq_lens):
             for r, L in enumerate(seq_lens)]
 
 
+def token_units(seq_lens, tokens_per_seq):
+    """Per-query-token units of a multi-token decode ([feat] row "Indexer-selected
+    sparse attention": the model's selection is shaped [B, H_idx, S_q, topk], one
+    block list per query token). Sequence r has T = tokens_per_seq new tokens,
+    rows r*T + i at positions L-T+i (i < T), each a unit of its own: it scores the
+    blocks with its own indexer query, keeps its own diagonal block and top-k,
+    and attends causally. T = 1 is decode_units."""
+    T = int(tokens_per_seq)
+    units = []
+    for r, L in enumerate(seq_lens):
+        L = int(L)
+        assert L >= T
+        for i in range(T):
+            p = L - T + i
+            units.append(dict(r=r, tau=p // BLOCK, row0=r * T + i, row1=r * T + i + 1, pos0=p))
+    return units
+
+
 # ----------------------------------------------------------------------------
 # paged cache access
 # ----------------------------------------------------------------------------
@@ -278,6 +296,19 @@ def run_decode(q, q_idx, k_cache, v_cache, k_idx_cache, block_table, seq_lens, n
                topk, scale=None, row_len=None):
     """Index, select and attend for one decode step (one query per sequence)."""
     units = decode_units(seq_lens)
+    row_len = row_len or block_table.shape[1]
+    scores = index_scores(units, q_idx, k_idx_cache, block_table, n_sel, row_len)
+    ids = select(scores, units, topk)
+    out, lse = attention(units, ids, q, k_cache, v_cache, block_table, seq_lens, n_sel,
+                         scale)
+    return dict(units=units, scores=scores, ids=ids, out=out, lse=lse)
+
+
+def run_tokens(q, q_idx, k_cache, v_cache, k_idx_cache, block_table, seq_lens,
+               tokens_per_seq, n_sel, topk, scale=None, row_len=None):
+    """Index, select and attend for a multi-token decode step with per-token
+    selection (token_units): rows r*T + i of q and q_idx."""
+    units = token_units(seq_lens, tokens_per_seq)
     row_len = row_len or block_table.shape[1]
     scores = index_scores(units, q_idx, k_idx_cache, block_table, n_sel, row_len)
     ids = select(scores, units, topk)

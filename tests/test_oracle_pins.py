@@ -716,3 +716,109 @@ def test_insert_fp8_is_quantized_insert():
         c_ref, s_ref = O.mx_quantize(ref.transpose(0, 2, 1, 3)[new])
         assert np.array_equal(out[codes].transpose(0, 2, 1, 3)[new], c_ref), codes
         assert np.array_equal(out[sc].transpose(0, 2, 1, 3)[new], s_ref), sc
+
+
+# ----------------------------------------------------------------------------
+# per-query-token selection (multi-token decode)
+# ----------------------------------------------------------------------------
+
+def test_token_units_one_token_is_decode():
+    seq = [1, 128, 129, 700, 4096]
+    assert O.token_units(seq, 1) == O.decode_units(seq)
+
+
+@pytest.mark.parametrize("seq_lens,T", [([300, 129, 1000], 4), ([130, 640], 3), ([8, 256], 8)])
+def test_token_units_rows_positions_and_diagonals(seq_lens, T):
+    units = O.token_units(seq_lens, T)
+    assert len(units) == len(seq_lens) * T
+    for r, L in enumerate(seq_lens):
+        for i in range(T):
+            un = units[r * T + i]
+            p = L - T + i
+            assert (un["r"], un["row0"], un["row1"], un["pos0"]) == (r, r * T + i, r * T + i + 1, p)
+            assert un["tau"] * BLK <= p < (un["tau"] + 1) * BLK
+
+
+def _tokens_case(rng, seq_lens, T, Hq=8, Hkv=2, D=16, Hi=4, Di=8):
+    kc, bt = paged(rng, seq_lens, Hkv, D)
+    vc = rng.standard_normal(kc.shape)
+    ki = rng.standard_normal((kc.shape[0], Hi, BLK, Di))
+    n = len(seq_lens) * T
+    return kc, vc, ki, bt, rng.standard_normal((n, Hq, D)), rng.standard_normal((n, Hi, Di))
+
+
+@pytest.mark.parametrize("nsel", [2, 1])
+def test_token_scores_pool_to_the_tile_scores(nsel):
+    """Max-pooling the per-token block scores over tokens that share a diagonal
+    block gives the tile-level score of those tokens (the prefill unit)."""
+    rng = np.random.default_rng(21)
+    seq_lens, T = [700, 300, 1000], 5           # all three keep their T tokens in one block
+    kc, vc, ki, bt, q, qi = _tokens_case(rng, seq_lens, T)
+    tok = O.token_units(seq_lens, T)
+    per_tok = O.index_scores(tok, qi, ki, bt, nsel, bt.shape[1])
+    tile_units = O.prefill_units(seq_lens, [T] * len(seq_lens))
+    assert len(tile_units) == len(seq_lens)
+    tile = O.index_scores(tile_units, qi, ki, bt, nsel, bt.shape[1])
+    for r in range(len(seq_lens)):
+        pooled = per_tok[r * T:(r + 1) * T].max(axis=0)
+        inf = ~np.isfinite(tile[r])
+        np.testing.assert_array_equal(pooled[inf], tile[r][inf])
+        # the library product sums in another order for another number of rows
+        np.testing.assert_allclose(pooled[~inf], tile[r][~inf], rtol=1e-13, atol=1e-13)
+
+
+def test_token_scores_brute_force():
+    """Per-token scores by explicit loops over keys, heads and channels."""
+    rng = np.random.default_rng(22)
+    seq_lens, T, nsel = [260, 131], 3, 2         # the second sequence straddles blocks 0/1
+    kc, vc, ki, bt, q, qi = _tokens_case(rng, seq_lens, T)
+    res = O.index_scores(O.token_units(seq_lens, T), qi, ki, bt, nsel, bt.shape[1])
+    Hs = ki.shape[1] // nsel
+    for r, L in enumerate(seq_lens):
+        for i in range(T):
+            p = L - T + i
+            tau = p // BLK
+            for g in range(nsel):
+                for b in range(bt.shape[1]):
+                    got = res[r * T + i, g, b]
+                    if b > tau:
+                        assert got == -np.inf
+                    elif b == tau:
+                        assert got == np.inf
+                    else:
+                        best = -np.inf
+                        for s in range(BLK):
+                            acc = 0.0
+                            for h in range(g * Hs, (g + 1) * Hs):
+                                for d in range(ki.shape[3]):
+                                    acc += qi[r * T + i, h, d] * ki[bt[r][b], h, s, d]
+                            best = max(best, acc)
+                        assert abs(got - best) <= 1e-12 * max(1.0, abs(best))
+
+
+@pytest.mark.parametrize("seq_lens,T", [([700, 260, 129], 4), ([130, 1000], 2), ([8], 8)])
+def test_tokens_dense_when_topk_covers_all_blocks(seq_lens, T):
+    """k >= number of blocks: every token attends densely and causally."""
+    rng = np.random.default_rng(23)
+    kc, vc, ki, bt, q, qi = _tokens_case(rng, seq_lens, T)
+    res = O.run_tokens(q, qi, kc, vc, ki, bt, seq_lens, T, 2, bt.shape[1] + 2)
+    for r, L in enumerate(seq_lens):
+        rows = slice(r * T, (r + 1) * T)
+        out, lse = dense_reference(q[rows], logical(kc, bt[r], L), logical(vc, bt[r], L),
+                                   np.arange(L - T, L), 1 / math.sqrt(q.shape[2]))
+        np.testing.assert_allclose(res["out"][rows], out, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(res["lse"][rows], lse, rtol=1e-12, atol=1e-12)
+
+
+def test_tokens_last_token_is_the_decode_step():
+    """The last of a sequence's T tokens sees what a one-token decode at the same
+    position sees: same scores, ids and output."""
+    rng = np.random.default_rng(24)
+    seq_lens, T = [900, 333], 4
+    kc, vc, ki, bt, q, qi = _tokens_case(rng, seq_lens, T)
+    res = O.run_tokens(q, qi, kc, vc, ki, bt, seq_lens, T, 2, 3)
+    last = [r * T + T - 1 for r in range(len(seq_lens))]
+    dec = O.run_decode(q[last], qi[last], kc, vc, ki, bt, seq_lens, 2, 3)
+    np.testing.assert_array_equal(res["scores"][last], dec["scores"])
+    np.testing.assert_array_equal(res["ids"][last], dec["ids"])
+    np.testing.assert_allclose(res["out"][last], dec["out"], rtol=0, atol=0)
