@@ -80,9 +80,10 @@ def selected_kv_tokens(w, ids, units):
 
 
 def plan_units(w):
-    if w.is_decode:
-        return [dict(r=r, tau=(L - 1) // BLK, pos0=L - 1, num_rows=1)
-                for r, L in enumerate(w.seq_lens)]
+    if w.is_decode:   # one unit per new token (T = tokens_per_seq per sequence)
+        T = w.tokens_per_seq
+        return [dict(r=r, tau=(L - T + i) // BLK, pos0=L - T + i, num_rows=1)
+                for r, L in enumerate(w.seq_lens) for i in range(T)]
     plan = msa.msa_prefill_plan(w.seq_lens, w.q_lens)
     return [dict(r=int(p[0]), tau=int(p[1]), row0=int(p[2]), num_rows=int(p[3]),
                  pos0=int(p[4])) for p in plan]
@@ -92,8 +93,8 @@ def index_decode_bytes(w):
     """Indexer keys every non-diagonal block must stream, plus q_idx and scores."""
     per_block = w.num_idx_heads * BLK * cache_row_bytes(w, w.idx_head_dim)
     blocks = sum(w.blocks(r) - 1 for r in range(w.num_seqs))
-    q = w.num_seqs * w.num_idx_heads * w.idx_head_dim * 2
-    scores = w.num_seqs * w.num_sel_groups * w.max_blocks * 4
+    q = w.total_q * w.num_idx_heads * w.idx_head_dim * 2
+    scores = w.total_q * w.num_sel_groups * w.max_blocks * 4
     return blocks * per_block + q + scores
 
 
@@ -114,7 +115,7 @@ class Runner:
                                self.inp["k_idx_cache"], self.inp["block_table"],
                                self.inp["seq_lens"], self.inp.get("k_scale"),
                                self.inp.get("v_scale"), self.inp.get("k_idx_scale"))
-        U = w.num_seqs if w.is_decode else len(msa.msa_prefill_plan(w.seq_lens, w.q_lens))
+        U = w.total_q if w.is_decode else len(msa.msa_prefill_plan(w.seq_lens, w.q_lens))
         self.batch = None if w.is_decode else msa.make_batch(w.seq_lens, w.q_lens, dev)
         self.scores = torch.empty((U, w.num_sel_groups, self.cache.max_blocks),
                                   dtype=torch.float32, device=dev)
@@ -122,7 +123,7 @@ class Runner:
         self.out = torch.empty_like(self.inp["q"])
         self.lse = torch.empty(self.inp["q"].shape[:2], dtype=torch.float32, device=dev)
         if w.is_decode:
-            self.ws = msa.workspace(msa.msa_decode_workspace_size(self.geom, w.num_seqs,
+            self.ws = msa.workspace(msa.msa_decode_workspace_size(self.geom, w.total_q,
                                                                   w.topk, 0), dev)
         self.names = ["index_scores", "select_topk_blocks",
                       "sparse_attn_decode" if w.is_decode else "sparse_attn_prefill"]
@@ -130,15 +131,22 @@ class Runner:
     def step(self, events=None):
         w, i = self.w, self.inp
         ev = events or [None] * 4
+        T = w.tokens_per_seq
         if ev[0] is not None:
             ev[0].record()
-        msa.msa_index_scores(self.geom, self.cache, self.batch, i["q_idx"], self.scores)
+        if w.is_decode and T > 1:
+            msa.msa_index_scores_per_token(self.geom, self.cache, T, i["q_idx"], self.scores)
+        else:
+            msa.msa_index_scores(self.geom, self.cache, self.batch, i["q_idx"], self.scores)
         if ev[1] is not None:
             ev[1].record()
         msa.msa_select_topk_blocks(self.scores, w.topk, self.ids)
         if ev[2] is not None:
             ev[2].record()
-        if w.is_decode:
+        if w.is_decode and T > 1:
+            msa.msa_sparse_attn_decode_per_token(self.geom, self.cache, T, i["q"], self.ids,
+                                                 w.topk, self.out, self.ws, self.lse)
+        elif w.is_decode:
             msa.msa_sparse_attn_decode(self.geom, self.cache, i["q"], self.ids, w.topk,
                                        self.out, self.ws, self.lse)
         else:
@@ -204,7 +212,7 @@ def measure(w, dev, steps, warmup):
                                algorithmic_bytes=nbytes)
         # whole decode step against HBM: the algorithmic bytes of all four launches
         kv = tokens * cache_row_bytes(w, w.head_dim) * 2   # K and V rows of the selected keys
-        step_bytes = nbytes + kv + 2 * w.num_seqs * w.num_q_heads * w.head_dim * 2
+        step_bytes = nbytes + kv + 2 * w.total_q * w.num_q_heads * w.head_dim * 2
         res["step_hbm_frac"] = step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
         res["step_algorithmic_bytes"] = step_bytes
     else:
@@ -241,8 +249,12 @@ def measure_insert(runner, launches=20, warmup=10):
     new = synth.make_new_tokens(w, dev)
     rope = synth.ROPE
 
+    batch = runner.batch
+    if w.is_decode and w.tokens_per_seq > 1:   # several tokens per sequence: a planned batch
+        batch = msa.make_batch(w.seq_lens, [w.tokens_per_seq] * w.num_seqs, dev)
+
     def launch():
-        msa.msa_qk_norm_rope_insert(runner.geom, runner.cache, runner.batch, new["q"], new["k"],
+        msa.msa_qk_norm_rope_insert(runner.geom, runner.cache, batch, new["q"], new["k"],
                                     new["v"], new["k_idx"], new["q_norm_w"], new["k_norm_w"],
                                     rope["eps"], rope["theta"], rope["rotary_dim"], runner.out)
 
@@ -325,9 +337,9 @@ def main():
     ap.add_argument("--workload", default="prefill_32k", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--second", default="decode_1m_b8",
                     help="second workload measured in the same run ('none' to skip)")
-    ap.add_argument("--fp8", default="decode_1m_b8_fp8,prefill_32k_fp8",
-                    help="FP8-cache workloads measured in the same run, comma-separated "
-                         "('none' to skip)")
+    ap.add_argument("--extra", default="decode_1m_b8_fp8,prefill_32k_fp8,decode_1m_b8_t4",
+                    help="more workloads measured in the same run (FP8 caches, several "
+                         "tokens per sequence), comma-separated ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -375,8 +387,8 @@ def main():
         del second["_runner"]
         torch.cuda.empty_cache()
 
-    fp8 = []
-    for name in ([] if args.fp8 == "none" else args.fp8.split(",")):
+    extra = []
+    for name in ([] if args.extra == "none" else args.extra.split(",")):
         if name in (args.workload, args.second):
             continue
         w3 = synth.WORKLOADS[name]
@@ -386,7 +398,7 @@ def main():
         log(f"{w3.name}: insert {inserts[-1]['us_per_launch']:.1f} us")
         del res["_runner"]
         torch.cuda.empty_cache()
-        fp8.append(res)
+        extra.append(res)
 
     config = dict(workload=w.name, batch=w.num_seqs,
                   seq_lens=w.seq_lens if len(set(w.seq_lens)) > 1 else w.seq_lens[0],
@@ -416,12 +428,13 @@ def main():
         line["second_workload"] = {k: second[k] for k in (
             "workload", "value", "ms_per_step", "kernel_ms", "roofline", "step_hbm_frac")
             if k in second}
-    if fp8:
+    if extra:
         # the same workloads on FP8 caches (E4M3 codes, power-of-two scale per 32
-        # channels): fewer cache bytes for the same selections
-        line["fp8_cache_workloads"] = [{k: r[k] for k in (
+        # channels), and decode with several new tokens per sequence, each selecting
+        # its own blocks
+        line["extra_workloads"] = [{k: r[k] for k in (
             "workload", "value", "ms_per_step", "kernel_ms", "roofline", "step_hbm_frac")
-            if k in r} for r in fp8]
+            if k in r} for r in extra]
     # the new-token step before the path (QK-norm + partial RoPE + cache insert),
     # timed on its own: not part of the step above
     line["qk_norm_rope_insert"] = inserts

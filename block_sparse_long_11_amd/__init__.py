@@ -88,6 +88,13 @@ EXPORTS = {
                                                ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
                                                ctypes.c_int32, ctypes.c_void_p,
                                                ctypes.c_void_p]),
+    "msa_index_scores_per_token": (ctypes.c_int, [ctypes.POINTER(_Geom), ctypes.POINTER(_Cache),
+                                                  ctypes.c_int32, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_void_p]),
+    "msa_sparse_attn_decode_per_token": (ctypes.c_int, [
+        ctypes.POINTER(_Geom), ctypes.POINTER(_Cache), ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "msa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "msa_last_error": (ctypes.c_char_p, []),
     "msa_version": (ctypes.c_int32, []),
@@ -386,6 +393,66 @@ def msa_qk_norm_rope_insert(geom: Geometry, cache: Cache, batch, q, k, v, k_idx,
                                          float(eps), float(rope_theta), int(rotary_dim),
                                          _ptr(q_out), _stream(stream)))
     return q_out
+
+
+def msa_index_scores_per_token(geom: Geometry, cache: Cache, tokens_per_seq, q_idx, scores,
+                               stream=None):
+    """Per-token decode indexer: q_idx [B*T][H_i][D_i] -> scores [B*T][n_sel][max_blocks]."""
+    cache.check(geom)
+    dev = cache.block_table.device
+    rows = cache.num_seqs * tokens_per_seq
+    _need(q_idx, "q_idx", geom.torch_dtype, 3, dev)
+    _need(scores, "scores", torch.float32, 3, dev)
+    if tuple(q_idx.shape) != (rows, geom.num_idx_heads, geom.idx_head_dim):
+        raise ValueError(f"q_idx must be [{rows}][H_i][D_i]")
+    if tuple(scores.shape) != (rows, geom.num_sel_groups, cache.max_blocks):
+        raise ValueError(f"scores must be [{rows}][n_sel][{cache.max_blocks}]")
+    g, c = geom.c(), cache.c()
+    _check(lib().msa_index_scores_per_token(ctypes.byref(g), ctypes.byref(c), tokens_per_seq,
+                                            _ptr(q_idx), _ptr(scores), _stream(stream)))
+
+
+def msa_sparse_attn_decode_per_token(geom: Geometry, cache: Cache, tokens_per_seq, q, ids, topk,
+                                     out, workspace, lse=None, num_splits=0, softmax_scale=0.0,
+                                     stream=None):
+    """Per-token decode attention: q/out [B*T][H_q][D], ids [B*T][n_sel][topk]."""
+    cache.check(geom)
+    dev = cache.block_table.device
+    rows = cache.num_seqs * tokens_per_seq
+    _need(q, "q", geom.torch_dtype, 3, dev)
+    _need(out, "out", geom.torch_dtype, 3, dev)
+    _need(ids, "ids", torch.int32, 3, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    shape = (rows, geom.num_q_heads, geom.head_dim)
+    if tuple(q.shape) != shape or tuple(out.shape) != shape:
+        raise ValueError(f"q and out must be {shape}")
+    if tuple(ids.shape) != (rows, geom.num_sel_groups, topk):
+        raise ValueError("ids must be [B*T][n_sel][topk]")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+    g, c = geom.c(), cache.c()
+    _check(lib().msa_sparse_attn_decode_per_token(
+        ctypes.byref(g), ctypes.byref(c), tokens_per_seq, _ptr(q), _ptr(ids), topk,
+        float(softmax_scale), num_splits, _ptr(workspace), workspace.numel(), _ptr(out),
+        _ptr(lse), _stream(stream)))
+
+
+def decode_per_token(geom: Geometry, cache: Cache, tokens_per_seq, q, q_idx, topk, num_splits=0,
+                     softmax_scale=0.0, stream=None):
+    """Index, select and attend T new tokens per sequence, each with its own blocks."""
+    dev = q.device
+    rows = cache.num_seqs * tokens_per_seq
+    scores = torch.empty((rows, geom.num_sel_groups, cache.max_blocks), dtype=torch.float32,
+                         device=dev)
+    ids = torch.empty((rows, geom.num_sel_groups, topk), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    ws = workspace(msa_decode_workspace_size(geom, rows, topk, num_splits), dev)
+    msa_index_scores_per_token(geom, cache, tokens_per_seq, q_idx, scores, stream)
+    msa_select_topk_blocks(scores, topk, ids, stream)
+    msa_sparse_attn_decode_per_token(geom, cache, tokens_per_seq, q, ids, topk, out, ws, lse,
+                                     num_splits, softmax_scale, stream)
+    return dict(scores=scores, ids=ids, out=out, lse=lse)
 
 
 def workspace(nbytes, device):

@@ -8,7 +8,11 @@
 // concatenation": the G query heads that share a KV head are stacked against
 // each KV block. Row "Grouped-query attention": query head i reads KV head i / G.
 //
-// Phase 1: one work-group (4 waves) per (sequence, KV head j, split). Its G <= 16
+// A sequence may bring T new tokens, each with its own kept blocks (multi-token
+// decode, per-token selection): token row x = r T + i of sequence r sits at
+// seq_len - T + i, and everything below is per token row (T = 1: one per sequence).
+//
+// Phase 1: one work-group (4 waves) per (token row, KV head j, split). Its G <= 16
 // query heads form the N = 16 columns of MFMA 16x16x32 bf16 products; each wave
 // takes 32 keys of every kept block of the split and reads its operands straight
 // from HBM with 16-byte loads (K rows token-major, V rows d-major):
@@ -36,7 +40,7 @@
 namespace msa {
 
 hipError_t launch_attn_f32(const Geom &g, const msa_cache_t &c, const msa_unit_t *units,
-                           int num_units, const void *q, const int32_t *ids, int topk,
+                           int num_units, int T, const void *q, const int32_t *ids, int topk,
                            float scale, void *out, float *lse, hipStream_t st);
 
 namespace {
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
     const void *__restrict__ vtc_, const uint8_t *__restrict__ ksc,
     const uint8_t *__restrict__ vsc, const int32_t *__restrict__ block_table,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ ids, int topk,
-    int max_blocks, int Hq, int Hkv, int nsel, int num_splits, int per_split, float c,
+    int max_blocks, int Hq, int Hkv, int nsel, int T, int num_splits, int per_split, float c,
     float *__restrict__ o_part, float *__restrict__ lse_part) {
   constexpr int KS = D / 32;   // k steps of S^T (one FP8 scale block each)
   constexpr int DT = D / 16;   // d tiles of O^T
@@ -83,12 +87,13 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
   __shared__ float Ow[4][16][D + 1];
   __shared__ float Mw[4][16], Lw[4][16];
 
-  const int r = blockIdx.x / Hkv, j = blockIdx.x % Hkv, sp = blockIdx.y;
+  const int x = blockIdx.x / Hkv, j = blockIdx.x % Hkv, sp = blockIdx.y;   // token row x
+  const int r = x / T;                                                       // its sequence
   const int G = Hq / Hkv;
   const int g = (nsel == Hkv) ? j : 0;
-  const int32_t *sel = ids + (static_cast<size_t>(r) * nsel + g) * topk;
+  const int32_t *sel = ids + (static_cast<size_t>(x) * nsel + g) * topk;
   const int32_t *bt = block_table + static_cast<size_t>(r) * max_blocks;
-  const int qpos = seq_lens[r] - 1;
+  const int qpos = seq_lens[r] - T + x % T;
   const int slot0 = sp * per_split, slot1 = min(topk, slot0 + per_split);
 
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
@@ -99,7 +104,7 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
   {
     const bool live = n < G;
     const uint16_t *qp =
-        q + (static_cast<size_t>(r) * Hq + j * G + (live ? n : 0)) * D + q4 * 8;
+        q + (static_cast<size_t>(x) * Hq + j * G + (live ? n : 0)) * D + q4 * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = *reinterpret_cast<const uint4 *>(qp + ks * 32);
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) Ow[wave][n][dt * 16 + q4 * 4 + i] = o[dt][i];
   __syncthreads();
-  const size_t part0 = static_cast<size_t>(r) * Hq * num_splits;
+  const size_t part0 = static_cast<size_t>(x) * Hq * num_splits;
   for (int e = t; e < G * D; e += kDecThreads) {
     const int hn = e / D, d = e % D;
     const size_t pi = part0 + static_cast<size_t>(j * G + hn) * num_splits + sp;
@@ -289,34 +294,35 @@ size_t decode_workspace_bytes(const Geom &g, int num_seqs, int num_splits) {
   return o_bytes + ((parts * sizeof(float) + 255) & ~static_cast<size_t>(255));
 }
 
-hipError_t launch_attn_decode(const Geom &g, const msa_cache_t &c, const void *q,
+hipError_t launch_attn_decode(const Geom &g, const msa_cache_t &c, int T, const void *q,
                               const int32_t *ids, int topk, float scale, int num_splits,
                               void *workspace, void *out, float *lse, hipStream_t st) {
   if (c.num_seqs == 0) return hipSuccess;
+  const int rows = c.num_seqs * T;        // token rows
   if (!g.bf16)
-    return launch_attn_f32(g, c, nullptr, c.num_seqs, q, ids, topk, scale, out, lse, st);
+    return launch_attn_f32(g, c, nullptr, rows, T, q, ids, topk, scale, out, lse, st);
   const int per = (topk + num_splits - 1) / num_splits;
-  const size_t parts = static_cast<size_t>(c.num_seqs) * g.Hq * num_splits;
+  const size_t parts = static_cast<size_t>(rows) * g.Hq * num_splits;
   float *o_part = static_cast<float *>(workspace);
   float *lse_part = reinterpret_cast<float *>(
       static_cast<char *>(workspace) +
       ((parts * g.D * sizeof(float) + 255) & ~static_cast<size_t>(255)));
-  const dim3 grid(c.num_seqs * g.Hkv, num_splits);
+  const dim3 grid(rows * g.Hkv, num_splits);
   const uint16_t *qb = static_cast<const uint16_t *>(q);
   const float sl2 = scale * kLog2e;
 #define MSA_DEC(DD, F8)                                                                    \
   attn_decode_bf16_kernel<DD, F8><<<grid, kDecThreads, 0, st>>>(                           \
       qb, c.k_cache, c.v_cache, c.k_scale, c.v_scale, c.block_table, c.seq_lens, ids,     \
-      topk, c.max_blocks_per_seq, g.Hq, g.Hkv, g.nsel, num_splits, per, sl2, o_part,       \
+      topk, c.max_blocks_per_seq, g.Hq, g.Hkv, g.nsel, T, num_splits, per, sl2, o_part,    \
       lse_part)
   if (g.D == 64) {
     if (g.fp8) MSA_DEC(64, true); else MSA_DEC(64, false);
-    combine_kernel<64, true><<<c.num_seqs * g.Hq, 64, 0, st>>>(o_part, lse_part, num_splits,
-                                                                out, lse);
+    combine_kernel<64, true><<<rows * g.Hq, 64, 0, st>>>(o_part, lse_part, num_splits, out,
+                                                          lse);
   } else {
     if (g.fp8) MSA_DEC(128, true); else MSA_DEC(128, false);
-    combine_kernel<128, true><<<c.num_seqs * g.Hq, 128, 0, st>>>(o_part, lse_part,
-                                                                  num_splits, out, lse);
+    combine_kernel<128, true><<<rows * g.Hq, 128, 0, st>>>(o_part, lse_part, num_splits,
+                                                            out, lse);
   }
 #undef MSA_DEC
   return hipGetLastError();

@@ -618,13 +618,14 @@ void attn_prefill_fp8_kernel(
 
 }  // namespace
 
-// fp32 attention, shared by prefill (units from the plan) and decode (one query
-// per sequence at position seq_len - 1). One thread per (query row, head).
+// fp32 attention, shared by prefill (units from the plan) and decode (T query rows
+// per sequence, row r T + i at position seq_len - T + i). One thread per (query
+// row, head).
 template <int D>
 __global__ __launch_bounds__(128) void attn_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vtc,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
-    const msa_unit_t *__restrict__ units, const int32_t *__restrict__ ids, int topk,
+    const msa_unit_t *__restrict__ units, int T, const int32_t *__restrict__ ids, int topk,
     int max_blocks, int Hq, int Hkv, int nsel, float scale, float *__restrict__ out,
     float *__restrict__ lse) {
   const int u = blockIdx.x, head = blockIdx.y;
@@ -632,8 +633,8 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
   if (units != nullptr) {
     un = units[u];
   } else {
-    const int L = seq_lens[u];
-    un = msa_unit_t{u, (L - 1) / kBlk, u, 1, L - 1};
+    const int r = u / T, p = seq_lens[r] - T + u % T;
+    un = msa_unit_t{r, p / kBlk, u, 1, p};
   }
   const int t = threadIdx.x;
   if (t >= un.num_rows) return;
@@ -673,7 +674,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
 }
 
 hipError_t launch_attn_f32(const Geom &g, const msa_cache_t &c, const msa_unit_t *units,
-                           int num_units, const void *q, const int32_t *ids, int topk,
+                           int num_units, int T, const void *q, const int32_t *ids, int topk,
                            float scale, void *out, float *lse, hipStream_t st) {
   const dim3 grid(num_units, g.Hq);
   const float *qf = static_cast<const float *>(q);
@@ -681,11 +682,11 @@ hipError_t launch_attn_f32(const Geom &g, const msa_cache_t &c, const msa_unit_t
   const float *vf = static_cast<const float *>(c.v_cache);
   if (g.D == 64)
     attn_f32_kernel<64><<<grid, 128, 0, st>>>(qf, kf, vf, c.block_table, c.seq_lens, units,
-                                              ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
+                                              T, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
                                               g.nsel, scale, static_cast<float *>(out), lse);
   else
     attn_f32_kernel<128><<<grid, 128, 0, st>>>(qf, kf, vf, c.block_table, c.seq_lens, units,
-                                               ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
+                                               T, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
                                                g.nsel, scale, static_cast<float *>(out), lse);
   return hipGetLastError();
 }
@@ -695,7 +696,7 @@ hipError_t launch_attn_prefill(const Geom &g, const msa_cache_t &c, const msa_ba
                                void *out, float *lse, hipStream_t st) {
   if (b.total_units == 0) return hipSuccess;
   if (!g.bf16)
-    return launch_attn_f32(g, c, b.units, b.total_units, q, ids, topk, scale, out, lse, st);
+    return launch_attn_f32(g, c, b.units, b.total_units, 1, q, ids, topk, scale, out, lse, st);
   constexpr int NW = kPrefWaves;
   const int pairs = (g.G() + NW / 4 - 1) / (NW / 4);   // work-groups per (unit, KV head)
   const int num_uj = b.total_units * g.Hkv;

@@ -27,44 +27,67 @@ namespace {
 // ---------------------------------------------------------------------------
 // decode: one work-group of 256 threads per (sequence, logical block)
 // ---------------------------------------------------------------------------
+//
+// A sequence may bring T new tokens (multi-token decode with per-token
+// selection): token i sits at seq_len - T + i, is score row (r T + i), and the
+// block's keys, streamed once, are scored against each token's query in turn.
+// Block b is the diagonal of token i when b == (seq_len - T + i) / 128 (+inf),
+// after it when larger (-inf).
+
+constexpr int kMaxOutRows = 128;   // T * n_sel per sequence at most
+
+// Writes the +inf / -inf entries of token rows whose diagonal is at or before b;
+// returns whether some token of the sequence needs block b scored.
+__device__ __forceinline__ bool decode_edges(float *out, int b, int L, int T, int nsel,
+                                             int max_blocks) {
+  if (b < (L - 1) / kBlk) return true;       // before the last token's diagonal
+  for (int e = threadIdx.x; e < T * nsel; e += blockDim.x) {
+    const int tau = (L - T + e / nsel) / kBlk;
+    out[static_cast<size_t>(e) * max_blocks] = (b == tau) ? pos_inf() : neg_inf();
+  }
+  return false;
+}
+
+// Final per-token scores of block b from the waves' maxima (red[w][i n_sel + g]).
+template <int NWAVE>
+__device__ __forceinline__ void decode_finish(float *out, const float (*red)[kMaxOutRows],
+                                              int b, int L, int T, int nsel, int max_blocks) {
+  for (int e = threadIdx.x; e < T * nsel; e += blockDim.x) {
+    const int tau = (L - T + e / nsel) / kBlk;
+    float m = red[0][e];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) m = fmaxf(m, red[w][e]);
+    out[static_cast<size_t>(e) * max_blocks] = b < tau ? m : (b == tau ? pos_inf() : neg_inf());
+  }
+}
 
 template <bool BF16, int DI, int HS>
 __global__ __launch_bounds__(256) void index_decode_kernel(
     const void *__restrict__ q_idx, const void *__restrict__ k_idx,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
-    int max_blocks, int nsel, float *__restrict__ scores) {
+    int max_blocks, int nsel, int T, float *__restrict__ scores) {
   constexpr int EPV = BF16 ? 8 : 4;      // elements per 16-byte load
   constexpr int LPR = DI / EPV;          // lanes covering one token row of one head
   constexpr int ROWS = 256 / LPR;        // token rows per pass
   constexpr int PASSES = kBlk / ROWS;
   constexpr int ESZ = BF16 ? 2 : 4;
-  __shared__ float red[4][16];
+  __shared__ float red[4][kMaxOutRows];
 
   const int Hi = nsel * HS;
   const int r = blockIdx.x / max_blocks;
   const int b = blockIdx.x - r * max_blocks;
   const int L = seq_lens[r];
-  const int tau = (L - 1) / kBlk;
-  float *out = scores + static_cast<size_t>(r) * nsel * max_blocks + b;
-  if (b >= tau) {
-    if (threadIdx.x < nsel) out[static_cast<size_t>(threadIdx.x) * max_blocks] =
-        (b == tau) ? pos_inf() : neg_inf();
-    return;
-  }
+  float *out = scores + static_cast<size_t>(r) * T * nsel * max_blocks + b;
+  if (!decode_edges(out, b, L, T, nsel, max_blocks)) return;
   const int64_t phys = block_table[static_cast<size_t>(r) * max_blocks + b];
   const int t = threadIdx.x;
   const int piece = t % LPR;
   const int row = t / LPR;
   const char *kblk = static_cast<const char *>(k_idx) +
                      static_cast<size_t>(phys) * Hi * kBlk * DI * ESZ;
-  const char *qrow = static_cast<const char *>(q_idx) + static_cast<size_t>(r) * Hi * DI * ESZ;
   const int wave = t / kWave, lane = t % kWave;
 
   for (int g = 0; g < nsel; ++g) {
-    uint4 qv[HS];
-#pragma unroll
-    for (int hh = 0; hh < HS; ++hh)
-      qv[hh] = *reinterpret_cast<const uint4 *>(qrow + ((g * HS + hh) * DI + piece * EPV) * ESZ);
     uint4 kv[PASSES][HS];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p)
@@ -73,34 +96,41 @@ __global__ __launch_bounds__(256) void index_decode_kernel(
         kv[p][hh] = load_stream16(
             kblk + ((static_cast<size_t>(g * HS + hh) * kBlk + p * ROWS + row) * DI +
                     piece * EPV) * ESZ);
-    float m = neg_inf();
+    for (int i = 0; i < T; ++i) {
+      const char *qrow =
+          static_cast<const char *>(q_idx) + static_cast<size_t>(r * T + i) * Hi * DI * ESZ;
+      uint4 qv[HS];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      float acc = 0.f;
+      for (int hh = 0; hh < HS; ++hh)
+        qv[hh] =
+            *reinterpret_cast<const uint4 *>(qrow + ((g * HS + hh) * DI + piece * EPV) * ESZ);
+      float m = neg_inf();
 #pragma unroll
-      for (int hh = 0; hh < HS; ++hh) {
-        if constexpr (BF16) {
-          acc = dot2_bf16(qv[hh].x, kv[p][hh].x, acc);
-          acc = dot2_bf16(qv[hh].y, kv[p][hh].y, acc);
-          acc = dot2_bf16(qv[hh].z, kv[p][hh].z, acc);
-          acc = dot2_bf16(qv[hh].w, kv[p][hh].w, acc);
-        } else {
-          acc = fmaf(__uint_as_float(qv[hh].x), __uint_as_float(kv[p][hh].x), acc);
-          acc = fmaf(__uint_as_float(qv[hh].y), __uint_as_float(kv[p][hh].y), acc);
-          acc = fmaf(__uint_as_float(qv[hh].z), __uint_as_float(kv[p][hh].z), acc);
-          acc = fmaf(__uint_as_float(qv[hh].w), __uint_as_float(kv[p][hh].w), acc);
+      for (int p = 0; p < PASSES; ++p) {
+        float acc = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < HS; ++hh) {
+          if constexpr (BF16) {
+            acc = dot2_bf16(qv[hh].x, kv[p][hh].x, acc);
+            acc = dot2_bf16(qv[hh].y, kv[p][hh].y, acc);
+            acc = dot2_bf16(qv[hh].z, kv[p][hh].z, acc);
+            acc = dot2_bf16(qv[hh].w, kv[p][hh].w, acc);
+          } else {
+            acc = fmaf(__uint_as_float(qv[hh].x), __uint_as_float(kv[p][hh].x), acc);
+            acc = fmaf(__uint_as_float(qv[hh].y), __uint_as_float(kv[p][hh].y), acc);
+            acc = fmaf(__uint_as_float(qv[hh].z), __uint_as_float(kv[p][hh].z), acc);
+            acc = fmaf(__uint_as_float(qv[hh].w), __uint_as_float(kv[p][hh].w), acc);
+          }
         }
+        acc = group_sum<LPR>(acc);   // full dot product of token row p*ROWS+row
+        m = fmaxf(m, acc);
       }
-      acc = group_sum<LPR>(acc);   // full dot product of token row p*ROWS+row
-      m = fmaxf(m, acc);
+      m = group_max<kWave>(m);
+      if (lane == 0) red[wave][i * nsel + g] = m;
     }
-    m = group_max<kWave>(m);
-    if (lane == 0) red[wave][g] = m;
   }
   __syncthreads();
-  if (t < nsel)
-    out[static_cast<size_t>(t) * max_blocks] =
-        fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+  decode_finish<4>(out, red, b, L, T, nsel, max_blocks);
 }
 
 // ---------------------------------------------------------------------------
@@ -119,25 +149,20 @@ template <int DI, int HS>
 __global__ __launch_bounds__(256) void index_decode_fp8_kernel(
     const uint16_t *__restrict__ q_idx, const uint8_t *__restrict__ k_idx,
     const uint8_t *__restrict__ k_scale, const int32_t *__restrict__ block_table,
-    const int32_t *__restrict__ seq_lens, int max_blocks, int nsel,
+    const int32_t *__restrict__ seq_lens, int max_blocks, int nsel, int T,
     float *__restrict__ scores) {
   constexpr int LPR = DI / 16;           // lanes per token row of one head
   constexpr int ROWS = 256 / LPR;        // token rows per pass
   constexpr int PASSES = kBlk / ROWS;
   constexpr int SPR = DI / 32;           // scale bytes per token row
-  __shared__ float red[4][16];
+  __shared__ float red[4][kMaxOutRows];
 
   const int Hi = nsel * HS;
   const int r = blockIdx.x / max_blocks;
   const int b = blockIdx.x - r * max_blocks;
   const int L = seq_lens[r];
-  const int tau = (L - 1) / kBlk;
-  float *out = scores + static_cast<size_t>(r) * nsel * max_blocks + b;
-  if (b >= tau) {
-    if (threadIdx.x < nsel) out[static_cast<size_t>(threadIdx.x) * max_blocks] =
-        (b == tau) ? pos_inf() : neg_inf();
-    return;
-  }
+  float *out = scores + static_cast<size_t>(r) * T * nsel * max_blocks + b;
+  if (!decode_edges(out, b, L, T, nsel, max_blocks)) return;
   const int64_t phys = block_table[static_cast<size_t>(r) * max_blocks + b];
   const int t = threadIdx.x;
   const int piece = t % LPR;
@@ -145,19 +170,9 @@ __global__ __launch_bounds__(256) void index_decode_fp8_kernel(
   const int chunk = piece / 2;           // 32-channel scale block of this lane
   const uint8_t *kblk = k_idx + static_cast<size_t>(phys) * Hi * kBlk * DI;
   const uint8_t *sblk = k_scale + static_cast<size_t>(phys) * Hi * kBlk * SPR;
-  const uint16_t *qrow = q_idx + static_cast<size_t>(r) * Hi * DI;
   const int wave = t / kWave, lane = t % kWave;
 
   for (int g = 0; g < nsel; ++g) {
-    uint32_t qw[HS][8];                  // this lane's 16 query channels, bf16 pairs
-#pragma unroll
-    for (int hh = 0; hh < HS; ++hh) {
-      const uint16_t *qp = qrow + (g * HS + hh) * DI + piece * 16;
-      const uint4 a = *reinterpret_cast<const uint4 *>(qp);
-      const uint4 c = *reinterpret_cast<const uint4 *>(qp + 8);
-      qw[hh][0] = a.x; qw[hh][1] = a.y; qw[hh][2] = a.z; qw[hh][3] = a.w;
-      qw[hh][4] = c.x; qw[hh][5] = c.y; qw[hh][6] = c.z; qw[hh][7] = c.w;
-    }
     uint4 kv[PASSES][HS];
     uint32_t sc[PASSES][HS];
 #pragma unroll
@@ -168,33 +183,43 @@ __global__ __launch_bounds__(256) void index_decode_fp8_kernel(
         kv[p][hh] = load_stream16(kblk + tok * DI + piece * 16);
         sc[p][hh] = sblk[tok * SPR + chunk];
       }
-    float m = neg_inf();
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      float acc = 0.f;
+    for (int ti = 0; ti < T; ++ti) {
+      const uint16_t *qrow = q_idx + static_cast<size_t>(r * T + ti) * Hi * DI;
+      uint32_t qw[HS][8];                // this lane's 16 query channels, bf16 pairs
 #pragma unroll
       for (int hh = 0; hh < HS; ++hh) {
-        const uint32_t w[4] = {kv[p][hh].x, kv[p][hh].y, kv[p][hh].z, kv[p][hh].w};
-        float part = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
-          const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
-          part = dot2_bf16(qw[hh][2 * i], __builtin_bit_cast(uint32_t, lo), part);
-          part = dot2_bf16(qw[hh][2 * i + 1], __builtin_bit_cast(uint32_t, hi), part);
-        }
-        acc = fmaf(part, ldexpf(1.0f, static_cast<int>(sc[p][hh]) - 127), acc);
+        const uint16_t *qp = qrow + (g * HS + hh) * DI + piece * 16;
+        const uint4 a = *reinterpret_cast<const uint4 *>(qp);
+        const uint4 c = *reinterpret_cast<const uint4 *>(qp + 8);
+        qw[hh][0] = a.x; qw[hh][1] = a.y; qw[hh][2] = a.z; qw[hh][3] = a.w;
+        qw[hh][4] = c.x; qw[hh][5] = c.y; qw[hh][6] = c.z; qw[hh][7] = c.w;
       }
-      acc = group_sum<LPR>(acc);   // full group score of token row p*ROWS+row
-      m = fmaxf(m, acc);
+      float m = neg_inf();
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        float acc = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < HS; ++hh) {
+          const uint32_t w[4] = {kv[p][hh].x, kv[p][hh].y, kv[p][hh].z, kv[p][hh].w};
+          float part = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
+            const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+            part = dot2_bf16(qw[hh][2 * i], __builtin_bit_cast(uint32_t, lo), part);
+            part = dot2_bf16(qw[hh][2 * i + 1], __builtin_bit_cast(uint32_t, hi), part);
+          }
+          acc = fmaf(part, ldexpf(1.0f, static_cast<int>(sc[p][hh]) - 127), acc);
+        }
+        acc = group_sum<LPR>(acc);   // full group score of token row p*ROWS+row
+        m = fmaxf(m, acc);
+      }
+      m = group_max<kWave>(m);
+      if (lane == 0) red[wave][ti * nsel + g] = m;
     }
-    m = group_max<kWave>(m);
-    if (lane == 0) red[wave][g] = m;
   }
   __syncthreads();
-  if (t < nsel)
-    out[static_cast<size_t>(t) * max_blocks] =
-        fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+  decode_finish<4>(out, red, b, L, T, nsel, max_blocks);
 }
 
 // ---------------------------------------------------------------------------
@@ -539,7 +564,7 @@ __global__ __launch_bounds__(128) void index_prefill_f32_kernel(
 }
 
 template <bool BF16, int DI>
-hipError_t dispatch_decode_hs(const Geom &g, const msa_cache_t &c, const void *q_idx,
+hipError_t dispatch_decode_hs(const Geom &g, const msa_cache_t &c, int T, const void *q_idx,
                               float *scores, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(c.num_seqs) * c.max_blocks_per_seq);
   switch (g.Hs()) {
@@ -547,7 +572,7 @@ hipError_t dispatch_decode_hs(const Geom &g, const msa_cache_t &c, const void *q
   case HS:                                                                               \
     index_decode_kernel<BF16, DI, HS><<<grid, 256, 0, st>>>(                             \
         q_idx, c.k_idx_cache, c.block_table, c.seq_lens, c.max_blocks_per_seq, g.nsel,   \
-        scores);                                                                         \
+        T, scores);                                                                      \
     break;
     MSA_CASE(1) MSA_CASE(2) MSA_CASE(4) MSA_CASE(8)
 #undef MSA_CASE
@@ -557,7 +582,7 @@ hipError_t dispatch_decode_hs(const Geom &g, const msa_cache_t &c, const void *q
 }
 
 template <int DI>
-hipError_t dispatch_decode_fp8(const Geom &g, const msa_cache_t &c, const void *q_idx,
+hipError_t dispatch_decode_fp8(const Geom &g, const msa_cache_t &c, int T, const void *q_idx,
                                float *scores, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(c.num_seqs) * c.max_blocks_per_seq);
   const uint16_t *q = static_cast<const uint16_t *>(q_idx);
@@ -567,7 +592,7 @@ hipError_t dispatch_decode_fp8(const Geom &g, const msa_cache_t &c, const void *
   case HS:                                                                               \
     index_decode_fp8_kernel<DI, HS><<<grid, 256, 0, st>>>(                               \
         q, k, c.k_idx_scale, c.block_table, c.seq_lens, c.max_blocks_per_seq, g.nsel,    \
-        scores);                                                                         \
+        T, scores);                                                                      \
     break;
     MSA_CASE(1) MSA_CASE(2) MSA_CASE(4) MSA_CASE(8)
 #undef MSA_CASE
@@ -615,18 +640,18 @@ hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_
 
 }  // namespace
 
-hipError_t launch_index_decode(const Geom &g, const msa_cache_t &c, const void *q_idx,
+hipError_t launch_index_decode(const Geom &g, const msa_cache_t &c, int T, const void *q_idx,
                                float *scores, hipStream_t st) {
   if (g.fp8) {
-    return g.Di == 64 ? dispatch_decode_fp8<64>(g, c, q_idx, scores, st)
-                      : dispatch_decode_fp8<32>(g, c, q_idx, scores, st);
+    return g.Di == 64 ? dispatch_decode_fp8<64>(g, c, T, q_idx, scores, st)
+                      : dispatch_decode_fp8<32>(g, c, T, q_idx, scores, st);
   }
   if (g.bf16) {
-    return g.Di == 64 ? dispatch_decode_hs<true, 64>(g, c, q_idx, scores, st)
-                      : dispatch_decode_hs<true, 32>(g, c, q_idx, scores, st);
+    return g.Di == 64 ? dispatch_decode_hs<true, 64>(g, c, T, q_idx, scores, st)
+                      : dispatch_decode_hs<true, 32>(g, c, T, q_idx, scores, st);
   }
-  return g.Di == 64 ? dispatch_decode_hs<false, 64>(g, c, q_idx, scores, st)
-                    : dispatch_decode_hs<false, 32>(g, c, q_idx, scores, st);
+  return g.Di == 64 ? dispatch_decode_hs<false, 64>(g, c, T, q_idx, scores, st)
+                    : dispatch_decode_hs<false, 32>(g, c, T, q_idx, scores, st);
 }
 
 hipError_t launch_index_prefill(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,

@@ -114,12 +114,69 @@ msa_status_t check_batch(const msa_batch_t *b) {
 
 float resolve_scale(float s, int D) { return s > 0.f ? s : 1.0f / std::sqrt(float(D)); }
 
+
 // Bit-level NaN test: the library is built with -fno-honor-nans, under which
 // `x != x` may be folded away.
 bool is_nan_bits(float x) {
   uint32_t u;
   std::memcpy(&u, &x, sizeof(u));
   return (u & 0x7fffffffu) > 0x7f800000u;
+}
+
+constexpr int kMaxTokensPerSeq = 8;
+
+msa_status_t check_tokens(int T, const msa::Geom &g) {
+  MSA_REQUIRE(T >= 1 && T <= kMaxTokensPerSeq, MSA_ERR_UNSUPPORTED,
+              "tokens_per_seq %d unsupported (1 .. %d)", T, kMaxTokensPerSeq);
+  MSA_REQUIRE(T * g.nsel <= 128, MSA_ERR_UNSUPPORTED,
+              "tokens_per_seq * num_sel_groups (%d) exceeds 128", T * g.nsel);
+  return MSA_OK;
+}
+
+// Decode indexer for T tokens per sequence (validated arguments).
+msa_status_t index_decode(const msa_geom_t *geom, const msa_cache_t *cache, int T,
+                          const void *q_idx, float *scores, void *stream) {
+  msa::Geom g;
+  msa_status_t st = check_geom(geom, &g);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache(cache, false, true, g.fp8)) != MSA_OK) return st;
+  if ((st = check_tokens(T, g)) != MSA_OK) return st;
+  MSA_REQUIRE(q_idx != nullptr && scores != nullptr, MSA_ERR_INVALID_ARG,
+              "q_idx / scores is NULL");
+  return hip_status(msa::launch_index_decode(g, *cache, T, q_idx, scores,
+                                             static_cast<hipStream_t>(stream)),
+                    "index_decode");
+}
+
+// Split-KV decode attention for T tokens per sequence.
+msa_status_t attn_decode(const msa_geom_t *geom, const msa_cache_t *cache, int T, const void *q,
+                         const int32_t *ids, int32_t topk, float softmax_scale,
+                         int32_t num_splits, void *workspace, size_t workspace_bytes,
+                         void *out, float *lse, void *stream) {
+  msa::Geom g;
+  msa_status_t st = check_geom(geom, &g);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache(cache, true, false, g.fp8)) != MSA_OK) return st;
+  if ((st = check_tokens(T, g)) != MSA_OK) return st;
+  MSA_REQUIRE(q != nullptr && ids != nullptr && out != nullptr, MSA_ERR_INVALID_ARG,
+              "q / ids / out is NULL");
+  MSA_REQUIRE(topk >= 1, MSA_ERR_INVALID_ARG, "topk must be positive");
+  MSA_REQUIRE(!is_nan_bits(softmax_scale), MSA_ERR_INVALID_ARG, "softmax_scale is NaN");
+  const int rows = cache->num_seqs * T;
+  const int s = num_splits > 0 ? (num_splits < topk ? num_splits : topk)
+                               : msa::decode_auto_splits(g, rows, topk);
+  if (g.bf16) {
+    const size_t need = msa::decode_workspace_bytes(g, rows, s);
+    MSA_REQUIRE(workspace != nullptr, MSA_ERR_INVALID_ARG, "workspace is NULL");
+    MSA_REQUIRE(reinterpret_cast<uintptr_t>(workspace) % 256 == 0, MSA_ERR_INVALID_ARG,
+                "workspace must be 256-byte aligned");
+    MSA_REQUIRE(workspace_bytes >= need, MSA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  }
+  return hip_status(msa::launch_attn_decode(g, *cache, T, q, ids, topk,
+                                            resolve_scale(softmax_scale, g.D), s, workspace,
+                                            out, lse, static_cast<hipStream_t>(stream)),
+                    "sparse_attn_decode");
 }
 
 }  // namespace
@@ -172,12 +229,11 @@ msa_status_t msa_index_scores(const msa_geom_t *geom, const msa_cache_t *cache,
                 "the prefill indexer reads FP8 caches for groups of at most 128 channels");
     if (batch->total_units == 0) return ok();   // nothing to score
   }
+  if (batch == nullptr) return index_decode(geom, cache, 1, q_idx, scores, stream);
   MSA_REQUIRE(q_idx != nullptr && scores != nullptr, MSA_ERR_INVALID_ARG,
               "q_idx / scores is NULL");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (batch == nullptr) return hip_status(msa::launch_index_decode(g, *cache, q_idx, scores, s),
-                                          "index_decode");
-  return hip_status(msa::launch_index_prefill(g, *cache, *batch, q_idx, scores, s),
+  return hip_status(msa::launch_index_prefill(g, *cache, *batch, q_idx, scores,
+                                              static_cast<hipStream_t>(stream)),
                     "index_prefill");
 }
 
@@ -227,28 +283,24 @@ msa_status_t msa_sparse_attn_decode(const msa_geom_t *geom, const msa_cache_t *c
                                     float softmax_scale, int32_t num_splits,
                                     void *workspace, size_t workspace_bytes, void *out,
                                     float *lse, void *stream) {
-  msa::Geom g;
-  msa_status_t st = check_geom(geom, &g);
-  if (st != MSA_OK) return st;
-  if ((st = check_cache(cache, true, false, g.fp8)) != MSA_OK) return st;
-  MSA_REQUIRE(q != nullptr && ids != nullptr && out != nullptr, MSA_ERR_INVALID_ARG,
-              "q / ids / out is NULL");
-  MSA_REQUIRE(topk >= 1, MSA_ERR_INVALID_ARG, "topk must be positive");
-  MSA_REQUIRE(!is_nan_bits(softmax_scale), MSA_ERR_INVALID_ARG, "softmax_scale is NaN");
-  const int s = num_splits > 0 ? (num_splits < topk ? num_splits : topk)
-                               : msa::decode_auto_splits(g, cache->num_seqs, topk);
-  if (g.bf16) {
-    const size_t need = msa::decode_workspace_bytes(g, cache->num_seqs, s);
-    MSA_REQUIRE(workspace != nullptr, MSA_ERR_INVALID_ARG, "workspace is NULL");
-    MSA_REQUIRE(reinterpret_cast<uintptr_t>(workspace) % 256 == 0, MSA_ERR_INVALID_ARG,
-                "workspace must be 256-byte aligned");
-    MSA_REQUIRE(workspace_bytes >= need, MSA_ERR_WORKSPACE_TOO_SMALL,
-                "workspace %zu bytes < %zu needed", workspace_bytes, need);
-  }
-  return hip_status(msa::launch_attn_decode(g, *cache, q, ids, topk,
-                                            resolve_scale(softmax_scale, g.D), s, workspace,
-                                            out, lse, static_cast<hipStream_t>(stream)),
-                    "sparse_attn_decode");
+  return attn_decode(geom, cache, 1, q, ids, topk, softmax_scale, num_splits, workspace,
+                     workspace_bytes, out, lse, stream);
+}
+
+msa_status_t msa_index_scores_per_token(const msa_geom_t *geom, const msa_cache_t *cache,
+                                        int32_t tokens_per_seq, const void *q_idx,
+                                        float *scores, void *stream) {
+  return index_decode(geom, cache, tokens_per_seq, q_idx, scores, stream);
+}
+
+msa_status_t msa_sparse_attn_decode_per_token(const msa_geom_t *geom, const msa_cache_t *cache,
+                                              int32_t tokens_per_seq, const void *q,
+                                              const int32_t *ids, int32_t topk,
+                                              float softmax_scale, int32_t num_splits,
+                                              void *workspace, size_t workspace_bytes,
+                                              void *out, float *lse, void *stream) {
+  return attn_decode(geom, cache, tokens_per_seq, q, ids, topk, softmax_scale, num_splits,
+                     workspace, workspace_bytes, out, lse, stream);
 }
 
 const char *msa_status_string(msa_status_t status) {

@@ -17,7 +17,8 @@ struct Geom {
   int Hs() const { return Hi / nsel; }
 };
 
-hipError_t launch_index_decode(const Geom &g, const msa_cache_t &c, const void *q_idx,
+// Decode with T new tokens per sequence (T = 1: one), each selecting its own blocks.
+hipError_t launch_index_decode(const Geom &g, const msa_cache_t &c, int T, const void *q_idx,
                                float *scores, hipStream_t st);
 hipError_t launch_index_prefill(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                 const void *q_idx, float *scores, hipStream_t st);
@@ -29,7 +30,7 @@ hipError_t launch_attn_prefill(const Geom &g, const msa_cache_t &c, const msa_ba
 // Split count used when the caller passes num_splits <= 0.
 int decode_auto_splits(const Geom &g, int num_seqs, int topk);
 size_t decode_workspace_bytes(const Geom &g, int num_seqs, int num_splits);
-hipError_t launch_attn_decode(const Geom &g, const msa_cache_t &c, const void *q,
+hipError_t launch_attn_decode(const Geom &g, const msa_cache_t &c, int T, const void *q,
                               const int32_t *ids, int topk, float scale, int num_splits,
                               void *workspace, void *out, float *lse, hipStream_t st);
 

@@ -22,6 +22,8 @@ of context):
                       8 planted blocks per 32-block span
   decode_1m_b8_fp8,   the 1M decode and the 32k prefill on FP8 caches (E4M3
   prefill_32k_fp8     codes, a power-of-two scale per 32 channels of a row)
+  decode_1m_b8_t4     the 1M decode with 4 new tokens per sequence, each
+                      selecting its own blocks (speculative verification)
 
 Planting ("relevant blocks"): for every (sequence, selection group g) a seeded
 unit direction u_h is drawn per indexer head h of the group; a * u_h is added to
@@ -70,6 +72,7 @@ class Workload:
     plant_span: Optional[int] = 32  # span in blocks; None = whole context
     seed: int = 0
     cache_format: str = "plain"     # "plain" or "fp8" (E4M3 codes + power-of-two scales)
+    tokens_per_seq: int = 1         # decode: new tokens per sequence, each selecting its own
 
     @property
     def is_decode(self):
@@ -92,7 +95,7 @@ class Workload:
 
     @property
     def total_q(self):
-        return self.num_seqs if self.is_decode else sum(self.q_lens)
+        return self.num_seqs * self.tokens_per_seq if self.is_decode else sum(self.q_lens)
 
     def replace(self, **kw):
         return dataclasses.replace(self, **kw)
@@ -122,6 +125,9 @@ WORKLOADS = {
     "prefill_32k_fp8": Workload(
         "prefill_32k_fp8", "bf16", [32768], [32768], topk=16, plant_count=8,
         plant_span=32, seed=1002, cache_format="fp8"),
+    "decode_1m_b8_t4": Workload(
+        "decode_1m_b8_t4", "bf16", [1048576] * 8, None, topk=64, plant_count=63,
+        plant_span=None, seed=1004, tokens_per_seq=4),
 }
 
 
@@ -206,7 +212,7 @@ def make_inputs(w: Workload, device="cpu", permute=False, chunk_blocks=2048):
     [P][H_kv][128][D], v_cache [P][H_kv][D][128] (each block's values stored
     d-major), k_idx_cache [P][H_i][128][D_i] (all in the workload dtype),
     block_table int32 [B][max_blocks], seq_lens int32 [B], q_lens int32 [B]
-    (decode: ones) and cu_q_lens int32 [B+1]. The caches are drawn chunk by chunk
+    (decode: tokens_per_seq each) and cu_q_lens int32 [B+1]. The caches are drawn chunk by chunk
     of physical blocks so that only one fp32 chunk is alive at a time.
 
     With w.cache_format == "fp8" the caches are uint8 E4M3 codes and the dict also
@@ -223,7 +229,7 @@ def make_inputs(w: Workload, device="cpu", permute=False, chunk_blocks=2048):
     a = plant_amplitude(w)
     bt = block_table(w, permute)
     perm = physical_permutation(w, permute)
-    q_lens = [1] * B if w.is_decode else list(w.q_lens)
+    q_lens = [w.tokens_per_seq] * B if w.is_decode else list(w.q_lens)
     cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
 
     # packed block index of (request, logical block): base[r] + b

@@ -203,7 +203,8 @@ msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *
 
 /* Bytes of device workspace msa_sparse_attn_decode needs. num_splits <= 0 picks
  * the library's own split count for this shape (the same one the decode call
- * picks for num_splits <= 0). */
+ * picks for num_splits <= 0). For msa_sparse_attn_decode_per_token pass the
+ * number of token rows, num_seqs * tokens_per_seq, as num_seqs. */
 size_t msa_decode_workspace_size(const msa_geom_t *geom, int32_t num_seqs,
                                  int32_t topk, int32_t num_splits);
 
@@ -222,6 +223,31 @@ msa_status_t msa_sparse_attn_decode(const msa_geom_t *geom, const msa_cache_t *c
                                     float softmax_scale, int32_t num_splits,
                                     void *workspace, size_t workspace_bytes, void *out,
                                     float *lse, void *stream);
+
+/* Per-query-token selection for T new tokens per sequence (multi-token decode:
+ * speculative verification, multi-token prediction). [feat] row "Indexer-selected
+ * sparse attention": the model selects per query token ([B, H_idx, S_q, topk]).
+ * Sequence r has T = tokens_per_seq (1 <= T <= 8, T * num_sel_groups <= 128) new
+ * tokens at positions seq_lens[r] - T + i, stored as rows r * T + i; each token
+ * row is its own unit: it scores the blocks with its own indexer query, keeps its
+ * own diagonal block (position / 128) and top-k, and attends causally. T = 1 is
+ * the decode path of msa_index_scores / msa_sparse_attn_decode.
+ *   msa_index_scores_per_token:  q_idx [num_seqs * T][H_i][D_i]
+ *       -> scores fp32 [num_seqs * T][num_sel_groups][max_blocks_per_seq]
+ *   msa_select_topk_blocks over those rows -> ids [num_seqs * T][num_sel_groups][topk]
+ *   msa_sparse_attn_decode_per_token:  q [num_seqs * T][H_q][D], ids as above
+ *       -> out [num_seqs * T][H_q][D], lse fp32 [num_seqs * T][H_q] or NULL;
+ *       workspace >= msa_decode_workspace_size(geom, num_seqs * T, topk, num_splits).
+ * Requires seq_lens[r] >= T (device values are not checked). */
+msa_status_t msa_index_scores_per_token(const msa_geom_t *geom, const msa_cache_t *cache,
+                                        int32_t tokens_per_seq, const void *q_idx,
+                                        float *scores, void *stream);
+msa_status_t msa_sparse_attn_decode_per_token(const msa_geom_t *geom, const msa_cache_t *cache,
+                                              int32_t tokens_per_seq, const void *q,
+                                              const int32_t *ids, int32_t topk,
+                                              float softmax_scale, int32_t num_splits,
+                                              void *workspace, size_t workspace_bytes,
+                                              void *out, float *lse, void *stream);
 
 /* Step 0, the new tokens before step 1: per-head RMSNorm of queries and keys,
  * partial rotary embedding, and the insert of K, V and the indexer keys into the

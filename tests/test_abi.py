@@ -246,3 +246,19 @@ def test_fp8_cache_checks(lib):
     # plain caches ignore the scale pointers
     g0, c0 = _geom(), _cache(k_scale=None, v_scale=None, k_idx_scale=None)
     assert _insert(lib, g0, c0, msa._Batch(None, 0, 0)) == OK
+
+
+def test_per_token_checks(lib):
+    g, c = _geom(), _cache()
+    for T in (0, 9, -1):
+        assert lib.msa_index_scores_per_token(ctypes.byref(g), ctypes.byref(c), T, FAKE, FAKE,
+                                              None) == UNSUPPORTED, T
+        assert lib.msa_sparse_attn_decode_per_token(ctypes.byref(g), ctypes.byref(c), T, FAKE,
+                                                    FAKE, 16, 0.0, 0, FAKE, 1 << 30, FAKE, None,
+                                                    None) == UNSUPPORTED, T
+    assert lib.msa_index_scores_per_token(ctypes.byref(g), ctypes.byref(c), 4, None, FAKE,
+                                          None) == INVALID
+    need = lib.msa_decode_workspace_size(ctypes.byref(g), 2 * 4, 16, 0)
+    assert lib.msa_sparse_attn_decode_per_token(ctypes.byref(g), ctypes.byref(c), 4, FAKE, FAKE,
+                                                16, 0.0, 0, FAKE, need - 1, FAKE, None,
+                                                None) == WS_SMALL
