@@ -192,6 +192,29 @@ def measured_traffic(kernel_key, source_file):
         return None
 
 
+def graph_ms_per_step(runner, steps, warmup):
+    """The same step captured once in a HIP graph and replayed: the time per
+    replay, without the launch gaps between the step's kernels."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        runner.step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        runner.step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 def measure(w, dev, steps, warmup):
     r = Runner(w, dev)
     ms, per, wall = r.timed(steps, warmup)
@@ -200,7 +223,8 @@ def measure(w, dev, steps, warmup):
     tokens = selected_kv_tokens(w, ids, units)
     G = w.num_q_heads // w.num_kv_heads
     res = dict(workload=w.name, ms_per_step=ms, kernel_ms=per, wall_s=wall,
-               selected_kv_tokens_per_step=tokens, value=tokens / (ms * 1e-3))
+               selected_kv_tokens_per_step=tokens, value=tokens / (ms * 1e-3),
+               graph_ms_per_step=graph_ms_per_step(r, steps, warmup))
     if w.is_decode:
         nbytes = index_decode_bytes(w)
         t = per["index_scores"] * 1e-3
@@ -337,7 +361,8 @@ def main():
     ap.add_argument("--workload", default="prefill_32k", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--second", default="decode_1m_b8",
                     help="second workload measured in the same run ('none' to skip)")
-    ap.add_argument("--extra", default="decode_1m_b8_fp8,prefill_32k_fp8,decode_1m_b8_t4",
+    ap.add_argument("--extra", default="decode_1m_b8_fp8,prefill_32k_fp8,decode_1m_b8_t4,"
+                                      "decode_ragged_b64",
                     help="more workloads measured in the same run (FP8 caches, several "
                          "tokens per sequence), comma-separated ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -420,21 +445,22 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) with planted blocks), inputs resident in HBM",
         "config": config,
+        "graph_ms_per_step": main_res["graph_ms_per_step"],
         "kernel_ms": main_res["kernel_ms"],
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
     }
     if second is not None:
         line["second_workload"] = {k: second[k] for k in (
-            "workload", "value", "ms_per_step", "kernel_ms", "roofline", "step_hbm_frac")
-            if k in second}
+            "workload", "value", "ms_per_step", "graph_ms_per_step", "kernel_ms", "roofline",
+            "step_hbm_frac") if k in second}
     if extra:
         # the same workloads on FP8 caches (E4M3 codes, power-of-two scale per 32
         # channels), and decode with several new tokens per sequence, each selecting
         # its own blocks
         line["extra_workloads"] = [{k: r[k] for k in (
-            "workload", "value", "ms_per_step", "kernel_ms", "roofline", "step_hbm_frac")
-            if k in r} for r in extra]
+            "workload", "value", "ms_per_step", "graph_ms_per_step", "kernel_ms", "roofline",
+            "step_hbm_frac") if k in r} for r in extra]
     # the new-token step before the path (QK-norm + partial RoPE + cache insert),
     # timed on its own: not part of the step above
     line["qk_norm_rope_insert"] = inserts

@@ -18,6 +18,8 @@
 // coalesced loads and reduces with cross-lane shuffles. Prefill (128 queries per
 // unit) is a dense 128 x 128 x (H_s * D_i) contraction per (tile, block) and runs
 // on bf16 MFMA with a max-pool epilogue.
+#include <algorithm>
+
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -61,24 +63,123 @@ __device__ __forceinline__ void decode_finish(float *out, const float (*red)[kMa
   }
 }
 
+// Work schedule of the decode indexers, for ragged batches (sequences of mixed
+// lengths, block tables wider than most sequences). With `compact`, each
+// work-group first builds in LDS (pfx, num_seqs + 1 ints) the prefix sum of the
+// blocks every sequence needs scored (those before its last token's diagonal,
+// (seq_len - 1) / 128) and works on that compacted list of (sequence, block)
+// items (sequence by binary search), so a batch costs what its real blocks cost;
+// the +inf / -inf entries at and after each sequence's last diagonal are written
+// by a loop strided over all threads of the grid. Without `compact` (more
+// sequences than the LDS prefix sum holds) the items are all (sequence, block)
+// pairs and the empty ones only write their entries.
+//
+// Items are handed out by guided self-scheduling: the grid is four times the
+// work-groups that fit on the device at once; the first quarter (dispatched
+// first, all resident) take three quarters of the items in equal contiguous
+// chunks, and the other work-groups take small chunks of the rest, dispatched in
+// block-id order as slots free up, so that CUs that run slower end up with less
+// work. `score(r, b, L, out)` scores one block (its own barriers included) and is
+// called uniformly by the whole work-group.
+__device__ __forceinline__ void guided_chunk(int64_t n, int64_t &it0, int64_t &it1) {
+  const int64_t G = gridDim.x, w = blockIdx.x;
+  if (G == 1) {
+    it0 = 0;
+    it1 = n;
+    return;
+  }
+  const int64_t R = G >= 4 ? G / 4 : 1;   // G - R >= 1
+  const int64_t c1 = (3 * n / 4) / R;
+  if (w < R) {
+    it0 = w * c1;
+    it1 = it0 + c1;
+    return;
+  }
+  const int64_t rest = n - c1 * R, c2 = (rest + (G - R) - 1) / (G - R);
+  it0 = c1 * R + (w - R) * c2;
+  it1 = it0 + c2 < n ? it0 + c2 : n;
+}
+
+template <typename Score>
+__device__ __forceinline__ void decode_schedule(const int32_t *__restrict__ seq_lens,
+                                                int num_seqs, int max_blocks, int T, int nsel,
+                                                float *scores, bool compact, int *pfx,
+                                                Score score) {
+  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+  const size_t row_stride = static_cast<size_t>(T) * nsel * max_blocks;   // per sequence
+  if (!compact) {
+    int64_t it0, it1;
+    guided_chunk(static_cast<int64_t>(num_seqs) * max_blocks, it0, it1);
+    for (int64_t it = it0; it < it1; ++it) {
+      const int r = static_cast<int>(it / max_blocks);
+      const int b = static_cast<int>(it - static_cast<int64_t>(r) * max_blocks);
+      const int L = seq_lens[r];
+      float *out = scores + r * row_stride + b;
+      if (decode_edges(out, b, L, T, nsel, max_blocks)) score(r, b, L, out);
+    }
+    return;
+  }
+  __shared__ int wsum[4];
+  int carry = 0;
+  for (int base = 0; base < num_seqs; base += 256) {
+    const int r = base + t;
+    int x = r < num_seqs ? max((seq_lens[r] - 1) / kBlk, 0) : 0;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {   // inclusive scan inside the wave
+      const int y = __shfl_up(x, off, kWave);
+      if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) wsum[wave] = x;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    if (r < num_seqs) pfx[r + 1] = before + x;
+    carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  if (t == 0) pfx[0] = 0;
+  __syncthreads();
+  const int64_t total = static_cast<int64_t>(num_seqs) * max_blocks;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + t; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int r = static_cast<int>(e / max_blocks);
+    const int b = static_cast<int>(e - static_cast<int64_t>(r) * max_blocks);
+    const int L = seq_lens[r];
+    if (b < (L - 1) / kBlk) continue;          // scored below
+    float *out = scores + r * row_stride + b;
+    for (int k = 0; k < T * nsel; ++k) {
+      const int tau = (L - T + k / nsel) / kBlk;
+      out[static_cast<size_t>(k) * max_blocks] = (b == tau) ? pos_inf() : neg_inf();
+    }
+  }
+  int64_t it0, it1;
+  guided_chunk(pfx[num_seqs], it0, it1);
+  for (int it = static_cast<int>(it0); it < it1; ++it) {
+    int lo = 0, hi = num_seqs;                 // pfx[lo] <= it < pfx[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (pfx[mid] <= it) lo = mid; else hi = mid;
+    }
+    score(lo, it - pfx[lo], seq_lens[lo], scores + lo * row_stride + (it - pfx[lo]));
+  }
+}
+
 template <bool BF16, int DI, int HS>
 __global__ __launch_bounds__(256) void index_decode_kernel(
     const void *__restrict__ q_idx, const void *__restrict__ k_idx,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
-    int max_blocks, int nsel, int T, float *__restrict__ scores) {
+    int num_seqs, int max_blocks, int nsel, int T, bool compact, float *__restrict__ scores) {
   constexpr int EPV = BF16 ? 8 : 4;      // elements per 16-byte load
   constexpr int LPR = DI / EPV;          // lanes covering one token row of one head
   constexpr int ROWS = 256 / LPR;        // token rows per pass
   constexpr int PASSES = kBlk / ROWS;
   constexpr int ESZ = BF16 ? 2 : 4;
   __shared__ float red[4][kMaxOutRows];
-
+  extern __shared__ int pfx[];
   const int Hi = nsel * HS;
-  const int r = blockIdx.x / max_blocks;
-  const int b = blockIdx.x - r * max_blocks;
-  const int L = seq_lens[r];
-  float *out = scores + static_cast<size_t>(r) * T * nsel * max_blocks + b;
-  if (!decode_edges(out, b, L, T, nsel, max_blocks)) return;
+
+  decode_schedule(seq_lens, num_seqs, max_blocks, T, nsel, scores, compact, pfx,
+                  [&](int r, int b, int L, float *out) __attribute__((always_inline)) {
   const int64_t phys = block_table[static_cast<size_t>(r) * max_blocks + b];
   const int t = threadIdx.x;
   const int piece = t % LPR;
@@ -131,6 +232,8 @@ __global__ __launch_bounds__(256) void index_decode_kernel(
   }
   __syncthreads();
   decode_finish<4>(out, red, b, L, T, nsel, max_blocks);
+  __syncthreads();   // red is refilled by the next block
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -149,20 +252,18 @@ template <int DI, int HS>
 __global__ __launch_bounds__(256) void index_decode_fp8_kernel(
     const uint16_t *__restrict__ q_idx, const uint8_t *__restrict__ k_idx,
     const uint8_t *__restrict__ k_scale, const int32_t *__restrict__ block_table,
-    const int32_t *__restrict__ seq_lens, int max_blocks, int nsel, int T,
-    float *__restrict__ scores) {
+    const int32_t *__restrict__ seq_lens, int num_seqs, int max_blocks, int nsel, int T,
+    bool compact, float *__restrict__ scores) {
   constexpr int LPR = DI / 16;           // lanes per token row of one head
   constexpr int ROWS = 256 / LPR;        // token rows per pass
   constexpr int PASSES = kBlk / ROWS;
   constexpr int SPR = DI / 32;           // scale bytes per token row
   __shared__ float red[4][kMaxOutRows];
-
+  extern __shared__ int pfx[];
   const int Hi = nsel * HS;
-  const int r = blockIdx.x / max_blocks;
-  const int b = blockIdx.x - r * max_blocks;
-  const int L = seq_lens[r];
-  float *out = scores + static_cast<size_t>(r) * T * nsel * max_blocks + b;
-  if (!decode_edges(out, b, L, T, nsel, max_blocks)) return;
+
+  decode_schedule(seq_lens, num_seqs, max_blocks, T, nsel, scores, compact, pfx,
+                  [&](int r, int b, int L, float *out) __attribute__((always_inline)) {
   const int64_t phys = block_table[static_cast<size_t>(r) * max_blocks + b];
   const int t = threadIdx.x;
   const int piece = t % LPR;
@@ -220,6 +321,8 @@ __global__ __launch_bounds__(256) void index_decode_fp8_kernel(
   }
   __syncthreads();
   decode_finish<4>(out, red, b, L, T, nsel, max_blocks);
+  __syncthreads();   // red is refilled by the next block
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -563,16 +666,47 @@ __global__ __launch_bounds__(128) void index_prefill_f32_kernel(
   if (threadIdx.x == 0) out[b] = fmaxf(red[0], red[1]);
 }
 
+// Grid of the decode indexers: four times the work-groups resident at once (CUs x
+// work-groups per CU for this kernel and LDS size), never more than there are
+// (sequence, block) pairs; the compacted schedule when the per-sequence prefix
+// sum fits in LDS.
+constexpr int kMaxCompactSeqs = 16384;
+
+struct DecodeLaunch {
+  dim3 grid;
+  size_t lds;
+  bool compact;
+};
+
+template <typename Kernel>
+DecodeLaunch decode_launch(const msa_cache_t &c, Kernel kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  (void)hipGetDevice(&dev);
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  const bool compact = c.num_seqs <= kMaxCompactSeqs;
+  const size_t lds = compact ? (static_cast<size_t>(c.num_seqs) + 1) * sizeof(int) : 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 1;
+  const int64_t pairs = static_cast<int64_t>(c.num_seqs) * c.max_blocks_per_seq;
+  const int64_t groups = std::min<int64_t>(pairs, static_cast<int64_t>(cus) * per_cu * 4);
+  return DecodeLaunch{dim3(static_cast<unsigned>(std::max<int64_t>(groups, 1))), lds, compact};
+}
+
 template <bool BF16, int DI>
 hipError_t dispatch_decode_hs(const Geom &g, const msa_cache_t &c, int T, const void *q_idx,
                               float *scores, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(c.num_seqs) * c.max_blocks_per_seq);
   switch (g.Hs()) {
 #define MSA_CASE(HS)                                                                     \
   case HS:                                                                               \
-    index_decode_kernel<BF16, DI, HS><<<grid, 256, 0, st>>>(                             \
-        q_idx, c.k_idx_cache, c.block_table, c.seq_lens, c.max_blocks_per_seq, g.nsel,   \
-        T, scores);                                                                      \
+    {                                                                                    \
+    const DecodeLaunch dl = decode_launch(c, index_decode_kernel<BF16, DI, HS>);        \
+    index_decode_kernel<BF16, DI, HS><<<dl.grid, 256, dl.lds, st>>>(                     \
+        q_idx, c.k_idx_cache, c.block_table, c.seq_lens, c.num_seqs,                     \
+        c.max_blocks_per_seq, g.nsel, T, dl.compact, scores);                            \
+    }                                                                                    \
     break;
     MSA_CASE(1) MSA_CASE(2) MSA_CASE(4) MSA_CASE(8)
 #undef MSA_CASE
@@ -584,15 +718,17 @@ hipError_t dispatch_decode_hs(const Geom &g, const msa_cache_t &c, int T, const 
 template <int DI>
 hipError_t dispatch_decode_fp8(const Geom &g, const msa_cache_t &c, int T, const void *q_idx,
                                float *scores, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(c.num_seqs) * c.max_blocks_per_seq);
   const uint16_t *q = static_cast<const uint16_t *>(q_idx);
   const uint8_t *k = static_cast<const uint8_t *>(c.k_idx_cache);
   switch (g.Hs()) {
 #define MSA_CASE(HS)                                                                     \
   case HS:                                                                               \
-    index_decode_fp8_kernel<DI, HS><<<grid, 256, 0, st>>>(                               \
-        q, k, c.k_idx_scale, c.block_table, c.seq_lens, c.max_blocks_per_seq, g.nsel,    \
-        T, scores);                                                                      \
+    {                                                                                    \
+    const DecodeLaunch dl = decode_launch(c, index_decode_fp8_kernel<DI, HS>);          \
+    index_decode_fp8_kernel<DI, HS><<<dl.grid, 256, dl.lds, st>>>(                       \
+        q, k, c.k_idx_scale, c.block_table, c.seq_lens, c.num_seqs, c.max_blocks_per_seq, \
+        g.nsel, T, dl.compact, scores);                                                  \
+    }                                                                                    \
     break;
     MSA_CASE(1) MSA_CASE(2) MSA_CASE(4) MSA_CASE(8)
 #undef MSA_CASE

@@ -22,6 +22,8 @@ of context):
                       8 planted blocks per 32-block span
   decode_1m_b8_fp8,   the 1M decode and the 32k prefill on FP8 caches (E4M3
   prefill_32k_fp8     codes, a power-of-two scale per 32 channels of a row)
+  decode_ragged_b64   bf16, 64 sequences of mixed context (1 x 1M, 3 x 256k,
+                      12 x 64k, 48 x 4k tokens), top-k 32: a ragged decode batch
   decode_1m_b8_t4     the 1M decode with 4 new tokens per sequence, each
                       selecting its own blocks (speculative verification)
 
@@ -125,6 +127,10 @@ WORKLOADS = {
     "prefill_32k_fp8": Workload(
         "prefill_32k_fp8", "bf16", [32768], [32768], topk=16, plant_count=8,
         plant_span=32, seed=1002, cache_format="fp8"),
+    "decode_ragged_b64": Workload(
+        "decode_ragged_b64", "bf16",
+        [1048576] + [262144] * 3 + [65536] * 12 + [4096] * 48, None, topk=32,
+        plant_count=31, plant_span=None, seed=1006),
     "decode_1m_b8_t4": Workload(
         "decode_1m_b8_t4", "bf16", [1048576] * 8, None, topk=64, plant_count=63,
         plant_span=None, seed=1004, tokens_per_seq=4),
@@ -149,6 +155,8 @@ def planted_blocks(w: Workload, r: int, g: int) -> np.ndarray:
     which holds the query, is never a candidate and is not planted."""
     nb = w.blocks(r)
     limit = nb - 1 if w.is_decode else nb
+    if limit <= 0:                       # one block, the query's own: nothing to plant
+        return np.zeros(0, dtype=np.int64)
     rng = _np_rng(w, _T_PLANT_POS, r, g)
     span = w.plant_span or limit
     out = []

@@ -287,7 +287,7 @@ def test_full_size_prefill_sampled(name, gpu_device):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["decode_128k_b64", "decode_1m_b8"])
+@pytest.mark.parametrize("name", ["decode_128k_b64", "decode_1m_b8", "decode_ragged_b64"])
 def test_full_size_decode_sampled(name, gpu_device):
     w = synth.WORKLOADS[name]
     say(f"{name} generate")
@@ -296,8 +296,34 @@ def test_full_size_decode_sampled(name, gpu_device):
     res = run_gpu(w, inp, geom, cache, gpu_device)
     units = O.decode_units(w.seq_lens)
     sampled_parity(w, inp, res, units, _sample_units(units, 2, 2), rows_per_unit=1)
-    # every row of scores has the diagonal +inf at the last block and no -inf before it
+    # every row is finite before its diagonal, +inf there and -inf after it
     sc = res["scores"].numpy()
-    assert np.isposinf(sc[:, :, -1]).all() and np.isfinite(sc[:, :, :-1]).all()
+    for u, un in enumerate(units):
+        tau = un["tau"]
+        assert np.isfinite(sc[u, :, :tau]).all() and np.isposinf(sc[u, :, tau]).all()
+        assert np.isneginf(sc[u, :, tau + 1:]).all()
     del inp, cache
     torch.cuda.empty_cache()
+
+
+def test_decode_many_sequences(gpu_device):
+    """More sequences than the decode indexer's compacted schedule holds (16384):
+    it falls back to visiting every (sequence, block) pair. Sampled sequences are
+    checked against the oracle, every row's +inf / -inf pattern in full."""
+    rng = np.random.default_rng(8)
+    lens = rng.integers(1, 390, size=16500).tolist()
+    w = synth.small_workload(seq_lens=lens, q_lens=None, num_q_heads=4, num_kv_heads=1,
+                             head_dim=64, num_idx_heads=1, idx_head_dim=32, num_sel_groups=1,
+                             topk=2, plant_count=1, plant_span=None)
+    say("decode 16500 sequences")
+    inp, geom, cache = setup(w, gpu_device)
+    res = run_gpu(w, inp, geom, cache, gpu_device)
+    units = O.decode_units(w.seq_lens)
+    sampled_parity(w, inp, res, units, _sample_units(units, 24, 9), rows_per_unit=1)
+    sc = res["scores"].numpy()
+    tau = np.array([un["tau"] for un in units])
+    cols = np.arange(sc.shape[2])[None, :]
+    s0 = sc[:, 0, :]
+    assert np.isfinite(s0[cols < tau[:, None]]).all()
+    assert np.isposinf(s0[cols == tau[:, None]]).all()
+    assert np.isneginf(s0[cols > tau[:, None]]).all()
