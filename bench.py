@@ -215,6 +215,24 @@ def graph_ms_per_step(runner, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def cold_ms_per_step(runner, steps, flush_bytes=1 << 30):
+    """The step timed with cold caches: before every step a 1 GiB buffer is
+    written (four times the 256 MB Infinity Cache, far more than the L2s), so
+    the step's inputs come from HBM. Only the step is inside the events."""
+    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device=runner.dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        scratch.fill_(float(i))
+        a.record()
+        runner.step()
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    del scratch
+    return ms
+
+
 def measure(w, dev, steps, warmup):
     r = Runner(w, dev)
     ms, per, wall = r.timed(steps, warmup)
@@ -224,7 +242,8 @@ def measure(w, dev, steps, warmup):
     G = w.num_q_heads // w.num_kv_heads
     res = dict(workload=w.name, ms_per_step=ms, kernel_ms=per, wall_s=wall,
                selected_kv_tokens_per_step=tokens, value=tokens / (ms * 1e-3),
-               graph_ms_per_step=graph_ms_per_step(r, steps, warmup))
+               graph_ms_per_step=graph_ms_per_step(r, steps, warmup),
+               cold_ms_per_step=cold_ms_per_step(r, steps))
     if w.is_decode:
         nbytes = index_decode_bytes(w)
         t = per["index_scores"] * 1e-3
@@ -446,21 +465,22 @@ def main():
         "data": "synthetic (seeded N(0,1) with planted blocks), inputs resident in HBM",
         "config": config,
         "graph_ms_per_step": main_res["graph_ms_per_step"],
+        "cold_ms_per_step": main_res["cold_ms_per_step"],
         "kernel_ms": main_res["kernel_ms"],
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
     }
     if second is not None:
         line["second_workload"] = {k: second[k] for k in (
-            "workload", "value", "ms_per_step", "graph_ms_per_step", "kernel_ms", "roofline",
-            "step_hbm_frac") if k in second}
+            "workload", "value", "ms_per_step", "graph_ms_per_step", "cold_ms_per_step",
+            "kernel_ms", "roofline", "step_hbm_frac") if k in second}
     if extra:
         # the same workloads on FP8 caches (E4M3 codes, power-of-two scale per 32
         # channels), and decode with several new tokens per sequence, each selecting
         # its own blocks
         line["extra_workloads"] = [{k: r[k] for k in (
-            "workload", "value", "ms_per_step", "graph_ms_per_step", "kernel_ms", "roofline",
-            "step_hbm_frac") if k in r} for r in extra]
+            "workload", "value", "ms_per_step", "graph_ms_per_step", "cold_ms_per_step",
+            "kernel_ms", "roofline", "step_hbm_frac") if k in r} for r in extra]
     # the new-token step before the path (QK-norm + partial RoPE + cache insert),
     # timed on its own: not part of the step above
     line["qk_norm_rope_insert"] = inserts

@@ -64,6 +64,7 @@ DECODE_CASES = {
                                    head_dim=64, num_idx_heads=4, idx_head_dim=32,
                                    num_sel_groups=1, topk=7),
     "topk_covers_all": dict(seq_lens=(900, 300), topk=12),
+    "kept_blocks_over_64": dict(seq_lens=(12000, 700), topk=80),
 }
 
 
@@ -74,6 +75,22 @@ def test_fp8_decode_parity(name, gpu_device):
     inp, geom, cache = T.setup(w, gpu_device, permute=True)
     res = T.run_gpu(w, inp, geom, cache, gpu_device)
     decode_parity(w, inp, cache, res, name)
+
+
+@pytest.mark.parametrize("num_seqs", [5000, 16500])
+def test_fp8_decode_many_sequences(num_seqs, gpu_device):
+    """Many short sequences: the decode indexer's dynamic LDS holds the schedule's
+    prefix sums (up to 16384 sequences; beyond, every (sequence, block) pair is
+    visited) followed by the block's staged scale bytes."""
+    rng = np.random.default_rng(num_seqs)
+    lens = rng.integers(1, 390, size=num_seqs).tolist()
+    w = synth.small_workload(seq_lens=lens, q_lens=None, num_q_heads=4, num_kv_heads=1,
+                             head_dim=64, num_idx_heads=2, idx_head_dim=64, num_sel_groups=1,
+                             topk=2, plant_count=1, plant_span=None, cache_format="fp8")
+    say(f"fp8 decode {num_seqs} sequences")
+    inp, geom, cache = T.setup(w, gpu_device)
+    res = T.run_gpu(w, inp, geom, cache, gpu_device)
+    decode_parity(w, inp, cache, res, f"fp8 {num_seqs} sequences")
 
 
 def test_fp8_decode_split_counts_agree(gpu_device):
@@ -338,6 +355,7 @@ PREFILL_FULL = {
     "g16_d64_di32": dict(seq_lens=(1300,), q_lens=(700,), num_q_heads=16, num_kv_heads=1,
                          head_dim=64, num_idx_heads=2, idx_head_dim=32, num_sel_groups=1),
     "topk_covers_all": dict(seq_lens=(1000,), q_lens=(1000,), topk=16),
+    "kept_blocks_over_64": dict(seq_lens=(10245,), q_lens=(261,), topk=80),
 }
 
 

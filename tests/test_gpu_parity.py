@@ -85,6 +85,8 @@ SMALL_PREFILL = {
                        num_kv_heads=1, head_dim=64, num_idx_heads=2, idx_head_dim=32,
                        num_sel_groups=1),
     "f32_d128": dict(dtype="f32", seq_lens=(520,), q_lens=(400,)),
+    # more than 64 kept blocks per unit: the kernel's block ids come in chunks of 64
+    "kept_blocks_over_64": dict(seq_lens=(10245,), q_lens=(261,), topk=80),
 }
 
 
@@ -109,6 +111,7 @@ SMALL_DECODE = {
     "topk_covers_all": dict(seq_lens=(900, 300), topk=12),
     "f32": dict(dtype="f32", seq_lens=(3000, 700), num_q_heads=4, num_kv_heads=1,
                 head_dim=64, num_idx_heads=1, idx_head_dim=32, num_sel_groups=1, topk=4),
+    "kept_blocks_over_64": dict(seq_lens=(12000, 700), topk=80),
 }
 
 
