@@ -124,6 +124,16 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
     any = true;
     const int64_t phys = bt[b];
     const size_t off = (static_cast<size_t>(phys) * Hkv + j) * kBlk * D;
+    // bf16: the block's V^T operands are requested with its K rows, ahead of the
+    // softmax that decides nothing about them (one memory round trip per block;
+    // measured slower for FP8 caches, which load V after the softmax)
+    uint4 vraw[FP8 ? 1 : DT];
+    if constexpr (!FP8) {
+      const uint16_t *vr = vtc + off + n * kBlk + wave * 32 + q4 * 8;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        vraw[dt] = *reinterpret_cast<const uint4 *>(vr + dt * 16 * kBlk);
+    }
     // S^T: 2 tiles of 16 keys x 16 heads over this wave's 32 keys
     f32x4 s[2];
 #pragma unroll
@@ -209,12 +219,9 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
     } else {
       const bf16x8 pb = as_bf16x8(uint4{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]),
                                         cvt_pk_bf16(p[4], p[5]), cvt_pk_bf16(p[6], p[7])});
-      const uint16_t *vr = vtc + off + n * kBlk + wave * 32 + q4 * 8;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(vr + dt * 16 * kBlk));
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
-      }
+      for (int dt = 0; dt < DT; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vraw[dt]), pb, o[dt], 0, 0, 0);
     }
   }
 
