@@ -452,10 +452,11 @@ __global__ __launch_bounds__(256) void index_prefill_wide_kernel(
 // next block is in flight while this one is scored; one staged block serves every
 // query row of the group. Wave w owns 64 rows (two 32-row MFMA tiles) of tile
 // w/2: every key fragment read from LDS feeds two MFMAs. A = query rows in
-// registers, B = key rows from LDS. Per 32-key sub-tile the two MFMA chains run
-// one after the other, each accumulator max-pooled while the other chain runs,
-// and the next sub-tile's fragments are read meanwhile. Rows past a unit's end
-// repeat its last row, so they never change a maximum.
+// registers, B = key rows from LDS. Per 32-key sub-tile the two rows' MFMA
+// chains alternate (no MFMA waits on the result of the one just issued), then
+// both accumulators are max-pooled, and the next sub-tile's fragments are read
+// meanwhile. Rows past a unit's end repeat its last row, so they never change a
+// maximum.
 //
 // FP8 indexer keys: the staged rows are the group's E4M3 codes (GD bytes a key,
 // swizzled in 16-byte chunks by key / (16 / chunks per row) so a 16-lane read
@@ -616,18 +617,17 @@ void index_prefill_bf16_kernel(
       for (int nt = 0; nt < 4; ++nt) {
         const int cb = nt & 1;
         if (nt < 3) rd(nt + 1, kf[cb ^ 1]);
+        // the two rows' chains alternate, so no MFMA waits on the one just issued
         acc0 = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[cb][ks], acc0, 0, 0, 0);
-        if (nt > 0) pool(acc1);
         acc1 = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks) {
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[cb][ks], acc0, 0, 0, 0);
           acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], kf[cb][ks], acc1, 0, 0, 0);
+        }
         pool(acc0);
+        pool(acc1);
       }
-      pool(acc1);
     }
     m = group_max<kWave>(m);
     if (lane == 0) red[wave][bi] = m;
