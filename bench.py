@@ -381,9 +381,10 @@ def main():
     ap.add_argument("--second", default="decode_1m_b8",
                     help="second workload measured in the same run ('none' to skip)")
     ap.add_argument("--extra", default="decode_1m_b8_fp8,prefill_32k_fp8,decode_1m_b8_t4,"
-                                      "decode_ragged_b64",
+                                      "decode_ragged_b64,chunked_prefill,decode_128k_b64",
                     help="more workloads measured in the same run (FP8 caches, several "
-                         "tokens per sequence), comma-separated ('none' to skip)")
+                         "tokens per sequence, ragged batches, the chunked prefill and the "
+                         "128k batched decode), comma-separated ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -476,8 +477,9 @@ def main():
             "kernel_ms", "roofline", "step_hbm_frac") if k in second}
     if extra:
         # the same workloads on FP8 caches (E4M3 codes, power-of-two scale per 32
-        # channels), and decode with several new tokens per sequence, each selecting
-        # its own blocks
+        # channels), decode with several new tokens per sequence (each selecting its
+        # own blocks), a ragged decode batch, the chunked prefill over long cached
+        # prefixes and the 64-sequence 128k decode
         line["extra_workloads"] = [{k: r[k] for k in (
             "workload", "value", "ms_per_step", "graph_ms_per_step", "cold_ms_per_step",
             "kernel_ms", "roofline", "step_hbm_frac") if k in r} for r in extra]
