@@ -135,11 +135,123 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
   for (int i = K + t; i < topk; i += kTopkThreads) out[i] = -1;
 }
 
+// Rows of at most 512 * KPT entries: the same selection with the row's keys held
+// in registers (thread t owns the KPT consecutive entries from t * KPT, so the
+// ascending output order needs no reshuffle) and three barriers per radix pass:
+// the 256-bin suffix sums are wave-level scans joined through the four wave
+// totals, and two histogram buffers alternate so that clearing the next one
+// needs no barrier of its own.
+template <int KPT>
+__global__ __launch_bounds__(kTopkThreads) void topk_rows_reg_kernel(
+    const float *__restrict__ scores, int row_len, int topk, int32_t *__restrict__ ids) {
+  __shared__ int hist[2][256];
+  __shared__ int wtot[4];
+  __shared__ int tmp[kTopkThreads / kWave];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_remaining;
+
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const float *row = scores + static_cast<size_t>(blockIdx.x) * row_len;
+  int32_t *out = ids + static_cast<size_t>(blockIdx.x) * topk;
+  const int i0 = t * KPT;
+
+  uint32_t key[KPT];
+  int nvalid = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    key[j] = (i0 + j < row_len) ? order_key(row[i0 + j]) : 0u;   // 0: below every score
+    nvalid += key[j] > kNegInfKey;
+  }
+  if (t < 256) {
+    hist[0][t] = 0;
+    hist[1][t] = 0;
+  }
+  int total;
+  (void)block_exclusive_scan(nvalid, tmp, total);   // its barriers also order the clears
+  const int K = min(topk, total);
+
+  uint32_t prefix = 0, mask = 0;
+  int remaining = K;
+  if (K > 0) {
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass, cur = pass & 1;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if (key[j] > kNegInfKey && (key[j] & mask) == prefix)
+          atomicAdd(&hist[cur][(key[j] >> shift) & 255u], 1);
+      if (t < 256) hist[cur ^ 1][t] = 0;        // for the next pass; unused in this one
+      __syncthreads();
+      int h = 0, sfx = 0;
+      if (t < 256) {
+        h = hist[cur][t];
+        sfx = h;                                // inclusive suffix sum inside the wave
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int v = __shfl_down(sfx, o, kWave);
+          if (lane + o < kWave) sfx += v;
+        }
+        if (lane == 0) wtot[wave] = sfx;
+      }
+      __syncthreads();
+      if (t < 256) {
+        for (int w = wave + 1; w < 4; ++w) sfx += wtot[w];   // bins of the higher waves
+        const int above = sfx - h;
+        if (above < remaining && remaining <= sfx) {
+          s_prefix = prefix | (static_cast<uint32_t>(t) << shift);
+          s_remaining = remaining - above;
+        }
+      }
+      __syncthreads();
+      prefix = s_prefix;
+      remaining = s_remaining;
+      mask |= 255u << shift;
+    }
+  }
+  // prefix is the exact key of the K-th largest entry; `remaining` entries equal
+  // to it are taken, lowest index first.
+  const uint32_t thr = prefix;
+  int n_eq = 0;
+  if (K > 0)
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) n_eq += key[j] == thr;
+  const int eq_before = block_exclusive_scan(n_eq, tmp, total);
+  int n_sel = 0;
+  if (K > 0) {
+    int e = eq_before;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (key[j] > thr) ++n_sel;
+      else if (key[j] == thr) { n_sel += e < remaining; ++e; }
+    }
+  }
+  int pos = block_exclusive_scan(n_sel, tmp, total);
+  if (K > 0) {
+    int e = eq_before;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      bool take = false;
+      if (key[j] > thr) take = true;
+      else if (key[j] == thr) { take = e < remaining; ++e; }
+      if (take) out[pos++] = i0 + j;
+    }
+  }
+  for (int i = K + t; i < topk; i += kTopkThreads) out[i] = -1;
+}
+
 }  // namespace
 
 hipError_t launch_topk(const float *scores, int rows, int row_len, int topk, int32_t *ids,
                        hipStream_t st) {
   if (rows == 0) return hipSuccess;
+  const int per = (row_len + kTopkThreads - 1) / kTopkThreads;   // entries per thread
+#define MSA_TOPK(KPT)                                                                 \
+  if (per <= KPT) {                                                                   \
+    topk_rows_reg_kernel<KPT><<<rows, kTopkThreads, 0, st>>>(scores, row_len, topk, ids); \
+    return hipGetLastError();                                                         \
+  }
+  MSA_TOPK(1) MSA_TOPK(2) MSA_TOPK(4) MSA_TOPK(8) MSA_TOPK(16) MSA_TOPK(32)
+#undef MSA_TOPK
   topk_rows_kernel<<<rows, kTopkThreads, 0, st>>>(scores, row_len, topk, ids);
   return hipGetLastError();
 }

@@ -178,7 +178,9 @@ def test_topk_rows_exact(gpu_device):
     rows.append(np.array([3, 1, 3, 2, np.inf, -np.inf, -np.inf], np.float32))
     rows.append(np.array([-0.0, 0.0, -1e-30, 1e-30, np.inf], np.float32))
     rows.append(np.full(9, -np.inf, np.float32))                    # nothing to keep
-    for n in (1, 2, 31, 128, 1000, 8256, 20011):
+    # lengths on both sides of the register-resident kernel's sizes (512 * 1, 2, 4, 8, 16,
+    # 32 entries) and of its limit, past which rows take the streaming kernel
+    for n in (1, 2, 31, 128, 513, 1000, 2048, 4000, 8192, 8256, 16384, 16385, 20011):
         r = rng.integers(-4, 5, size=n).astype(np.float32)           # heavy ties
         r[rng.integers(0, n)] = np.inf
         r[rng.random(n) < 0.2] = -np.inf
