@@ -267,15 +267,32 @@ __global__ __launch_bounds__(D) void combine_kernel(const float *__restrict__ o_
   const size_t row = blockIdx.x;   // sequence * Hq + head
   const int d = threadIdx.x;
   const float *lp = lse_part + row * num_splits;
+  const float *op = o_part + row * num_splits * D + d;
   float M = neg_inf();
   for (int s = 0; s < num_splits; ++s) M = fmaxf(M, lp[s]);
+  // M is finite: the part holding the diagonal block sees the query's own key.
+  // An empty part has lse -inf and o 0, so it adds exp(-inf) * 0 = 0: no branch,
+  // and eight parts' loads are issued before they are used.
   float L = 0.f, acc = 0.f;
-  for (int s = 0; s < num_splits; ++s) {
-    const float ls = lp[s];
-    if (ls == neg_inf()) continue;
-    const float w = __expf(ls - M);
+  int s = 0;
+  for (; s + 8 <= num_splits; s += 8) {
+    float lv[8], ov[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      lv[u] = lp[s + u];
+      ov[u] = op[static_cast<size_t>(s + u) * D];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = __expf(lv[u] - M);
+      L += w;
+      acc += w * ov[u];
+    }
+  }
+  for (; s < num_splits; ++s) {
+    const float w = __expf(lp[s] - M);
     L += w;
-    acc += w * o_part[(row * num_splits + s) * D + d];
+    acc += w * op[static_cast<size_t>(s) * D];
   }
   const float v = acc / L;
   if constexpr (BF16)
@@ -287,9 +304,12 @@ __global__ __launch_bounds__(D) void combine_kernel(const float *__restrict__ o_
 
 }  // namespace
 
+// About 512 work-groups (two per CU): more parts cost more in the combine than
+// they win in latency (measured over 32-256 units: 1M decode 16 parts 28 us
+// against 64 parts 37 us, 128k batch of 64 2 parts 109 us against 8 parts 121 us).
 int decode_auto_splits(const Geom &g, int num_seqs, int topk) {
   const int units = num_seqs * g.Hkv;
-  int s = (2048 + units - 1) / units;
+  int s = (512 + units - 1) / units;
   s = s < 1 ? 1 : (s > topk ? topk : s);
   const int per = (topk + s - 1) / s;
   return (topk + per - 1) / per;

@@ -125,7 +125,7 @@ def test_null_and_size_errors(lib):
 def test_decode_workspace_checks(lib):
     g, c = _geom(), _cache(num_seqs=8)
     need = lib.msa_decode_workspace_size(ctypes.byref(g), 8, 64, 0)
-    auto = (2048 + 31) // 32            # splits for 8 x 4 units, capped at topk
+    auto = (512 + 31) // 32             # splits for 8 x 4 units (about 512 work-groups)
     parts = 8 * 64 * min(auto, 64)
     assert need == ((parts * 128 * 4 + 255) // 256) * 256 + ((parts * 4 + 255) // 256) * 256
     assert lib.msa_decode_workspace_size(ctypes.byref(g), 8, 64, 3) < need
