@@ -106,10 +106,10 @@ class Runner:
     """Holds a workload's resident inputs and outputs and launches one step,
     recording HIP events around each launch on the current stream."""
 
-    def __init__(self, w, dev):
+    def __init__(self, w, dev, permute=False):
         self.w, self.dev = w, dev
-        log(f"{w.name}: generating inputs on {dev}")
-        self.inp = synth.make_inputs(w, dev)
+        log(f"{w.name}: generating inputs on {dev}" + (" (permuted block table)" if permute else ""))
+        self.inp = synth.make_inputs(w, dev, permute=permute)
         self.geom = geometry(w)
         self.cache = msa.Cache(self.inp["k_cache"], self.inp["v_cache"],
                                self.inp["k_idx_cache"], self.inp["block_table"],
@@ -233,8 +233,8 @@ def cold_ms_per_step(runner, steps, flush_bytes=1 << 30):
     return ms
 
 
-def measure(w, dev, steps, warmup):
-    r = Runner(w, dev)
+def measure(w, dev, steps, warmup, permute=False):
+    r = Runner(w, dev, permute)
     ms, per, wall = r.timed(steps, warmup)
     units = plan_units(w)
     ids = r.ids.cpu().numpy()
@@ -386,6 +386,9 @@ def main():
                          "tokens per sequence, ragged batches, the chunked prefill and the "
                          "128k batched decode), comma-separated ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--permute", action="store_true",
+                    help="scatter every workload's blocks over the physical cache by a seeded "
+                         "permutation (the default block table is the identity)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -411,7 +414,7 @@ def main():
     msa.lib()
 
     w = synth.WORKLOADS[args.workload]
-    main_res = measure(w, dev, args.steps, args.warmup)
+    main_res = measure(w, dev, args.steps, args.warmup, args.permute)
     log(f"{w.name}: {main_res['ms_per_step']:.3f} ms/step, kernels {main_res['kernel_ms']}")
     cpu = None
     if not args.no_cpu_baseline:
@@ -425,7 +428,7 @@ def main():
     second = None
     if args.second != "none" and args.second != args.workload:
         w2 = synth.WORKLOADS[args.second]
-        second = measure(w2, dev, args.steps, args.warmup)
+        second = measure(w2, dev, args.steps, args.warmup, args.permute)
         log(f"{w2.name}: {second['ms_per_step']:.3f} ms/step, kernels {second['kernel_ms']}")
         inserts.append(measure_insert(second["_runner"]))
         log(f"{w2.name}: insert {inserts[-1]['us_per_launch']:.1f} us")
@@ -437,7 +440,7 @@ def main():
         if name in (args.workload, args.second):
             continue
         w3 = synth.WORKLOADS[name]
-        res = measure(w3, dev, args.steps, args.warmup)
+        res = measure(w3, dev, args.steps, args.warmup, args.permute)
         log(f"{w3.name}: {res['ms_per_step']:.3f} ms/step, kernels {res['kernel_ms']}")
         inserts.append(measure_insert(res["_runner"]))
         log(f"{w3.name}: insert {inserts[-1]['us_per_launch']:.1f} us")
@@ -463,7 +466,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded N(0,1) with planted blocks), inputs resident in HBM",
+        "data": "synthetic (seeded N(0,1) with planted blocks), inputs resident in HBM"
+                + (", block table permuted" if args.permute else ""),
         "config": config,
         "graph_ms_per_step": main_res["graph_ms_per_step"],
         "cold_ms_per_step": main_res["cold_ms_per_step"],
