@@ -381,10 +381,12 @@ def main():
     ap.add_argument("--second", default="decode_1m_b8",
                     help="second workload measured in the same run ('none' to skip)")
     ap.add_argument("--extra", default="decode_1m_b8_fp8,prefill_32k_fp8,decode_1m_b8_t4,"
-                                      "decode_ragged_b64,chunked_prefill,decode_128k_b64",
+                                      "decode_ragged_b64,chunked_prefill,decode_128k_b64,"
+                                      "prefill_32k_sel1,decode_1m_b8_sel1",
                     help="more workloads measured in the same run (FP8 caches, several "
-                         "tokens per sequence, ragged batches, the chunked prefill and the "
-                         "128k batched decode), comma-separated ('none' to skip)")
+                         "tokens per sequence, ragged batches, the chunked prefill, the "
+                         "128k batched decode, one selection group), comma-separated "
+                         "('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--permute", action="store_true",
                     help="scatter every workload's blocks over the physical cache by a seeded "
@@ -483,7 +485,8 @@ def main():
         # the same workloads on FP8 caches (E4M3 codes, power-of-two scale per 32
         # channels), decode with several new tokens per sequence (each selecting its
         # own blocks), a ragged decode batch, the chunked prefill over long cached
-        # prefixes and the 64-sequence 128k decode
+        # prefixes, the 64-sequence 128k decode, and one selection group summing all
+        # indexer heads
         line["extra_workloads"] = [{k: r[k] for k in (
             "workload", "value", "ms_per_step", "graph_ms_per_step", "cold_ms_per_step",
             "kernel_ms", "roofline", "step_hbm_frac") if k in r} for r in extra]

@@ -352,89 +352,123 @@ __global__ __launch_bounds__(256) void index_decode_fp8_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// prefill, bf16, group width above 128: MFMA 32x32x16, one work-group per
-// (unit, group, block chunk), keys read straight from L2
+// prefill, bf16, group width 256 or 512 (one selection group over all indexer
+// heads): MFMA 32x32x16 on LDS-staged keys, 128 channels at a time
 // ---------------------------------------------------------------------------
 //
-// Each of the 4 waves holds 32 query rows of the tile as the A operand
-// (lane l: row l%32, 8 consecutive group-dim elements at (l/32)*8 of each
-// 16-wide k step) and streams the indexer keys of the block as the B operand
-// (lane l: key l%32, the same 8 elements), 4 tiles of 32 keys per block.
-// The accumulator element (lane l, register i) is query row
-// (i/4)*8 + (l/32)*4 + i%4 and key l%32; rows past the unit's last query are
-// masked before the max.
+// A work-group of 4 waves scores one query tile (wave w: rows 32w .. 32w+31, the
+// A operand, the whole group width in registers) against a chunk of kChunkW
+// candidate blocks. A block's group keys (128 keys x GD channels) do not fit
+// twice in LDS, so they are staged 128 channels (32 KiB) at a time by direct
+// global->LDS loads, double-buffered across (block, channel chunk) stages, with
+// the same 16-byte swizzle as the narrow kernel; the four 32-key accumulators of
+// a block gather the contraction over its channel chunks and are max-pooled
+// after the last. Rows past the unit's end repeat its last row.
 
-constexpr int kChunk = 16;   // blocks per work-group
+constexpr int kChunkW = 16;   // blocks per work-group
 
+// (512 channels of query rows take 128 registers: that width runs one wave per SIMD)
 template <int DI, int HS>
-__global__ __launch_bounds__(256) void index_prefill_wide_kernel(
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(HS * DI > 256 ? 1 : 2, HS * DI > 256 ? 1 : 2)))
+void index_prefill_wide_kernel(
     const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const int32_t *__restrict__ block_table, const msa_unit_t *__restrict__ units,
     int max_blocks, int nsel, float *__restrict__ scores) {
-  constexpr int GD = HS * DI;          // group dim
-  constexpr int KS = GD / 16;          // k steps
-  __shared__ float red[4][kChunk];
+  constexpr int GD = HS * DI;          // group width
+  constexpr int KS = GD / 16;          // k steps of the whole group
+  constexpr int CW = 128;              // channels per staged chunk
+  constexpr int NCC = GD / CW;         // channel chunks per block
+  constexpr int KSC = CW / 16;         // k steps per chunk
+  constexpr int CHG = CW / 8;          // 16-byte chunks per staged key row
+  constexpr int CPH = DI / 8;          // 16-byte chunks per head row
+  constexpr int HPC = CW / DI;         // heads per channel chunk
+  constexpr int NLD = kBlk * CHG / 256;
+  static_assert(GD % CW == 0 && NCC % 2 == 0, "group width 256 or 512");
+  __shared__ u32x4 Kb[2][kBlk * CHG];
+  __shared__ float red[4][kChunkW];
+  auto swz = [](int key) { return key % CHG; };
 
   const int u = blockIdx.x, g = blockIdx.z;
   const msa_unit_t un = units[u];
   const int Hi = nsel * HS;
-  const int b0 = blockIdx.y * kChunk;
+  const int b0 = blockIdx.y * kChunkW;
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   float *out = scores + (static_cast<size_t>(u) * nsel + g) * max_blocks;
-  if (b0 >= un.tau) {
-    for (int i = t; i < kChunk && b0 + i < max_blocks; i += 256)
-      out[b0 + i] = (b0 + i == un.tau) ? pos_inf() : neg_inf();
-    return;
+  for (int i = t; i < kChunkW; i += 256) {
+    const int b = b0 + i;
+    if (b >= un.tau && b < max_blocks) out[b] = (b == un.tau) ? pos_inf() : neg_inf();
   }
-  const int nblk = min(kChunk, un.tau - b0);
+  if (b0 >= un.tau) return;
+  const int nblk = min(kChunkW, un.tau - b0);
 
-  // A operand: this wave's 32 query rows (clamped; masked rows are ignored)
-  const int qr = wave * 32 + (lane % 32);
-  const int qrow = un.row0 + min(qr, un.num_rows - 1);
-  bf16x8 a[KS];
+  // A operand: this wave's 32 query rows over the whole group width
+  const int qrow = un.row0 + min(wave * 32 + lane % 32, un.num_rows - 1);
+  bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int kk = ks * 16 + (lane / 32) * 8;
     const int h = g * HS + kk / DI, d = kk % DI;
-    a[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+    qf[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(
         q_idx + (static_cast<size_t>(qrow) * Hi + h) * DI + d));
   }
-  // rows of the accumulator held by this lane that are real queries
-  bool rv[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    rv[i] = (wave * 32 + (i / 4) * 8 + (lane / 32) * 4 + (i % 4)) < un.num_rows;
 
   const int32_t *bt = block_table + static_cast<size_t>(un.r) * max_blocks;
+  // stage st = block (st / NCC), channel chunk (st % NCC) into buffer st % 2
+  auto issue = [&](int st) __attribute__((always_inline)) {
+    const size_t phys = static_cast<size_t>(bt[b0 + st / NCC]);
+    const int cc = st % NCC;
+    u32x4 *dst = Kb[st % 2];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int base = (4 * i + wave) * 64;
+      const int p = base + lane, key = p / CHG, c = (p % CHG) ^ swz(key);
+      const int h = g * HS + cc * HPC + c / CPH;
+      __builtin_amdgcn_global_load_lds(
+          k_idx + ((phys * Hi + h) * kBlk + key) * DI + (c % CPH) * 8,
+          (__attribute__((address_space(3))) void *)(dst + base), 16, 0, 0);
+    }
+  };
+
+  const int nst = nblk * NCC;
+  issue(0);
   for (int bi = 0; bi < nblk; ++bi) {
-    const int64_t phys = bt[b0 + bi];
-    const uint16_t *kb = k_idx + static_cast<size_t>(phys) * Hi * kBlk * DI;
+    f32x16 acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x16{};
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+      const int st = bi * NCC + cc;
+      __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this stage's keys landed
+      __syncthreads();
+      if (st + 1 < nst) issue(st + 1);
+      const u32x4 *src = Kb[cc % 2];          // NCC is even: stage st sits in buffer st % 2
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int key = nt * 32 + lane % 32;
+        // the key fragments are read as they are used: the whole group width of
+        // query rows already takes half the registers
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) {
+          const bf16x8 kf =
+              __builtin_bit_cast(bf16x8, src[key * CHG + ((2 * ks + lane / 32) ^ swz(key))]);
+          acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[cc * KSC + ks], kf, acc[nt],
+                                                            0, 0, 0);
+        }
+      }
+    }
     float m = neg_inf();
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int key = nt * 32 + (lane % 32);
-      f32x16 acc = {};
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int kk = ks * 16 + (lane / 32) * 8;
-        const int h = g * HS + kk / DI, d = kk % DI;
-        const bf16x8 bv = as_bf16x8(*reinterpret_cast<const uint4 *>(
-            kb + (static_cast<size_t>(h) * kBlk + key) * DI + d));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], bv, acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m = rv[i] ? fmaxf(m, acc[i]) : m;
-    }
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[nt][i]);
     m = group_max<kWave>(m);
     if (lane == 0) red[wave][bi] = m;
   }
   __syncthreads();
   if (t < nblk)
     out[b0 + t] = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
-  else if (t < kChunk && b0 + t < max_blocks)   // the diagonal and the future blocks
-    out[b0 + t] = (b0 + t == un.tau) ? pos_inf() : neg_inf();
 }
-
 
 // ---------------------------------------------------------------------------
 // prefill, bf16, group width <= 128: MFMA 32x32x16 on LDS-staged keys
@@ -789,14 +823,17 @@ hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_
     return hipGetLastError();
   }
   if (FP8) return hipErrorInvalidValue;   // wide groups read bf16 keys only
-  const dim3 grid(b.total_units, (c.max_blocks_per_seq + kChunk - 1) / kChunk, g.nsel);
+  const dim3 grid(b.total_units, (c.max_blocks_per_seq + kChunkW - 1) / kChunkW, g.nsel);
   switch (hs) {
 #define MSA_CASE(HS)                                                                     \
   case HS:                                                                               \
-    index_prefill_wide_kernel<DI, HS><<<grid, 256, 0, st>>>(                             \
-        q, k, c.block_table, b.units, c.max_blocks_per_seq, g.nsel, scores);             \
+    if constexpr (HS * DI == 256 || HS * DI == 512)                                      \
+      index_prefill_wide_kernel<DI, HS><<<grid, 256, 0, st>>>(                           \
+          q, k, c.block_table, b.units, c.max_blocks_per_seq, g.nsel, scores);           \
+    else                                                                                 \
+      return hipErrorInvalidValue;                                                       \
     break;
-    MSA_CASE(2) MSA_CASE(4) MSA_CASE(8)
+    MSA_CASE(4) MSA_CASE(8)
 #undef MSA_CASE
     default: return hipErrorInvalidValue;
   }

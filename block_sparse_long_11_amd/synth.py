@@ -134,6 +134,14 @@ WORKLOADS = {
     "decode_1m_b8_t4": Workload(
         "decode_1m_b8_t4", "bf16", [1048576] * 8, None, topk=64, plant_count=63,
         plant_span=None, seed=1004, tokens_per_seq=4),
+    # one selection group: the 8 indexer heads summed into one score that selects the
+    # blocks of every KV head (the same bytes as the 4-group layout)
+    "prefill_32k_sel1": Workload(
+        "prefill_32k_sel1", "bf16", [32768], [32768], num_sel_groups=1, topk=16,
+        plant_count=8, plant_span=32, seed=1002),
+    "decode_1m_b8_sel1": Workload(
+        "decode_1m_b8_sel1", "bf16", [1048576] * 8, None, num_sel_groups=1, topk=64,
+        plant_count=63, plant_span=None, seed=1004),
 }
 
 

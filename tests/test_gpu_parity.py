@@ -87,6 +87,10 @@ SMALL_PREFILL = {
     "f32_d128": dict(dtype="f32", seq_lens=(520,), q_lens=(400,)),
     # more than 64 kept blocks per unit: the kernel's block ids come in chunks of 64
     "kept_blocks_over_64": dict(seq_lens=(10245,), q_lens=(261,), topk=80),
+    # one selection group 256 channels wide over 32-channel indexer heads (the 512-wide
+    # groups are m3_heads_one_group: 8 heads of 64 channels)
+    "one_group_di32_w256": dict(seq_lens=(1500, 200), q_lens=(700, 200), num_idx_heads=8,
+                                idx_head_dim=32, num_sel_groups=1, topk=5),
 }
 
 
