@@ -368,26 +368,34 @@ __global__ __launch_bounds__(256) void index_decode_fp8_kernel(
 constexpr int kChunkW = 16;   // blocks per work-group
 
 // (512 channels of query rows take 128 registers: that width runs one wave per SIMD)
-template <int DI, int HS>
+template <int DI, int HS, bool FP8>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(HS * DI > 256 ? 1 : 2, HS * DI > 256 ? 1 : 2)))
 void index_prefill_wide_kernel(
-    const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
-    const int32_t *__restrict__ block_table, const msa_unit_t *__restrict__ units,
-    int max_blocks, int nsel, float *__restrict__ scores) {
+    const uint16_t *__restrict__ q_idx, const void *__restrict__ k_idx_,
+    const uint8_t *__restrict__ k_scale, const int32_t *__restrict__ block_table,
+    const msa_unit_t *__restrict__ units, int max_blocks, int nsel,
+    float *__restrict__ scores) {
   constexpr int GD = HS * DI;          // group width
   constexpr int KS = GD / 16;          // k steps of the whole group
   constexpr int CW = 128;              // channels per staged chunk
   constexpr int NCC = GD / CW;         // channel chunks per block
   constexpr int KSC = CW / 16;         // k steps per chunk
-  constexpr int CHG = CW / 8;          // 16-byte chunks per staged key row
-  constexpr int CPH = DI / 8;          // 16-byte chunks per head row
+  constexpr int CHG = FP8 ? CW / 16 : CW / 8;   // 16-byte chunks per staged key row
+  constexpr int CPH = FP8 ? DI / 16 : DI / 8;   // 16-byte chunks per head row
   constexpr int HPC = CW / DI;         // heads per channel chunk
+  constexpr int NS = DI / 32;          // FP8 scale bytes per key and head
+  constexpr int SCH = FP8 ? HPC * kBlk * NS / 16 : 1;   // 16-byte chunks of a stage's scales
   constexpr int NLD = kBlk * CHG / 256;
   static_assert(GD % CW == 0 && NCC % 2 == 0, "group width 256 or 512");
+  static_assert(!FP8 || SCH <= kWave, "one wave stages the scales");
   __shared__ u32x4 Kb[2][kBlk * CHG];
+  __shared__ u32x4 Ks[2][SCH];
   __shared__ float red[4][kChunkW];
-  auto swz = [](int key) { return key % CHG; };
+  const uint16_t *k_idx = static_cast<const uint16_t *>(k_idx_);
+  const uint8_t *k_idx8 = static_cast<const uint8_t *>(k_idx_);
+  // FP8 row swizzle: keys sharing a 256-byte bank row get distinct chunk slots
+  auto swz = [](int key) { return FP8 ? (key / (16 / CHG)) % CHG : key % CHG; };
 
   const int u = blockIdx.x, g = blockIdx.z;
   const msa_unit_t un = units[u];
@@ -402,12 +410,14 @@ void index_prefill_wide_kernel(
   if (b0 >= un.tau) return;
   const int nblk = min(kChunkW, un.tau - b0);
 
-  // A operand: this wave's 32 query rows over the whole group width
+  // A operand: this wave's 32 query rows over the whole group width (FP8 keys: the
+  // channel order that keeps a lane's two k steps of a 16-byte read in one scale block)
   const int qrow = un.row0 + min(wave * 32 + lane % 32, un.num_rows - 1);
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const int kk = ks * 16 + (lane / 32) * 8;
+    const int kk = FP8 ? (ks / 2) * 32 + (lane / 32) * 16 + (ks % 2) * 8
+                       : ks * 16 + (lane / 32) * 8;
     const int h = g * HS + kk / DI, d = kk % DI;
     qf[ks] = as_bf16x8(*reinterpret_cast<const uint4 *>(
         q_idx + (static_cast<size_t>(qrow) * Hi + h) * DI + d));
@@ -424,9 +434,20 @@ void index_prefill_wide_kernel(
       const int base = (4 * i + wave) * 64;
       const int p = base + lane, key = p / CHG, c = (p % CHG) ^ swz(key);
       const int h = g * HS + cc * HPC + c / CPH;
+      const void *src;
+      if constexpr (FP8)
+        src = k_idx8 + ((phys * Hi + h) * kBlk + key) * DI + (c % CPH) * 16;
+      else
+        src = k_idx + ((phys * Hi + h) * kBlk + key) * DI + (c % CPH) * 8;
       __builtin_amdgcn_global_load_lds(
-          k_idx + ((phys * Hi + h) * kBlk + key) * DI + (c % CPH) * 8,
-          (__attribute__((address_space(3))) void *)(dst + base), 16, 0, 0);
+          src, (__attribute__((address_space(3))) void *)(dst + base), 16, 0, 0);
+    }
+    if constexpr (FP8) {
+      // the chunk's heads' scale bytes ([HPC][128][NS]) are contiguous
+      if (wave == 0 && lane < SCH)
+        __builtin_amdgcn_global_load_lds(
+            k_scale + (phys * Hi + g * HS + cc * HPC) * kBlk * NS + lane * 16,
+            (__attribute__((address_space(3))) void *)Ks[st % 2], 16, 0, 0);
     }
   };
 
@@ -443,17 +464,42 @@ void index_prefill_wide_kernel(
       __syncthreads();
       if (st + 1 < nst) issue(st + 1);
       const u32x4 *src = Kb[cc % 2];          // NCC is even: stage st sits in buffer st % 2
+      const uint8_t *sb = reinterpret_cast<const uint8_t *>(Ks[cc % 2]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int key = nt * 32 + lane % 32;
         // the key fragments are read as they are used: the whole group width of
         // query rows already takes half the registers
+        if constexpr (FP8) {
 #pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) {
-          const bf16x8 kf =
-              __builtin_bit_cast(bf16x8, src[key * CHG + ((2 * ks + lane / 32) ^ swz(key))]);
-          acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[cc * KSC + ks], kf, acc[nt],
-                                                            0, 0, 0);
+          for (int k2 = 0; k2 < KSC / 2; ++k2) {
+            const u32x4 w = src[key * CHG + ((2 * k2 + lane / 32) ^ swz(key))];
+            const int hh = (k2 * 32) / DI, sub = (k2 * 32 % DI) / 32;
+            const float sc =
+                ldexpf(1.0f, static_cast<int>(sb[(hh * kBlk + key) * NS + sub]) - 127);
+            uint32_t o[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              o[2 * i] = __builtin_bit_cast(
+                  uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, false));
+              o[2 * i + 1] = __builtin_bit_cast(
+                  uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, true));
+            }
+            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                qf[cc * KSC + 2 * k2], as_bf16x8(uint4{o[0], o[1], o[2], o[3]}), acc[nt], 0,
+                0, 0);
+            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                qf[cc * KSC + 2 * k2 + 1], as_bf16x8(uint4{o[4], o[5], o[6], o[7]}), acc[nt],
+                0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KSC; ++ks) {
+            const bf16x8 kf =
+                __builtin_bit_cast(bf16x8, src[key * CHG + ((2 * ks + lane / 32) ^ swz(key))]);
+            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[cc * KSC + ks], kf, acc[nt],
+                                                              0, 0, 0);
+          }
         }
       }
     }
@@ -804,7 +850,6 @@ template <int DI, bool FP8>
 hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                  const void *q_idx, float *scores, hipStream_t st) {
   const uint16_t *q = static_cast<const uint16_t *>(q_idx);
-  const uint16_t *k = static_cast<const uint16_t *>(c.k_idx_cache);
   const int hs = g.Hs();
   if (hs * DI <= 128) {
     const dim3 grid(b.total_units, (c.max_blocks_per_seq + kChunk2 - 1) / kChunk2, g.nsel);
@@ -822,14 +867,14 @@ hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_
     }
     return hipGetLastError();
   }
-  if (FP8) return hipErrorInvalidValue;   // wide groups read bf16 keys only
   const dim3 grid(b.total_units, (c.max_blocks_per_seq + kChunkW - 1) / kChunkW, g.nsel);
   switch (hs) {
 #define MSA_CASE(HS)                                                                     \
   case HS:                                                                               \
     if constexpr (HS * DI == 256 || HS * DI == 512)                                      \
-      index_prefill_wide_kernel<DI, HS><<<grid, 256, 0, st>>>(                           \
-          q, k, c.block_table, b.units, c.max_blocks_per_seq, g.nsel, scores);           \
+      index_prefill_wide_kernel<DI, HS, FP8><<<grid, 256, 0, st>>>(                      \
+          q, c.k_idx_cache, c.k_idx_scale, c.block_table, b.units, c.max_blocks_per_seq, \
+          g.nsel, scores);                                                               \
     else                                                                                 \
       return hipErrorInvalidValue;                                                       \
     break;

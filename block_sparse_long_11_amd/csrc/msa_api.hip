@@ -225,8 +225,6 @@ msa_status_t msa_index_scores(const msa_geom_t *geom, const msa_cache_t *cache,
   if ((st = check_cache(cache, false, true, g.fp8)) != MSA_OK) return st;
   if (batch != nullptr) {
     if ((st = check_batch(batch)) != MSA_OK) return st;
-    MSA_REQUIRE(!g.fp8 || g.Hs() * g.Di <= 128, MSA_ERR_UNSUPPORTED,
-                "the prefill indexer reads FP8 caches for groups of at most 128 channels");
     if (batch->total_units == 0) return ok();   // nothing to score
   }
   if (batch == nullptr) return index_decode(geom, cache, 1, q_idx, scores, stream);

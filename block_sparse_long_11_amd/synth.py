@@ -139,6 +139,9 @@ WORKLOADS = {
     "prefill_32k_sel1": Workload(
         "prefill_32k_sel1", "bf16", [32768], [32768], num_sel_groups=1, topk=16,
         plant_count=8, plant_span=32, seed=1002),
+    "prefill_32k_fp8_sel1": Workload(
+        "prefill_32k_fp8_sel1", "bf16", [32768], [32768], num_sel_groups=1, topk=16,
+        plant_count=8, plant_span=32, seed=1002, cache_format="fp8"),
     "decode_1m_b8_sel1": Workload(
         "decode_1m_b8_sel1", "bf16", [1048576] * 8, None, num_sel_groups=1, topk=64,
         plant_count=63, plant_span=None, seed=1004),

@@ -95,9 +95,8 @@ typedef enum {
  *   block_size must be 128.
  *   dtype applies to q, q_idx, out and (cache_format PLAIN) the three caches.
  *   cache_format MSA_CACHE_FP8_E4M3 needs dtype MSA_BF16; it is read by
- *     msa_index_scores (prefill: selection groups of at most 128 channels,
- *     H_s * D_i <= 128, else MSA_ERR_UNSUPPORTED), msa_sparse_attn_prefill and
- *     msa_sparse_attn_decode, and written by msa_qk_norm_rope_insert. */
+ *     msa_index_scores, msa_sparse_attn_prefill and msa_sparse_attn_decode, and
+ *     written by msa_qk_norm_rope_insert. */
 typedef struct {
   int32_t num_q_heads;
   int32_t num_kv_heads;

@@ -227,10 +227,6 @@ def test_fp8_cache_checks(lib):
     g = _geom(cache_format=msa.MSA_CACHE_FP8_E4M3)
     c = _cache()
     b = msa._Batch(FAKE, 3, 300)
-    # the prefill indexer reads FP8 caches for groups up to 128 channels only
-    g_wide = _geom(cache_format=msa.MSA_CACHE_FP8_E4M3, num_sel_groups=1)   # 8 x 64 channels
-    assert lib.msa_index_scores(ctypes.byref(g_wide), ctypes.byref(c), ctypes.byref(b), FAKE,
-                                FAKE, None) == UNSUPPORTED
     c = _cache(k_scale=None)
     assert lib.msa_sparse_attn_prefill(ctypes.byref(g), ctypes.byref(c), ctypes.byref(b), FAKE,
                                        FAKE, 4, 0.0, FAKE, None, None) == INVALID

@@ -356,6 +356,10 @@ PREFILL_FULL = {
                          head_dim=64, num_idx_heads=2, idx_head_dim=32, num_sel_groups=1),
     "topk_covers_all": dict(seq_lens=(1000,), q_lens=(1000,), topk=16),
     "kept_blocks_over_64": dict(seq_lens=(10245,), q_lens=(261,), topk=80),
+    "m3_heads_one_group": dict(seq_lens=(1500, 300), q_lens=(400, 300), num_q_heads=64,
+                               num_kv_heads=4, num_idx_heads=8, num_sel_groups=1, topk=6),
+    "one_group_di32_w256": dict(seq_lens=(1500, 200), q_lens=(700, 200), num_idx_heads=8,
+                                idx_head_dim=32, num_sel_groups=1, topk=5),
 }
 
 
