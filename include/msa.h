@@ -91,7 +91,8 @@ typedef enum {
  *   num_sel_groups is num_kv_heads (group g sums indexer heads
  *     [g*H_s, (g+1)*H_s), H_s = num_idx_heads / num_sel_groups, and selects the
  *     blocks of KV head g) or 1 (the sum over all indexer heads selects for every
- *     KV head); num_idx_heads % num_sel_groups == 0, H_s * idx_head_dim <= 512
+ *     KV head); num_idx_heads % num_sel_groups == 0, H_s in {1, 2, 4, 8},
+ *     H_s * idx_head_dim <= 512
  *   block_size must be 128.
  *   dtype applies to q, q_idx, out and (cache_format PLAIN) the three caches.
  *   cache_format MSA_CACHE_FP8_E4M3 needs dtype MSA_BF16; it is read by
