@@ -216,14 +216,19 @@ def graph_ms_per_step(runner, steps, warmup):
 
 
 def cold_ms_per_step(runner, steps, flush_bytes=1 << 30):
-    """The step timed with cold caches: before every step a 1 GiB buffer is
-    written (four times the 256 MB Infinity Cache, far more than the L2s), so
-    the step's inputs come from HBM. Only the step is inside the events."""
+    """The step timed with cold caches: before every step a 1 GiB buffer (four
+    times the 256 MB Infinity Cache, far more than the L2s) is written and then
+    read, so the step's inputs come from HBM and the caches hold clean lines (the
+    read writes the flush's dirty lines back before the step starts; after a
+    write alone the step would also pay for that write-back). Only the step is
+    inside the events."""
     scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device=runner.dev)
+    sink = torch.empty(1, dtype=torch.float32, device=runner.dev)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     for i, (a, b) in enumerate(evs):
         scratch.fill_(float(i))
+        torch.amax(scratch, dim=0, keepdim=True, out=sink)
         a.record()
         runner.step()
         b.record()
