@@ -279,7 +279,8 @@ def test_fp8_full_size_decode_1m_sampled(gpu_device):
             ok, _ = P.ids_acceptable(ids[u, g], ref[0], tau, w.topk)
             assert ok, f"u{u} g{g}: ids {ids[u, g]}"
         for j in range(w.num_kv_heads):
-            kept = [int(b) for b in ids[u, j] if b >= 0]
+            g = j if w.num_sel_groups == w.num_kv_heads else 0
+            kept = [int(b) for b in ids[u, g] if b >= 0]
             kc, btm = _mini_fp8(inp["k_cache"], inp["k_scale"], bt_all[r], kept, slice(j, j + 1))
             vc, _ = _mini_fp8(inp["v_cache"], inp["v_scale"], bt_all[r], kept, slice(j, j + 1),
                               d_major=True)
@@ -393,10 +394,12 @@ def test_fp8_insert_then_prefill_step(gpu_device):
     prefill_parity(w, inp, cache, res, "prefill after insert")
 
 
-def test_fp8_full_size_prefill_32k_sampled(gpu_device):
-    """The 32k prefill on FP8 caches (the benchmark's launch): sampled units, every
-    group's scores and ids, attention of sampled rows for every KV head."""
-    w = synth.WORKLOADS["prefill_32k_fp8"]
+@pytest.mark.parametrize("name", ["prefill_32k_fp8", "prefill_32k_fp8_sel1"])
+def test_fp8_full_size_prefill_32k_sampled(name, gpu_device):
+    """The 32k prefill on FP8 caches (the benchmark's launches, four selection groups
+    or one): sampled units, every group's scores and ids, attention of sampled rows
+    for every KV head."""
+    w = synth.WORKLOADS[name]
     say(f"{w.name} generate")
     inp, geom, cache = T.setup(w, gpu_device)
     say(f"{w.name} run")
@@ -424,13 +427,14 @@ def test_fp8_full_size_prefill_32k_sampled(gpu_device):
         n = un["row1"] - un["row0"]
         pick = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 8)]))
         for j in range(w.num_kv_heads):
-            kept = [int(b) for b in ids[u, j] if b >= 0]
+            g = j if w.num_sel_groups == w.num_kv_heads else 0
+            kept = [int(b) for b in ids[u, g] if b >= 0]
             kc, btm = _mini_fp8(inp["k_cache"], inp["k_scale"], bt_all[r], kept, slice(j, j + 1))
             vc, _ = _mini_fp8(inp["v_cache"], inp["v_scale"], bt_all[r], kept, slice(j, j + 1),
                               d_major=True)
             qh = host(inp["q"][rows, j * G:(j + 1) * G])
             for t in pick:
-                o, l = O.unit_attention(qh[t:t + 1], un["pos0"] + t, ids[u, j][None], kc, vc,
+                o, l = O.unit_attention(qh[t:t + 1], un["pos0"] + t, ids[u, g][None], kc, vc,
                                         btm, int(w.seq_lens[r]), 1)
                 P.check_attention(host(res["out"][un["row0"] + t, j * G:(j + 1) * G])[None],
                                   res["lse"][un["row0"] + t, j * G:(j + 1) * G].numpy()[None],

@@ -278,7 +278,7 @@ def _sample_units(units, n, seed):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("name", ["prefill_32k", "chunked_prefill"])
+@pytest.mark.parametrize("name", ["prefill_32k", "chunked_prefill", "prefill_32k_sel1"])
 def test_full_size_prefill_sampled(name, gpu_device):
     w = synth.WORKLOADS[name]
     say(f"{name} generate")
@@ -296,7 +296,8 @@ def test_full_size_prefill_sampled(name, gpu_device):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["decode_128k_b64", "decode_1m_b8", "decode_ragged_b64"])
+@pytest.mark.parametrize("name", ["decode_128k_b64", "decode_1m_b8", "decode_ragged_b64",
+                                  "decode_1m_b8_sel1"])
 def test_full_size_decode_sampled(name, gpu_device):
     w = synth.WORKLOADS[name]
     say(f"{name} generate")
