@@ -387,7 +387,7 @@ def main():
                     help="second workload measured in the same run ('none' to skip)")
     ap.add_argument("--extra", default="decode_1m_b8_fp8,prefill_32k_fp8,decode_1m_b8_t4,"
                                       "decode_ragged_b64,chunked_prefill,decode_128k_b64,"
-                                      "prefill_32k_sel1,decode_1m_b8_sel1",
+                                      "prefill_32k_sel1,prefill_32k_fp8_sel1,decode_1m_b8_sel1",
                     help="more workloads measured in the same run (FP8 caches, several "
                          "tokens per sequence, ragged batches, the chunked prefill, the "
                          "128k batched decode, one selection group), comma-separated "

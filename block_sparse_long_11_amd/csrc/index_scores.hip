@@ -367,12 +367,14 @@ __global__ __launch_bounds__(256) void index_decode_fp8_kernel(
 
 constexpr int kChunkW = 16;   // blocks per work-group
 
-// Two waves per SIMD at every width. At 512 channels the query rows take 128
-// registers and the compiler keeps a few values in scratch (outside the MFMA chains,
-// a handful of accesses per 32 MFMAs); that measured faster than one wave per SIMD
-// (32k prefill, one group: FP8 keys 612 -> 515 us, bf16 682 -> 675 us).
+// Waves per SIMD: at 512 channels the query rows take 128 registers. FP8 keys run
+// two waves per SIMD all the same (the compiler keeps a few values in scratch,
+// outside the MFMA chains); bf16 keys run one, as two spill more. Measured inside
+// the whole step of the 32k prefill with one group, same GPU: FP8 654 -> 566 us
+// with two waves, bf16 794 -> 831 us.
 template <int DI, int HS, bool FP8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(FP8 || HS * DI <= 256 ? 2 : 1, FP8 || HS * DI <= 256 ? 2 : 1)))
 void index_prefill_wide_kernel(
     const uint16_t *__restrict__ q_idx, const void *__restrict__ k_idx_,
     const uint8_t *__restrict__ k_scale, const int32_t *__restrict__ block_table,
