@@ -258,3 +258,16 @@ def test_per_token_checks(lib):
     assert lib.msa_sparse_attn_decode_per_token(ctypes.byref(g), ctypes.byref(c), 4, FAKE, FAKE,
                                                 16, 0.0, 0, FAKE, need - 1, FAKE, None,
                                                 None) == WS_SMALL
+
+
+def test_missing_library_raises(tmp_path, monkeypatch):
+    """Without the built library the binding refuses to run: there is no CPU path
+    to fall back to."""
+    monkeypatch.setattr(msa, "_LIB_PATH", tmp_path / "libmsa.so")
+    monkeypatch.setattr(msa, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        msa.lib()
+    scores = torch.zeros((1, 1, 4), dtype=torch.float32)
+    ids = torch.zeros((1, 1, 2), dtype=torch.int32)
+    with pytest.raises(RuntimeError, match="missing"):
+        msa.msa_select_topk_blocks(scores, 2, ids)
