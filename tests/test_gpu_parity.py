@@ -87,6 +87,7 @@ SMALL_PREFILL = {
     "f32_d128": dict(dtype="f32", seq_lens=(520,), q_lens=(400,)),
     # more than 64 kept blocks per unit: the kernel's block ids come in chunks of 64
     "kept_blocks_over_64": dict(seq_lens=(10245,), q_lens=(261,), topk=80),
+    "topk_150_of_157": dict(seq_lens=(20000,), q_lens=(160,), topk=150),
     # one selection group 256 channels wide over 32-channel indexer heads (the 512-wide
     # groups are m3_heads_one_group: 8 heads of 64 channels)
     "one_group_di32_w256": dict(seq_lens=(1500, 200), q_lens=(700, 200), num_idx_heads=8,
@@ -116,6 +117,7 @@ SMALL_DECODE = {
     "f32": dict(dtype="f32", seq_lens=(3000, 700), num_q_heads=4, num_kv_heads=1,
                 head_dim=64, num_idx_heads=1, idx_head_dim=32, num_sel_groups=1, topk=4),
     "kept_blocks_over_64": dict(seq_lens=(12000, 700), topk=80),
+    "topk_1000": dict(seq_lens=(150000, 9000, 128), topk=1000),
 }
 
 
