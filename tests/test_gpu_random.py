@@ -90,3 +90,41 @@ def test_random_per_token(seed, gpu_device):
     inp, geom, cache = T.setup(w, gpu_device, permute=permute)
     res = K.run_tokens(w, inp, geom, cache)
     K.tokens_parity(w, inp, cache, res, where)
+
+
+def draw_rope(seed, w):
+    rng = np.random.default_rng(5000 + seed)
+    dims = [0] + [r for r in (8, 16, 32, 64, 128)
+                  if r <= w.head_dim and (r >= 16 or w.dtype == "f32")]
+    return dict(rotary_dim=int(rng.choice(dims)), eps=float(rng.choice([1e-6, 1e-5])),
+                theta=float(rng.choice([1e4, 5e5, 1e6])))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_insert_prefill(seed, gpu_device):
+    """The new-token step (QK-norm, partial RoPE, K / V / indexer-key insert) on random
+    geometries, chunks and rotary settings, on bf16, fp32 and FP8 caches."""
+    import torch
+    import block_sparse_long_11_amd as msa
+    from oracle import msa_oracle as O
+    import test_gpu_insert as I
+
+    w, fmt, permute = draw_case(200 + seed, False)
+    rope = draw_rope(seed, w)
+    where = f"insert seed {seed}: {describe(w, fmt, permute)} rope={rope}"
+    T.say(where)
+    inp, geom, cache = T.setup(w, gpu_device, permute=permute)
+    new = synth.make_new_tokens(w, gpu_device)
+    fp8 = fmt == "fp8"
+    before = F.fp8_host(cache) if fp8 else I.cache_host(cache)
+    bt = inp["block_table"].cpu().numpy()
+    units = O.prefill_units(w.seq_lens, w.q_lens)
+    batch = msa.make_batch(w.seq_lens, w.q_lens, gpu_device)
+    q_out = torch.full_like(new["q"], float("nan"))
+    I.run_insert(geom, cache, batch, new, rope, q_out)
+    if fp8:
+        F.compare_fp8_insert(w, units, bt, before, F.fp8_host(cache), T.host(q_out), new, rope,
+                             where)
+    else:
+        ref = I.oracle_insert(units, new, before, bt, rope)
+        I.compare_insert(w, units, bt, before, I.cache_host(cache), T.host(q_out), ref, where)
