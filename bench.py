@@ -401,7 +401,7 @@ def main():
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(sequences and KV heads shard with no exchange; see the design notes).",
               file=sys.stderr)
         sys.exit(2)
