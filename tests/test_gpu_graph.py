@@ -66,6 +66,13 @@ CASES = {
     "decode_per_token": dict(seq_lens=(3000, 700, 131), q_lens=None, tokens_per_seq=4, topk=5),
     "decode_fp8": dict(seq_lens=(3000, 700, 129), q_lens=None, topk=5, cache_format="fp8"),
     "prefill": dict(seq_lens=(1500, 700), q_lens=(600, 700), topk=4),
+    "prefill_fp8": dict(seq_lens=(1500, 700), q_lens=(600, 700), topk=4, cache_format="fp8"),
+    # one selection group over 8 heads of 64 channels: the wide prefill indexer
+    "prefill_one_group_fp8": dict(seq_lens=(1500, 300), q_lens=(400, 300), num_q_heads=16,
+                                  num_kv_heads=4, num_idx_heads=8, num_sel_groups=1, topk=5,
+                                  cache_format="fp8"),
+    "prefill_one_group": dict(seq_lens=(1500, 300), q_lens=(400, 300), num_q_heads=16,
+                              num_kv_heads=4, num_idx_heads=8, num_sel_groups=1, topk=5),
 }
 
 
