@@ -215,6 +215,10 @@ def unit_attention(q_rows, pos0, ids_unit, k_cache, v_cache, bt_row, seq_len, n_
     out = sum_s softmax(z)_s v_s and lse = log sum_s exp(z_s), natural log.
     The softmax is plain, with no sink logit and no output gate ([feat] row
     "Learnable attention sink").
+    The kept list is read as a set of block ids: the entries before its first -1
+    (the padding; anything after it is ignored), in any order; a block after the
+    query (or past seq_len) adds no key. A query with no visible key at all (a list the selection never makes:
+    no block up to its own position) has an empty softmax: out 0, lse -inf.
     Returns out [T][H_q][D] and lse [T][H_q], float64.
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
@@ -228,28 +232,36 @@ def unit_attention(q_rows, pos0, ids_unit, k_cache, v_cache, bt_row, seq_len, n_
     positions = pos0 + np.arange(T)
     for j in range(H_kv):
         g = j if n_sel == H_kv else 0
-        blocks = [int(b) for b in ids_unit[g] if b >= 0]
+        listed = []
+        for b in ids_unit[g]:
+            if b < 0:
+                break
+            listed.append(int(b))
+        # blocks holding at least one key of the request
+        blocks = [b for b in listed if b * BLOCK < seq_len]
         keys = np.concatenate([np.arange(b * BLOCK, min((b + 1) * BLOCK, seq_len))
-                               for b in blocks])
+                               for b in blocks] + [np.zeros(0, dtype=np.int64)])
         # K/V rows line up with `keys`: both walk the kept blocks in the same
         # order, each block cut at seq_len.
-        K, V = _trim_blocks(k_cache, v_cache, bt_row, blocks, seq_len, j)
+        K, V = _trim_blocks(k_cache, v_cache, bt_row, blocks, seq_len, j, D)
         visible = keys[None, :] <= positions[:, None]          # [T][nkeys]
+        seen = visible.any(axis=1)                              # [T]
         for i in range(j * G, (j + 1) * G):
             z = scale * (q_rows[:, i, :] @ K.T)                 # [T][nkeys]
             z = np.where(visible, z, -np.inf)
-            m = z.max(axis=1, keepdims=True)
-            e = np.exp(z - m)
+            m = np.where(seen, z.max(axis=1, initial=-np.inf), 0.0)[:, None]
+            e = np.where(visible, np.exp(z - m), 0.0)
             ssum = e.sum(axis=1, keepdims=True)
-            out[:, i, :] = (e / ssum) @ V
-            lse[:, i] = (m + np.log(ssum))[:, 0]
+            out[:, i, :] = np.where(seen[:, None], e / np.where(ssum > 0, ssum, 1.0), 0.0) @ V
+            lse[:, i] = np.where(seen, (m + np.log(np.where(ssum > 0, ssum, 1.0)))[:, 0],
+                                 -np.inf)
     return out, lse
 
 
-def _trim_blocks(k_cache, v_cache, bt_row, blocks, seq_len, j):
+def _trim_blocks(k_cache, v_cache, bt_row, blocks, seq_len, j, D):
     """K and V rows (float64 [nkeys][D]) of KV head j over the kept blocks, in
-    block order, each block cut at seq_len."""
-    ks, vs = [], []
+    block order, each block cut at seq_len (every block holds at least one key)."""
+    ks, vs = [np.zeros((0, D))], [np.zeros((0, D))]
     for b in blocks:
         n = min(BLOCK, seq_len - b * BLOCK)
         ks.append(logical_block(k_cache, bt_row, b, slice(j, j + 1))[:n, 0, :])

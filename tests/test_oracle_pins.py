@@ -822,3 +822,108 @@ def test_tokens_last_token_is_the_decode_step():
     np.testing.assert_array_equal(res["scores"][last], dec["scores"])
     np.testing.assert_array_equal(res["ids"][last], dec["ids"])
     np.testing.assert_allclose(res["out"][last], dec["out"], rtol=0, atol=0)
+
+
+# ----------------------------------------------------------------------------
+# new-token placement: hand-worked rows, requests and positions
+# ----------------------------------------------------------------------------
+
+def test_token_positions_golden():
+    """Which stored row is which (request, position), and where the insert writes
+    it: a ragged batch worked by hand (tests/golden/token_positions.json)."""
+    with open(os.path.join(GOLDEN, "token_positions.json")) as f:
+        gold = json.load(f)
+    units = O.prefill_units(gold["seq_lens"], gold["q_lens"])
+    assert units == gold["expected_units"]
+    toks = O.token_positions(units)
+    assert [list(t) for t in toks] == gold["expected_tokens"]
+    # the insert writes row `row` to logical block p // 128, row p % 128 of its request
+    rng = np.random.default_rng(21)
+    Hq, Hkv, D, Hi, Di = 2, 1, 8, 1, 4
+    T = sum(gold["q_lens"])
+    nb = [(L + 127) // 128 for L in gold["seq_lens"]]
+    bt = np.zeros((3, max(nb)), dtype=np.int64)
+    phys = rng.permutation(sum(nb))
+    base = 0
+    for r, n in enumerate(nb):
+        bt[r, :n] = phys[base:base + n]
+        base += n
+    # each new token's V row is its row number in every channel: the slot it lands
+    # in then names the row
+    v = np.repeat(np.arange(T, dtype=np.float64)[:, None, None] + 1, D, axis=2)
+    zeros = np.zeros((sum(nb), Hkv, 128, D))
+    _, _, vc, _ = O.qk_norm_rope_insert(
+        units, rng.standard_normal((T, Hq, D)), rng.standard_normal((T, Hkv, D)), v,
+        rng.standard_normal((T, Hi, Di)), np.ones(D), np.ones(D), 1e-6, 1e4, 0,
+        zeros, zeros, np.zeros((sum(nb), Hi, 128, Di)), bt)
+    req_of_row = [t[1] for t in gold["expected_tokens"]]
+    for row, b, slot in gold["expected_cache_slots"]:
+        r = req_of_row[row]
+        assert np.all(vc[bt[r][b], 0, slot] == row + 1), (row, b, slot)
+    assert np.count_nonzero(vc[:, 0, :, 0]) == T
+
+
+# ----------------------------------------------------------------------------
+# attention over an arbitrary id list (not the selection's own output)
+# ----------------------------------------------------------------------------
+
+def _block_masked_reference(q, k_log, v_log, positions, blocks, L, scale):
+    """Softmax attention over the keys of `blocks` (a set of logical block ids)
+    that are at or before each query's position: torch SDPA in float64 with that
+    mask, lse with scipy. Rows without any such key are left out (NaN)."""
+    keys = np.arange(k_log.shape[0])
+    member = np.isin(keys // BLK, np.array(sorted(blocks), dtype=np.int64)) & (keys < L)
+    mask = member[None, :] & (keys[None, :] <= np.asarray(positions)[:, None])
+    T, Hq, D = q.shape
+    G = Hq // k_log.shape[1]
+    qt = torch.from_numpy(q).permute(1, 0, 2)
+    kt = torch.from_numpy(k_log).permute(1, 0, 2).repeat_interleave(G, 0)
+    vt = torch.from_numpy(v_log).permute(1, 0, 2).repeat_interleave(G, 0)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=torch.from_numpy(mask), scale=scale).permute(1, 0, 2).numpy()
+    logits = (torch.matmul(qt, kt.transpose(1, 2)) * scale).numpy()
+    lse = scipy.special.logsumexp(np.where(mask[None], logits, -np.inf), axis=2).T
+    return out, lse, mask.any(axis=1)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_attention_over_any_id_list(case):
+    """The kept list is a set of blocks masked by position: order does not matter,
+    blocks after the unit's diagonal add nothing, a list without the diagonal
+    attends the remaining blocks, and a row with no visible key gets out 0 and
+    lse -inf (checked against SDPA over the same key set)."""
+    rng = np.random.default_rng(100 + case)
+    L, n, D, Hq, Hkv = 900, 200, 16, 4, 2       # blocks 0..7; units tau 5 and 6
+    kc, bt = paged(rng, [L], Hkv, D)
+    vc = rng.standard_normal(kc.shape)
+    q = rng.standard_normal((n, Hq, D))
+    units = O.prefill_units([L], [n])
+    k_log, v_log = logical(kc, bt[0], L), logical(vc, bt[0], L)
+    for un in units:
+        tau = un["tau"]
+        lists = {
+            0: [tau, 2, 0],                          # unsorted
+            1: [1, 3, -1, 4],                        # no diagonal; entries after -1 ignored
+            2: [0, tau + 1, tau],                    # a future block
+            3: [tau + 1],                            # only a future block: nothing visible
+            4: [tau, 4, 1, 3, 0, 2],                 # every block up to tau, shuffled
+            5: [-1, 0, 1],                           # empty list
+        }[case]
+        kept = []
+        for b in lists:
+            if b < 0:
+                break
+            kept.append(b)
+        ids = np.array([lists, lists], dtype=np.int32)      # both selection groups
+        rows = slice(un["row0"], un["row1"])
+        out, lse = O.unit_attention(q[rows], un["pos0"], ids, kc, vc, bt[0], L, Hkv)
+        pos = un["pos0"] + np.arange(un["row1"] - un["row0"])
+        ref, ref_lse, seen = _block_masked_reference(q[rows], k_log, v_log, pos, kept, L,
+                                                     1 / math.sqrt(D))
+        np.testing.assert_allclose(out[seen], ref[seen], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[seen], ref_lse[seen], rtol=1e-12, atol=1e-12)
+        assert np.all(out[~seen] == 0) and np.all(lse[~seen] == -np.inf)
+        if case in (3, 5):
+            assert not seen.any()
+        else:
+            assert seen.all()
