@@ -115,6 +115,21 @@ def token_units(seq_lens, tokens_per_seq):
     return units
 
 
+def prefill_token_units(seq_lens, q_lens):
+    """Per-query-token units of a (chunked) prefill batch ([feat] row
+    "Indexer-selected sparse attention": the selection is shaped [B, H_idx, S_q,
+    topk], one block list per query token). Every new token is a unit of its own:
+    its row (the same row layout as prefill_units), its position p, its diagonal
+    block p // 128. A batch of T new tokens per sequence is token_units."""
+    units = []
+    for un in prefill_units(seq_lens, q_lens):
+        for i in range(un["row1"] - un["row0"]):
+            p = un["pos0"] + i
+            units.append(dict(r=un["r"], tau=p // BLOCK, row0=un["row0"] + i,
+                              row1=un["row0"] + i + 1, pos0=p))
+    return units
+
+
 # ----------------------------------------------------------------------------
 # paged cache access
 # ----------------------------------------------------------------------------
@@ -321,6 +336,20 @@ def run_tokens(q, q_idx, k_cache, v_cache, k_idx_cache, block_table, seq_lens,
     """Index, select and attend for a multi-token decode step with per-token
     selection (token_units): rows r*T + i of q and q_idx."""
     units = token_units(seq_lens, tokens_per_seq)
+    row_len = row_len or block_table.shape[1]
+    scores = index_scores(units, q_idx, k_idx_cache, block_table, n_sel, row_len)
+    ids = select(scores, units, topk)
+    out, lse = attention(units, ids, q, k_cache, v_cache, block_table, seq_lens, n_sel,
+                         scale)
+    return dict(units=units, scores=scores, ids=ids, out=out, lse=lse)
+
+
+def run_prefill_tokens(q, q_idx, k_cache, v_cache, k_idx_cache, block_table, seq_lens,
+                       q_lens, n_sel, topk, scale=None, row_len=None):
+    """Index, select and attend for a prefill batch with per-query-token selection
+    (prefill_token_units): each new token scores the blocks with its own indexer
+    query, keeps its diagonal and its own top-k, and attends causally over them."""
+    units = prefill_token_units(seq_lens, q_lens)
     row_len = row_len or block_table.shape[1]
     scores = index_scores(units, q_idx, k_idx_cache, block_table, n_sel, row_len)
     ids = select(scores, units, topk)

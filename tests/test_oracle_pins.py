@@ -927,3 +927,139 @@ def test_attention_over_any_id_list(case):
             assert not seen.any()
         else:
             assert seen.all()
+
+
+# ----------------------------------------------------------------------------
+# per-query-token selection in prefill
+# ----------------------------------------------------------------------------
+
+PT_CASES = [([700, 260, 129], [300, 260, 1]), ([1000], [1000]), ([513, 384], [200, 129]),
+            ([5], [5])]
+
+
+@pytest.mark.parametrize("seq_lens,q_lens", PT_CASES)
+def test_prefill_token_units_rows_positions_and_diagonals(seq_lens, q_lens):
+    """One unit per new token, in row order: request r's tokens follow those of
+    requests 0..r-1, token i of request r sits at L_r - n_r + i, its diagonal
+    block is position // 128."""
+    units = O.prefill_token_units(seq_lens, q_lens)
+    assert len(units) == sum(q_lens)
+    row = 0
+    for r, (L, n) in enumerate(zip(seq_lens, q_lens)):
+        for i in range(n):
+            un = units[row]
+            p = L - n + i
+            assert (un["r"], un["row0"], un["row1"], un["pos0"], un["tau"]) == \
+                (r, row, row + 1, p, p // BLK)
+            row += 1
+
+
+def test_prefill_token_units_of_equal_chunks_are_the_multi_token_decode():
+    seq = [300, 129, 1000, 8]
+    for T in (1, 3, 8):
+        assert O.prefill_token_units(seq, [T] * len(seq)) == O.token_units(seq, T)
+
+
+@pytest.mark.parametrize("nsel", [2, 1])
+def test_prefill_token_scores_pool_to_the_tile_scores(nsel):
+    """Max-pooling the per-token block scores over the tokens of each prefill tile
+    gives the tile-level scores of the tile path, entry by entry."""
+    rng = np.random.default_rng(31)
+    seq_lens, q_lens = [700, 260, 129], [300, 260, 1]
+    kc, bt = paged(rng, seq_lens, 2, 16)
+    ki = rng.standard_normal((kc.shape[0], 4, BLK, 8))
+    qi = rng.standard_normal((sum(q_lens), 4, 8))
+    tok = O.index_scores(O.prefill_token_units(seq_lens, q_lens), qi, ki, bt, nsel, bt.shape[1])
+    tiles = O.prefill_units(seq_lens, q_lens)
+    tile = O.index_scores(tiles, qi, ki, bt, nsel, bt.shape[1])
+    for u, un in enumerate(tiles):
+        pooled = tok[un["row0"]:un["row1"]].max(axis=0)
+        inf = ~np.isfinite(tile[u])
+        np.testing.assert_array_equal(pooled[inf], tile[u][inf])
+        np.testing.assert_allclose(pooled[~inf], tile[u][~inf], rtol=1e-13, atol=1e-13)
+
+
+def test_prefill_token_scores_brute_force():
+    """Per-token scores of a chunked prefill by explicit loops over keys, heads and
+    channels, through the block table."""
+    rng = np.random.default_rng(32)
+    seq_lens, q_lens, nsel = [300, 140], [45, 20], 2      # chunks straddling blocks
+    kc, bt = paged(rng, seq_lens, 1, 8)
+    ki = rng.standard_normal((kc.shape[0], 2, BLK, 4))
+    qi = rng.standard_normal((sum(q_lens), 2, 4))
+    res = O.index_scores(O.prefill_token_units(seq_lens, q_lens), qi, ki, bt, nsel,
+                         bt.shape[1])
+    row = 0
+    for r, (L, n) in enumerate(zip(seq_lens, q_lens)):
+        for i in range(n):
+            p = L - n + i
+            tau = p // BLK
+            for g in range(nsel):
+                for b in range(bt.shape[1]):
+                    got = res[row, g, b]
+                    if b > tau:
+                        assert got == -np.inf
+                    elif b == tau:
+                        assert got == np.inf
+                    else:
+                        best = -np.inf
+                        for s in range(BLK):
+                            acc = 0.0
+                            for d in range(4):
+                                acc += qi[row, g, d] * ki[bt[r][b], g, s, d]
+                            best = max(best, acc)
+                        assert abs(got - best) <= 1e-12 * max(1.0, abs(best))
+            row += 1
+
+
+@pytest.mark.parametrize("seq_lens,q_lens", PT_CASES)
+def test_prefill_tokens_dense_when_topk_covers_all_blocks(seq_lens, q_lens):
+    """k >= number of blocks: every token attends densely and causally (SDPA)."""
+    rng = np.random.default_rng(33)
+    kc, bt = paged(rng, seq_lens, 2, 16)
+    vc = rng.standard_normal(kc.shape)
+    ki = rng.standard_normal((kc.shape[0], 4, BLK, 8))
+    T = sum(q_lens)
+    q, qi = rng.standard_normal((T, 8, 16)), rng.standard_normal((T, 4, 8))
+    res = O.run_prefill_tokens(q, qi, kc, vc, ki, bt, seq_lens, q_lens, 2, bt.shape[1] + 1)
+    row = 0
+    for r, (L, n) in enumerate(zip(seq_lens, q_lens)):
+        out, lse = dense_reference(q[row:row + n], logical(kc, bt[r], L), logical(vc, bt[r], L),
+                                   np.arange(L - n, L), 1 / math.sqrt(16))
+        np.testing.assert_allclose(res["out"][row:row + n], out, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(res["lse"][row:row + n], lse, rtol=1e-12, atol=1e-12)
+        row += n
+
+
+def test_prefill_tokens_select_per_token():
+    """Each token keeps its own diagonal and min(k, tau + 1) blocks, chosen by its own
+    scores; a dominant block planted for one token only is kept by that token and,
+    where it loses to nothing, not by the others."""
+    rng = np.random.default_rng(34)
+    seq_lens, q_lens, topk = [1000], [300], 3
+    kc, bt = paged(rng, seq_lens, 1, 8)
+    vc = rng.standard_normal(kc.shape)
+    ki = rng.standard_normal((kc.shape[0], 1, BLK, 8)) * 0.01
+    qi = rng.standard_normal((300, 1, 8)) * 0.01
+    # token 150 (position 850, block 6) gets a direction that block 2's keys share;
+    # the other tokens have no component along it
+    u = np.zeros(8)
+    u[0] = 1.0
+    qi[:, 0, 0] = 0.0
+    base = O.run_prefill_tokens(rng.standard_normal((300, 2, 8)), qi, kc, vc, ki, bt,
+                                seq_lens, q_lens, 1, topk)
+    ki[bt[0][2], 0] += 10 * u
+    qi[150, 0] += 10 * u
+    q = rng.standard_normal((300, 2, 8))
+    res = O.run_prefill_tokens(q, qi, kc, vc, ki, bt, seq_lens, q_lens, 1, topk)
+    for row, un in enumerate(res["units"]):
+        kept = [b for b in res["ids"][row, 0] if b >= 0]
+        assert un["tau"] in kept and len(kept) == min(topk, un["tau"] + 1)
+        assert kept == sorted(kept) and max(kept) == un["tau"]
+        assert kept == O.select_blocks(res["scores"][row, 0], un["tau"], topk)[:len(kept)]
+    assert 2 in res["ids"][150, 0] and 2 not in base["ids"][150, 0]
+    # every other token's scores and selection are those of the unplanted keys
+    others = [row for row in range(300) if row != 150]
+    np.testing.assert_allclose(res["scores"][others], base["scores"][others], rtol=0,
+                               atol=1e-15)
+    np.testing.assert_array_equal(res["ids"][others], base["ids"][others])
