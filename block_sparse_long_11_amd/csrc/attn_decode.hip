@@ -94,9 +94,18 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
   const int32_t *sel = ids + (static_cast<size_t>(x) * nsel + g) * topk;
   const int32_t *bt = block_table + static_cast<size_t>(r) * max_blocks;
   const int qpos = seq_lens[r] - T + x % T;
-  const int slot0 = sp * per_split, slot1 = min(topk, slot0 + per_split);
-
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+  // the kept list ends at its first -1: nk ids, found by a ballot per 64 slots
+  int nk = topk;
+  for (int c0 = 0; c0 < topk; c0 += kWave) {
+    const uint64_t pad = __ballot(c0 + lane < topk && sel[c0 + lane] < 0);
+    if (pad != 0) {
+      nk = c0 + static_cast<int>(__builtin_ctzll(pad));
+      break;
+    }
+  }
+  const int slot0 = sp * per_split, slot1 = min(nk, slot0 + per_split);
+
   const int n = lane % 16;               // stacked query head (column)
   const int q4 = lane / 16;              // lane quarter: 8 d (or 8 keys) per k step
 
@@ -120,7 +129,7 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_bf16_kernel(
 
   for (int slot = slot0; slot < slot1; ++slot) {
     const int b = sel[slot];
-    if (b < 0) break;
+    if (b > qpos / kBlk) continue;       // only future keys: not read
     any = true;
     const int64_t phys = bt[b];
     const size_t off = (static_cast<size_t>(phys) * Hkv + j) * kBlk * D;
@@ -270,9 +279,9 @@ __global__ __launch_bounds__(D) void combine_kernel(const float *__restrict__ o_
   const float *op = o_part + row * num_splits * D + d;
   float M = neg_inf();
   for (int s = 0; s < num_splits; ++s) M = fmaxf(M, lp[s]);
-  // M is finite: the part holding the diagonal block sees the query's own key.
   // An empty part has lse -inf and o 0, so it adds exp(-inf) * 0 = 0: no branch,
-  // and eight parts' loads are issued before they are used.
+  // and eight parts' loads are issued before they are used. M is finite whenever
+  // some part saw a key (the part holding the diagonal block sees the query's own).
   float L = 0.f, acc = 0.f;
   int s = 0;
   for (; s + 8 <= num_splits; s += 8) {
@@ -294,12 +303,15 @@ __global__ __launch_bounds__(D) void combine_kernel(const float *__restrict__ o_
     L += w;
     acc += w * op[static_cast<size_t>(s) * D];
   }
-  const float v = acc / L;
+  // no part saw a key (an id list without any block up to the query's own):
+  // out = 0 and lse = -inf
+  const bool seen = M != neg_inf();
+  const float v = seen ? acc / L : 0.f;
   if constexpr (BF16)
     static_cast<uint16_t *>(out)[row * D + d] = static_cast<uint16_t>(f32_to_bf16_bits(v));
   else
     static_cast<float *>(out)[row * D + d] = v;
-  if (lse != nullptr && d == 0) lse[row] = M + __logf(L);
+  if (lse != nullptr && d == 0) lse[row] = seen ? M + __logf(L) : neg_inf();
 }
 
 }  // namespace

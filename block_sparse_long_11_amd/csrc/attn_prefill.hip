@@ -9,8 +9,12 @@
 //
 // Query t of unit u (positions pos0 .. pos0+num_rows-1, diagonal block tau),
 // head i, attends to every key s of the kept blocks of its group with
-// s <= pos(t). Only the diagonal block needs the causal test: every other kept
-// block lies entirely before the unit's first query.
+// s <= pos(t). The causal test runs on every kept block that reaches the unit's
+// first query (id >= tau): for the selection's own output that is the diagonal
+// block alone, attended first, so the steady state has no masking work. A kept
+// id past tau holds only future keys: it is not read (the diagonal's physical
+// block stands in, fully masked). A row that sees no key at all (an id list
+// without any block up to its diagonal) gets out = 0 and lse = -inf.
 //
 // bf16 path (MFMA 32x32x16, fp32 accumulate). A work-group of 8 waves owns (unit,
 // KV head j, 2 query heads): 128 token rows x 2 heads, one wave per (head, 32
@@ -61,6 +65,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kPrefWaves = 8;
 constexpr float kSlack = 8.f;
 
+// Initial reference maximum (log2 units): finite and far below any logit, so a
+// tile whose keys are all masked for a row before it has seen a visible key adds
+// exp2(-inf) = 0 instead of NaN.
+constexpr float kMaxFloor = -1e30f;
+
 // S^T tile row m (0..31) -> key inside the 32-key tile: swap bits 2 and 3.
 __device__ __forceinline__ int srow_key(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -105,6 +114,31 @@ __device__ __forceinline__ void load_lds16(uint32_t lds, const void *gbase, uint
 
 template <int V>
 using ic = std::integral_constant<int, V>;
+
+// Output of one query row and head from O^T (lane half a holds d = 32 dt + 8 i4 +
+// 4 a .. +3), the row sum and the reference maximum. A row without any visible
+// key (sum 0) gets out = 0 and lse = -inf.
+template <int D>
+__device__ __forceinline__ void store_row(uint16_t *__restrict__ out, float *__restrict__ lse,
+                                          int qrow, int Hq, int head, int a, const f32x16 *o,
+                                          float sum, float m_ref) {
+  constexpr int DT = D / 32;
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  uint16_t *op = out + (static_cast<size_t>(qrow) * Hq + head) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = dt * 32 + i4 * 8 + a * 4;
+      uint2 w;
+      w.x = cvt_pk_bf16(o[dt][i4 * 4 + 0] * inv, o[dt][i4 * 4 + 1] * inv);
+      w.y = cvt_pk_bf16(o[dt][i4 * 4 + 2] * inv, o[dt][i4 * 4 + 3] * inv);
+      *reinterpret_cast<uint2 *>(op + d) = w;
+    }
+  if (lse != nullptr && a == 0)
+    lse[static_cast<size_t>(qrow) * Hq + head] =
+        sum > 0.f ? (m_ref + __builtin_log2f(sum)) * kLn2 : neg_inf();
+}
 
 template <int D>
 __global__ __launch_bounds__(kPrefWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -168,24 +202,49 @@ void attn_prefill_bf16_kernel(
   const int qrow = un.row0 + min(row_in_tile, un.num_rows - 1);
   const int qpos = row_ok ? un.pos0 + row_in_tile : 0x7fffffff;
 
-  // Kept blocks, attended in the order: diagonal block (the last kept id) first,
-  // then the others in id order. Lane p of phys holds the physical block of
-  // position 64 * phys_chunk + p.
+  // Kept blocks, attended in the order: the last kept id (the diagonal block, for
+  // the selection's ascending output) first, then the others in list order. Lane
+  // p of phys holds the physical block of position 64 * phys_chunk + p, its
+  // logical id; bit p of late marks the positions whose block reaches the unit's
+  // first query (id >= tau) and so takes the causal test.
   int nk = 0;
   while (nk < topk && sel[nk] >= 0) ++nk;
-  if (nk == 0) return;                    // nothing kept (never produced by the selection)
-  const int diag_b = sel[nk - 1];
+  if (nk == 0) {                          // nothing kept: no visible key
+    if (active && row_ok) {
+      f32x16 z[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) z[dt] = f32x16{};
+      store_row<D>(out, lse, qrow, Hq, head, a, z, 0.f, 0.f);
+    }
+    return;
+  }
+  const int first_b = sel[nk - 1];
   const int NH = 2 * nk;                  // half-blocks
   int phys_chunk = -1, phys = 0;
   auto phys_at = [&](int p) __attribute__((always_inline)) {
     if ((p >> 6) != phys_chunk) {
       phys_chunk = p >> 6;
       const int pl = 64 * phys_chunk + lane;
-      phys = pl < nk ? bt[sel[pl == 0 ? nk - 1 : pl - 1]] : 0;
+      phys = pl < nk ? bt[min(sel[pl == 0 ? nk - 1 : pl - 1], un.tau)] : 0;
       wait_vm<0>();   // completes here, so no wait is needed where phys is read
     }
     return __builtin_amdgcn_readlane(phys, p & 63);
   };
+  // Same positions, for the causal test: lane p of logical holds the id, bit p
+  // of late is set when that block reaches the unit's first query (id >= tau).
+  // Loaded up front for the first 64 positions, so the loop reloads only past 64.
+  int late_chunk = -1, logical = 0;
+  uint64_t late = 0;
+  auto late_at = [&](int p) __attribute__((always_inline)) {
+    if ((p >> 6) != late_chunk) {
+      late_chunk = p >> 6;
+      const int pl = 64 * late_chunk + lane;
+      logical = pl < nk ? sel[pl == 0 ? nk - 1 : pl - 1] : 0;
+      late = __ballot(pl < nk && logical >= un.tau);
+    }
+    return ((late >> (p & 63)) & 1) != 0;
+  };
+  late_at(0);
 
   bf16x8 qf[KS];
   {
@@ -236,7 +295,7 @@ void attn_prefill_bf16_kernel(
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
   f32x16 s = f32x16{};
   bf16x8 kf[KS], vf[2 * DT], pf[2];
-  float m_ref = neg_inf();                // reference maximum, log2 units
+  float m_ref = kMaxFloor;                // reference maximum, log2 units
   float l_run = 0.f;                      // this lane's share of the row sum
 
   auto read_k = [&](auto r, int kt2) __attribute__((always_inline)) {
@@ -271,11 +330,15 @@ void attn_prefill_bf16_kernel(
     }
   };
 
-  // Softmax of tile kt (0..3) of a block; masked for the diagonal block.
-  auto softmax = [&](auto mask_tag, int kt) __attribute__((always_inline)) {
+  // Softmax of tile kt (0..3) of the block at position bp; the first block is
+  // always masked (MASK), any other one only when it reaches the unit's first query.
+  auto softmax = [&](auto mask_tag, int kt, int bp) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    if constexpr (MASK) {
-      const int lim = qpos - diag_b * kBlk - kt * 32;   // tile keys with offset > lim are masked
+    bool do_mask = MASK;
+    if constexpr (!MASK) do_mask = late_at(bp);
+    if (do_mask) {
+      const int b = MASK ? first_b : __builtin_amdgcn_readlane(logical, bp & 63);
+      const int lim = qpos - b * kBlk - kt * 32;   // tile keys with offset > lim are masked
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (16 * (i / 8) + 8 * a + (i % 8) > lim) s[i] = neg_inf();
@@ -331,7 +394,7 @@ void attn_prefill_bf16_kernel(
       else if (T + 1 < 4 * nk) read_k(ic<R0 + 2>{}, 0);
       if (kt < 2) read_v(ic<R0>{}, kt);
       else read_v(ic<R0 + 1>{}, kt - 2);
-      softmax(mask_tag, kt);
+      softmax(mask_tag, kt, bp);
       if (kt == 1) {
         if (2 * bp + 3 < NH) issue(2 * bp + 3, ic<R0 + 3>{});
       } else if (kt == 3) {
@@ -377,20 +440,7 @@ void attn_prefill_bf16_kernel(
     sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
   if (!row_ok) return;
-  const float inv = 1.f / sum;
-  uint16_t *op = out + (static_cast<size_t>(qrow) * Hq + head) * D;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = dt * 32 + i4 * 8 + a * 4;
-      uint2 w;
-      w.x = cvt_pk_bf16(o[dt][i4 * 4 + 0] * inv, o[dt][i4 * 4 + 1] * inv);
-      w.y = cvt_pk_bf16(o[dt][i4 * 4 + 2] * inv, o[dt][i4 * 4 + 3] * inv);
-      *reinterpret_cast<uint2 *>(op + d) = w;
-    }
-  if (lse != nullptr && a == 0)
-    lse[static_cast<size_t>(qrow) * Hq + head] = (m_ref + __builtin_log2f(sum)) * kLn2;
+  store_row<D>(out, lse, qrow, Hq, head, a, o, sum, m_ref);
 }
 
 // FP8 K/V: same tiles as attn_prefill_bf16_kernel, staged through registers.
@@ -446,10 +496,20 @@ void attn_prefill_fp8_kernel(
 
   int nk = 0;
   while (nk < topk && sel[nk] >= 0) ++nk;
-  if (nk == 0) return;
-  const int diag_b = sel[nk - 1];
-  const int NH = 2 * nk;                  // half-blocks, the diagonal block's first
-  auto phys_of = [&](int p) { return bt[sel[p == 0 ? nk - 1 : p - 1]]; };
+  if (nk == 0) {                          // nothing kept: no visible key
+    if (active && row_ok) {
+      f32x16 z[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) z[dt] = f32x16{};
+      store_row<D>(out, lse, qrow, Hq, head, a, z, 0.f, 0.f);
+    }
+    return;
+  }
+  const int NH = 2 * nk;                  // half-blocks, the last kept id's first
+  // logical id at position p (the last kept id first); a block past tau holds
+  // only future keys and is read from the diagonal's physical block, masked
+  auto id_of = [&](int p) { return sel[p == 0 ? nk - 1 : p - 1]; };
+  auto phys_of = [&](int p) { return bt[min(id_of(p), un.tau)]; };
 
   bf16x8 qf[KS];
   {
@@ -525,7 +585,7 @@ void attn_prefill_fp8_kernel(
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
-  float m_ref = neg_inf(), l_run = 0.f;
+  float m_ref = kMaxFloor, l_run = 0.f;
 
   load(0);
   for (int hb = 0; hb < NH; ++hb) {
@@ -533,6 +593,9 @@ void attn_prefill_fp8_kernel(
     store(slot);
     __syncthreads();
     if (hb + 1 < NH) load(hb + 1);
+    // the causal test, for a block that reaches the unit's first query
+    const int blk_id = id_of(hb >> 1);
+    const bool late = blk_id >= un.tau;
 #pragma unroll
     for (int kt2 = 0; kt2 < 2; ++kt2) {
       bf16x8 kf[KS], vf[2 * DT], pf[2];
@@ -544,8 +607,8 @@ void attn_prefill_fp8_kernel(
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
-      if (hb < 2) {   // the diagonal block: keys past the query are masked
-        const int lim = qpos - diag_b * kBlk - (hb * 2 + kt2) * 32;
+      if (late) {     // keys past the query are masked
+        const int lim = qpos - blk_id * kBlk - ((hb & 1) * 2 + kt2) * 32;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (16 * (i / 8) + 8 * a + (i % 8) > lim) s[i] = neg_inf();
@@ -600,20 +663,7 @@ void attn_prefill_fp8_kernel(
     sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
   if (!row_ok) return;
-  const float inv = 1.f / sum;
-  uint16_t *op = out + (static_cast<size_t>(qrow) * Hq + head) * D;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = dt * 32 + i4 * 8 + a * 4;
-      uint2 w;
-      w.x = cvt_pk_bf16(o[dt][i4 * 4 + 0] * inv, o[dt][i4 * 4 + 1] * inv);
-      w.y = cvt_pk_bf16(o[dt][i4 * 4 + 2] * inv, o[dt][i4 * 4 + 3] * inv);
-      *reinterpret_cast<uint2 *>(op + d) = w;
-    }
-  if (lse != nullptr && a == 0)
-    lse[static_cast<size_t>(qrow) * Hq + head] = (m_ref + __builtin_log2f(sum)) * kLn2;
+  store_row<D>(out, lse, qrow, Hq, head, a, o, sum, m_ref);
 }
 
 }  // namespace
@@ -652,6 +702,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
   for (int slot = 0; slot < topk; ++slot) {
     const int b = sel[slot];
     if (b < 0) break;
+    if (b > qpos / kBlk) continue;       // only future keys
     const int64_t phys = bt[b];
     const float *kb = kc + (static_cast<size_t>(phys) * Hkv + j) * kBlk * D;
     const float *vb = vtc + (static_cast<size_t>(phys) * Hkv + j) * D * kBlk;
@@ -668,9 +719,10 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
       m = m_new;
     }
   }
+  // a row without any visible key gets out = 0 and lse = -inf
   float *op = out + (static_cast<size_t>(qrow) * Hq + head) * D;
-  for (int d = 0; d < D; ++d) op[d] = acc[d] / l;
-  if (lse != nullptr) lse[static_cast<size_t>(qrow) * Hq + head] = m + logf(l);
+  for (int d = 0; d < D; ++d) op[d] = l > 0.f ? acc[d] / l : 0.f;
+  if (lse != nullptr) lse[static_cast<size_t>(qrow) * Hq + head] = l > 0.f ? m + logf(l) : neg_inf();
 }
 
 hipError_t launch_attn_f32(const Geom &g, const msa_cache_t &c, const msa_unit_t *units,

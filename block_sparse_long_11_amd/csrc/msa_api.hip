@@ -123,6 +123,13 @@ bool is_nan_bits(float x) {
   return (u & 0x7fffffffu) > 0x7f800000u;
 }
 
+// Neither NaN nor +-inf, by the bits (see is_nan_bits).
+bool finite_bits(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, sizeof(u));
+  return (u & 0x7f800000u) != 0x7f800000u;
+}
+
 constexpr int kMaxTokensPerSeq = 8;
 
 msa_status_t check_tokens(int T, const msa::Geom &g) {
@@ -161,7 +168,8 @@ msa_status_t attn_decode(const msa_geom_t *geom, const msa_cache_t *cache, int T
   MSA_REQUIRE(q != nullptr && ids != nullptr && out != nullptr, MSA_ERR_INVALID_ARG,
               "q / ids / out is NULL");
   MSA_REQUIRE(topk >= 1, MSA_ERR_INVALID_ARG, "topk must be positive");
-  MSA_REQUIRE(!is_nan_bits(softmax_scale), MSA_ERR_INVALID_ARG, "softmax_scale is NaN");
+  MSA_REQUIRE(finite_bits(softmax_scale), MSA_ERR_INVALID_ARG,
+              "softmax_scale must be finite (<= 0 selects 1/sqrt(head_dim))");
   const int rows = cache->num_seqs * T;
   const int s = num_splits > 0 ? (num_splits < topk ? num_splits : topk)
                                : msa::decode_auto_splits(g, rows, topk);
@@ -260,7 +268,8 @@ msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *
   if (batch->total_units == 0) return ok();     // no queries
   MSA_REQUIRE(q != nullptr && ids != nullptr && out != nullptr, MSA_ERR_INVALID_ARG,
               "q / ids / out is NULL");
-  MSA_REQUIRE(!is_nan_bits(softmax_scale), MSA_ERR_INVALID_ARG, "softmax_scale is NaN");
+  MSA_REQUIRE(finite_bits(softmax_scale), MSA_ERR_INVALID_ARG,
+              "softmax_scale must be finite (<= 0 selects 1/sqrt(head_dim))");
   return hip_status(msa::launch_attn_prefill(g, *cache, *batch, q, ids, topk,
                                              resolve_scale(softmax_scale, g.D), out, lse,
                                              static_cast<hipStream_t>(stream)),

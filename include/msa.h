@@ -185,16 +185,23 @@ msa_status_t msa_select_topk_blocks(const float *scores, int32_t num_rows,
 /* Step 3, sparse prefill attention ([dd] "Serving options": prefill kernel for
  * sparse GQA; [feat] rows "Grouped-query attention", "Learnable attention sink":
  * plain softmax, no sink, no output gate).
- *   q    [total_q][H_q][D];  ids int32 [total_units][num_sel_groups][topk] (the
- *        output of step 2, ascending, -1 padded)
+ *   q    [total_q][H_q][D];  ids int32 [total_units][num_sel_groups][topk]
  *   out  [total_q][H_q][D] (dtype, rounded to nearest even);
  *   lse  fp32 [total_q][H_q] natural-log logsumexp of the logits, or NULL.
  * Query t of unit u, head i (KV head j = i / G, selection group g = j or 0)
  * attends to every key s of the blocks ids[u][g][*] with s <= pos(t):
  *   out = softmax(softmax_scale * q . k) . v  (fp32 softmax).
- * softmax_scale <= 0 selects 1/sqrt(D). bf16 runs on MFMA with fp32 accumulation;
- * probabilities are rounded to bf16 for the P.V product. A batch with no units
- * enqueues nothing (q, ids and out may be NULL). */
+ * ids rows: distinct block ids, ended by the first -1 (entries after it are
+ * ignored); step 2's output (ascending, the unit's diagonal block last) is the
+ * fast case. Every listed block is masked by position, so any order and any
+ * subset give the result above: a listed id after the unit's diagonal block tau
+ * holds only future keys and is not read; ids must lie in [0,
+ * max_blocks_per_seq) (out-of-range values are undefined behaviour). A query row
+ * with no visible key (its list holds no block up to its own position) gets
+ * out = 0 and lse = -inf.
+ * softmax_scale must be finite; <= 0 selects 1/sqrt(D). bf16 runs on MFMA with
+ * fp32 accumulation; probabilities are rounded to bf16 for the P.V product. A
+ * batch with no units enqueues nothing (q, ids and out may be NULL). */
 msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *cache,
                                      const msa_batch_t *batch, const void *q,
                                      const int32_t *ids, int32_t topk,
@@ -212,12 +219,16 @@ size_t msa_decode_workspace_size(const msa_geom_t *geom, int32_t num_seqs,
  * options": decode kernel for sparse GQA; [feat] methods "Two-phase forward" and
  * "LSE fusion").
  *   q   [num_seqs][H_q][D], the new query of sequence r at position seq_lens[r]-1
- *   ids int32 [num_seqs][num_sel_groups][topk]
+ *   ids int32 [num_seqs][num_sel_groups][topk], rows as for the prefill call
+ *       (distinct ids, ended by -1; keys after the query are masked by position,
+ *       later blocks are not read; a query with no visible key gets out = 0 and
+ *       lse = -inf)
  *   workspace >= msa_decode_workspace_size(...) bytes, device, 256-byte aligned
  *   out [num_seqs][H_q][D] (dtype); lse fp32 [num_seqs][H_q] or NULL.
  * The selected slots are split into num_splits parts (<= 0: automatic), each
  * part is attended separately and the parts are merged by their logsumexp; the
- * result equals one softmax over all selected keys up to fp32 rounding. */
+ * result equals one softmax over all selected keys up to fp32 rounding.
+ * softmax_scale must be finite; <= 0 selects 1/sqrt(D). */
 msa_status_t msa_sparse_attn_decode(const msa_geom_t *geom, const msa_cache_t *cache,
                                     const void *q, const int32_t *ids, int32_t topk,
                                     float softmax_scale, int32_t num_splits,

@@ -271,3 +271,18 @@ def test_missing_library_raises(tmp_path, monkeypatch):
     ids = torch.zeros((1, 1, 2), dtype=torch.int32)
     with pytest.raises(RuntimeError, match="missing"):
         msa.msa_select_topk_blocks(scores, 2, ids)
+
+
+@pytest.mark.parametrize("scale", [float("inf"), float("-inf"), float("nan")])
+def test_softmax_scale_must_be_finite(lib, scale):
+    """A non-finite scale is rejected by every attention call before any launch
+    (<= 0 selects 1/sqrt(D); +inf would make the online softmax NaN)."""
+    g, c, b = _geom(), _cache(), msa._Batch(FAKE, 3, 300)
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(g), ctypes.byref(c), ctypes.byref(b), FAKE,
+                                       FAKE, 4, scale, FAKE, None, None) == INVALID
+    assert b"finite" in lib.msa_last_error()
+    assert lib.msa_sparse_attn_decode(ctypes.byref(g), ctypes.byref(c), FAKE, FAKE, 16, scale, 0,
+                                      FAKE, 1 << 30, FAKE, None, None) == INVALID
+    assert lib.msa_sparse_attn_decode_per_token(ctypes.byref(g), ctypes.byref(c), 2, FAKE, FAKE,
+                                                16, scale, 0, FAKE, 1 << 30, FAKE, None,
+                                                None) == INVALID
