@@ -81,6 +81,10 @@ EXPORTS = {
                                               ctypes.c_float, ctypes.c_int32, ctypes.c_void_p,
                                               ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p]),
+    "msa_sparse_attn_decode_static": (ctypes.c_int, [
+        ctypes.POINTER(_Geom), ctypes.POINTER(_Cache), ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p]),
     "msa_qk_norm_rope_insert": (ctypes.c_int, [ctypes.POINTER(_Geom), ctypes.POINTER(_Cache),
                                                ctypes.POINTER(_Batch), ctypes.c_void_p,
                                                ctypes.c_void_p, ctypes.c_void_p,
@@ -363,6 +367,33 @@ def msa_sparse_attn_decode(geom: Geometry, cache: Cache, q, ids, topk, out, work
                                         topk, float(softmax_scale), num_splits, _ptr(workspace),
                                         workspace.numel(), _ptr(out), _ptr(lse),
                                         _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 16 * 1024 * 1024   # MSA_STATIC_SCRATCH_BYTES
+
+
+def msa_sparse_attn_decode_static(geom: Geometry, cache: Cache, q, ids, topk, out, lse=None,
+                                  num_splits=0, softmax_scale=0.0, stream=None):
+    """msa_sparse_attn_decode without a workspace: the library's static scratch
+    holds the split partials (for callers that cannot allocate)."""
+    cache.check(geom)
+    dev = cache.block_table.device
+    B = cache.num_seqs
+    _need(q, "q", geom.torch_dtype, 3, dev)
+    _need(out, "out", geom.torch_dtype, 3, dev)
+    _need(ids, "ids", torch.int32, 3, dev)
+    shape = (B, geom.num_q_heads, geom.head_dim)
+    if tuple(q.shape) != shape or tuple(out.shape) != shape:
+        raise ValueError(f"q and out must be {shape}")
+    if tuple(ids.shape) != (B, geom.num_sel_groups, topk):
+        raise ValueError("ids must be [B][n_sel][topk]")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+    g, c = geom.c(), cache.c()
+    _check(lib().msa_sparse_attn_decode_static(ctypes.byref(g), ctypes.byref(c), _ptr(q),
+                                               _ptr(ids), topk, float(softmax_scale),
+                                               num_splits, _ptr(out), _ptr(lse),
+                                               _stream(stream)))
 
 
 def msa_qk_norm_rope_insert(geom: Geometry, cache: Cache, batch, q, k, v, k_idx, q_norm_w,

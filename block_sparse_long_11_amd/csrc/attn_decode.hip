@@ -34,8 +34,17 @@
 // 32-channel block c the probabilities are multiplied by 2^e(c, key) before
 // their bf16 rounding (exact, a power of two commutes with the rounding) and the
 // V codes convert unscaled.
+#include <mutex>
+
 #include "msa_device.h"
 #include "msa_launch.h"
+
+// Scratch of msa_sparse_attn_decode_static: the split partials (o_part, lse_part)
+// of the decode attention, for callers that cannot allocate. Each GPU the library
+// runs on holds its own copy until the process ends. In host code this name is a
+// stand-in, not a device address: kernels and copies take the address resolved by
+// static_decode_scratch() below.
+static __device__ __align__(256) unsigned char scratch[MSA_STATIC_SCRATCH_BYTES];
 
 namespace msa {
 
@@ -331,6 +340,27 @@ size_t decode_workspace_bytes(const Geom &g, int num_seqs, int num_splits) {
   const size_t parts = static_cast<size_t>(num_seqs) * g.Hq * num_splits;
   const size_t o_bytes = (parts * g.D * sizeof(float) + 255) & ~static_cast<size_t>(255);
   return o_bytes + ((parts * sizeof(float) + 255) & ~static_cast<size_t>(255));
+}
+
+// Device address of the current GPU's copy of `scratch`, resolved once per device
+// (with that device current) and kept.
+hipError_t static_decode_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attn_decode(const Geom &g, const msa_cache_t &c, int T, const void *q,

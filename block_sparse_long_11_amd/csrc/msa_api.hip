@@ -156,10 +156,12 @@ msa_status_t index_decode(const msa_geom_t *geom, const msa_cache_t *cache, int 
 }
 
 // Split-KV decode attention for T tokens per sequence.
+// With static_scratch the split partials go to the library's static array instead
+// of the caller's workspace.
 msa_status_t attn_decode(const msa_geom_t *geom, const msa_cache_t *cache, int T, const void *q,
                          const int32_t *ids, int32_t topk, float softmax_scale,
                          int32_t num_splits, void *workspace, size_t workspace_bytes,
-                         void *out, float *lse, void *stream) {
+                         bool static_scratch, void *out, float *lse, void *stream) {
   msa::Geom g;
   msa_status_t st = check_geom(geom, &g);
   if (st != MSA_OK) return st;
@@ -173,7 +175,15 @@ msa_status_t attn_decode(const msa_geom_t *geom, const msa_cache_t *cache, int T
   const int rows = cache->num_seqs * T;
   const int s = num_splits > 0 ? (num_splits < topk ? num_splits : topk)
                                : msa::decode_auto_splits(g, rows, topk);
-  if (g.bf16) {
+  if (g.bf16 && static_scratch) {
+    const size_t need = msa::decode_workspace_bytes(g, rows, s);
+    MSA_REQUIRE(need <= MSA_STATIC_SCRATCH_BYTES, MSA_ERR_WORKSPACE_TOO_SMALL,
+                "static scratch: %zu bytes needed, the limit is %zu (fewer sequences or "
+                "splits, or msa_sparse_attn_decode with a workspace)",
+                need, static_cast<size_t>(MSA_STATIC_SCRATCH_BYTES));
+    hipError_t e = msa::static_decode_scratch(&workspace);
+    if (e != hipSuccess) return hip_status(e, "static scratch address");
+  } else if (g.bf16) {
     const size_t need = msa::decode_workspace_bytes(g, rows, s);
     MSA_REQUIRE(workspace != nullptr, MSA_ERR_INVALID_ARG, "workspace is NULL");
     MSA_REQUIRE(reinterpret_cast<uintptr_t>(workspace) % 256 == 0, MSA_ERR_INVALID_ARG,
@@ -291,7 +301,15 @@ msa_status_t msa_sparse_attn_decode(const msa_geom_t *geom, const msa_cache_t *c
                                     void *workspace, size_t workspace_bytes, void *out,
                                     float *lse, void *stream) {
   return attn_decode(geom, cache, 1, q, ids, topk, softmax_scale, num_splits, workspace,
-                     workspace_bytes, out, lse, stream);
+                     workspace_bytes, false, out, lse, stream);
+}
+
+msa_status_t msa_sparse_attn_decode_static(const msa_geom_t *geom, const msa_cache_t *cache,
+                                           const void *q, const int32_t *ids, int32_t topk,
+                                           float softmax_scale, int32_t num_splits, void *out,
+                                           float *lse, void *stream) {
+  return attn_decode(geom, cache, 1, q, ids, topk, softmax_scale, num_splits, nullptr, 0, true,
+                     out, lse, stream);
 }
 
 msa_status_t msa_index_scores_per_token(const msa_geom_t *geom, const msa_cache_t *cache,
@@ -307,7 +325,7 @@ msa_status_t msa_sparse_attn_decode_per_token(const msa_geom_t *geom, const msa_
                                               void *workspace, size_t workspace_bytes,
                                               void *out, float *lse, void *stream) {
   return attn_decode(geom, cache, tokens_per_seq, q, ids, topk, softmax_scale, num_splits,
-                     workspace, workspace_bytes, out, lse, stream);
+                     workspace, workspace_bytes, false, out, lse, stream);
 }
 
 const char *msa_status_string(msa_status_t status) {

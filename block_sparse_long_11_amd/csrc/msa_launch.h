@@ -33,6 +33,9 @@ size_t decode_workspace_bytes(const Geom &g, int num_seqs, int num_splits);
 hipError_t launch_attn_decode(const Geom &g, const msa_cache_t &c, int T, const void *q,
                               const int32_t *ids, int topk, float scale, int num_splits,
                               void *workspace, void *out, float *lse, hipStream_t st);
+// Device address of this GPU's static scratch (MSA_STATIC_SCRATCH_BYTES), the
+// workspace of msa_sparse_attn_decode_static; resolved on the first call per device.
+hipError_t static_decode_scratch(void **ptr);
 
 hipError_t launch_qk_norm_rope_insert(const Geom &g, const msa_cache_t &c, const msa_batch_t *b,
                                       const void *q, const void *k, const void *v,

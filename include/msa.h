@@ -235,6 +235,28 @@ msa_status_t msa_sparse_attn_decode(const msa_geom_t *geom, const msa_cache_t *c
                                     void *workspace, size_t workspace_bytes, void *out,
                                     float *lse, void *stream);
 
+/* Bytes of the static scratch that msa_sparse_attn_decode_static uses, per GPU. */
+#define MSA_STATIC_SCRATCH_BYTES (16u * 1024u * 1024u)
+
+/* msa_sparse_attn_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and result as msa_sparse_attn_decode without the workspace: the
+ * split partials go to a scratch array of MSA_STATIC_SCRATCH_BYTES that the
+ * library keeps in static device memory, one copy on each GPU it runs on, held
+ * until the process ends (its address is looked up once per device, on the
+ * first call there). The call allocates and frees nothing.
+ *   MSA_ERR_WORKSPACE_TOO_SMALL when msa_decode_workspace_size(geom, num_seqs,
+ *   topk, num_splits) exceeds MSA_STATIC_SCRATCH_BYTES (nothing is enqueued).
+ * Every call on one GPU shares that GPU's array and leaves the last call's
+ * partials in it; each call writes every entry it reads, so nothing needs to
+ * start at zero. Calls that overlap in time on one GPU (streams with no order
+ * between them) race on the array and give undefined results; calls ordered on
+ * one stream are safe. */
+msa_status_t msa_sparse_attn_decode_static(const msa_geom_t *geom, const msa_cache_t *cache,
+                                           const void *q, const int32_t *ids, int32_t topk,
+                                           float softmax_scale, int32_t num_splits, void *out,
+                                           float *lse, void *stream);
+
 /* Per-query-token selection for T new tokens per sequence (multi-token decode:
  * speculative verification, multi-token prediction). [feat] row "Indexer-selected
  * sparse attention": the model selects per query token ([B, H_idx, S_q, topk]).

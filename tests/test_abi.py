@@ -286,3 +286,33 @@ def test_softmax_scale_must_be_finite(lib, scale):
     assert lib.msa_sparse_attn_decode_per_token(ctypes.byref(g), ctypes.byref(c), 2, FAKE, FAKE,
                                                 16, scale, 0, FAKE, 1 << 30, FAKE, None,
                                                 None) == INVALID
+    assert lib.msa_sparse_attn_decode_static(ctypes.byref(g), ctypes.byref(c), FAKE, FAKE, 16,
+                                             scale, 0, FAKE, None, None) == INVALID
+
+
+def test_static_decode_rejects_what_does_not_fit(lib):
+    """The static-scratch decode refuses, before touching the GPU, a shape whose
+    partials exceed MSA_STATIC_SCRATCH_BYTES, and checks arguments like the
+    workspace form."""
+    g = _geom()
+    limit = msa.STATIC_SCRATCH_BYTES
+    text = open(HEADER).read()
+    assert f"#define MSA_STATIC_SCRATCH_BYTES ({limit // (1 << 20)}u * 1024u * 1024u)" in text
+    # 64 sequences of 64 query heads, one split each: 64 * 64 * 128 * 4 B = 2 MiB fits;
+    # 8192 sequences need 256 MiB
+    small = lib.msa_decode_workspace_size(ctypes.byref(g), 64, 16, 1)
+    assert 0 < small <= limit
+    big = lib.msa_decode_workspace_size(ctypes.byref(g), 8192, 16, 1)
+    assert big > limit
+    c = _cache(num_seqs=8192)
+    assert lib.msa_sparse_attn_decode_static(ctypes.byref(g), ctypes.byref(c), FAKE, FAKE, 16,
+                                             0.0, 1, FAKE, None, None) == WS_SMALL
+    assert b"static scratch" in lib.msa_last_error()
+    c = _cache(num_seqs=8)
+    assert lib.msa_sparse_attn_decode_static(ctypes.byref(g), ctypes.byref(c), None, FAKE, 16,
+                                             0.0, 0, FAKE, None, None) == INVALID
+    assert lib.msa_sparse_attn_decode_static(ctypes.byref(g), ctypes.byref(c), FAKE, FAKE, 0,
+                                             0.0, 0, FAKE, None, None) == INVALID
+    assert lib.msa_sparse_attn_decode_static(ctypes.byref(_geom(head_dim=96)), ctypes.byref(c),
+                                             FAKE, FAKE, 16, 0.0, 0, FAKE, None,
+                                             None) == UNSUPPORTED
