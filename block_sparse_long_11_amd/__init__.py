@@ -99,6 +99,15 @@ EXPORTS = {
         ctypes.POINTER(_Geom), ctypes.POINTER(_Cache), ctypes.c_int32, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p,
         ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "msa_index_scores_prefill_tokens": (ctypes.c_int, [
+        ctypes.POINTER(_Geom), ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p]),
+    "msa_prefill_tokens_workspace_size": (ctypes.c_size_t, [
+        ctypes.POINTER(_Geom), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
+    "msa_sparse_attn_prefill_tokens": (ctypes.c_int, [
+        ctypes.POINTER(_Geom), ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "msa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "msa_last_error": (ctypes.c_char_p, []),
     "msa_version": (ctypes.c_int32, []),
@@ -483,6 +492,74 @@ def decode_per_token(geom: Geometry, cache: Cache, tokens_per_seq, q, q_idx, top
     msa_select_topk_blocks(scores, topk, ids, stream)
     msa_sparse_attn_decode_per_token(geom, cache, tokens_per_seq, q, ids, topk, out, ws, lse,
                                      num_splits, softmax_scale, stream)
+    return dict(scores=scores, ids=ids, out=out, lse=lse)
+
+
+def msa_index_scores_prefill_tokens(geom: Geometry, cache: Cache, batch: Batch, q_idx, scores,
+                                    stream=None):
+    """Per-token prefill indexer: q_idx [total_q][H_i][D_i] -> scores
+    [total_q][n_sel][max_blocks], one row per new token."""
+    cache.check(geom)
+    dev = cache.block_table.device
+    _need(q_idx, "q_idx", geom.torch_dtype, 3, dev)
+    _need(scores, "scores", torch.float32, 3, dev)
+    if tuple(q_idx.shape) != (batch.total_q, geom.num_idx_heads, geom.idx_head_dim):
+        raise ValueError(f"q_idx must be [{batch.total_q}][H_i][D_i]")
+    if tuple(scores.shape) != (batch.total_q, geom.num_sel_groups, cache.max_blocks):
+        raise ValueError(f"scores must be [{batch.total_q}][n_sel][{cache.max_blocks}]")
+    g, c, b = geom.c(), cache.c(), batch.c()
+    _check(lib().msa_index_scores_prefill_tokens(ctypes.byref(g), ctypes.byref(c),
+                                                 ctypes.byref(b), _ptr(q_idx), _ptr(scores),
+                                                 _stream(stream)))
+
+
+def msa_prefill_tokens_workspace_size(geom: Geometry, total_units, total_q, topk):
+    g = geom.c()
+    return int(lib().msa_prefill_tokens_workspace_size(ctypes.byref(g), total_units, total_q,
+                                                       topk))
+
+
+def msa_sparse_attn_prefill_tokens(geom: Geometry, cache: Cache, batch: Batch, q, ids, topk, out,
+                                   workspace, lse=None, softmax_scale=0.0, stream=None):
+    """Per-token prefill attention: ids [total_q][n_sel][topk], one list per row."""
+    cache.check(geom)
+    dev = cache.block_table.device
+    _need(q, "q", geom.torch_dtype, 3, dev)
+    _need(out, "out", geom.torch_dtype, 3, dev)
+    _need(ids, "ids", torch.int32, 3, dev)
+    shape = (batch.total_q, geom.num_q_heads, geom.head_dim)
+    if tuple(q.shape) != shape or tuple(out.shape) != shape:
+        raise ValueError(f"q and out must be {shape}")
+    if tuple(ids.shape) != (batch.total_q, geom.num_sel_groups, topk):
+        raise ValueError("ids must be [total_q][n_sel][topk]")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+        if tuple(lse.shape) != shape[:2]:
+            raise ValueError("lse must be [total_q][H_q]")
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1, dev)
+    g, c, b = geom.c(), cache.c(), batch.c()
+    _check(lib().msa_sparse_attn_prefill_tokens(
+        ctypes.byref(g), ctypes.byref(c), ctypes.byref(b), _ptr(q), _ptr(ids), topk,
+        float(softmax_scale), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def prefill_tokens(geom: Geometry, cache: Cache, batch: Batch, q, q_idx, topk, softmax_scale=0.0,
+                   stream=None):
+    """Index, select and attend a prefill batch with one selection per new token."""
+    dev = q.device
+    Q = batch.total_q
+    scores = torch.empty((Q, geom.num_sel_groups, cache.max_blocks), dtype=torch.float32,
+                         device=dev)
+    ids = torch.empty((Q, geom.num_sel_groups, topk), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    ws = workspace(msa_prefill_tokens_workspace_size(geom, batch.total_units, Q, topk), dev)
+    msa_index_scores_prefill_tokens(geom, cache, batch, q_idx, scores, stream)
+    msa_select_topk_blocks(scores, topk, ids, stream)
+    msa_sparse_attn_prefill_tokens(geom, cache, batch, q, ids, topk, out, ws, lse, softmax_scale,
+                                   stream)
     return dict(scores=scores, ids=ids, out=out, lse=lse)
 
 

@@ -50,7 +50,8 @@ namespace msa {
 
 hipError_t launch_attn_f32(const Geom &g, const msa_cache_t &c, const msa_unit_t *units,
                            int num_units, int T, const void *q, const int32_t *ids, int topk,
-                           float scale, void *out, float *lse, hipStream_t st);
+                           float scale, void *out, float *lse, hipStream_t st,
+                           bool per_token = false);
 
 namespace {
 

@@ -115,6 +115,25 @@ __device__ __forceinline__ void load_lds16(uint32_t lds, const void *gbase, uint
 template <int V>
 using ic = std::integral_constant<int, V>;
 
+}  // namespace
+
+// Per-query-token prefill (each token row keeps its own blocks): for every (unit,
+// group) the union of its rows' kept ids, ascending, and for each union entry
+// four 32-bit row masks (bit n of word w: tile row 32 w + n keeps the block).
+// Entry lists of unit u, group g start at base(): the same extent as the rows'
+// own id lists, which bound the union's size.
+struct TokenUnion {
+  const int32_t *count;     // [U][n_sel] union sizes
+  const int32_t *ids;       // union ids
+  const uint32_t *masks;    // [entry][4]
+  __device__ __forceinline__ size_t base(const msa_unit_t &un, int nsel, int g,
+                                         int topk) const {
+    return (static_cast<size_t>(un.row0) * nsel + static_cast<size_t>(g) * un.num_rows) * topk;
+  }
+};
+
+namespace {
+
 // Output of one query row and head from O^T (lane half a holds d = 32 dt + 8 i4 +
 // 4 a .. +3), the row sum and the reference maximum. A row without any visible
 // key (sum 0) gets out = 0 and lse = -inf.
@@ -140,14 +159,14 @@ __device__ __forceinline__ void store_row(uint16_t *__restrict__ out, float *__r
         sum > 0.f ? (m_ref + __builtin_log2f(sum)) * kLn2 : neg_inf();
 }
 
-template <int D>
+template <int D, bool PT>
 __global__ __launch_bounds__(kPrefWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vtc, const int32_t *__restrict__ block_table,
     const msa_unit_t *__restrict__ units, const int32_t *__restrict__ ids, int topk,
     int max_blocks, int Hq, int Hkv, int nsel, int num_uj, int pairs, float c,
-    uint16_t *__restrict__ out, float *__restrict__ lse) {
+    TokenUnion tu, uint16_t *__restrict__ out, float *__restrict__ lse) {
   constexpr int NW = kPrefWaves;
   constexpr int KS = D / 16;              // 16-wide d steps of S^T
   constexpr int DT = D / 32;              // 32-row d tiles of O^T
@@ -184,7 +203,9 @@ void attn_prefill_bf16_kernel(
   const msa_unit_t un = units[u];
   const int G = Hq / Hkv;
   const int g = (nsel == Hkv) ? j : 0;
-  const int32_t *sel = ids + (static_cast<size_t>(u) * nsel + g) * topk;
+  // per token: the union of the unit's rows' lists (ascending) and its row masks
+  const size_t ubase = PT ? tu.base(un, nsel, g, topk) : 0;
+  const int32_t *sel = PT ? tu.ids + ubase : ids + (static_cast<size_t>(u) * nsel + g) * topk;
   const int32_t *bt = block_table + static_cast<size_t>(un.r) * max_blocks;
 
   const int t = threadIdx.x, lane = t % kWave;
@@ -208,7 +229,10 @@ void attn_prefill_bf16_kernel(
   // logical id; bit p of late marks the positions whose block reaches the unit's
   // first query (id >= tau) and so takes the causal test.
   int nk = 0;
-  while (nk < topk && sel[nk] >= 0) ++nk;
+  if constexpr (PT)
+    nk = tu.count[static_cast<size_t>(u) * nsel + g];
+  else
+    while (nk < topk && sel[nk] >= 0) ++nk;
   if (nk == 0) {                          // nothing kept: no visible key
     if (active && row_ok) {
       f32x16 z[DT];
@@ -233,13 +257,18 @@ void attn_prefill_bf16_kernel(
   // Same positions, for the causal test: lane p of logical holds the id, bit p
   // of late is set when that block reaches the unit's first query (id >= tau).
   // Loaded up front for the first 64 positions, so the loop reloads only past 64.
+  // Per token, lane p of keepw also holds the row-mask word of this wave's 32
+  // rows for that position (bit n: row 32 slab + n keeps the block).
   int late_chunk = -1, logical = 0;
   uint64_t late = 0;
+  uint32_t keepw = 0;
   auto late_at = [&](int p) __attribute__((always_inline)) {
     if ((p >> 6) != late_chunk) {
       late_chunk = p >> 6;
       const int pl = 64 * late_chunk + lane;
-      logical = pl < nk ? sel[pl == 0 ? nk - 1 : pl - 1] : 0;
+      const int ix = pl == 0 ? nk - 1 : pl - 1;
+      logical = pl < nk ? sel[ix] : 0;
+      if constexpr (PT) keepw = pl < nk ? tu.masks[(ubase + ix) * 4 + slab] : 0u;
       late = __ballot(pl < nk && logical >= un.tau);
     }
     return ((late >> (p & 63)) & 1) != 0;
@@ -335,7 +364,10 @@ void attn_prefill_bf16_kernel(
   auto softmax = [&](auto mask_tag, int kt, int bp) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     bool do_mask = MASK;
-    if constexpr (!MASK) do_mask = late_at(bp);
+    if constexpr (!MASK || PT) {
+      const bool lt = late_at(bp);
+      if constexpr (!MASK) do_mask = lt;
+    }
     if (do_mask) {
       const int b = MASK ? first_b : __builtin_amdgcn_readlane(logical, bp & 63);
       const int lim = qpos - b * kBlk - kt * 32;   // tile keys with offset > lim are masked
@@ -352,6 +384,14 @@ void attn_prefill_bf16_kernel(
                                                         false, false);
       x = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * c;
     }
+    // per token: a row that does not keep this block sees none of its keys (its
+    // maximum ignores the tile, its probabilities are exp2(-inf) = 0)
+    float msub = 0.f;
+    if constexpr (PT) {
+      const bool keep = ((__builtin_amdgcn_readlane(keepw, bp & 63) >> n) & 1u) != 0;
+      x = keep ? x : neg_inf();
+      msub = keep ? 0.f : pos_inf();
+    }
     const bool need = x > m_ref + kSlack;
     if (__any(need)) {
       const float nm = need ? x : m_ref;
@@ -361,13 +401,14 @@ void attn_prefill_bf16_kernel(
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
     }
+    const float mr = PT ? m_ref + msub : m_ref;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t w[4];
 #pragma unroll
       for (int jj = 0; jj < 8; jj += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj], c, -m_ref));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj + 1], c, -m_ref));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj], c, -mr));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj + 1], c, -mr));
         w[jj / 2] = cvt_pk_bf16(p0, p1);
         l_run += p0 + p1;
       }
@@ -444,7 +485,7 @@ void attn_prefill_bf16_kernel(
 }
 
 // FP8 K/V: same tiles as attn_prefill_bf16_kernel, staged through registers.
-template <int D>
+template <int D, bool PT>
 __global__ __launch_bounds__(kPrefWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_fp8_kernel(
     const uint16_t *__restrict__ q, const uint8_t *__restrict__ kc8,
@@ -452,7 +493,7 @@ void attn_prefill_fp8_kernel(
     const uint8_t *__restrict__ vsc, const int32_t *__restrict__ block_table,
     const msa_unit_t *__restrict__ units, const int32_t *__restrict__ ids, int topk,
     int max_blocks, int Hq, int Hkv, int nsel, int num_uj, int pairs, float c,
-    uint16_t *__restrict__ out, float *__restrict__ lse) {
+    TokenUnion tu, uint16_t *__restrict__ out, float *__restrict__ lse) {
   constexpr int NW = kPrefWaves;
   constexpr int NT = NW * kWave;          // threads
   constexpr int KS = D / 16;
@@ -479,7 +520,8 @@ void attn_prefill_fp8_kernel(
   const msa_unit_t un = units[u];
   const int G = Hq / Hkv;
   const int g = (nsel == Hkv) ? j : 0;
-  const int32_t *sel = ids + (static_cast<size_t>(u) * nsel + g) * topk;
+  const size_t ubase = PT ? tu.base(un, nsel, g, topk) : 0;
+  const int32_t *sel = PT ? tu.ids + ubase : ids + (static_cast<size_t>(u) * nsel + g) * topk;
   const int32_t *bt = block_table + static_cast<size_t>(un.r) * max_blocks;
 
   const int t = threadIdx.x, lane = t % kWave;
@@ -495,7 +537,10 @@ void attn_prefill_fp8_kernel(
   const int qpos = row_ok ? un.pos0 + row_in_tile : 0x7fffffff;
 
   int nk = 0;
-  while (nk < topk && sel[nk] >= 0) ++nk;
+  if constexpr (PT)
+    nk = tu.count[static_cast<size_t>(u) * nsel + g];
+  else
+    while (nk < topk && sel[nk] >= 0) ++nk;
   if (nk == 0) {                          // nothing kept: no visible key
     if (active && row_ok) {
       f32x16 z[DT];
@@ -508,7 +553,8 @@ void attn_prefill_fp8_kernel(
   const int NH = 2 * nk;                  // half-blocks, the last kept id's first
   // logical id at position p (the last kept id first); a block past tau holds
   // only future keys and is read from the diagonal's physical block, masked
-  auto id_of = [&](int p) { return sel[p == 0 ? nk - 1 : p - 1]; };
+  auto ix_of = [&](int p) { return p == 0 ? nk - 1 : p - 1; };
+  auto id_of = [&](int p) { return sel[ix_of(p)]; };
   auto phys_of = [&](int p) { return bt[min(id_of(p), un.tau)]; };
 
   bf16x8 qf[KS];
@@ -596,6 +642,9 @@ void attn_prefill_fp8_kernel(
     // the causal test, for a block that reaches the unit's first query
     const int blk_id = id_of(hb >> 1);
     const bool late = blk_id >= un.tau;
+    // per token: whether this lane's row keeps the block
+    bool keep = true;
+    if constexpr (PT) keep = ((tu.masks[(ubase + ix_of(hb >> 1)) * 4 + slab] >> n) & 1u) != 0;
 #pragma unroll
     for (int kt2 = 0; kt2 < 2; ++kt2) {
       bf16x8 kf[KS], vf[2 * DT], pf[2];
@@ -621,6 +670,8 @@ void attn_prefill_fp8_kernel(
                                                           false, false);
         x = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * c;
       }
+      x = keep ? x : neg_inf();
+      const float mr_add = keep ? 0.f : pos_inf();
       const bool need = x > m_ref + kSlack;
       if (__any(need)) {
         const float nm = need ? x : m_ref;
@@ -635,8 +686,8 @@ void attn_prefill_fp8_kernel(
         uint32_t w[4];
 #pragma unroll
         for (int jj = 0; jj < 8; jj += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj], c, -m_ref));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj + 1], c, -m_ref));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj], c, -(m_ref + mr_add)));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj + 1], c, -(m_ref + mr_add)));
           w[jj / 2] = cvt_pk_bf16(p0, p1);
           l_run += p0 + p1;
         }
@@ -676,8 +727,8 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vtc,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seq_lens,
     const msa_unit_t *__restrict__ units, int T, const int32_t *__restrict__ ids, int topk,
-    int max_blocks, int Hq, int Hkv, int nsel, float scale, float *__restrict__ out,
-    float *__restrict__ lse) {
+    int max_blocks, int Hq, int Hkv, int nsel, float scale, bool per_token,
+    float *__restrict__ out, float *__restrict__ lse) {
   const int u = blockIdx.x, head = blockIdx.y;
   msa_unit_t un;
   if (units != nullptr) {
@@ -690,9 +741,10 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
   if (t >= un.num_rows) return;
   const int G = Hq / Hkv, j = head / G;
   const int g = (nsel == Hkv) ? j : 0;
-  const int32_t *sel = ids + (static_cast<size_t>(u) * nsel + g) * topk;
-  const int32_t *bt = block_table + static_cast<size_t>(un.r) * max_blocks;
   const int qrow = un.row0 + t, qpos = un.pos0 + t;
+  // per token, every query row has its own list
+  const int32_t *sel = ids + (static_cast<size_t>(per_token ? qrow : u) * nsel + g) * topk;
+  const int32_t *bt = block_table + static_cast<size_t>(un.r) * max_blocks;
   float qv[D], acc[D];
   for (int d = 0; d < D; ++d) {
     qv[d] = q[(static_cast<size_t>(qrow) * Hq + head) * D + d];
@@ -727,7 +779,8 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
 
 hipError_t launch_attn_f32(const Geom &g, const msa_cache_t &c, const msa_unit_t *units,
                            int num_units, int T, const void *q, const int32_t *ids, int topk,
-                           float scale, void *out, float *lse, hipStream_t st) {
+                           float scale, void *out, float *lse, hipStream_t st,
+                           bool per_token) {
   const dim3 grid(num_units, g.Hq);
   const float *qf = static_cast<const float *>(q);
   const float *kf = static_cast<const float *>(c.k_cache);
@@ -735,20 +788,144 @@ hipError_t launch_attn_f32(const Geom &g, const msa_cache_t &c, const msa_unit_t
   if (g.D == 64)
     attn_f32_kernel<64><<<grid, 128, 0, st>>>(qf, kf, vf, c.block_table, c.seq_lens, units,
                                               T, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
-                                              g.nsel, scale, static_cast<float *>(out), lse);
+                                              g.nsel, scale, per_token, static_cast<float *>(out),
+                                              lse);
   else
     attn_f32_kernel<128><<<grid, 128, 0, st>>>(qf, kf, vf, c.block_table, c.seq_lens, units,
                                                T, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
-                                               g.nsel, scale, static_cast<float *>(out), lse);
+                                               g.nsel, scale, per_token, static_cast<float *>(out),
+                                               lse);
   return hipGetLastError();
 }
+
+// Union of the kept lists of one (unit, group) for the per-token prefill: one
+// work-group per pair. Each row's list ends at its first -1; ids outside [0, tau]
+// hold no key visible to the unit's rows and are left out. The ids set bits of an
+// LDS bitmap over [0, tau]; an exclusive scan of the words' popcounts gives every
+// block its rank, so the union comes out ascending; each kept (row, id) then ORs
+// the row's bit into the mask words of its block's entry (zeroed first).
+constexpr int kUnionThreads = 256;
+
+__global__ __launch_bounds__(kUnionThreads) void token_union_kernel(
+    const msa_unit_t *__restrict__ units, const int32_t *__restrict__ ids, int topk, int nsel,
+    TokenUnion tu, int32_t *__restrict__ count, int32_t *__restrict__ uids,
+    uint32_t *__restrict__ masks) {
+  extern __shared__ uint32_t bits[];      // [W] bitmap, then [W] exclusive prefix
+  __shared__ int nkr[kBlk];               // each row's list length
+  __shared__ int wsum[kUnionThreads / kWave];
+  const int u = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  const int lane = t % kWave, wave = t / kWave;
+  const msa_unit_t un = units[u];
+  const int n = un.num_rows, tau = un.tau;
+  const int W = tau / 32 + 1;             // words covering blocks [0, tau]
+  uint32_t *pre = bits + W;
+  const size_t base = tu.base(un, nsel, g, topk);
+  auto row_ids = [&](int i) {
+    return ids + (static_cast<size_t>(un.row0 + i) * nsel + g) * topk;
+  };
+  for (int w = t; w < W; w += kUnionThreads) bits[w] = 0u;
+  for (int i = t; i < n; i += kUnionThreads) {
+    const int32_t *r = row_ids(i);
+    int k = 0;
+    while (k < topk && r[k] >= 0) ++k;
+    nkr[i] = k;
+  }
+  __syncthreads();
+  for (int e = t; e < n * topk; e += kUnionThreads) {
+    const int i = e / topk, k = e % topk;
+    if (k >= nkr[i]) continue;
+    const int b = row_ids(i)[k];
+    if (b >= 0 && b <= tau) atomicOr(&bits[b / 32], 1u << (b % 32));
+  }
+  __syncthreads();
+  // exclusive scan of popcounts: thread t owns words [t * per, (t + 1) * per)
+  const int per = (W + kUnionThreads - 1) / kUnionThreads;
+  const int w0 = min(W, t * per), w1 = min(W, w0 + per);
+  int local = 0;
+  for (int w = w0; w < w1; ++w) local += __popc(bits[w]);
+  int x = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = x;
+  __syncthreads();
+  int before = x - local;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  int total = 0;
+  for (int w = 0; w < kUnionThreads / kWave; ++w) total += wsum[w];
+  for (int w = w0; w < w1; ++w) {
+    pre[w] = before;
+    uint32_t m = bits[w];
+    while (m != 0u) {
+      const int bit = __ffs(m) - 1;
+      uids[base + before++] = w * 32 + bit;
+      m &= m - 1u;
+    }
+  }
+  for (int e = t; e < total * 4; e += kUnionThreads) masks[base * 4 + e] = 0u;
+  if (t == 0) count[static_cast<size_t>(u) * nsel + g] = total;
+  __threadfence();                        // the zeros reach L2 before the ORs below
+  __syncthreads();
+  for (int e = t; e < n * topk; e += kUnionThreads) {
+    const int i = e / topk, k = e % topk;
+    if (k >= nkr[i]) continue;
+    const int b = row_ids(i)[k];
+    if (b < 0 || b > tau) continue;
+    const int pos = pre[b / 32] + __popc(bits[b / 32] & ((1u << (b % 32)) - 1u));
+    atomicOr(&masks[(base + pos) * 4 + i / 32], 1u << (i % 32));
+  }
+}
+
+size_t tokens_workspace_bytes(const Geom &g, int total_units, int total_q, int topk) {
+  if (!g.bf16) return 0;
+  auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const size_t entries = static_cast<size_t>(total_q) * g.nsel * topk;
+  return al(static_cast<size_t>(total_units) * g.nsel * 4) + al(entries * 4) + al(entries * 16);
+}
+
+template <bool PT>
+hipError_t launch_prefill_attention(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
+                                    const void *q, const int32_t *ids, int topk, float scale,
+                                    void *workspace, void *out, float *lse, hipStream_t st);
 
 hipError_t launch_attn_prefill(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                const void *q, const int32_t *ids, int topk, float scale,
                                void *out, float *lse, hipStream_t st) {
+  return launch_prefill_attention<false>(g, c, b, q, ids, topk, scale, nullptr, out, lse, st);
+}
+
+hipError_t launch_attn_prefill_tokens(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
+                                      const void *q, const int32_t *ids, int topk, float scale,
+                                      void *workspace, void *out, float *lse, hipStream_t st) {
+  return launch_prefill_attention<true>(g, c, b, q, ids, topk, scale, workspace, out, lse, st);
+}
+
+template <bool PT>
+hipError_t launch_prefill_attention(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
+                                    const void *q, const int32_t *ids, int topk, float scale,
+                                    void *workspace, void *out, float *lse, hipStream_t st) {
   if (b.total_units == 0) return hipSuccess;
   if (!g.bf16)
-    return launch_attn_f32(g, c, b.units, b.total_units, 1, q, ids, topk, scale, out, lse, st);
+    return launch_attn_f32(g, c, b.units, b.total_units, 1, q, ids, topk, scale, out, lse, st,
+                           PT);
+  TokenUnion tu{nullptr, nullptr, nullptr};
+  if constexpr (PT) {
+    auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    const size_t entries = static_cast<size_t>(b.total_q) * g.nsel * topk;
+    char *ws = static_cast<char *>(workspace);
+    int32_t *cnt = reinterpret_cast<int32_t *>(ws);
+    int32_t *uids = reinterpret_cast<int32_t *>(ws + al(static_cast<size_t>(b.total_units) *
+                                                         g.nsel * 4));
+    uint32_t *msk = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(uids) +
+                                                 al(entries * 4));
+    tu = TokenUnion{cnt, uids, msk};
+    const int W = c.max_blocks_per_seq / 32 + 1;   // bitmap words for any tau of the table
+    token_union_kernel<<<dim3(b.total_units, g.nsel), kUnionThreads,
+                         2 * W * sizeof(uint32_t), st>>>(b.units, ids, topk, g.nsel, tu, cnt,
+                                                         uids, msk);
+  }
   constexpr int NW = kPrefWaves;
   const int pairs = (g.G() + NW / 4 - 1) / (NW / 4);   // work-groups per (unit, KV head)
   const int num_uj = b.total_units * g.Hkv;
@@ -763,23 +940,23 @@ hipError_t launch_attn_prefill(const Geom &g, const msa_cache_t &c, const msa_ba
     const uint8_t *k8 = static_cast<const uint8_t *>(c.k_cache);
     const uint8_t *v8 = static_cast<const uint8_t *>(c.v_cache);
     if (g.D == 64)
-      attn_prefill_fp8_kernel<64><<<grid, NW * 64, 0, st>>>(
+      attn_prefill_fp8_kernel<64, PT><<<grid, NW * 64, 0, st>>>(
           qb, k8, v8, c.k_scale, c.v_scale, c.block_table, b.units, ids, topk,
-          c.max_blocks_per_seq, g.Hq, g.Hkv, g.nsel, num_uj, pairs, sl2, ob, lse);
+          c.max_blocks_per_seq, g.Hq, g.Hkv, g.nsel, num_uj, pairs, sl2, tu, ob, lse);
     else
-      attn_prefill_fp8_kernel<128><<<grid, NW * 64, 0, st>>>(
+      attn_prefill_fp8_kernel<128, PT><<<grid, NW * 64, 0, st>>>(
           qb, k8, v8, c.k_scale, c.v_scale, c.block_table, b.units, ids, topk,
-          c.max_blocks_per_seq, g.Hq, g.Hkv, g.nsel, num_uj, pairs, sl2, ob, lse);
+          c.max_blocks_per_seq, g.Hq, g.Hkv, g.nsel, num_uj, pairs, sl2, tu, ob, lse);
     return hipGetLastError();
   }
   if (g.D == 64)
-    attn_prefill_bf16_kernel<64><<<grid, NW * 64, 0, st>>>(
+    attn_prefill_bf16_kernel<64, PT><<<grid, NW * 64, 0, st>>>(
         qb, kb, vb, c.block_table, b.units, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
-        g.nsel, num_uj, pairs, sl2, ob, lse);
+        g.nsel, num_uj, pairs, sl2, tu, ob, lse);
   else
-    attn_prefill_bf16_kernel<128><<<grid, NW * 64, 0, st>>>(
+    attn_prefill_bf16_kernel<128, PT><<<grid, NW * 64, 0, st>>>(
         qb, kb, vb, c.block_table, b.units, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
-        g.nsel, num_uj, pairs, sl2, ob, lse);
+        g.nsel, num_uj, pairs, sl2, tu, ob, lse);
   return hipGetLastError();
 }
 

@@ -352,13 +352,67 @@ __global__ __launch_bounds__(256) void index_decode_fp8_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// work order of the prefill indexers
+// ---------------------------------------------------------------------------
+//
+// [feat] method list "Pre-scheduled tile chunking"; [blog] shaam.blog "Serving AI
+// agents at scale", section "What makes MiniMax M3 different": KV outer, each key
+// block read once. An item is (x, block chunk y, selection group z), x a tile
+// pair (group width <= 128) or a tile (wider groups). Work-group ids are dealt
+// to the 8 XCDs round-robin (id % 8), each XCD with its own L2. Every XCD owns a
+// fixed set of (z, y) combos: with Z dividing 8, one group and every (8 / Z)-th
+// chunk, taken in boustrophedon order (class c, then 8/Z - 1 - c, ...) so that
+// the causal work, heavier in early chunks, evens out between XCDs; with Z a
+// multiple of 8, Z / 8 groups and every chunk. An XCD runs its items in x-blocks
+// of XB: for each x-block, each of its combos in turn, and inside a combo the XB
+// consecutive x. The work-groups resident on one XCD then read one key chunk
+// (fetched into that L2 once for the whole x-block) and, combo after combo, the
+// same query rows. Items past the end (x >= X, y >= Y) do nothing.
+struct ItemOrder {
+  int X;      // x items
+  int Y;      // block chunks
+  int Z;      // selection groups
+  int XB;     // x per x-block
+  int CPX;    // combos per XCD
+
+  static ItemOrder make(int X, int Y, int Z, int XB) {
+    int cpx;
+    if (8 % Z == 0) cpx = (Y + 8 / Z - 1) / (8 / Z);
+    else if (Z % 8 == 0) cpx = (Z / 8) * Y;
+    else cpx = (Y * Z + 7) / 8;
+    return ItemOrder{X, Y, Z, XB, cpx};
+  }
+  int64_t grid() const {
+    return int64_t{8} * ((X + XB - 1) / XB) * XB * CPX;
+  }
+  __device__ __forceinline__ bool item(int L, int &x, int &y, int &z) const {
+    const int xcd = L % 8, k = L / 8;
+    const int xi = k % XB, cc = (k / XB) % CPX, xb = k / (XB * CPX);
+    x = xb * XB + xi;
+    if (8 % Z == 0) {
+      const int nc = 8 / Z, cls = xcd / Z;
+      z = xcd % Z;
+      y = cc * nc + ((cc & 1) ? nc - 1 - cls : cls);
+    } else if (Z % 8 == 0) {
+      z = (cc / Y) * 8 + xcd;
+      y = cc % Y;
+    } else {
+      const int c = cc * 8 + ((cc & 1) ? 7 - xcd : xcd);
+      y = c / Z;
+      z = c % Z;
+    }
+    return x < X && y < Y && z < Z;
+  }
+};
+
+// ---------------------------------------------------------------------------
 // prefill, bf16, group width 256 or 512 (one selection group over all indexer
 // heads): MFMA 32x32x16 on LDS-staged keys, 128 channels at a time
 // ---------------------------------------------------------------------------
 //
 // A work-group of 4 waves scores one query tile (wave w: rows 32w .. 32w+31, the
 // A operand, the whole group width in registers) against a chunk of kChunkW
-// candidate blocks. A block's group keys (128 keys x GD channels) do not fit
+// candidate blocks, in the XCD-aware order of ItemOrder. A block's group keys (128 keys x GD channels) do not fit
 // twice in LDS, so they are staged 128 channels (32 KiB) at a time by direct
 // global->LDS loads, double-buffered across (block, channel chunk) stages, with
 // the same 16-byte swizzle as the narrow kernel; the four 32-key accumulators of
@@ -372,13 +426,13 @@ constexpr int kChunkW = 16;   // blocks per work-group
 // outside the MFMA chains); bf16 keys run one, as two spill more. Measured inside
 // the whole step of the 32k prefill with one group, same GPU: FP8 654 -> 566 us
 // with two waves, bf16 794 -> 831 us.
-template <int DI, int HS, bool FP8>
+template <int DI, int HS, bool FP8, bool PT>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(FP8 || HS * DI <= 256 ? 2 : 1, FP8 || HS * DI <= 256 ? 2 : 1)))
 void index_prefill_wide_kernel(
     const uint16_t *__restrict__ q_idx, const void *__restrict__ k_idx_,
     const uint8_t *__restrict__ k_scale, const int32_t *__restrict__ block_table,
-    const msa_unit_t *__restrict__ units, int max_blocks, int nsel,
+    const msa_unit_t *__restrict__ units, int max_blocks, int nsel, ItemOrder order,
     float *__restrict__ scores) {
   constexpr int GD = HS * DI;          // group width
   constexpr int KS = GD / 16;          // k steps of the whole group
@@ -401,15 +455,25 @@ void index_prefill_wide_kernel(
   // FP8 row swizzle: keys sharing a 256-byte bank row get distinct chunk slots
   auto swz = [](int key) { return FP8 ? (key / (16 / CHG)) % CHG : key % CHG; };
 
-  const int u = blockIdx.x, g = blockIdx.z;
+  int u, y, g;                           // item: tile u, block chunk y, group g
+  if (!order.item(static_cast<int>(blockIdx.x), u, y, g)) return;
   const msa_unit_t un = units[u];
   const int Hi = nsel * HS;
-  const int b0 = blockIdx.y * kChunkW;
+  const int b0 = y * kChunkW;
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   float *out = scores + (static_cast<size_t>(u) * nsel + g) * max_blocks;
-  for (int i = t; i < kChunkW; i += 256) {
-    const int b = b0 + i;
-    if (b >= un.tau && b < max_blocks) out[b] = (b == un.tau) ? pos_inf() : neg_inf();
+  if constexpr (PT) {     // every row's entries at and after the diagonal
+    for (int e = t; e < kBlk * kChunkW; e += 256) {
+      const int i = e / kChunkW, b = b0 + e % kChunkW;
+      if (i < un.num_rows && b >= un.tau && b < max_blocks)
+        scores[(static_cast<size_t>(un.row0 + i) * nsel + g) * max_blocks + b] =
+            (b == un.tau) ? pos_inf() : neg_inf();
+    }
+  } else {
+    for (int i = t; i < kChunkW; i += 256) {
+      const int b = b0 + i;
+      if (b >= un.tau && b < max_blocks) out[b] = (b == un.tau) ? pos_inf() : neg_inf();
+    }
   }
   if (b0 >= un.tau) return;
   const int nblk = min(kChunkW, un.tau - b0);
@@ -489,20 +553,31 @@ void index_prefill_wide_kernel(
               o[2 * i + 1] = __builtin_bit_cast(
                   uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, true));
             }
-            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                qf[cc * KSC + 2 * k2], as_bf16x8(uint4{o[0], o[1], o[2], o[3]}), acc[nt], 0,
-                0, 0);
-            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                qf[cc * KSC + 2 * k2 + 1], as_bf16x8(uint4{o[4], o[5], o[6], o[7]}), acc[nt],
-                0, 0, 0);
+            const bf16x8 k0 = as_bf16x8(uint4{o[0], o[1], o[2], o[3]});
+            const bf16x8 k1 = as_bf16x8(uint4{o[4], o[5], o[6], o[7]});
+            if constexpr (PT) {   // keys x queries: a lane holds one query and 16 keys
+              acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[cc * KSC + 2 * k2],
+                                                                acc[nt], 0, 0, 0);
+              acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[cc * KSC + 2 * k2 + 1],
+                                                                acc[nt], 0, 0, 0);
+            } else {
+              acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[cc * KSC + 2 * k2], k0,
+                                                                acc[nt], 0, 0, 0);
+              acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[cc * KSC + 2 * k2 + 1], k1,
+                                                                acc[nt], 0, 0, 0);
+            }
           }
         } else {
 #pragma unroll
           for (int ks = 0; ks < KSC; ++ks) {
             const bf16x8 kf =
                 __builtin_bit_cast(bf16x8, src[key * CHG + ((2 * ks + lane / 32) ^ swz(key))]);
-            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[cc * KSC + ks], kf, acc[nt],
-                                                              0, 0, 0);
+            if constexpr (PT)
+              acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cc * KSC + ks], acc[nt],
+                                                                0, 0, 0);
+            else
+              acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[cc * KSC + ks], kf, acc[nt],
+                                                                0, 0, 0);
           }
         }
       }
@@ -512,9 +587,20 @@ void index_prefill_wide_kernel(
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[nt][i]);
-    m = group_max<kWave>(m);
-    if (lane == 0) red[wave][bi] = m;
+    if constexpr (PT) {
+      // the two lane halves hold the same query's other 16 keys of each tile
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                       false, false);
+      m = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const int rit = wave * 32 + lane;
+      if (lane < 32 && rit < un.num_rows)
+        scores[(static_cast<size_t>(un.row0 + rit) * nsel + g) * max_blocks + b0 + bi] = m;
+    } else {
+      m = group_max<kWave>(m);
+      if (lane == 0) red[wave][bi] = m;
+    }
   }
+  if constexpr (PT) return;
   __syncthreads();
   if (t < nblk)
     out[b0 + t] = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
@@ -524,13 +610,10 @@ void index_prefill_wide_kernel(
 // prefill, bf16, group width <= 128: MFMA 32x32x16 on LDS-staged keys
 // ---------------------------------------------------------------------------
 //
-// A work-group handles up to kTiles adjacent query tiles of one request (128
-// query rows each) and one selection group, over a chunk of kChunk2 candidate
-// blocks. Tiles are grouped inside a request: a unit whose tau is a multiple of
-// kTiles, or that opens its request, leads; it takes the following units of the
-// same request until the next leader. Work-group ids visit the even units first
-// (block ids are spread over the XCDs round-robin, and the leaders are normally
-// the even units, so this keeps every XCD busy). Each block's group keys (128
+// A work-group handles two adjacent query tiles of one request (units 2x and
+// 2x + 1 of the plan, 128 query rows each; a pair split by a request boundary
+// is done as two passes of one tile) and one selection group, over a chunk of
+// kChunk2 candidate blocks, in the XCD-aware order of ItemOrder. Each block's group keys (128
 // keys x GD, the group's indexer heads side by side) are staged in LDS by direct
 // global->LDS loads, 16-byte chunks XOR-swizzled by key, double-buffered so the
 // next block is in flight while this one is scored; one staged block serves every
@@ -555,14 +638,19 @@ constexpr int kChunk2 = 32;   // blocks per work-group (16: 1-3% slower, 64: slo
 // Query tiles per work-group: two (256 query rows, 4 waves, two work-groups per CU).
 constexpr int kTiles = 2;
 constexpr int kIdxThreads = kTiles * 2 * kWave;
+// x-block sizes of ItemOrder: 32 tile pairs (their query rows of one group, 2 MiB
+// at 128 channels, and the current 1 MiB key chunk fit one XCD's 4 MB L2); 16
+// tiles for the wide kernel (512 channels: 2 MiB of query rows, 2 MiB chunks)
+constexpr int kPairBlock = 32;
+constexpr int kTileBlock = 16;
 
-template <int DI, int HS, bool FP8>
+template <int DI, int HS, bool FP8, bool PT>
 __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void index_prefill_bf16_kernel(
     const uint16_t *__restrict__ q_idx, const void *__restrict__ k_idx_,
     const uint8_t *__restrict__ k_scale, const int32_t *__restrict__ block_table,
     const msa_unit_t *__restrict__ units, int num_units, int max_blocks, int nsel,
-    float *__restrict__ scores) {
+    ItemOrder order, float *__restrict__ scores) {
   constexpr int GD = HS * DI;            // group width
   constexpr int KS = GD / 16;            // k steps
   constexpr int CHG = FP8 ? GD / 16 : GD / 8;   // 16-byte chunks per staged key row
@@ -581,31 +669,46 @@ void index_prefill_bf16_kernel(
   // FP8 row swizzle: keys sharing a 256-byte bank row get distinct chunk slots
   auto swz = [](int key) { return FP8 ? (key / (16 / CHG)) % CHG : key % CHG; };
 
-  const int half = (num_units + 1) / 2;
-  const int u0 = 2 * (static_cast<int>(blockIdx.x) % half) + static_cast<int>(blockIdx.x) / half;
-  if (u0 >= num_units) return;
-  const int g = blockIdx.z;
-  const msa_unit_t un0 = units[u0];
-  const bool first = (u0 == 0) || (units[u0 - 1].r != un0.r);
-  if ((un0.tau % kTiles) != 0 && !first) return;          // taken by its leader
-  int ntile = 1;
-  while (ntile < kTiles && u0 + ntile < num_units && units[u0 + ntile].r == un0.r &&
-         (units[u0 + ntile].tau % kTiles) != 0)
-    ++ntile;
+  // item: tile pair x (units 2x and 2x + 1), block chunk y, selection group g
+  int x, y, g;
+  if (!order.item(static_cast<int>(blockIdx.x), x, y, g)) return;
+  const int u_first = 2 * x;
+  if (u_first >= num_units) return;
+  // units of one request go together; a pair split by a request boundary is two
+  // passes of one tile each
+  const bool paired =
+      u_first + 1 < num_units && units[u_first + 1].r == units[u_first].r;
+  const int npass = (!paired && u_first + 1 < num_units) ? 2 : 1;
   const int Hi = nsel * HS;
-  const int tau_max = units[u0 + ntile - 1].tau;
-  const int b0 = blockIdx.y * kChunk2;
+  const int b0 = y * kChunk2;
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+  for (int pass = 0; pass < npass; ++pass) {
+  if (pass > 0) __syncthreads();          // the previous pass is done with LDS
+  const int u0 = u_first + pass;
+  const int ntile = paired ? kTiles : 1;
+  const msa_unit_t un0 = units[u0];
+  const int tau_max = units[u0 + ntile - 1].tau;
 
-  // the +inf / -inf entries of every tile inside this chunk
-  for (int e = t; e < ntile * kChunk2; e += kIdxThreads) {
-    const int tt = e / kChunk2, b = b0 + e % kChunk2;
-    const int tau = units[u0 + tt].tau;
-    if (b >= tau && b < max_blocks)
-      scores[(static_cast<size_t>(u0 + tt) * nsel + g) * max_blocks + b] =
-          (b == tau) ? pos_inf() : neg_inf();
+  // the +inf / -inf entries of every tile inside this chunk (per token: of every
+  // row of the tile; consecutive threads take consecutive blocks of one row)
+  if constexpr (PT) {
+    for (int e = t; e < ntile * kBlk * kChunk2; e += kIdxThreads) {
+      const int tt = e / (kBlk * kChunk2), i = (e / kChunk2) % kBlk, b = b0 + e % kChunk2;
+      const msa_unit_t ut = units[u0 + tt];
+      if (i < ut.num_rows && b >= ut.tau && b < max_blocks)
+        scores[(static_cast<size_t>(ut.row0 + i) * nsel + g) * max_blocks + b] =
+            (b == ut.tau) ? pos_inf() : neg_inf();
+    }
+  } else {
+    for (int e = t; e < ntile * kChunk2; e += kIdxThreads) {
+      const int tt = e / kChunk2, b = b0 + e % kChunk2;
+      const int tau = units[u0 + tt].tau;
+      if (b >= tau && b < max_blocks)
+        scores[(static_cast<size_t>(u0 + tt) * nsel + g) * max_blocks + b] =
+            (b == tau) ? pos_inf() : neg_inf();
+    }
   }
-  if (b0 >= tau_max) return;
+  if (b0 >= tau_max) continue;
   const int nblk = min(kChunk2, tau_max - b0);
 
   // this wave's tile and its two 32-row MFMA tiles
@@ -661,6 +764,7 @@ void index_prefill_bf16_kernel(
   auto score = [&](int bi, const u32x4 *src, const u32x4 *ssrc) __attribute__((always_inline)) {
     const int b = b0 + bi;
     float m = neg_inf();
+    float ma = neg_inf(), mb = neg_inf();   // per token: this lane's query of each row set
     if (wave_live && b < mine.tau) {
       bf16x8 kf[2][KS];
       f32x16 acc0, acc1;
@@ -692,9 +796,9 @@ void index_prefill_bf16_kernel(
                                          src[key * CHG + ((2 * ks + lane / 32) ^ swz(key))]);
         }
       };
-      auto pool = [&](const f32x16 &v) __attribute__((always_inline)) {
+      auto pool = [&](float &mm, const f32x16 &v) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) m = fmaxf(m, fmaxf(v[i], v[i + 1]));
+        for (int i = 0; i < 16; i += 2) mm = fmaxf(mm, fmaxf(v[i], v[i + 1]));
       };
       rd(0, kf[0]);
 #pragma unroll
@@ -706,15 +810,39 @@ void index_prefill_bf16_kernel(
         acc1 = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[cb][ks], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], kf[cb][ks], acc1, 0, 0, 0);
+          if constexpr (PT) {
+            // keys x queries: a lane holds one query column and 16 keys of the tile
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cb][ks], qa[ks], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cb][ks], qb[ks], acc1, 0, 0, 0);
+          } else {
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[cb][ks], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], kf[cb][ks], acc1, 0, 0, 0);
+          }
         }
-        pool(acc0);
-        pool(acc1);
+        if constexpr (PT) {
+          pool(ma, acc0);
+          pool(mb, acc1);
+        } else {
+          pool(m, acc0);
+          pool(m, acc1);
+        }
       }
     }
-    m = group_max<kWave>(m);
-    if (lane == 0) red[wave][bi] = m;
+    if constexpr (PT) {
+      // lanes 0..31 take the other half's keys of row set a, lanes 32..63 those of
+      // row set b: lane l then holds the block score of tile row 64 (wave % 2) + l
+      if (wave_live && b < mine.tau) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ma), __float_as_uint(mb),
+                                                         false, false);
+        const float v = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        const int rit = (wave % 2) * 64 + lane;
+        if (rit < mine.num_rows)
+          scores[(static_cast<size_t>(mine.row0 + rit) * nsel + g) * max_blocks + b] = v;
+      }
+    } else {
+      m = group_max<kWave>(m);
+      if (lane == 0) red[wave][bi] = m;
+    }
   };
 
   issue(b0, Kb0, Ks0);
@@ -730,14 +858,17 @@ void index_prefill_bf16_kernel(
     score(bi, Kb1, Ks1);
     if (++bi >= nblk) break;
   }
-  __syncthreads();
-  // finished rows: tile t owns blocks b < tau_t
-  for (int e = t; e < ntile * nblk; e += kIdxThreads) {
-    const int tile = e / nblk, bi = e % nblk, b = b0 + bi;
-    if (b >= units[u0 + tile].tau) continue;
-    scores[(static_cast<size_t>(u0 + tile) * nsel + g) * max_blocks + b] =
-        fmaxf(red[2 * tile][bi], red[2 * tile + 1][bi]);
+  if constexpr (!PT) {                    // per-token scores are already stored
+    __syncthreads();
+    // finished rows: tile t owns blocks b < tau_t
+    for (int e = t; e < ntile * nblk; e += kIdxThreads) {
+      const int tile = e / nblk, bi = e % nblk, b = b0 + bi;
+      if (b >= units[u0 + tile].tau) continue;
+      scores[(static_cast<size_t>(u0 + tile) * nsel + g) * max_blocks + b] =
+          fmaxf(red[2 * tile][bi], red[2 * tile + 1][bi]);
+    }
   }
+  }   // pass
 }
 
 // ---------------------------------------------------------------------------
@@ -747,12 +878,40 @@ void index_prefill_bf16_kernel(
 __global__ __launch_bounds__(128) void index_prefill_f32_kernel(
     const float *__restrict__ q_idx, const float *__restrict__ k_idx,
     const int32_t *__restrict__ block_table, const msa_unit_t *__restrict__ units,
-    int max_blocks, int nsel, int Hi, int Di, float *__restrict__ scores) {
+    int max_blocks, int nsel, int Hi, int Di, bool per_token, float *__restrict__ scores) {
   __shared__ float red[2];
   const int u = blockIdx.x, g = blockIdx.z, b = blockIdx.y;
   const msa_unit_t un = units[u];
   const int Hs = Hi / nsel;
   float *out = scores + (static_cast<size_t>(u) * nsel + g) * max_blocks;
+  if (per_token) {
+    // one row per query token: max over the block's keys only
+    auto row_out = [&](int t) {
+      return scores + (static_cast<size_t>(un.row0 + t) * nsel + g) * max_blocks;
+    };
+    if (b >= un.tau) {
+      for (int t = threadIdx.x; t < un.num_rows; t += 128)
+        row_out(t)[b] = (b == un.tau) ? pos_inf() : neg_inf();
+      return;
+    }
+    const int s = threadIdx.x;
+    const int64_t phys = block_table[static_cast<size_t>(un.r) * max_blocks + b];
+    for (int t = 0; t < un.num_rows; ++t) {
+      float acc = 0.f;
+      for (int hh = 0; hh < Hs; ++hh) {
+        const int h = g * Hs + hh;
+        const float *qv = q_idx + (static_cast<size_t>(un.row0 + t) * Hi + h) * Di;
+        const float *kv = k_idx + ((static_cast<size_t>(phys) * Hi + h) * kBlk + s) * Di;
+        for (int d = 0; d < Di; ++d) acc = fmaf(qv[d], kv[d], acc);
+      }
+      acc = group_max<kWave>(acc);
+      if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = acc;
+      __syncthreads();
+      if (threadIdx.x == 0) row_out(t)[b] = fmaxf(red[0], red[1]);
+      __syncthreads();
+    }
+    return;
+  }
   if (b >= un.tau) {
     if (threadIdx.x == 0) out[b] = (b == un.tau) ? pos_inf() : neg_inf();
     return;
@@ -850,20 +1009,24 @@ hipError_t dispatch_decode_fp8(const Geom &g, const msa_cache_t &c, int T, const
   return hipGetLastError();
 }
 
-template <int DI, bool FP8>
+template <int DI, bool FP8, bool PT>
 hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                  const void *q_idx, float *scores, hipStream_t st) {
   const uint16_t *q = static_cast<const uint16_t *>(q_idx);
   const int hs = g.Hs();
   if (hs * DI <= 128) {
-    const dim3 grid(b.total_units, (c.max_blocks_per_seq + kChunk2 - 1) / kChunk2, g.nsel);
+    const ItemOrder ord = ItemOrder::make((b.total_units + 1) / 2,
+                                          (c.max_blocks_per_seq + kChunk2 - 1) / kChunk2,
+                                          g.nsel, kPairBlock);
+    if (ord.grid() > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<unsigned>(ord.grid()));
     switch (hs) {
 #define MSA_CASE(HS)                                                                     \
   case HS:                                                                               \
     if constexpr (HS * DI <= 128)                                                        \
-      index_prefill_bf16_kernel<DI, HS, FP8><<<grid, kIdxThreads, 0, st>>>(              \
+      index_prefill_bf16_kernel<DI, HS, FP8, PT><<<grid, kIdxThreads, 0, st>>>(          \
           q, c.k_idx_cache, c.k_idx_scale, c.block_table, b.units, b.total_units,        \
-          c.max_blocks_per_seq, g.nsel, scores);                                         \
+          c.max_blocks_per_seq, g.nsel, ord, scores);                                    \
     break;
       MSA_CASE(1) MSA_CASE(2) MSA_CASE(4)
 #undef MSA_CASE
@@ -871,14 +1034,18 @@ hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_
     }
     return hipGetLastError();
   }
-  const dim3 grid(b.total_units, (c.max_blocks_per_seq + kChunkW - 1) / kChunkW, g.nsel);
+  const ItemOrder ord = ItemOrder::make(b.total_units,
+                                        (c.max_blocks_per_seq + kChunkW - 1) / kChunkW, g.nsel,
+                                        kTileBlock);
+  if (ord.grid() > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(ord.grid()));
   switch (hs) {
 #define MSA_CASE(HS)                                                                     \
   case HS:                                                                               \
     if constexpr (HS * DI == 256 || HS * DI == 512)                                      \
-      index_prefill_wide_kernel<DI, HS, FP8><<<grid, 256, 0, st>>>(                      \
+      index_prefill_wide_kernel<DI, HS, FP8, PT><<<grid, 256, 0, st>>>(                  \
           q, c.k_idx_cache, c.k_idx_scale, c.block_table, b.units, c.max_blocks_per_seq, \
-          g.nsel, scores);                                                               \
+          g.nsel, ord, scores);                                                          \
     else                                                                                 \
       return hipErrorInvalidValue;                                                       \
     break;
@@ -905,22 +1072,34 @@ hipError_t launch_index_decode(const Geom &g, const msa_cache_t &c, int T, const
                     : dispatch_decode_hs<false, 32>(g, c, T, q_idx, scores, st);
 }
 
-hipError_t launch_index_prefill(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
-                                const void *q_idx, float *scores, hipStream_t st) {
+template <bool PT>
+hipError_t launch_prefill_scores(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
+                                 const void *q_idx, float *scores, hipStream_t st) {
   if (b.total_units == 0) return hipSuccess;
   if (g.fp8) {
-    return g.Di == 64 ? dispatch_prefill_bf16<64, true>(g, c, b, q_idx, scores, st)
-                      : dispatch_prefill_bf16<32, true>(g, c, b, q_idx, scores, st);
+    return g.Di == 64 ? dispatch_prefill_bf16<64, true, PT>(g, c, b, q_idx, scores, st)
+                      : dispatch_prefill_bf16<32, true, PT>(g, c, b, q_idx, scores, st);
   }
   if (g.bf16) {
-    return g.Di == 64 ? dispatch_prefill_bf16<64, false>(g, c, b, q_idx, scores, st)
-                      : dispatch_prefill_bf16<32, false>(g, c, b, q_idx, scores, st);
+    return g.Di == 64 ? dispatch_prefill_bf16<64, false, PT>(g, c, b, q_idx, scores, st)
+                      : dispatch_prefill_bf16<32, false, PT>(g, c, b, q_idx, scores, st);
   }
   const dim3 grid(b.total_units, c.max_blocks_per_seq, g.nsel);
   index_prefill_f32_kernel<<<grid, 128, 0, st>>>(
       static_cast<const float *>(q_idx), static_cast<const float *>(c.k_idx_cache),
-      c.block_table, b.units, c.max_blocks_per_seq, g.nsel, g.Hi, g.Di, scores);
+      c.block_table, b.units, c.max_blocks_per_seq, g.nsel, g.Hi, g.Di, PT, scores);
   return hipGetLastError();
+}
+
+hipError_t launch_index_prefill(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
+                                const void *q_idx, float *scores, hipStream_t st) {
+  return launch_prefill_scores<false>(g, c, b, q_idx, scores, st);
+}
+
+hipError_t launch_index_prefill_tokens(const Geom &g, const msa_cache_t &c,
+                                       const msa_batch_t &b, const void *q_idx, float *scores,
+                                       hipStream_t st) {
+  return launch_prefill_scores<true>(g, c, b, q_idx, scores, st);
 }
 
 }  // namespace msa

@@ -286,6 +286,64 @@ msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *
                     "sparse_attn_prefill");
 }
 
+msa_status_t msa_index_scores_prefill_tokens(const msa_geom_t *geom, const msa_cache_t *cache,
+                                             const msa_batch_t *batch, const void *q_idx,
+                                             float *scores, void *stream) {
+  msa::Geom g;
+  msa_status_t st = check_geom(geom, &g);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache(cache, false, true, g.fp8)) != MSA_OK) return st;
+  if ((st = check_batch(batch)) != MSA_OK) return st;
+  if (batch->total_units == 0) return ok();
+  MSA_REQUIRE(q_idx != nullptr && scores != nullptr, MSA_ERR_INVALID_ARG,
+              "q_idx / scores is NULL");
+  return hip_status(msa::launch_index_prefill_tokens(g, *cache, *batch, q_idx, scores,
+                                                     static_cast<hipStream_t>(stream)),
+                    "index_scores_prefill_tokens");
+}
+
+size_t msa_prefill_tokens_workspace_size(const msa_geom_t *geom, int32_t total_units,
+                                         int32_t total_q, int32_t topk) {
+  msa::Geom g;
+  if (check_geom(geom, &g) != MSA_OK || total_units < 0 || total_q < 0 || topk <= 0) return 0;
+  return msa::tokens_workspace_bytes(g, total_units, total_q, topk);
+}
+
+msa_status_t msa_sparse_attn_prefill_tokens(const msa_geom_t *geom, const msa_cache_t *cache,
+                                            const msa_batch_t *batch, const void *q,
+                                            const int32_t *ids, int32_t topk,
+                                            float softmax_scale, void *workspace,
+                                            size_t workspace_bytes, void *out, float *lse,
+                                            void *stream) {
+  msa::Geom g;
+  msa_status_t st = check_geom(geom, &g);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache(cache, true, false, g.fp8)) != MSA_OK) return st;
+  if ((st = check_batch(batch)) != MSA_OK) return st;
+  MSA_REQUIRE(topk >= 1, MSA_ERR_INVALID_ARG, "topk must be positive");
+  if (batch->total_units == 0) return ok();
+  MSA_REQUIRE(q != nullptr && ids != nullptr && out != nullptr, MSA_ERR_INVALID_ARG,
+              "q / ids / out is NULL");
+  MSA_REQUIRE(finite_bits(softmax_scale), MSA_ERR_INVALID_ARG,
+              "softmax_scale must be finite (<= 0 selects 1/sqrt(head_dim))");
+  MSA_REQUIRE(cache->max_blocks_per_seq <= msa::kMaxTokenBlocks, MSA_ERR_UNSUPPORTED,
+              "per-token prefill attention takes at most %d blocks per sequence",
+              msa::kMaxTokenBlocks);
+  const size_t need = msa::tokens_workspace_bytes(g, batch->total_units, batch->total_q, topk);
+  if (need > 0) {
+    MSA_REQUIRE(workspace != nullptr, MSA_ERR_INVALID_ARG, "workspace is NULL");
+    MSA_REQUIRE(reinterpret_cast<uintptr_t>(workspace) % 256 == 0, MSA_ERR_INVALID_ARG,
+                "workspace must be 256-byte aligned");
+    MSA_REQUIRE(workspace_bytes >= need, MSA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  }
+  return hip_status(msa::launch_attn_prefill_tokens(g, *cache, *batch, q, ids, topk,
+                                                    resolve_scale(softmax_scale, g.D),
+                                                    workspace, out, lse,
+                                                    static_cast<hipStream_t>(stream)),
+                    "sparse_attn_prefill_tokens");
+}
+
 size_t msa_decode_workspace_size(const msa_geom_t *geom, int32_t num_seqs, int32_t topk,
                                  int32_t num_splits) {
   msa::Geom g;

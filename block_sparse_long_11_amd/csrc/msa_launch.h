@@ -22,11 +22,25 @@ hipError_t launch_index_decode(const Geom &g, const msa_cache_t &c, int T, const
                                float *scores, hipStream_t st);
 hipError_t launch_index_prefill(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                 const void *q_idx, float *scores, hipStream_t st);
+// Per-query-token scores of a prefill batch: scores [total_q][n_sel][max_blocks].
+hipError_t launch_index_prefill_tokens(const Geom &g, const msa_cache_t &c,
+                                       const msa_batch_t &b, const void *q_idx, float *scores,
+                                       hipStream_t st);
 hipError_t launch_topk(const float *scores, int rows, int row_len, int topk, int32_t *ids,
                        hipStream_t st);
 hipError_t launch_attn_prefill(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                const void *q, const int32_t *ids, int topk, float scale,
                                void *out, float *lse, hipStream_t st);
+// Per-query-token prefill attention: ids [total_q][n_sel][topk]; workspace of
+// tokens_workspace_bytes (bf16: per (unit, group) the union of its rows' lists and
+// the row masks; fp32 needs none).
+size_t tokens_workspace_bytes(const Geom &g, int total_units, int total_q, int topk);
+hipError_t launch_attn_prefill_tokens(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
+                                      const void *q, const int32_t *ids, int topk, float scale,
+                                      void *workspace, void *out, float *lse, hipStream_t st);
+// Largest block table width the per-token prefill attention takes (its union bitmap
+// lives in LDS).
+constexpr int kMaxTokenBlocks = 131072;
 // Split count used when the caller passes num_splits <= 0.
 int decode_auto_splits(const Geom &g, int num_seqs, int topk);
 size_t decode_workspace_bytes(const Geom &g, int num_seqs, int num_splits);

@@ -26,6 +26,8 @@ of context):
                       12 x 64k, 48 x 4k tokens), top-k 32: a ragged decode batch
   decode_1m_b8_t4     the 1M decode with 4 new tokens per sequence, each
                       selecting its own blocks (speculative verification)
+  prefill_32k_tokens  the 32k prefill with per-query-token selection: every new
+                      token selects its own 16 blocks
 
 Planting ("relevant blocks"): for every (sequence, selection group g) a seeded
 unit direction u_h is drawn per indexer head h of the group; a * u_h is added to
@@ -75,6 +77,7 @@ class Workload:
     seed: int = 0
     cache_format: str = "plain"     # "plain" or "fp8" (E4M3 codes + power-of-two scales)
     tokens_per_seq: int = 1         # decode: new tokens per sequence, each selecting its own
+    per_token: bool = False         # prefill: every new token selects its own blocks
 
     @property
     def is_decode(self):
@@ -142,6 +145,11 @@ WORKLOADS = {
     "prefill_32k_fp8_sel1": Workload(
         "prefill_32k_fp8_sel1", "bf16", [32768], [32768], num_sel_groups=1, topk=16,
         plant_count=8, plant_span=32, seed=1002, cache_format="fp8"),
+    # per-query-token selection in prefill: every one of the 32768 new tokens scores,
+    # selects and attends its own 16 blocks
+    "prefill_32k_tokens": Workload(
+        "prefill_32k_tokens", "bf16", [32768], [32768], topk=16, plant_count=8,
+        plant_span=32, seed=1002, per_token=True),
     "decode_1m_b8_sel1": Workload(
         "decode_1m_b8_sel1", "bf16", [1048576] * 8, None, num_sel_groups=1, topk=64,
         plant_count=63, plant_span=None, seed=1004),

@@ -282,6 +282,40 @@ msa_status_t msa_sparse_attn_decode_per_token(const msa_geom_t *geom, const msa_
                                               void *workspace, size_t workspace_bytes,
                                               void *out, float *lse, void *stream);
 
+/* Per-query-token selection in prefill ([feat] row "Indexer-selected sparse
+ * attention": the model selects per query token, [B, H_idx, S_q, topk]). Every
+ * new token of a planned prefill batch is its own selection unit: row t (of
+ * unit u, position p = u.pos0 + t - u.row0, diagonal block p / 128) scores the
+ * blocks with its own indexer query, keeps its own top-k and attends causally
+ * over its own blocks. A batch of T new tokens per sequence gives the same rows
+ * as msa_index_scores_per_token.
+ *   msa_index_scores_prefill_tokens: q_idx [total_q][H_i][D_i] ->
+ *       scores fp32 [total_q][num_sel_groups][max_blocks_per_seq]; for row t
+ *       and group g, block b < p/128 scores the max over its 128 keys s of
+ *       sum_{h in g} q_idx[t,h,:] . k_idx[s,h,:]; b == p/128 is +inf, later -inf.
+ *   msa_select_topk_blocks over those rows -> ids [total_q][num_sel_groups][topk]
+ *   msa_sparse_attn_prefill_tokens: q [total_q][H_q][D], ids as above (rows as
+ *       for msa_sparse_attn_prefill: distinct ids, ended by the first -1,
+ *       masked by position) -> out [total_q][H_q][D], lse fp32 [total_q][H_q] or
+ *       NULL. The 128 rows of a unit are attended together over the union of
+ *       their lists, each row over its own blocks only. workspace (device,
+ *       256-byte aligned) of msa_prefill_tokens_workspace_size(geom, total_units,
+ *       total_q, topk) bytes holds the unions (0 bytes for fp32: workspace may
+ *       be NULL). max_blocks_per_seq <= 131072.
+ * softmax_scale as for msa_sparse_attn_prefill. A batch with no units enqueues
+ * nothing. */
+msa_status_t msa_index_scores_prefill_tokens(const msa_geom_t *geom, const msa_cache_t *cache,
+                                             const msa_batch_t *batch, const void *q_idx,
+                                             float *scores, void *stream);
+size_t msa_prefill_tokens_workspace_size(const msa_geom_t *geom, int32_t total_units,
+                                         int32_t total_q, int32_t topk);
+msa_status_t msa_sparse_attn_prefill_tokens(const msa_geom_t *geom, const msa_cache_t *cache,
+                                            const msa_batch_t *batch, const void *q,
+                                            const int32_t *ids, int32_t topk,
+                                            float softmax_scale, void *workspace,
+                                            size_t workspace_bytes, void *out, float *lse,
+                                            void *stream);
+
 /* Step 0, the new tokens before step 1: per-head RMSNorm of queries and keys,
  * partial rotary embedding, and the insert of K, V and the indexer keys into the
  * caches ([feat] table "Checked in its code", rows "QK normalization" and

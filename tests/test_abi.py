@@ -316,3 +316,30 @@ def test_static_decode_rejects_what_does_not_fit(lib):
     assert lib.msa_sparse_attn_decode_static(ctypes.byref(_geom(head_dim=96)), ctypes.byref(c),
                                              FAKE, FAKE, 16, 0.0, 0, FAKE, None,
                                              None) == UNSUPPORTED
+
+
+def test_prefill_tokens_checks(lib):
+    """Per-token prefill calls: argument checks before any launch, workspace size."""
+    g, c, b = _geom(), _cache(), msa._Batch(FAKE, 3, 300)
+    assert lib.msa_index_scores_prefill_tokens(ctypes.byref(g), ctypes.byref(c), None, FAKE,
+                                               FAKE, None) == INVALID
+    assert lib.msa_index_scores_prefill_tokens(ctypes.byref(g), ctypes.byref(c), ctypes.byref(b),
+                                               None, FAKE, None) == INVALID
+    empty = msa._Batch(None, 0, 0)
+    assert lib.msa_index_scores_prefill_tokens(ctypes.byref(g), ctypes.byref(c),
+                                               ctypes.byref(empty), None, None, None) == OK
+    need = lib.msa_prefill_tokens_workspace_size(ctypes.byref(g), 3, 300, 16)
+    al = lambda x: (x + 255) // 256 * 256
+    assert need == al(3 * 4 * 4) + al(300 * 4 * 16 * 4) + al(300 * 4 * 16 * 16)
+    assert lib.msa_prefill_tokens_workspace_size(ctypes.byref(_geom(dtype=msa.MSA_F32)), 3, 300,
+                                                 16) == 0
+    call = lambda ws, nbytes, **kw: lib.msa_sparse_attn_prefill_tokens(
+        ctypes.byref(kw.get("g", g)), ctypes.byref(kw.get("c", c)), ctypes.byref(b), FAKE, FAKE,
+        kw.get("topk", 16), kw.get("scale", 0.0), ws, nbytes, FAKE, None, None)
+    assert call(FAKE * 256, need - 1) == WS_SMALL
+    assert call(None, need) == INVALID
+    assert call(FAKE + 4, need) == INVALID               # misaligned
+    assert call(FAKE * 256, need, topk=0) == INVALID
+    assert call(FAKE * 256, need, scale=float("inf")) == INVALID
+    assert call(FAKE * 256, need, c=_cache(max_blocks_per_seq=131073)) == UNSUPPORTED
+    assert call(FAKE * 256, need, g=_geom(head_dim=96)) == UNSUPPORTED
