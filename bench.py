@@ -45,6 +45,62 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# ----------------------------------------------------------------------------
+# measured peaks: the probes of libmsa_probe.so (include/msa_probe.h)
+# ----------------------------------------------------------------------------
+
+def measured_peaks(dev):
+    """Practical ceilings on this GPU: a streaming read of 4 GiB with 16-byte
+    non-temporal loads (best of several grid sizes) and a dense bf16 MFMA loop on
+    register operands. Timed with HIP events on the launch stream."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_long_11_amd", "libmsa_probe.so"))
+    lib.msa_probe_stream_read.restype = ctypes.c_int
+    lib.msa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    lib.msa_probe_mfma_bf16.restype = ctypes.c_int
+    lib.msa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(65536 * 4, dtype=torch.float32, device=dev)
+
+    def timed(launch, reps):
+        best = float("inf")
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            rc = launch()
+            b.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed ({rc})")
+            best = min(best, a.elapsed_time(b) * 1e-3)
+        return best
+
+    hbm = {}
+    for groups in (2048, 4096, 8192, 16384):
+        t = timed(lambda: lib.msa_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                                     groups, ctypes.c_void_p(sink.data_ptr()),
+                                                     stream), 4)
+        hbm[groups] = nbytes / t / 1e9
+    del buf
+    groups, iters = 1024, 20000
+    flops = groups * 4 * iters * 8 * 32768
+    timed(lambda: lib.msa_probe_mfma_bf16(groups, 2000, ctypes.c_void_p(sink.data_ptr()),
+                                          stream), 1)      # clock ramp
+    t = timed(lambda: lib.msa_probe_mfma_bf16(groups, iters, ctypes.c_void_p(sink.data_ptr()),
+                                              stream), 3)
+    best_g = max(hbm, key=hbm.get)
+    return dict(hbm_gbs=hbm[best_g], mfma_bf16_tflops=flops / t / 1e12,
+                hbm_probe=f"streaming read of 4 GiB, 16-byte non-temporal loads, 8 in flight "
+                          f"per thread, best of {sorted(hbm)} work-groups (best {best_g})",
+                mfma_probe="v_mfma_f32_32x32x16_bf16, 8 independent chains per wave, "
+                           f"{groups} work-groups of 4 waves, register operands")
+
+
 def geometry(w):
     return msa.Geometry(w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_idx_heads,
                         w.idx_head_dim, w.num_sel_groups, w.dtype, w.cache_format)
@@ -76,6 +132,20 @@ def selected_kv_tokens(w, ids, units):
             first = un["pos0"] - tau * BLK + 1
             diag = n * first + n * (n - 1) // 2
             total += n * full + diag
+    return total
+
+
+def selected_kv_tokens_rows(w, ids):
+    """Per-token prefill: sum over (new token, KV head) of the visible keys of that
+    token's own kept blocks (ids [total_q][n_sel][topk])."""
+    pos = np.concatenate([np.arange(L - n, L) for L, n in zip(w.seq_lens, w.q_lens)])
+    tau = pos // BLK
+    total = 0
+    for j in range(w.num_kv_heads):
+        g = j if w.num_sel_groups == w.num_kv_heads else 0
+        kept = ids[:, g, :]
+        full = ((kept >= 0) & (kept < tau[:, None])).sum(axis=1) * BLK
+        total += int(full.sum() + (pos - tau * BLK + 1).sum())
     return total
 
 
@@ -115,7 +185,8 @@ class Runner:
                                self.inp["k_idx_cache"], self.inp["block_table"],
                                self.inp["seq_lens"], self.inp.get("k_scale"),
                                self.inp.get("v_scale"), self.inp.get("k_idx_scale"))
-        U = w.total_q if w.is_decode else len(msa.msa_prefill_plan(w.seq_lens, w.q_lens))
+        U = w.total_q if (w.is_decode or w.per_token) else \
+            len(msa.msa_prefill_plan(w.seq_lens, w.q_lens))
         self.batch = None if w.is_decode else msa.make_batch(w.seq_lens, w.q_lens, dev)
         self.scores = torch.empty((U, w.num_sel_groups, self.cache.max_blocks),
                                   dtype=torch.float32, device=dev)
@@ -125,6 +196,9 @@ class Runner:
         if w.is_decode:
             self.ws = msa.workspace(msa.msa_decode_workspace_size(self.geom, w.total_q,
                                                                   w.topk, 0), dev)
+        elif w.per_token:
+            self.ws = msa.workspace(msa.msa_prefill_tokens_workspace_size(
+                self.geom, self.batch.total_units, w.total_q, w.topk), dev)
         self.names = ["index_scores", "select_topk_blocks",
                       "sparse_attn_decode" if w.is_decode else "sparse_attn_prefill"]
 
@@ -136,6 +210,9 @@ class Runner:
             ev[0].record()
         if w.is_decode and T > 1:
             msa.msa_index_scores_per_token(self.geom, self.cache, T, i["q_idx"], self.scores)
+        elif w.per_token:
+            msa.msa_index_scores_prefill_tokens(self.geom, self.cache, self.batch, i["q_idx"],
+                                                self.scores)
         else:
             msa.msa_index_scores(self.geom, self.cache, self.batch, i["q_idx"], self.scores)
         if ev[1] is not None:
@@ -149,6 +226,9 @@ class Runner:
         elif w.is_decode:
             msa.msa_sparse_attn_decode(self.geom, self.cache, i["q"], self.ids, w.topk,
                                        self.out, self.ws, self.lse)
+        elif w.per_token:
+            msa.msa_sparse_attn_prefill_tokens(self.geom, self.cache, self.batch, i["q"],
+                                               self.ids, w.topk, self.out, self.ws, self.lse)
         else:
             msa.msa_sparse_attn_prefill(self.geom, self.cache, self.batch, i["q"], self.ids,
                                         w.topk, self.out, self.lse)
@@ -243,7 +323,8 @@ def measure(w, dev, steps, warmup, permute=False):
     ms, per, wall = r.timed(steps, warmup)
     units = plan_units(w)
     ids = r.ids.cpu().numpy()
-    tokens = selected_kv_tokens(w, ids, units)
+    tokens = selected_kv_tokens_rows(w, ids) if w.per_token else \
+        selected_kv_tokens(w, ids, units)
     G = w.num_q_heads // w.num_kv_heads
     res = dict(workload=w.name, ms_per_step=ms, kernel_ms=per, wall_s=wall,
                selected_kv_tokens_per_step=tokens, value=tokens / (ms * 1e-3),
@@ -340,7 +421,20 @@ def _mini(cache_t, bt_row, blocks):
     return mini, bt
 
 
-def cpu_baseline(w, runner, budget_s=15.0):
+def blas_info():
+    """BLAS library and thread count numpy's products run on."""
+    try:
+        import threadpoolctl
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            return dict(blas=f"{info[0].get('internal_api')} {info[0].get('version')}",
+                        blas_threads=info[0].get("num_threads"))
+    except Exception:   # threadpoolctl missing or failing: report what numpy says
+        pass
+    return dict(blas="unknown", blas_threads=None)
+
+
+def cpu_baseline(w, runner, budget_s=15.0, max_units=None):
     """The oracle as it stands, timed on this host's cores over a seeded sample of
     units (the copies of each unit's inputs to the host are not timed)."""
     from oracle import msa_oracle as O
@@ -351,6 +445,8 @@ def cpu_baseline(w, runner, budget_s=15.0):
     cores = len(os.sched_getaffinity(0))
     done, tokens, t_used = 0, 0, 0.0
     for u in order:
+        if max_units is not None and done >= max_units:
+            break
         un = units[u]
         r, tau = un["r"], un["tau"]
         rows = slice(r, r + 1) if w.is_decode else slice(un["row0"], un["row0"] + un["num_rows"])
@@ -371,10 +467,15 @@ def cpu_baseline(w, runner, budget_s=15.0):
         done += 1
         if t_used > budget_s:
             break
-    return dict(value=tokens / t_used, unit="selected-KV tokens/s", cores=cores, kind="oracle",
+    rate = tokens / t_used
+    return dict(value=rate, unit="selected-KV tokens/s", cores=cores, kind="oracle",
                 sample=f"{done} of {len(units)} units of {w.name} (seeded order), whole oracle "
                        f"path per unit (scores, top-k, attention) in float64, {t_used:.1f} s "
-                       f"of oracle time")
+                       f"of oracle time",
+                extrapolated_step_s=t_used * len(units) / done,
+                extrapolation="sampled units' oracle time scaled by units per step "
+                              "(units are independent)",
+                **blas_info())
 
 
 def main():
@@ -387,12 +488,15 @@ def main():
                     help="second workload measured in the same run ('none' to skip)")
     ap.add_argument("--extra", default="decode_1m_b8_fp8,prefill_32k_fp8,decode_1m_b8_t4,"
                                       "decode_ragged_b64,chunked_prefill,decode_128k_b64,"
-                                      "prefill_32k_sel1,prefill_32k_fp8_sel1,decode_1m_b8_sel1",
+                                      "prefill_32k_sel1,prefill_32k_fp8_sel1,decode_1m_b8_sel1,"
+                                      "prefill_32k_tokens",
                     help="more workloads measured in the same run (FP8 caches, several "
                          "tokens per sequence, ragged batches, the chunked prefill, the "
                          "128k batched decode, one selection group), comma-separated "
                          "('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the measured-peak probes (streaming read, MFMA loop)")
     ap.add_argument("--permute", action="store_true",
                     help="scatter every workload's blocks over the physical cache by a seeded "
                          "permutation (the default block table is the identity)")
@@ -419,6 +523,12 @@ def main():
                           "bytes_written": dst.numel() * 4}))
         return
     msa.lib()
+    peaks = None
+    if not args.no_probes:
+        peaks = measured_peaks(dev)
+        log(f"measured peaks: HBM read {peaks['hbm_gbs']:.0f} GB/s, bf16 MFMA "
+            f"{peaks['mfma_bf16_tflops']:.0f} TFLOP/s")
+        torch.cuda.empty_cache()
 
     w = synth.WORKLOADS[args.workload]
     main_res = measure(w, dev, args.steps, args.warmup, args.permute)
@@ -437,6 +547,10 @@ def main():
         w2 = synth.WORKLOADS[args.second]
         second = measure(w2, dev, args.steps, args.warmup, args.permute)
         log(f"{w2.name}: {second['ms_per_step']:.3f} ms/step, kernels {second['kernel_ms']}")
+        if not args.no_cpu_baseline:
+            log("timing the CPU oracle on a sample of the second workload")
+            second["cpu_baseline"] = cpu_baseline(w2, second["_runner"], args.cpu_budget / 2,
+                                                  max_units=2)
         inserts.append(measure_insert(second["_runner"]))
         log(f"{w2.name}: insert {inserts[-1]['us_per_launch']:.1f} us")
         del second["_runner"]
@@ -454,6 +568,17 @@ def main():
         del res["_runner"]
         torch.cuda.empty_cache()
         extra.append(res)
+
+    def add_measured(res):
+        rf = res["roofline"]
+        if peaks is None:
+            return
+        mp = peaks["hbm_gbs"] if rf["bound"] == "hbm" else peaks["mfma_bf16_tflops"]
+        rf["measured_peak"] = mp
+        rf["frac_of_measured_peak"] = rf["achieved"] / mp
+
+    for r in [main_res] + ([second] if second else []) + extra:
+        add_measured(r)
 
     config = dict(workload=w.name, batch=w.num_seqs,
                   seq_lens=w.seq_lens if len(set(w.seq_lens)) > 1 else w.seq_lens[0],
@@ -481,11 +606,12 @@ def main():
         "kernel_ms": main_res["kernel_ms"],
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
+        "measured_peaks": peaks,
     }
     if second is not None:
         line["second_workload"] = {k: second[k] for k in (
             "workload", "value", "ms_per_step", "graph_ms_per_step", "cold_ms_per_step",
-            "kernel_ms", "roofline", "step_hbm_frac") if k in second}
+            "kernel_ms", "roofline", "step_hbm_frac", "cpu_baseline") if k in second}
     if extra:
         # the same workloads on FP8 caches (E4M3 codes, power-of-two scale per 32
         # channels), decode with several new tokens per sequence (each selecting its

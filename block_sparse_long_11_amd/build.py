@@ -14,6 +14,8 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 BUILD = ROOT / "_build"
 LIB = PKG / "libmsa.so"
+PROBE = CSRC / "probe"
+PROBE_LIB = PKG / "libmsa_probe.so"      # peak-rate probes used by bench.py
 ARCH = "gfx950"
 
 CFLAGS = [
@@ -42,21 +44,29 @@ def _compile(src: pathlib.Path, extra):
     return obj
 
 
-def build(verbose=False, extra=()):
-    """Compile every kernel source and link libmsa.so. Returns the library path."""
-    BUILD.mkdir(exist_ok=True)
-    srcs = sorted(CSRC.glob("*.hip"))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
-    tmp = LIB.with_suffix(".so.tmp")
+def _link(objs, lib):
+    tmp = lib.with_suffix(".so.tmp")
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp),
            *map(str, objs)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False, extra=()):
+    """Compile every kernel source and link libmsa.so (and the peak-rate probes into
+    libmsa_probe.so). Returns the library path."""
+    BUILD.mkdir(exist_ok=True)
+    srcs = sorted(CSRC.glob("*.hip"))
+    probes = sorted(PROBE.glob("*.hip"))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probes))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs + probes))
+    _link(objs[:len(srcs)], LIB)
+    if probes:
+        _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB}" + (f" and {PROBE_LIB.name}" if probes else ""))
     return LIB
 
 
