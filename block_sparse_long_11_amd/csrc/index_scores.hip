@@ -407,80 +407,104 @@ struct ItemOrder {
 
 // ---------------------------------------------------------------------------
 // prefill, bf16, group width 256 or 512 (one selection group over all indexer
-// heads): MFMA 32x32x16 on LDS-staged keys, 128 channels at a time
+// heads): MFMA 32x32x16 on LDS-staged keys, one 32-key tile at a time
 // ---------------------------------------------------------------------------
 //
-// A work-group of 4 waves scores one query tile (wave w: rows 32w .. 32w+31, the
-// A operand, the whole group width in registers) against a chunk of kChunkW
-// candidate blocks, in the XCD-aware order of ItemOrder. A block's group keys (128 keys x GD channels) do not fit
-// twice in LDS, so they are staged 128 channels (32 KiB) at a time by direct
-// global->LDS loads, double-buffered across (block, channel chunk) stages, with
-// the same 16-byte swizzle as the narrow kernel; the four 32-key accumulators of
-// a block gather the contraction over its channel chunks and are max-pooled
-// after the last. Rows past the unit's end repeat its last row.
+// A work-group of 8 waves (two per SIMD) scores two adjacent query tiles of one
+// request (units 2x and 2x + 1 of the plan; a pair split by a request boundary
+// runs as two passes of one tile) against a chunk of kChunkW candidate blocks,
+// in the XCD-aware order of ItemOrder. Wave w holds 32 query rows of tile w / 4
+// over the whole group width in registers (the A operand). The keys go through
+// LDS one 32-key tile of a block at a time, all GD channels of it (32 KiB of
+// bf16 at 512 channels), double-buffered across (block, key tile) stages by
+// direct global->LDS loads with 16-byte chunks XOR-swizzled by key: every wave
+// contracts one staged tile over the whole width into two accumulators (even and
+// odd k steps, so consecutive MFMAs do not depend on each other), adds them and
+// max-pools. One accumulator pair per wave (32 registers) leaves room for two
+// waves per SIMD next to the 128 registers of query rows, and one staged tile
+// serves all 256 query rows. Rows past a unit's end repeat its last row.
+//
+// FP8 indexer keys: a staged key row is GD codes (16 per chunk) plus the tile's
+// scale bytes; the group channels are contracted in the order
+// (ks / 2) * 32 + (lane / 32) * 16 + (ks % 2) * 8 (the query operand uses the same
+// order), so one 16-byte read gives a lane two k steps in one 32-channel scale
+// block, converted with that block's power of two.
 
 constexpr int kChunkW = 16;   // blocks per work-group
+constexpr int kWideThreads = 512;
 
-// Waves per SIMD: at 512 channels the query rows take 128 registers. FP8 keys run
-// two waves per SIMD all the same (the compiler keeps a few values in scratch,
-// outside the MFMA chains); bf16 keys run one, as two spill more. Measured inside
-// the whole step of the 32k prefill with one group, same GPU: FP8 654 -> 566 us
-// with two waves, bf16 794 -> 831 us.
 template <int DI, int HS, bool FP8, bool PT>
-__global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(FP8 || HS * DI <= 256 ? 2 : 1, FP8 || HS * DI <= 256 ? 2 : 1)))
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void index_prefill_wide_kernel(
     const uint16_t *__restrict__ q_idx, const void *__restrict__ k_idx_,
     const uint8_t *__restrict__ k_scale, const int32_t *__restrict__ block_table,
-    const msa_unit_t *__restrict__ units, int max_blocks, int nsel, ItemOrder order,
-    float *__restrict__ scores) {
+    const msa_unit_t *__restrict__ units, int num_units, int max_blocks, int nsel,
+    ItemOrder order, float *__restrict__ scores) {
   constexpr int GD = HS * DI;          // group width
   constexpr int KS = GD / 16;          // k steps of the whole group
-  constexpr int CW = 128;              // channels per staged chunk
-  constexpr int NCC = GD / CW;         // channel chunks per block
-  constexpr int KSC = CW / 16;         // k steps per chunk
-  constexpr int CHG = FP8 ? CW / 16 : CW / 8;   // 16-byte chunks per staged key row
+  constexpr int CHG = FP8 ? GD / 16 : GD / 8;   // 16-byte chunks per staged key row
   constexpr int CPH = FP8 ? DI / 16 : DI / 8;   // 16-byte chunks per head row
-  constexpr int HPC = CW / DI;         // heads per channel chunk
   constexpr int NS = DI / 32;          // FP8 scale bytes per key and head
-  constexpr int SCH = FP8 ? HPC * kBlk * NS / 16 : 1;   // 16-byte chunks of a stage's scales
-  constexpr int NLD = kBlk * CHG / 256;
-  static_assert(GD % CW == 0 && NCC % 2 == 0, "group width 256 or 512");
+  constexpr int TK = 32;               // keys per stage
+  constexpr int NWV = kWideThreads / kWave;
+  constexpr int NLD = TK * CHG / kWideThreads;  // direct loads per thread per stage
+  constexpr int SCH = FP8 ? HS * TK * NS / 16 : 1;   // 16-byte chunks of a stage's scales
+  static_assert(GD == 256 || GD == 512, "group width 256 or 512");
+  static_assert(TK * CHG % kWideThreads == 0, "staging split");
   static_assert(!FP8 || SCH <= kWave, "one wave stages the scales");
-  __shared__ u32x4 Kb[2][kBlk * CHG];
+  __shared__ u32x4 Kb[2][TK * CHG];
   __shared__ u32x4 Ks[2][SCH];
-  __shared__ float red[4][kChunkW];
+  __shared__ float red[NWV][kChunkW];
   const uint16_t *k_idx = static_cast<const uint16_t *>(k_idx_);
   const uint8_t *k_idx8 = static_cast<const uint8_t *>(k_idx_);
-  // FP8 row swizzle: keys sharing a 256-byte bank row get distinct chunk slots
-  auto swz = [](int key) { return FP8 ? (key / (16 / CHG)) % CHG : key % CHG; };
+  // chunk c of key row r sits at c ^ (r % 16): the 16 rows one LDS pass reads at
+  // the same chunk land on 16 distinct 16-byte bank positions
+  auto swz = [](int key) { return key % 16; };
 
-  int u, y, g;                           // item: tile u, block chunk y, group g
-  if (!order.item(static_cast<int>(blockIdx.x), u, y, g)) return;
-  const msa_unit_t un = units[u];
+  int x, y, g;                          // item: tile pair x, block chunk y, group g
+  if (!order.item(static_cast<int>(blockIdx.x), x, y, g)) return;
+  const int u_first = 2 * x;
+  if (u_first >= num_units) return;
+  const bool paired =
+      u_first + 1 < num_units && units[u_first + 1].r == units[u_first].r;
+  const int npass = (!paired && u_first + 1 < num_units) ? 2 : 1;
   const int Hi = nsel * HS;
   const int b0 = y * kChunkW;
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
-  float *out = scores + (static_cast<size_t>(u) * nsel + g) * max_blocks;
-  if constexpr (PT) {     // every row's entries at and after the diagonal
-    for (int e = t; e < kBlk * kChunkW; e += 256) {
-      const int i = e / kChunkW, b = b0 + e % kChunkW;
-      if (i < un.num_rows && b >= un.tau && b < max_blocks)
-        scores[(static_cast<size_t>(un.row0 + i) * nsel + g) * max_blocks + b] =
-            (b == un.tau) ? pos_inf() : neg_inf();
+  for (int pass = 0; pass < npass; ++pass) {
+  if (pass > 0) __syncthreads();        // the previous pass is done with LDS
+  const int u0 = u_first + pass;
+  const int ntile = paired ? 2 : 1;
+  const msa_unit_t un0 = units[u0];
+  const int tau_max = units[u0 + ntile - 1].tau;
+
+  // +inf / -inf entries of the tiles inside this chunk (per token: of every row)
+  if constexpr (PT) {
+    for (int e = t; e < ntile * kBlk * kChunkW; e += kWideThreads) {
+      const int tt = e / (kBlk * kChunkW), i = (e / kChunkW) % kBlk, b = b0 + e % kChunkW;
+      const msa_unit_t ut = units[u0 + tt];
+      if (i < ut.num_rows && b >= ut.tau && b < max_blocks)
+        scores[(static_cast<size_t>(ut.row0 + i) * nsel + g) * max_blocks + b] =
+            (b == ut.tau) ? pos_inf() : neg_inf();
     }
   } else {
-    for (int i = t; i < kChunkW; i += 256) {
-      const int b = b0 + i;
-      if (b >= un.tau && b < max_blocks) out[b] = (b == un.tau) ? pos_inf() : neg_inf();
+    for (int e = t; e < ntile * kChunkW; e += kWideThreads) {
+      const int tt = e / kChunkW, b = b0 + e % kChunkW;
+      const int tau = units[u0 + tt].tau;
+      if (b >= tau && b < max_blocks)
+        scores[(static_cast<size_t>(u0 + tt) * nsel + g) * max_blocks + b] =
+            (b == tau) ? pos_inf() : neg_inf();
     }
   }
-  if (b0 >= un.tau) return;
-  const int nblk = min(kChunkW, un.tau - b0);
+  if (b0 >= tau_max) continue;
+  const int nblk = min(kChunkW, tau_max - b0);
 
-  // A operand: this wave's 32 query rows over the whole group width (FP8 keys: the
-  // channel order that keeps a lane's two k steps of a 16-byte read in one scale block)
-  const int qrow = un.row0 + min(wave * 32 + lane % 32, un.num_rows - 1);
+  // this wave's 32 query rows over the whole group width
+  const int tt = wave / 4;
+  const bool tile_live = tt < ntile;
+  const msa_unit_t mine = units[u0 + (tile_live ? tt : 0)];
+  const bool wave_live = tile_live && (wave % 4) * 32 < mine.num_rows;
+  const int qrow = mine.row0 + min((wave % 4) * 32 + lane % 32, mine.num_rows - 1);
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -491,119 +515,119 @@ void index_prefill_wide_kernel(
         q_idx + (static_cast<size_t>(qrow) * Hi + h) * DI + d));
   }
 
-  const int32_t *bt = block_table + static_cast<size_t>(un.r) * max_blocks;
-  // stage st = block (st / NCC), channel chunk (st % NCC) into buffer st % 2
+  const int32_t *bt = block_table + static_cast<size_t>(un0.r) * max_blocks;
+  // stage st = block st / 4, key tile st % 4, into buffer st % 2
   auto issue = [&](int st) __attribute__((always_inline)) {
-    const size_t phys = static_cast<size_t>(bt[b0 + st / NCC]);
-    const int cc = st % NCC;
+    const size_t phys = static_cast<size_t>(bt[b0 + st / 4]);
+    const int key0 = (st % 4) * TK;
     u32x4 *dst = Kb[st % 2];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int base = (4 * i + wave) * 64;
+      const int base = (NWV * i + wave) * 64;
       const int p = base + lane, key = p / CHG, c = (p % CHG) ^ swz(key);
-      const int h = g * HS + cc * HPC + c / CPH;
+      const int h = g * HS + c / CPH;
       const void *src;
       if constexpr (FP8)
-        src = k_idx8 + ((phys * Hi + h) * kBlk + key) * DI + (c % CPH) * 16;
+        src = k_idx8 + ((phys * Hi + h) * kBlk + key0 + key) * DI + (c % CPH) * 16;
       else
-        src = k_idx + ((phys * Hi + h) * kBlk + key) * DI + (c % CPH) * 8;
+        src = k_idx + ((phys * Hi + h) * kBlk + key0 + key) * DI + (c % CPH) * 8;
       __builtin_amdgcn_global_load_lds(
           src, (__attribute__((address_space(3))) void *)(dst + base), 16, 0, 0);
     }
     if constexpr (FP8) {
-      // the chunk's heads' scale bytes ([HPC][128][NS]) are contiguous
-      if (wave == 0 && lane < SCH)
+      // scales of the tile: head hh's 32 keys x NS bytes are contiguous
+      if (wave == 0 && lane < SCH) {
+        const int hh = lane / (TK * NS / 16), off = (lane % (TK * NS / 16)) * 16;
         __builtin_amdgcn_global_load_lds(
-            k_scale + (phys * Hi + g * HS + cc * HPC) * kBlk * NS + lane * 16,
+            k_scale + ((phys * Hi + g * HS + hh) * kBlk + key0) * NS + off,
             (__attribute__((address_space(3))) void *)Ks[st % 2], 16, 0, 0);
+      }
     }
   };
 
-  const int nst = nblk * NCC;
+  const int key = lane % 32;
+  const int nst = 4 * nblk;
+  float m = neg_inf();                  // tile pooling: this lane's running maximum
+  float mt = neg_inf();                 // per token: this lane's query over the block
   issue(0);
-  for (int bi = 0; bi < nblk; ++bi) {
-    f32x16 acc[4];
+  for (int st = 0; st < nst; ++st) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this stage's keys landed
+    __syncthreads();
+    if (st + 1 < nst) issue(st + 1);
+    const int bi = st / 4, b = b0 + bi;
+    const u32x4 *src = Kb[st % 2];
+    const uint8_t *sb = reinterpret_cast<const uint8_t *>(Ks[st % 2]);
+    if (wave_live && b < mine.tau) {
+      f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+      auto mma = [&](f32x16 &acc, const bf16x8 &kf, int ks) __attribute__((always_inline)) {
+        if constexpr (PT)   // keys x queries: a lane holds one query and 16 keys
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], acc, 0, 0, 0);
+        else
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf, acc, 0, 0, 0);
+      };
+      if constexpr (FP8) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x16{};
+        for (int k2 = 0; k2 < KS / 2; ++k2) {
+          const u32x4 w = src[key * CHG + ((2 * k2 + lane / 32) ^ swz(key))];
+          const int hh = (k2 * 32) / DI, sub = (k2 * 32 % DI) / 32;
+          const float sc = ldexpf(1.0f, static_cast<int>(sb[(hh * TK + key) * NS + sub]) - 127);
+          uint32_t o[8];
 #pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) {
-      const int st = bi * NCC + cc;
-      __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this stage's keys landed
-      __syncthreads();
-      if (st + 1 < nst) issue(st + 1);
-      const u32x4 *src = Kb[cc % 2];          // NCC is even: stage st sits in buffer st % 2
-      const uint8_t *sb = reinterpret_cast<const uint8_t *>(Ks[cc % 2]);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int key = nt * 32 + lane % 32;
-        // the key fragments are read as they are used: the whole group width of
-        // query rows already takes half the registers
-        if constexpr (FP8) {
-#pragma unroll
-          for (int k2 = 0; k2 < KSC / 2; ++k2) {
-            const u32x4 w = src[key * CHG + ((2 * k2 + lane / 32) ^ swz(key))];
-            const int hh = (k2 * 32) / DI, sub = (k2 * 32 % DI) / 32;
-            const float sc =
-                ldexpf(1.0f, static_cast<int>(sb[(hh * kBlk + key) * NS + sub]) - 127);
-            uint32_t o[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              o[2 * i] = __builtin_bit_cast(
-                  uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, false));
-              o[2 * i + 1] = __builtin_bit_cast(
-                  uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, true));
-            }
-            const bf16x8 k0 = as_bf16x8(uint4{o[0], o[1], o[2], o[3]});
-            const bf16x8 k1 = as_bf16x8(uint4{o[4], o[5], o[6], o[7]});
-            if constexpr (PT) {   // keys x queries: a lane holds one query and 16 keys
-              acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[cc * KSC + 2 * k2],
-                                                                acc[nt], 0, 0, 0);
-              acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[cc * KSC + 2 * k2 + 1],
-                                                                acc[nt], 0, 0, 0);
-            } else {
-              acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[cc * KSC + 2 * k2], k0,
-                                                                acc[nt], 0, 0, 0);
-              acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[cc * KSC + 2 * k2 + 1], k1,
-                                                                acc[nt], 0, 0, 0);
-            }
+          for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, false));
+            o[2 * i + 1] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], sc, true));
           }
-        } else {
+          mma(acc0, as_bf16x8(uint4{o[0], o[1], o[2], o[3]}), 2 * k2);
+          mma(acc1, as_bf16x8(uint4{o[4], o[5], o[6], o[7]}), 2 * k2 + 1);
+        }
+      } else {
 #pragma unroll
-          for (int ks = 0; ks < KSC; ++ks) {
-            const bf16x8 kf =
-                __builtin_bit_cast(bf16x8, src[key * CHG + ((2 * ks + lane / 32) ^ swz(key))]);
-            if constexpr (PT)
-              acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[cc * KSC + ks], acc[nt],
-                                                                0, 0, 0);
-            else
-              acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[cc * KSC + ks], kf, acc[nt],
-                                                                0, 0, 0);
-          }
+        for (int ks = 0; ks < KS; ks += 2) {
+          mma(acc0, __builtin_bit_cast(bf16x8, src[key * CHG + ((2 * ks + lane / 32) ^ swz(key))]),
+              ks);
+          mma(acc1,
+              __builtin_bit_cast(bf16x8, src[key * CHG + ((2 * ks + 2 + lane / 32) ^ swz(key))]),
+              ks + 1);
         }
       }
+      float v = neg_inf();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v = fmaxf(v, acc0[i] + acc1[i]);
+      if constexpr (PT) mt = fmaxf(mt, v); else m = fmaxf(m, v);
     }
-    float m = neg_inf();
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[nt][i]);
-    if constexpr (PT) {
-      // the two lane halves hold the same query's other 16 keys of each tile
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
-                                                       false, false);
-      m = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      const int rit = wave * 32 + lane;
-      if (lane < 32 && rit < un.num_rows)
-        scores[(static_cast<size_t>(un.row0 + rit) * nsel + g) * max_blocks + b0 + bi] = m;
-    } else {
-      m = group_max<kWave>(m);
-      if (lane == 0) red[wave][bi] = m;
+    if (st % 4 == 3) {                  // the block is complete
+      if constexpr (PT) {
+        // the two lane halves hold the same query's other 16 keys of each tile
+        if (wave_live && b < mine.tau) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
+                                                           __float_as_uint(mt), false, false);
+          const float sv = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+          const int rit = (wave % 4) * 32 + lane;
+          if (lane < 32 && rit < mine.num_rows)
+            scores[(static_cast<size_t>(mine.row0 + rit) * nsel + g) * max_blocks + b] = sv;
+        }
+        mt = neg_inf();
+      } else {
+        const float mm = group_max<kWave>(m);
+        if (lane == 0) red[wave][bi] = mm;
+        m = neg_inf();
+      }
     }
   }
-  if constexpr (PT) return;
-  __syncthreads();
-  if (t < nblk)
-    out[b0 + t] = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+  if constexpr (!PT) {
+    __syncthreads();
+    // tile tt owns blocks b < tau_tt: the maximum over its four waves
+    for (int e = t; e < ntile * nblk; e += kWideThreads) {
+      const int tile = e / nblk, bi = e % nblk, b = b0 + bi;
+      if (b >= units[u0 + tile].tau) continue;
+      scores[(static_cast<size_t>(u0 + tile) * nsel + g) * max_blocks + b] =
+          fmaxf(fmaxf(red[4 * tile][bi], red[4 * tile + 1][bi]),
+                fmaxf(red[4 * tile + 2][bi], red[4 * tile + 3][bi]));
+    }
+  }
+  }   // pass
 }
 
 // ---------------------------------------------------------------------------
@@ -639,10 +663,10 @@ constexpr int kChunk2 = 32;   // blocks per work-group (16: 1-3% slower, 64: slo
 constexpr int kTiles = 2;
 constexpr int kIdxThreads = kTiles * 2 * kWave;
 // x-block sizes of ItemOrder: 32 tile pairs (their query rows of one group, 2 MiB
-// at 128 channels, and the current 1 MiB key chunk fit one XCD's 4 MB L2); 16
-// tiles for the wide kernel (512 channels: 2 MiB of query rows, 2 MiB chunks)
+// at 128 channels, and the current 1 MiB key chunk fit one XCD's 4 MB L2); 8 tile
+// pairs for the wide kernel (512 channels: 2 MiB of query rows, 2 MiB chunks)
 constexpr int kPairBlock = 32;
-constexpr int kTileBlock = 16;
+constexpr int kWidePairBlock = 8;
 
 template <int DI, int HS, bool FP8, bool PT>
 __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -1034,18 +1058,18 @@ hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_
     }
     return hipGetLastError();
   }
-  const ItemOrder ord = ItemOrder::make(b.total_units,
+  const ItemOrder ord = ItemOrder::make((b.total_units + 1) / 2,
                                         (c.max_blocks_per_seq + kChunkW - 1) / kChunkW, g.nsel,
-                                        kTileBlock);
+                                        kWidePairBlock);
   if (ord.grid() > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(ord.grid()));
   switch (hs) {
 #define MSA_CASE(HS)                                                                     \
   case HS:                                                                               \
     if constexpr (HS * DI == 256 || HS * DI == 512)                                      \
-      index_prefill_wide_kernel<DI, HS, FP8, PT><<<grid, 256, 0, st>>>(                  \
-          q, c.k_idx_cache, c.k_idx_scale, c.block_table, b.units, c.max_blocks_per_seq, \
-          g.nsel, ord, scores);                                                          \
+      index_prefill_wide_kernel<DI, HS, FP8, PT><<<grid, kWideThreads, 0, st>>>(         \
+          q, c.k_idx_cache, c.k_idx_scale, c.block_table, b.units, b.total_units,        \
+          c.max_blocks_per_seq, g.nsel, ord, scores);                                    \
     else                                                                                 \
       return hipErrorInvalidValue;                                                       \
     break;

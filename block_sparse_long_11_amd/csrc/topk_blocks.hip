@@ -5,7 +5,8 @@
 // selections whose score is -inf become -1. Method list "Exp-free TopK kernel":
 // raw scores are ranked directly, no softmax.
 //
-// One work-group per row. Scores are mapped to order-preserving uint32 keys and
+// Rows of up to 512 entries: one wave per row (topk_rows_wave_kernel). Longer rows:
+// one work-group per row. Scores are mapped to order-preserving uint32 keys and
 // the K-th largest key is found exactly by a 4-pass radix select (8 bits per
 // pass, LDS histograms with integer atomics, so the result does not depend on
 // thread timing). The kept entries (key above the threshold, plus the lowest
@@ -239,11 +240,86 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_reg_kernel(
   for (int i = K + t; i < topk; i += kTopkThreads) out[i] = -1;
 }
 
+// Rows of at most 64 * E entries: one wave per row, four rows per work-group, no
+// LDS and no barriers. Lane l holds the E consecutive entries from l * E. The
+// K-th largest key is found bit by bit from the top: the largest threshold with
+// at least K keys at or above it, each count being the popcounts of one ballot
+// per register. Entries above it are kept, and of those equal to it the lowest
+// indices, counted with v_mbcnt (set bits of lower lanes); the same counts give
+// every kept entry its output slot, so the ids come out ascending.
+template <int E>
+__global__ __launch_bounds__(256) void topk_rows_wave_kernel(const float *__restrict__ scores,
+                                                             int rows, int row_len, int topk,
+                                                             int32_t *__restrict__ ids) {
+  const int lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * 4 + static_cast<int>(threadIdx.x) / kWave;
+  if (row >= rows) return;                     // the whole wave
+  const float *rp = scores + static_cast<size_t>(row) * row_len;
+  int32_t *out = ids + static_cast<size_t>(row) * topk;
+  const int i0 = lane * E;
+  auto below = [](uint64_t m) {                // set bits of m in lanes below this one
+    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+        static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+  };
+  uint32_t key[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j)
+    key[j] = (i0 + j < row_len) ? order_key(rp[i0 + j]) : 0u;   // 0: below every score
+  int total = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) total += __popcll(__ballot(key[j] > kNegInfKey));
+  const int K = min(topk, total);
+  if (K > 0) {
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < E; ++j) c += __popcll(__ballot(key[j] >= cand));
+      if (c >= K) thr = cand;
+    }
+    // thr is the key of the K-th largest entry (every one of the K largest is
+    // above -inf); `remaining` entries equal to it are taken, lowest index first
+    int n_gt = 0, eq_before = 0;
+    uint64_t eq[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      n_gt += __popcll(__ballot(key[j] > thr));
+      eq[j] = __ballot(key[j] == thr);
+      eq_before += below(eq[j]);
+    }
+    const int remaining = K - n_gt;
+    bool take[E];
+    int e = eq_before;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      take[j] = key[j] > thr || (key[j] == thr && e < remaining);
+      e += key[j] == thr;
+    }
+    int pos = 0;                               // kept entries of lower lanes
+#pragma unroll
+    for (int j = 0; j < E; ++j) pos += below(__ballot(take[j]));
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      if (take[j]) out[pos++] = i0 + j;
+  }
+  for (int i = K + lane; i < topk; i += kWave) out[i] = -1;
+}
+
 }  // namespace
 
 hipError_t launch_topk(const float *scores, int rows, int row_len, int topk, int32_t *ids,
                        hipStream_t st) {
   if (rows == 0) return hipSuccess;
+  const int per_lane = (row_len + kWave - 1) / kWave;
+#define MSA_TOPK_WAVE(E)                                                              \
+  if (per_lane <= E) {                                                                \
+    topk_rows_wave_kernel<E><<<(rows + 3) / 4, 256, 0, st>>>(scores, rows, row_len, topk, \
+                                                             ids);                    \
+    return hipGetLastError();                                                         \
+  }
+  MSA_TOPK_WAVE(1) MSA_TOPK_WAVE(2) MSA_TOPK_WAVE(4) MSA_TOPK_WAVE(8)
+#undef MSA_TOPK_WAVE
   const int per = (row_len + kTopkThreads - 1) / kTopkThreads;   // entries per thread
 #define MSA_TOPK(KPT)                                                                 \
   if (per <= KPT) {                                                                   \

@@ -280,6 +280,31 @@ def _sample_units(units, n, seed):
     return sorted(picks)
 
 
+def all_unit_indexing(w, inp, res, units):
+    """Scores (dot-product bound) and ids (near-tie rule) of EVERY unit and group
+    against the oracle, one sequence's blocks on the host at a time."""
+    bt_all = inp["block_table"].cpu().numpy()
+    scores, ids = res["scores"].numpy(), res["ids"].numpy()
+    near = 0
+    for r in range(w.num_seqs):
+        us = [u for u, un in enumerate(units) if un["r"] == r]
+        tau_max = max(units[u]["tau"] for u in us)
+        blocks = list(range(max(tau_max, 1)))
+        ki, btm = _mini_cache(inp["k_idx_cache"], bt_all[r], blocks, slice(None))
+        for u in us:
+            un = units[u]
+            qi = host(inp["q_idx"][un["row0"]:un["row1"]])
+            ref = O.unit_block_scores(qi, ki, btm, un["tau"], w.num_sel_groups, scores.shape[2])
+            P.check_scores(scores[u][None], ref[None], P.score_tolerance(qi, ki, w.num_sel_groups),
+                           f"{w.name} u{u}")
+            for g in range(w.num_sel_groups):
+                ok, exact = P.ids_acceptable(ids[u, g], ref[g], un["tau"], w.topk)
+                assert ok, f"{w.name} u{u} g{g}: ids {ids[u, g]}"
+                near += not exact
+        del ki
+    say(f"{w.name}: scores and ids of all {len(units)} units checked ({near} near-tie rows)")
+
+
 @pytest.mark.parametrize("name", ["prefill_32k", "chunked_prefill", "prefill_32k_sel1"])
 def test_full_size_prefill_sampled(name, gpu_device):
     w = synth.WORKLOADS[name]
@@ -288,6 +313,8 @@ def test_full_size_prefill_sampled(name, gpu_device):
     say(f"{name} run")
     res = run_gpu(w, inp, geom, cache, gpu_device)
     units = O.prefill_units(w.seq_lens, w.q_lens)
+    if name != "chunked_prefill":       # 1.5e13 oracle flop: sampled below
+        all_unit_indexing(w, inp, res, units)
     picks = _sample_units(units, 4, 1)
     # the first and last tile of every request
     for r in range(w.num_seqs):
@@ -307,6 +334,7 @@ def test_full_size_decode_sampled(name, gpu_device):
     say(f"{name} run")
     res = run_gpu(w, inp, geom, cache, gpu_device)
     units = O.decode_units(w.seq_lens)
+    all_unit_indexing(w, inp, res, units)
     sampled_parity(w, inp, res, units, _sample_units(units, 2, 2), rows_per_unit=1)
     # every row is finite before its diagonal, +inf there and -inf after it
     sc = res["scores"].numpy()
