@@ -407,7 +407,7 @@ struct ItemOrder {
 
 // ---------------------------------------------------------------------------
 // prefill, bf16, group width 256 or 512 (one selection group over all indexer
-// heads): MFMA 32x32x16 on LDS-staged keys, one 32-key tile at a time
+// heads): MFMA 32x32x16 on LDS-staged keys, 32 or 64 keys at a time
 // ---------------------------------------------------------------------------
 //
 // A work-group of 8 waves (two per SIMD) scores two adjacent query tiles of one
@@ -415,13 +415,13 @@ struct ItemOrder {
 // runs as two passes of one tile) against a chunk of kChunkW candidate blocks,
 // in the XCD-aware order of ItemOrder. Wave w holds 32 query rows of tile w / 4
 // over the whole group width in registers (the A operand). The keys go through
-// LDS one 32-key tile of a block at a time, all GD channels of it (32 KiB of
-// bf16 at 512 channels), double-buffered across (block, key tile) stages by
-// direct global->LDS loads with 16-byte chunks XOR-swizzled by key: every wave
-// contracts one staged tile over the whole width into two accumulators (even and
-// odd k steps, so consecutive MFMAs do not depend on each other), adds them and
-// max-pools. One accumulator pair per wave (32 registers) leaves room for two
-// waves per SIMD next to the 128 registers of query rows, and one staged tile
+// LDS a stage at a time: 32 or 64 keys of a block over all GD channels (32 KiB of
+// bf16 keys at 512 channels), double-buffered by direct global->LDS loads with
+// 16-byte chunks XOR-swizzled by key. Every wave contracts each 32-key tile of a
+// stage over the whole width into two accumulators (even and odd k steps, so
+// consecutive MFMAs do not depend on each other), adds them and max-pools. One
+// accumulator pair per wave (32 registers) leaves room for two waves per SIMD
+// next to the 128 registers of query rows, and one staged tile
 // serves all 256 query rows. Rows past a unit's end repeat its last row.
 //
 // FP8 indexer keys: a staged key row is GD codes (16 per chunk) plus the tile's
@@ -445,7 +445,10 @@ void index_prefill_wide_kernel(
   constexpr int CHG = FP8 ? GD / 16 : GD / 8;   // 16-byte chunks per staged key row
   constexpr int CPH = FP8 ? DI / 16 : DI / 8;   // 16-byte chunks per head row
   constexpr int NS = DI / 32;          // FP8 scale bytes per key and head
-  constexpr int TK = 32;               // keys per stage
+  // keys per stage: 64 (two 32-key tiles, half the barriers) where the staging
+  // addresses fit beside the query rows; 32 for bf16 keys 512 channels wide
+  constexpr int TK = (FP8 || GD <= 256) ? 64 : 32;
+  constexpr int SPB = kBlk / TK;       // stages per block
   constexpr int NWV = kWideThreads / kWave;
   constexpr int NLD = TK * CHG / kWideThreads;  // direct loads per thread per stage
   constexpr int SCH = FP8 ? HS * TK * NS / 16 : 1;   // 16-byte chunks of a stage's scales
@@ -516,10 +519,10 @@ void index_prefill_wide_kernel(
   }
 
   const int32_t *bt = block_table + static_cast<size_t>(un0.r) * max_blocks;
-  // stage st = block st / 4, key tile st % 4, into buffer st % 2
+  // stage st = block st / SPB, keys (st % SPB) * TK .., into buffer st % 2
   auto issue = [&](int st) __attribute__((always_inline)) {
-    const size_t phys = static_cast<size_t>(bt[b0 + st / 4]);
-    const int key0 = (st % 4) * TK;
+    const size_t phys = static_cast<size_t>(bt[b0 + st / SPB]);
+    const int key0 = (st % SPB) * TK;
     u32x4 *dst = Kb[st % 2];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
@@ -545,8 +548,7 @@ void index_prefill_wide_kernel(
     }
   };
 
-  const int key = lane % 32;
-  const int nst = 4 * nblk;
+  const int nst = SPB * nblk;
   float m = neg_inf();                  // tile pooling: this lane's running maximum
   float mt = neg_inf();                 // per token: this lane's query over the block
   issue(0);
@@ -554,9 +556,12 @@ void index_prefill_wide_kernel(
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this stage's keys landed
     __syncthreads();
     if (st + 1 < nst) issue(st + 1);
-    const int bi = st / 4, b = b0 + bi;
+    const int bi = st / SPB, b = b0 + bi;
     const u32x4 *src = Kb[st % 2];
     const uint8_t *sb = reinterpret_cast<const uint8_t *>(Ks[st % 2]);
+#pragma unroll
+    for (int kt = 0; kt < TK / 32; ++kt) {
+    const int key = kt * 32 + lane % 32;
     if (wave_live && b < mine.tau) {
       f32x16 acc0 = f32x16{}, acc1 = f32x16{};
       auto mma = [&](f32x16 &acc, const bf16x8 &kf, int ks) __attribute__((always_inline)) {
@@ -597,7 +602,8 @@ void index_prefill_wide_kernel(
       for (int i = 0; i < 16; ++i) v = fmaxf(v, acc0[i] + acc1[i]);
       if constexpr (PT) mt = fmaxf(mt, v); else m = fmaxf(m, v);
     }
-    if (st % 4 == 3) {                  // the block is complete
+    }
+    if (st % SPB == SPB - 1) {          // the block is complete
       if constexpr (PT) {
         // the two lane halves hold the same query's other 16 keys of each tile
         if (wave_live && b < mine.tau) {
