@@ -255,6 +255,11 @@ class Runner:
         return total_ms / steps, per, wall
 
 
+TRAFFIC_SOURCE = ("committed rocprofv3 counter profile (profiles/pmc_traffic.json: FETCH_SIZE and "
+                  "WRITE_SIZE per launch, scaled by a plain-copy calibration), used only while the "
+                  "kernel's source file is unchanged; not measured in this run")
+
+
 def measured_traffic(kernel_key, source_file):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a plain copy), or
@@ -338,7 +343,7 @@ def measure(w, dev, steps, warmup, permute=False):
                                frac=nbytes / t / 1e9 / HBM_PEAK_GBS,
                                traffic=measured_traffic(f"{w.name}:index_decode",
                                                         "index_scores.hip"),
-                               algorithmic_bytes=nbytes)
+                               traffic_source=TRAFFIC_SOURCE, algorithmic_bytes=nbytes)
         # whole decode step against HBM: the algorithmic bytes of all four launches
         kv = tokens * cache_row_bytes(w, w.head_dim) * 2   # K and V rows of the selected keys
         step_bytes = nbytes + kv + 2 * w.total_q * w.num_q_heads * w.head_dim * 2
@@ -352,7 +357,7 @@ def measure(w, dev, steps, warmup, permute=False):
                                unit="TFLOP/s", frac=flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                                traffic=measured_traffic(f"{w.name}:attn_prefill",
                                                         "attn_prefill.hip"),
-                               algorithmic_flops=flops)
+                               traffic_source=TRAFFIC_SOURCE, algorithmic_flops=flops)
     res["_runner"] = r
     return res
 

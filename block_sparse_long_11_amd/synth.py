@@ -245,8 +245,9 @@ def make_inputs(w: Workload, device="cpu", permute=False, chunk_blocks=2048):
     With w.cache_format == "fp8" the caches are uint8 E4M3 codes and the dict also
     holds k_scale [P][H_kv][128][D/32], v_scale [P][H_kv][D/32][128] and
     k_idx_scale [P][H_i][128][D_i/32] (bytes e + 127): each 32-channel block of a
-    token row gets a seeded exponent e from {-1, 0, 1}, and its codes are torch's
-    float8_e4m3fn cast of the drawn values times 2^-e."""
+    token row gets a seeded exponent e from {-7, -6, -5} (the range the writer's
+    rule gives N(0,1) rows), and its codes are torch's float8_e4m3fn cast of the
+    drawn values times 2^-e, clamped to +-448 (beyond 3.5 sigma at e = -7)."""
     dt = _torch_dtype(w)
     B, P = w.num_seqs, w.num_phys_blocks
     T = w.total_q
@@ -302,7 +303,9 @@ def make_inputs(w: Workload, device="cpu", permute=False, chunk_blocks=2048):
                         x[idx, g * hs:(g + 1) * hs] += a * ut
             dst = torch.from_numpy(perm[c0:c1]).to(device)
             if fp8:
-                e = torch.randint(-1, 2, (c1 - c0, heads, BLOCK, dim // SCALE_BLOCK),
+                # exponents of the range a writer picks for N(0,1) rows (the smallest
+                # e with max|x| / 2^e <= 448 over 32 channels is about -7)
+                e = torch.randint(-7, -4, (c1 - c0, heads, BLOCK, dim // SCALE_BLOCK),
                                   generator=sgen, device=device, dtype=torch.int32)
                 y = x * torch.exp2(-e.float()).repeat_interleave(SCALE_BLOCK, dim=3)
                 codes = y.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)

@@ -244,7 +244,8 @@ msa_status_t msa_sparse_attn_decode(const msa_geom_t *geom, const msa_cache_t *c
  * split partials go to a scratch array of MSA_STATIC_SCRATCH_BYTES that the
  * library keeps in static device memory, one copy on each GPU it runs on, held
  * until the process ends (its address is looked up once per device, on the
- * first call there). The call allocates and frees nothing.
+ * first call there, with hipGetSymbolAddress: make that first call outside any
+ * graph capture). The call allocates and frees nothing.
  *   MSA_ERR_WORKSPACE_TOO_SMALL when msa_decode_workspace_size(geom, num_seqs,
  *   topk, num_splits) exceeds MSA_STATIC_SCRATCH_BYTES (nothing is enqueued).
  * Every call on one GPU shares that GPU's array and leaves the last call's

@@ -27,34 +27,48 @@ def capture(fn):
     return g
 
 
-def make_step(w, inp, geom, cache, dev):
-    """Pre-allocated outputs and a step that writes them (no allocation inside)."""
+def make_step(w, inp, geom, cache, dev, static=False):
+    """Pre-allocated outputs and a step that writes them (no allocation inside).
+    static: decode attention through msa_sparse_attn_decode_static (no workspace)."""
     T = w.tokens_per_seq
     if w.is_decode:
         rows, batch = w.total_q, None
     else:
         batch = msa.make_batch(w.seq_lens, w.q_lens, dev)
-        rows = batch.total_units
+        rows = batch.total_q if w.per_token else batch.total_units
     bufs = dict(scores=torch.empty((rows, w.num_sel_groups, cache.max_blocks),
                                    dtype=torch.float32, device=dev),
                 ids=torch.empty((rows, w.num_sel_groups, w.topk), dtype=torch.int32, device=dev),
                 out=torch.empty_like(inp["q"]),
                 lse=torch.empty(inp["q"].shape[:2], dtype=torch.float32, device=dev))
-    ws = msa.workspace(msa.msa_decode_workspace_size(geom, w.total_q, w.topk, 0), dev) \
-        if w.is_decode else None
+    if w.is_decode:
+        ws = msa.workspace(msa.msa_decode_workspace_size(geom, w.total_q, w.topk, 0), dev)
+    elif w.per_token:
+        ws = msa.workspace(msa.msa_prefill_tokens_workspace_size(geom, batch.total_units,
+                                                                 batch.total_q, w.topk), dev)
+    else:
+        ws = None
 
     def step():
         if w.is_decode and T > 1:
             msa.msa_index_scores_per_token(geom, cache, T, inp["q_idx"], bufs["scores"])
+        elif w.per_token:
+            msa.msa_index_scores_prefill_tokens(geom, cache, batch, inp["q_idx"], bufs["scores"])
         else:
             msa.msa_index_scores(geom, cache, batch, inp["q_idx"], bufs["scores"])
         msa.msa_select_topk_blocks(bufs["scores"], w.topk, bufs["ids"])
         if w.is_decode and T > 1:
             msa.msa_sparse_attn_decode_per_token(geom, cache, T, inp["q"], bufs["ids"], w.topk,
                                                  bufs["out"], ws, bufs["lse"])
+        elif w.is_decode and static:
+            msa.msa_sparse_attn_decode_static(geom, cache, inp["q"], bufs["ids"], w.topk,
+                                              bufs["out"], bufs["lse"])
         elif w.is_decode:
             msa.msa_sparse_attn_decode(geom, cache, inp["q"], bufs["ids"], w.topk, bufs["out"],
                                        ws, bufs["lse"])
+        elif w.per_token:
+            msa.msa_sparse_attn_prefill_tokens(geom, cache, batch, inp["q"], bufs["ids"], w.topk,
+                                               bufs["out"], ws, bufs["lse"])
         else:
             msa.msa_sparse_attn_prefill(geom, cache, batch, inp["q"], bufs["ids"], w.topk,
                                         bufs["out"], bufs["lse"])
@@ -73,15 +87,27 @@ CASES = {
                                   cache_format="fp8"),
     "prefill_one_group": dict(seq_lens=(1500, 300), q_lens=(400, 300), num_q_heads=16,
                               num_kv_heads=4, num_idx_heads=8, num_sel_groups=1, topk=5),
+    # per-token selection in prefill: the per-row indexer, the wave top-k, the union
+    # kernel (zeroes its masks, then ORs them: every replay rebuilds them) and attention
+    "prefill_tokens": dict(seq_lens=(1500, 700), q_lens=(600, 700), topk=4, per_token=True),
+    "prefill_tokens_fp8_one_group": dict(seq_lens=(1500, 300), q_lens=(400, 300),
+                                         num_q_heads=16, num_kv_heads=4, num_idx_heads=8,
+                                         num_sel_groups=1, topk=5, cache_format="fp8",
+                                         per_token=True),
+    # the decode attention that keeps its partials in the library's static scratch
+    "decode_static": dict(seq_lens=(3000, 700, 129, 20000), q_lens=None, topk=5,
+                          static=True),
 }
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_graph_replays_match_eager(name, gpu_device):
-    w = synth.small_workload(**CASES[name])
+    kw = dict(CASES[name])
+    static = kw.pop("static", False)
+    w = synth.small_workload(**kw)
     say(f"graph {name}")
     inp, geom, cache = T_.setup(w, gpu_device, permute=True)
-    step, bufs = make_step(w, inp, geom, cache, gpu_device)
+    step, bufs = make_step(w, inp, geom, cache, gpu_device, static)
     step()
     torch.cuda.synchronize()
     eager = {k: v.clone() for k, v in bufs.items()}
