@@ -199,6 +199,11 @@ class Runner:
         elif w.per_token:
             self.ws = msa.workspace(msa.msa_prefill_tokens_workspace_size(
                 self.geom, self.batch.total_units, w.total_q, w.topk), dev)
+        # FP8 prefill: the staged attention (kept blocks converted to bf16 once each)
+        self.staged = w.cache_format == "fp8" and not w.is_decode and not w.per_token
+        if self.staged:
+            self.ws = msa.workspace(msa.msa_prefill_workspace_size(
+                self.geom, self.cache, self.batch.total_units, w.topk), dev)
         self.names = ["index_scores", "select_topk_blocks",
                       "sparse_attn_decode" if w.is_decode else "sparse_attn_prefill"]
 
@@ -228,6 +233,9 @@ class Runner:
                                        self.out, self.ws, self.lse)
         elif w.per_token:
             msa.msa_sparse_attn_prefill_tokens(self.geom, self.cache, self.batch, i["q"],
+                                               self.ids, w.topk, self.out, self.ws, self.lse)
+        elif self.staged:
+            msa.msa_sparse_attn_prefill_staged(self.geom, self.cache, self.batch, i["q"],
                                                self.ids, w.topk, self.out, self.ws, self.lse)
         else:
             msa.msa_sparse_attn_prefill(self.geom, self.cache, self.batch, i["q"], self.ids,
@@ -352,7 +360,10 @@ def measure(w, dev, steps, warmup, permute=False):
     else:
         flops = 4.0 * w.head_dim * G * tokens       # QK^T and PV over the visible pairs
         t = per["sparse_attn_prefill"] * 1e-3
-        res["roofline"] = dict(kernel="sparse_attn_prefill", bound="mfma",
+        kname = "sparse_attn_prefill"
+        if r.staged:
+            kname += "_staged (kept FP8 blocks converted to bf16 once each, then attended)"
+        res["roofline"] = dict(kernel=kname, bound="mfma",
                                achieved=flops / t / 1e12, peak=MFMA_BF16_PEAK_TFLOPS,
                                unit="TFLOP/s", frac=flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                                traffic=measured_traffic(f"{w.name}:attn_prefill",

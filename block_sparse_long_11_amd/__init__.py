@@ -4,11 +4,9 @@ Argument marshalling only. Every step of the path runs in the HIP kernels of
 libmsa.so; torch supplies device memory and the current stream. There is no
 fallback: if the library is missing or a call fails, an exception is raised.
 
-Entry points (same names as the C ABI):
-  msa_prefill_plan, msa_index_scores, msa_select_topk_blocks,
-  msa_sparse_attn_prefill, msa_decode_workspace_size, msa_sparse_attn_decode
-plus two helpers that allocate outputs and run the whole path:
-  prefill(...) and decode(...).
+Entry points (same names as the C ABI): every function of include/msa.h (the
+EXPORTS table), plus helpers that allocate outputs and run the whole path:
+  prefill(...), decode(...), decode_per_token(...) and prefill_tokens(...).
 """
 
 import ctypes
@@ -74,6 +72,13 @@ EXPORTS = {
                                                ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
                                                ctypes.c_void_p, ctypes.c_void_p,
                                                ctypes.c_void_p]),
+    "msa_prefill_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(_Geom),
+                                                     ctypes.POINTER(_Cache), ctypes.c_int32,
+                                                     ctypes.c_int32]),
+    "msa_sparse_attn_prefill_staged": (ctypes.c_int, [
+        ctypes.POINTER(_Geom), ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "msa_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(_Geom), ctypes.c_int32,
                                                     ctypes.c_int32, ctypes.c_int32]),
     "msa_sparse_attn_decode": (ctypes.c_int, [ctypes.POINTER(_Geom), ctypes.POINTER(_Cache),
@@ -326,9 +331,7 @@ def msa_select_topk_blocks(scores, topk, ids, stream=None):
                                         _stream(stream)))
 
 
-def msa_sparse_attn_prefill(geom: Geometry, cache: Cache, batch: Batch, q, ids, topk, out,
-                            lse=None, softmax_scale=0.0, stream=None):
-    """Step 3 for prefill. q/out [total_q][H_q][D], lse fp32 [total_q][H_q] or None."""
+def _check_prefill_attn(geom, cache, batch, q, ids, topk, out, lse):
     cache.check(geom)
     dev = cache.block_table.device
     _need(q, "q", geom.torch_dtype, 3, dev)
@@ -343,10 +346,36 @@ def msa_sparse_attn_prefill(geom: Geometry, cache: Cache, batch: Batch, q, ids, 
         _need(lse, "lse", torch.float32, 2, dev)
         if tuple(lse.shape) != shape[:2]:
             raise ValueError("lse must be [total_q][H_q]")
+
+
+def msa_sparse_attn_prefill(geom: Geometry, cache: Cache, batch: Batch, q, ids, topk, out,
+                            lse=None, softmax_scale=0.0, stream=None):
+    """Step 3 for prefill. q/out [total_q][H_q][D], lse fp32 [total_q][H_q] or None."""
+    _check_prefill_attn(geom, cache, batch, q, ids, topk, out, lse)
     g, c, b = geom.c(), cache.c(), batch.c()
     _check(lib().msa_sparse_attn_prefill(ctypes.byref(g), ctypes.byref(c), ctypes.byref(b),
                                          _ptr(q), _ptr(ids), topk, float(softmax_scale),
                                          _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def msa_prefill_workspace_size(geom: Geometry, cache: Cache, total_units, topk):
+    g, c = geom.c(), cache.c()
+    return int(lib().msa_prefill_workspace_size(ctypes.byref(g), ctypes.byref(c), total_units,
+                                                topk))
+
+
+def msa_sparse_attn_prefill_staged(geom: Geometry, cache: Cache, batch: Batch, q, ids, topk,
+                                   out, workspace, lse=None, softmax_scale=0.0, stream=None):
+    """Step 3 for prefill with a workspace (FP8 caches: kept blocks converted to bf16
+    once each, then the bf16 attention)."""
+    _check_prefill_attn(geom, cache, batch, q, ids, topk, out, lse)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1, cache.block_table.device)
+    g, c, b = geom.c(), cache.c(), batch.c()
+    _check(lib().msa_sparse_attn_prefill_staged(
+        ctypes.byref(g), ctypes.byref(c), ctypes.byref(b), _ptr(q), _ptr(ids), topk,
+        float(softmax_scale), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def msa_decode_workspace_size(geom: Geometry, num_seqs, topk, num_splits=0):
@@ -575,8 +604,9 @@ def workspace(nbytes, device):
 # ----------------------------------------------------------------------------
 
 def prefill(geom: Geometry, cache: Cache, batch: Batch, q, q_idx, topk, softmax_scale=0.0,
-            stream=None):
-    """Index, select and attend for a prefill batch. Returns dict of device tensors."""
+            stream=None, staged=False):
+    """Index, select and attend for a prefill batch. Returns dict of device tensors.
+    staged: attention through msa_sparse_attn_prefill_staged (own workspace)."""
     dev = q.device
     U = batch.total_units
     scores = torch.empty((U, geom.num_sel_groups, cache.max_blocks), dtype=torch.float32,
@@ -586,7 +616,13 @@ def prefill(geom: Geometry, cache: Cache, batch: Batch, q, q_idx, topk, softmax_
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
     msa_index_scores(geom, cache, batch, q_idx, scores, stream)
     msa_select_topk_blocks(scores, topk, ids, stream)
-    msa_sparse_attn_prefill(geom, cache, batch, q, ids, topk, out, lse, softmax_scale, stream)
+    if staged:
+        ws = workspace(msa_prefill_workspace_size(geom, cache, U, topk), dev)
+        msa_sparse_attn_prefill_staged(geom, cache, batch, q, ids, topk, out, ws, lse,
+                                       softmax_scale, stream)
+    else:
+        msa_sparse_attn_prefill(geom, cache, batch, q, ids, topk, out, lse, softmax_scale,
+                                stream)
     return dict(scores=scores, ids=ids, out=out, lse=lse)
 
 

@@ -52,6 +52,7 @@
 // not ping-ponged (the staged registers leave no room for it).
 //
 // fp32 path: plain FMA, one thread per (query, head); for small exact checks.
+#include <algorithm>
 #include <type_traits>
 
 #include "msa_device.h"
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(kPrefWaves * 64) __attribute__((amdgpu_waves_per_eu
 void attn_prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vtc, const int32_t *__restrict__ block_table,
-    const msa_unit_t *__restrict__ units, const int32_t *__restrict__ ids, int topk,
+    const int32_t *__restrict__ remap, const msa_unit_t *__restrict__ units, const int32_t *__restrict__ ids, int topk,
     int max_blocks, int Hq, int Hkv, int nsel, int num_uj, int pairs, float c,
     TokenUnion tu, uint16_t *__restrict__ out, float *__restrict__ lse) {
   constexpr int NW = kPrefWaves;
@@ -225,9 +226,11 @@ void attn_prefill_bf16_kernel(
 
   // Kept blocks, attended in the order: the last kept id (the diagonal block, for
   // the selection's ascending output) first, then the others in list order. Lane
-  // p of phys holds the physical block of position 64 * phys_chunk + p, its
-  // logical id; bit p of late marks the positions whose block reaches the unit's
-  // first query (id >= tau) and so takes the causal test.
+  // p of phys holds the K/V block of position 64 * phys_chunk + p: the cache's
+  // (physical block, KV head j) index, or with remap (bf16 copies of FP8 blocks)
+  // the copy's slot; lane p of logical holds its logical id; bit p of late marks
+  // the positions whose block reaches the unit's first query (id >= tau) and so
+  // takes the causal test.
   int nk = 0;
   if constexpr (PT)
     nk = tu.count[static_cast<size_t>(u) * nsel + g];
@@ -249,7 +252,12 @@ void attn_prefill_bf16_kernel(
     if ((p >> 6) != phys_chunk) {
       phys_chunk = p >> 6;
       const int pl = 64 * phys_chunk + lane;
-      phys = pl < nk ? bt[min(sel[pl == 0 ? nk - 1 : pl - 1], un.tau)] : 0;
+      phys = 0;
+      if (pl < nk) {
+        const uint32_t bh = static_cast<uint32_t>(bt[min(sel[pl == 0 ? nk - 1 : pl - 1], un.tau)]) *
+                                static_cast<uint32_t>(Hkv) + static_cast<uint32_t>(j);
+        phys = remap != nullptr ? max(remap[bh], 0) : static_cast<int>(bh);
+      }
       wait_vm<0>();   // completes here, so no wait is needed where phys is read
     }
     return __builtin_amdgcn_readlane(phys, p & 63);
@@ -299,7 +307,7 @@ void attn_prefill_bf16_kernel(
   }
   auto issue = [&](int hb, auto r) __attribute__((always_inline)) {
     constexpr int R = decltype(r)::value % 4;
-    const size_t off = (static_cast<size_t>(phys_at(hb >> 1)) * Hkv + j) * kBlk * D;
+    const size_t off = static_cast<size_t>(static_cast<uint32_t>(phys_at(hb >> 1))) * kBlk * D;
     const uint16_t *kg = kc + off + (hb & 1) * HB * D;
     const uint16_t *vg = vtc + off + (hb & 1) * HB;
 #pragma unroll
@@ -878,6 +886,230 @@ __global__ __launch_bounds__(kUnionThreads) void token_union_kernel(
   }
 }
 
+// FP8 caches, staged: every (physical block, KV head) that a unit keeps is
+// converted once into bf16 copies laid out like the bf16 caches' blocks (K as
+// [128][D], V^T as [D][128]), and the bf16 kernel attends the copies. The
+// conversion is exact (an E4M3 code times a power of two is a bf16 value), so the
+// result equals attending the FP8 blocks directly up to the order of the fp32
+// sums; each block is converted once instead of once per work-group that reads it.
+// Two layouts, both of H_kv * min(num_phys, units * topk) copies:
+//   direct (num_phys <= units * topk): copy (block, head) sits where the cache
+//     holds it; the lists set a flag per kept pair, and the conversion takes the
+//     flagged pairs and clears their flags (a flag left set, e.g. by a workspace's
+//     first contents, only costs a conversion that nothing reads);
+//   claimed (larger caches): the slot map is reset, the first list entry to reach
+//     a pair claims the next slot for it, and the attention looks slots up.
+struct Stage {
+  int32_t *count;       // claimed: slots in use
+  int32_t *slot_of;     // [num_phys * Hkv]: claimed: slot of (block, head), -1 when not
+                        // kept; direct: nonzero when kept
+  int32_t *src;         // claimed: [S] (block, head) of each slot
+  uint16_t *k;          // [S][128][D]
+  uint16_t *vt;         // [S][D][128]
+  int64_t S;            // copies
+  bool direct;
+};
+
+namespace {
+
+constexpr int kStageThreads = 256;
+
+size_t al256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int64_t stage_slots(const Geom &g, int64_t num_phys, int total_units, int topk) {
+  return static_cast<int64_t>(g.Hkv) *
+         std::min<int64_t>(num_phys, static_cast<int64_t>(total_units) * topk);
+}
+
+Stage stage_layout(const Geom &g, int64_t num_phys, int total_units, int topk, char *ws) {
+  Stage st{};
+  st.S = stage_slots(g, num_phys, total_units, topk);
+  st.direct = num_phys <= static_cast<int64_t>(total_units) * topk;
+  const size_t map = al256(static_cast<size_t>(num_phys) * g.Hkv * 4);
+  const size_t src = al256(static_cast<size_t>(st.S) * 4);
+  const size_t blk = static_cast<size_t>(st.S) * kBlk * g.D * 2;
+  st.count = reinterpret_cast<int32_t *>(ws);
+  st.slot_of = reinterpret_cast<int32_t *>(ws + 256);
+  st.src = reinterpret_cast<int32_t *>(ws + 256 + map);
+  st.k = reinterpret_cast<uint16_t *>(ws + 256 + map + src);
+  st.vt = reinterpret_cast<uint16_t *>(ws + 256 + map + src + blk);
+  return st;
+}
+
+__global__ __launch_bounds__(kStageThreads) void stage_reset_kernel(Stage st, int64_t n) {
+  const int64_t step = static_cast<int64_t>(gridDim.x) * kStageThreads;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kStageThreads + threadIdx.x; i < n;
+       i += step)
+    st.slot_of[i] = -1;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *st.count = 0;
+}
+
+// One wave per (unit, selection group) list, a lane per id, 64 at a time. Lists
+// end at their first negative id; an id past the diagonal is read from the
+// diagonal's block, as the attention kernel reads it. Direct: every kept pair's
+// flag is set. Claimed: a lane that finds its pair unclaimed claims it, and the
+// wave's claims take consecutive slots from one atomic add.
+template <bool DIRECT>
+__global__ __launch_bounds__(kStageThreads) void stage_mark_kernel(
+    const msa_unit_t *__restrict__ units, const int32_t *__restrict__ ids, int topk, int nsel,
+    int Hkv, const int32_t *__restrict__ block_table, int max_blocks, int64_t num_phys,
+    int rows, Stage st) {
+  const int lane = threadIdx.x % kWave;
+  const int e = blockIdx.x * (kStageThreads / kWave) + threadIdx.x / kWave;
+  if (e >= rows) return;                  // uniform over the wave
+  const int u = e / nsel, g = e % nsel;
+  const msa_unit_t un = units[u];
+  const int32_t *row = ids + static_cast<size_t>(e) * topk;
+  const int32_t *bt = block_table + static_cast<size_t>(un.r) * max_blocks;
+  const int heads = Hkv / nsel;          // the KV heads that read group g's list
+  for (int c0 = 0; c0 < topk; c0 += kWave) {
+    const int i = c0 + lane;
+    const int id = i < topk ? row[i] : -1;
+    const uint64_t neg = __ballot(id < 0);
+    const int end = neg != 0 ? __builtin_ctzll(neg) : kWave;   // first ended lane
+    bool live = lane < end;
+    int pb = 0;
+    if (live) {
+      pb = bt[min(id, un.tau)];
+      live = pb >= 0 && pb < num_phys;
+    }
+    for (int h = 0; h < heads; ++h) {
+      const uint32_t bh = static_cast<uint32_t>(pb) * static_cast<uint32_t>(Hkv) +
+                          static_cast<uint32_t>(heads == 1 ? g : h);
+      if constexpr (DIRECT) {
+        if (live) st.slot_of[bh] = 1;
+        continue;
+      }
+      const bool claim = live && atomicCAS(&st.slot_of[bh], -1, -2) == -1;
+      const uint64_t cm = __ballot(claim);
+      if (cm == 0) continue;
+      const int first = __builtin_ctzll(cm);
+      int base = 0;
+      if (lane == first) base = atomicAdd(st.count, __popcll(cm));
+      base = __builtin_amdgcn_readlane(base, first);
+      const int slot = base + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                  static_cast<uint32_t>(cm >> 32),
+                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(cm), 0u)));
+      if (claim && slot < st.S) {
+        st.src[slot] = static_cast<int32_t>(bh);
+        st.slot_of[bh] = slot;
+      }
+    }
+    if (end < kWave) break;
+  }
+}
+
+// One work-group per copy: K rows in 16-code chunks of one key (one scale each)
+// and V^T rows in 16-key chunks of one channel (a scale per key). Direct: work-
+// group b converts pair b if its flag is set and then clears the flag; claimed:
+// work-group s converts the pair that claimed slot s.
+template <int D, bool DIRECT>
+__global__ __launch_bounds__(kStageThreads) void stage_convert_kernel(
+    const uint8_t *__restrict__ k8, const uint8_t *__restrict__ v8,
+    const uint8_t *__restrict__ ksc, const uint8_t *__restrict__ vsc, Stage st) {
+  constexpr int NS = D / 32;              // scale bytes per K row / V^T rows per scale row
+  const int slot = blockIdx.x;
+  size_t bh;
+  if constexpr (DIRECT) {
+    const bool kept = st.slot_of[slot] != 0;
+    __syncthreads();                      // every thread has read the flag before it is cleared
+    if (!kept) return;
+    bh = static_cast<size_t>(slot);
+  } else {
+    if (slot >= min(static_cast<int64_t>(*st.count), st.S)) return;
+    bh = static_cast<uint32_t>(st.src[slot]);
+  }
+  const uint8_t *kb = k8 + bh * kBlk * D;
+  const uint8_t *ks = ksc + bh * kBlk * NS;
+  uint16_t *ko = st.k + static_cast<size_t>(slot) * kBlk * D;
+  constexpr int IT = kBlk * D / 16 / kStageThreads;   // 16-code chunks per thread, K and V^T
+  static_assert(IT * kStageThreads * 16 == kBlk * D, "chunks per thread");
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int c = it * kStageThreads + threadIdx.x;
+    const int key = c / (D / 16), m = c % (D / 16);
+    const uint4 w = *reinterpret_cast<const uint4 *>(kb + static_cast<size_t>(key) * D + m * 16);
+    const float sc = ldexpf(1.0f, static_cast<int>(ks[key * NS + m / 2]) - 127);
+    const uint32_t wi[4] = {w.x, w.y, w.z, w.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __builtin_bit_cast(uint32_t,
+                                    __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wi[i], sc, false));
+      o[2 * i + 1] = __builtin_bit_cast(uint32_t,
+                                        __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wi[i], sc, true));
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(ko + static_cast<size_t>(key) * D + m * 16);
+    dst[0] = uint4{o[0], o[1], o[2], o[3]};
+    dst[1] = uint4{o[4], o[5], o[6], o[7]};
+  }
+  const uint8_t *vb = v8 + bh * D * kBlk;
+  const uint8_t *vs = vsc + bh * NS * kBlk;
+  uint16_t *vo = st.vt + static_cast<size_t>(slot) * D * kBlk;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int c = it * kStageThreads + threadIdx.x;
+    const int d = c / (kBlk / 16), m = c % (kBlk / 16);
+    const uint4 w = *reinterpret_cast<const uint4 *>(vb + static_cast<size_t>(d) * kBlk + m * 16);
+    const uint4 e = *reinterpret_cast<const uint4 *>(vs + static_cast<size_t>(d / 32) * kBlk +
+                                                     m * 16);
+    const uint32_t wi[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t ei[4] = {e.x, e.y, e.z, e.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wi[i], false);
+      const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(wi[i], true);
+      auto ex = [&](int b) { return static_cast<int>((ei[i] >> (8 * b)) & 0xffu) - 127; };
+      o[2 * i] = cvt_pk_bf16(ldexpf(lo.x, ex(0)), ldexpf(lo.y, ex(1)));
+      o[2 * i + 1] = cvt_pk_bf16(ldexpf(hi.x, ex(2)), ldexpf(hi.y, ex(3)));
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(vo + static_cast<size_t>(d) * kBlk + m * 16);
+    dst[0] = uint4{o[0], o[1], o[2], o[3]};
+    dst[1] = uint4{o[4], o[5], o[6], o[7]};
+  }
+  if constexpr (DIRECT)
+    if (threadIdx.x == 0) st.slot_of[slot] = 0;
+}
+
+template <int D>
+void stage_kept_blocks(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
+                       const int32_t *ids, int topk, const Stage &sg, hipStream_t st) {
+  const int rows = b.total_units * g.nsel;
+  constexpr int kMarkRows = kStageThreads / kWave;   // one wave per list
+  const int mark_groups = (rows + kMarkRows - 1) / kMarkRows;
+  const uint8_t *k8 = static_cast<const uint8_t *>(c.k_cache);
+  const uint8_t *v8 = static_cast<const uint8_t *>(c.v_cache);
+  const dim3 cgrid(static_cast<unsigned>(sg.S));
+  if (sg.direct) {
+    stage_mark_kernel<true><<<mark_groups, kStageThreads, 0, st>>>(
+        b.units, ids, topk, g.nsel, g.Hkv, c.block_table, c.max_blocks_per_seq,
+        c.num_phys_blocks, rows, sg);
+    stage_convert_kernel<D, true><<<cgrid, kStageThreads, 0, st>>>(k8, v8, c.k_scale, c.v_scale,
+                                                                  sg);
+    return;
+  }
+  const int64_t n = c.num_phys_blocks * g.Hkv;
+  const int reset_groups = static_cast<int>(std::min<int64_t>((n + kStageThreads - 1) /
+                                                              kStageThreads, 1024));
+  stage_reset_kernel<<<reset_groups, kStageThreads, 0, st>>>(sg, n);
+  stage_mark_kernel<false><<<mark_groups, kStageThreads, 0, st>>>(
+      b.units, ids, topk, g.nsel, g.Hkv, c.block_table, c.max_blocks_per_seq, c.num_phys_blocks,
+      rows, sg);
+  stage_convert_kernel<D, false><<<cgrid, kStageThreads, 0, st>>>(k8, v8, c.k_scale, c.v_scale,
+                                                                 sg);
+}
+
+}  // namespace
+
+size_t prefill_stage_bytes(const Geom &g, int64_t num_phys, int total_units, int topk) {
+  if (!g.fp8 || total_units <= 0 || topk <= 0 || num_phys <= 0) return 0;
+  const int64_t S = stage_slots(g, num_phys, total_units, topk);
+  return 256 + al256(static_cast<size_t>(num_phys) * g.Hkv * 4) + al256(static_cast<size_t>(S) * 4) +
+         2 * static_cast<size_t>(S) * kBlk * g.D * 2;
+}
+
 size_t tokens_workspace_bytes(const Geom &g, int total_units, int total_q, int topk) {
   if (!g.bf16) return 0;
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
@@ -888,24 +1120,28 @@ size_t tokens_workspace_bytes(const Geom &g, int total_units, int total_q, int t
 template <bool PT>
 hipError_t launch_prefill_attention(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                     const void *q, const int32_t *ids, int topk, float scale,
-                                    void *workspace, void *out, float *lse, hipStream_t st);
+                                    void *workspace, void *stage_ws, void *out, float *lse,
+                                    hipStream_t st);
 
 hipError_t launch_attn_prefill(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                const void *q, const int32_t *ids, int topk, float scale,
-                               void *out, float *lse, hipStream_t st) {
-  return launch_prefill_attention<false>(g, c, b, q, ids, topk, scale, nullptr, out, lse, st);
+                               void *stage_ws, void *out, float *lse, hipStream_t st) {
+  return launch_prefill_attention<false>(g, c, b, q, ids, topk, scale, nullptr, stage_ws, out,
+                                         lse, st);
 }
 
 hipError_t launch_attn_prefill_tokens(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                       const void *q, const int32_t *ids, int topk, float scale,
                                       void *workspace, void *out, float *lse, hipStream_t st) {
-  return launch_prefill_attention<true>(g, c, b, q, ids, topk, scale, workspace, out, lse, st);
+  return launch_prefill_attention<true>(g, c, b, q, ids, topk, scale, workspace, nullptr, out,
+                                        lse, st);
 }
 
 template <bool PT>
 hipError_t launch_prefill_attention(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                     const void *q, const int32_t *ids, int topk, float scale,
-                                    void *workspace, void *out, float *lse, hipStream_t st) {
+                                    void *workspace, void *stage_ws, void *out, float *lse,
+                                    hipStream_t st) {
   if (b.total_units == 0) return hipSuccess;
   if (!g.bf16)
     return launch_attn_f32(g, c, b.units, b.total_units, 1, q, ids, topk, scale, out, lse, st,
@@ -936,7 +1172,18 @@ hipError_t launch_prefill_attention(const Geom &g, const msa_cache_t &c, const m
   const uint16_t *vb = static_cast<const uint16_t *>(c.v_cache);
   uint16_t *ob = static_cast<uint16_t *>(out);
   const float sl2 = scale * kLog2e;
-  if (g.fp8) {
+  const int32_t *remap = nullptr;
+  if (g.fp8 && stage_ws != nullptr && !PT) {   // kept blocks to bf16 once, then the bf16 kernel
+    const Stage sg = stage_layout(g, c.num_phys_blocks, b.total_units, topk,
+                                  static_cast<char *>(stage_ws));
+    if (g.D == 64)
+      stage_kept_blocks<64>(g, c, b, ids, topk, sg, st);
+    else
+      stage_kept_blocks<128>(g, c, b, ids, topk, sg, st);
+    kb = sg.k;
+    vb = sg.vt;
+    remap = sg.direct ? nullptr : sg.slot_of;   // direct copies sit where the cache's blocks do
+  } else if (g.fp8) {
     const uint8_t *k8 = static_cast<const uint8_t *>(c.k_cache);
     const uint8_t *v8 = static_cast<const uint8_t *>(c.v_cache);
     if (g.D == 64)
@@ -951,11 +1198,11 @@ hipError_t launch_prefill_attention(const Geom &g, const msa_cache_t &c, const m
   }
   if (g.D == 64)
     attn_prefill_bf16_kernel<64, PT><<<grid, NW * 64, 0, st>>>(
-        qb, kb, vb, c.block_table, b.units, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
+        qb, kb, vb, c.block_table, remap, b.units, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
         g.nsel, num_uj, pairs, sl2, tu, ob, lse);
   else
     attn_prefill_bf16_kernel<128, PT><<<grid, NW * 64, 0, st>>>(
-        qb, kb, vb, c.block_table, b.units, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
+        qb, kb, vb, c.block_table, remap, b.units, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
         g.nsel, num_uj, pairs, sl2, tu, ob, lse);
   return hipGetLastError();
 }

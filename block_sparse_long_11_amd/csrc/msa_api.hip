@@ -265,10 +265,12 @@ msa_status_t msa_select_topk_blocks(const float *scores, int32_t num_rows, int32
                     "select_topk_blocks");
 }
 
-msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *cache,
-                                     const msa_batch_t *batch, const void *q,
-                                     const int32_t *ids, int32_t topk, float softmax_scale,
-                                     void *out, float *lse, void *stream) {
+namespace {
+
+msa_status_t attn_prefill(const msa_geom_t *geom, const msa_cache_t *cache,
+                          const msa_batch_t *batch, const void *q, const int32_t *ids,
+                          int32_t topk, float softmax_scale, bool staged, void *workspace,
+                          size_t workspace_bytes, void *out, float *lse, void *stream) {
   msa::Geom g;
   msa_status_t st = check_geom(geom, &g);
   if (st != MSA_OK) return st;
@@ -280,10 +282,51 @@ msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *
               "q / ids / out is NULL");
   MSA_REQUIRE(finite_bits(softmax_scale), MSA_ERR_INVALID_ARG,
               "softmax_scale must be finite (<= 0 selects 1/sqrt(head_dim))");
+  void *stage = nullptr;
+  if (staged) {
+    const size_t need = msa::prefill_stage_bytes(g, cache->num_phys_blocks, batch->total_units,
+                                                 topk);
+    if (need > 0) {
+      MSA_REQUIRE(workspace != nullptr, MSA_ERR_INVALID_ARG, "workspace is NULL");
+      MSA_REQUIRE(reinterpret_cast<uintptr_t>(workspace) % 256 == 0, MSA_ERR_INVALID_ARG,
+                  "workspace must be 256-byte aligned");
+      MSA_REQUIRE(workspace_bytes >= need, MSA_ERR_WORKSPACE_TOO_SMALL,
+                  "workspace %zu bytes < %zu needed", workspace_bytes, need);
+      stage = workspace;
+    }
+  }
   return hip_status(msa::launch_attn_prefill(g, *cache, *batch, q, ids, topk,
-                                             resolve_scale(softmax_scale, g.D), out, lse,
+                                             resolve_scale(softmax_scale, g.D), stage, out, lse,
                                              static_cast<hipStream_t>(stream)),
-                    "sparse_attn_prefill");
+                    staged ? "sparse_attn_prefill_staged" : "sparse_attn_prefill");
+}
+
+}  // namespace
+
+msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *cache,
+                                     const msa_batch_t *batch, const void *q,
+                                     const int32_t *ids, int32_t topk, float softmax_scale,
+                                     void *out, float *lse, void *stream) {
+  return attn_prefill(geom, cache, batch, q, ids, topk, softmax_scale, false, nullptr, 0, out,
+                      lse, stream);
+}
+
+size_t msa_prefill_workspace_size(const msa_geom_t *geom, const msa_cache_t *cache,
+                                  int32_t total_units, int32_t topk) {
+  msa::Geom g;
+  if (check_geom(geom, &g) != MSA_OK || cache == nullptr || total_units < 0 || topk <= 0)
+    return 0;
+  return msa::prefill_stage_bytes(g, cache->num_phys_blocks, total_units, topk);
+}
+
+msa_status_t msa_sparse_attn_prefill_staged(const msa_geom_t *geom, const msa_cache_t *cache,
+                                            const msa_batch_t *batch, const void *q,
+                                            const int32_t *ids, int32_t topk,
+                                            float softmax_scale, void *workspace,
+                                            size_t workspace_bytes, void *out, float *lse,
+                                            void *stream) {
+  return attn_prefill(geom, cache, batch, q, ids, topk, softmax_scale, true, workspace,
+                      workspace_bytes, out, lse, stream);
 }
 
 msa_status_t msa_index_scores_prefill_tokens(const msa_geom_t *geom, const msa_cache_t *cache,

@@ -28,9 +28,12 @@ hipError_t launch_index_prefill_tokens(const Geom &g, const msa_cache_t &c,
                                        hipStream_t st);
 hipError_t launch_topk(const float *scores, int rows, int row_len, int topk, int32_t *ids,
                        hipStream_t st);
+// stage_ws (FP8 caches; NULL: convert in the attention kernel) holds
+// prefill_stage_bytes: bf16 copies of the kept blocks, converted once each.
 hipError_t launch_attn_prefill(const Geom &g, const msa_cache_t &c, const msa_batch_t &b,
                                const void *q, const int32_t *ids, int topk, float scale,
-                               void *out, float *lse, hipStream_t st);
+                               void *stage_ws, void *out, float *lse, hipStream_t st);
+size_t prefill_stage_bytes(const Geom &g, int64_t num_phys, int total_units, int topk);
 // Per-query-token prefill attention: ids [total_q][n_sel][topk]; workspace of
 // tokens_workspace_bytes (bf16: per (unit, group) the union of its rows' lists and
 // the row masks; fp32 needs none).

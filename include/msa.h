@@ -73,7 +73,7 @@ typedef enum {
   MSA_OK = 0,
   MSA_ERR_INVALID_ARG = 1,          /* null pointer, bad size or inconsistent shape */
   MSA_ERR_UNSUPPORTED = 2,          /* valid but not built: dtype, D, D_i, block size */
-  MSA_ERR_WORKSPACE_TOO_SMALL = 3,  /* decode workspace smaller than required */
+  MSA_ERR_WORKSPACE_TOO_SMALL = 3,  /* a workspace smaller than required */
   MSA_ERR_HIP = 4                   /* a HIP launch failed */
 } msa_status_t;
 
@@ -95,9 +95,8 @@ typedef enum {
  *     H_s * idx_head_dim <= 512
  *   block_size must be 128.
  *   dtype applies to q, q_idx, out and (cache_format PLAIN) the three caches.
- *   cache_format MSA_CACHE_FP8_E4M3 needs dtype MSA_BF16; it is read by
- *     msa_index_scores, msa_sparse_attn_prefill and msa_sparse_attn_decode, and
- *     written by msa_qk_norm_rope_insert. */
+ *   cache_format MSA_CACHE_FP8_E4M3 needs dtype MSA_BF16; it is read by every
+ *     indexer and attention call and written by msa_qk_norm_rope_insert. */
 typedef struct {
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -207,6 +206,34 @@ msa_status_t msa_sparse_attn_prefill(const msa_geom_t *geom, const msa_cache_t *
                                      const int32_t *ids, int32_t topk,
                                      float softmax_scale, void *out, float *lse,
                                      void *stream);
+
+/* Bytes of device workspace msa_sparse_attn_prefill_staged needs for a batch of
+ * total_units units: 0 unless the caches are FP8; for FP8 a slot map over
+ * cache->num_phys_blocks x H_kv and room for H_kv * min(num_phys_blocks,
+ * total_units * topk) bf16 copies of a block's K and V rows (64 KiB each at
+ * D = 128). Returns 0 for invalid arguments. */
+size_t msa_prefill_workspace_size(const msa_geom_t *geom, const msa_cache_t *cache,
+                                  int32_t total_units, int32_t topk);
+
+/* Step 3 as msa_sparse_attn_prefill (same arguments, rows, masking and result),
+ * with a workspace. On FP8 caches ([dd] "What's coming": FP8 KV-cache paths) every
+ * (physical block, KV head) that some unit keeps is converted once, exactly, to
+ * bf16 in the workspace, and the bf16 attention reads those copies: the same
+ * result up to the order of fp32 sums, without converting a block again in every
+ * work-group that reads it. Other caches need no workspace (size 0; workspace may
+ * be NULL) and run as msa_sparse_attn_prefill.
+ *   workspace >= msa_prefill_workspace_size(geom, cache, batch->total_units, topk)
+ *   bytes, device, 256-byte aligned, owned by the caller; its contents are
+ *   rebuilt by every call (nothing needs clearing), and calls that share one
+ *   workspace must be ordered on a stream.
+ *   MSA_ERR_WORKSPACE_TOO_SMALL when workspace_bytes is below that size (nothing
+ *   is enqueued). Block-table entries must lie in [0, num_phys_blocks). */
+msa_status_t msa_sparse_attn_prefill_staged(const msa_geom_t *geom, const msa_cache_t *cache,
+                                            const msa_batch_t *batch, const void *q,
+                                            const int32_t *ids, int32_t topk,
+                                            float softmax_scale, void *workspace,
+                                            size_t workspace_bytes, void *out, float *lse,
+                                            void *stream);
 
 /* Bytes of device workspace msa_sparse_attn_decode needs. num_splits <= 0 picks
  * the library's own split count for this shape (the same one the decode call

@@ -343,3 +343,37 @@ def test_prefill_tokens_checks(lib):
     assert call(FAKE * 256, need, scale=float("inf")) == INVALID
     assert call(FAKE * 256, need, c=_cache(max_blocks_per_seq=131073)) == UNSUPPORTED
     assert call(FAKE * 256, need, g=_geom(head_dim=96)) == UNSUPPORTED
+
+
+def test_prefill_staged_checks(lib):
+    """Staged prefill attention: workspace size (0 off FP8; FP8: slot map, slot list and
+    bf16 copies of K and V for H_kv * min(blocks, units * topk) slots) and the argument
+    checks before any launch."""
+    fp8 = _geom(cache_format=msa.MSA_CACHE_FP8_E4M3)
+    c, b = _cache(), msa._Batch(FAKE, 3, 300)
+    size = lambda g, cache, units, topk: lib.msa_prefill_workspace_size(
+        ctypes.byref(g), None if cache is None else ctypes.byref(cache), units, topk)
+    assert size(_geom(), c, 3, 16) == 0
+    assert size(_geom(dtype=msa.MSA_F32), c, 3, 16) == 0
+    assert size(fp8, None, 3, 16) == 0
+    assert size(fp8, c, 3, 0) == 0
+    al = lambda x: (x + 255) // 256 * 256
+    for phys, units, topk in ((10, 3, 16), (1000, 3, 2), (4096, 256, 16)):
+        S = 4 * min(phys, units * topk)
+        expect = 256 + al(phys * 4 * 4) + al(S * 4) + 2 * S * 128 * 128 * 2
+        assert size(fp8, _cache(num_phys_blocks=phys), units, topk) == expect
+    need = size(fp8, c, 3, 16)
+    call = lambda ws, nbytes, **kw: lib.msa_sparse_attn_prefill_staged(
+        ctypes.byref(kw.get("g", fp8)), ctypes.byref(c), ctypes.byref(b), FAKE, FAKE,
+        kw.get("topk", 16), kw.get("scale", 0.0), ws, nbytes, FAKE, None, None)
+    assert call(FAKE * 256, need - 1) == WS_SMALL
+    assert call(None, need) == INVALID
+    assert call(FAKE + 4, need) == INVALID               # misaligned
+    assert call(FAKE * 256, need, topk=0) == INVALID
+    assert call(FAKE * 256, need, scale=float("nan")) == INVALID
+    assert call(FAKE * 256, need, g=_geom(head_dim=96, cache_format=msa.MSA_CACHE_FP8_E4M3)) \
+        == UNSUPPORTED
+    empty = msa._Batch(None, 0, 0)
+    assert lib.msa_sparse_attn_prefill_staged(ctypes.byref(fp8), ctypes.byref(c),
+                                              ctypes.byref(empty), None, None, 16, 0.0, None, 0,
+                                              None, None, None) == OK

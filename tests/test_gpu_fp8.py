@@ -361,16 +361,59 @@ PREFILL_FULL = {
                                num_kv_heads=4, num_idx_heads=8, num_sel_groups=1, topk=6),
     "one_group_di32_w256": dict(seq_lens=(1500, 200), q_lens=(700, 200), num_idx_heads=8,
                                 idx_head_dim=32, num_sel_groups=1, topk=5),
+    # more cache blocks than the units keep in all (staged: slots claimed per kept
+    # pair instead of copies where the cache holds the blocks)
+    "long_prefixes": dict(seq_lens=(20000, 3000), q_lens=(130, 200), topk=5),
+    "long_prefix_one_group": dict(seq_lens=(12000,), q_lens=(300,), num_sel_groups=1, topk=3),
 }
 
 
+@pytest.mark.parametrize("staged", [False, True], ids=["direct", "staged"])
 @pytest.mark.parametrize("name", list(PREFILL_FULL))
-def test_fp8_prefill_parity(name, gpu_device):
+def test_fp8_prefill_parity(name, staged, gpu_device):
+    """direct: the attention kernel converts the codes it reads; staged: every kept
+    (block, KV head) is converted once into the workspace and the bf16 kernel reads
+    the copies (msa_sparse_attn_prefill_staged)."""
     w = synth.small_workload(cache_format="fp8", **PREFILL_FULL[name])
-    say(f"fp8 prefill {name}")
+    say(f"fp8 prefill {name} {'staged' if staged else 'direct'}")
     inp, geom, cache = T.setup(w, gpu_device, permute=True)
-    res = T.run_gpu(w, inp, geom, cache, gpu_device)
+    res = T.run_gpu(w, inp, geom, cache, gpu_device, staged=staged)
     prefill_parity(w, inp, cache, res, name)
+
+
+STAGED_EXACT = {
+    # copies where the cache holds the blocks (blocks <= units * topk)
+    "in_place": dict(seq_lens=(1500, 700, 129), q_lens=(600, 700, 129), topk=5),
+    # claimed slots (blocks > units * topk), one selection group
+    "claimed": dict(seq_lens=(20000, 900), q_lens=(260, 129), topk=4, num_sel_groups=1),
+}
+
+
+@pytest.mark.parametrize("name", list(STAGED_EXACT))
+def test_fp8_prefill_staged_equals_bf16_path(name, gpu_device):
+    """The staged copies are exact: attending them equals the bf16 prefill call on
+    bf16 caches holding the decoded values, bit for bit (same kernel, same inputs)."""
+    w = synth.small_workload(cache_format="fp8", num_q_heads=64, num_kv_heads=4,
+                             num_idx_heads=8, **dict(dict(num_sel_groups=4), **STAGED_EXACT[name]))
+    say(f"fp8 staged ({name}) against bf16 caches of the decoded values")
+    inp, geom, cache = T.setup(w, gpu_device, permute=True)
+    batch = msa.make_batch(w.seq_lens, w.q_lens, gpu_device)
+    res = msa.prefill(geom, cache, batch, inp["q"], inp["q_idx"], w.topk, staged=True)
+    h = fp8_host(cache)
+    kd = torch.from_numpy(O.mx_dequantize(h["k"], h["k_s"])).to(torch.bfloat16)
+    vd = torch.from_numpy(O.mx_dequantize(h["v"], h["v_s"])).to(torch.bfloat16)
+    id_ = torch.from_numpy(O.mx_dequantize(h["i"], h["i_s"])).to(torch.bfloat16)
+    k16 = kd.to(gpu_device).contiguous()
+    v16 = vd.transpose(2, 3).to(gpu_device).contiguous()          # back to d-major
+    c16 = msa.Cache(k16, v16, id_.to(gpu_device), inp["block_table"], inp["seq_lens"])
+    g16 = msa.Geometry(w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_idx_heads,
+                       w.idx_head_dim, w.num_sel_groups, "bf16", "plain")
+    out = torch.empty_like(inp["q"])
+    lse = torch.empty(inp["q"].shape[:2], dtype=torch.float32, device=gpu_device)
+    msa.msa_sparse_attn_prefill(g16, c16, batch, inp["q"], res["ids"], w.topk, out, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), res["out"].cpu())
+    assert torch.equal(lse.cpu(), res["lse"].cpu())
 
 
 def test_fp8_insert_then_prefill_step(gpu_device):
@@ -394,16 +437,17 @@ def test_fp8_insert_then_prefill_step(gpu_device):
     prefill_parity(w, inp, cache, res, "prefill after insert")
 
 
-@pytest.mark.parametrize("name", ["prefill_32k_fp8", "prefill_32k_fp8_sel1"])
-def test_fp8_full_size_prefill_32k_sampled(name, gpu_device):
+@pytest.mark.parametrize("name,staged", [("prefill_32k_fp8", False), ("prefill_32k_fp8", True),
+                                         ("prefill_32k_fp8_sel1", True)])
+def test_fp8_full_size_prefill_32k_sampled(name, staged, gpu_device):
     """The 32k prefill on FP8 caches (the benchmark's launches, four selection groups
-    or one): sampled units, every group's scores and ids, attention of sampled rows
-    for every KV head."""
+    or one; the staged attention is the one the benchmark times): sampled units,
+    every group's scores and ids, attention of sampled rows for every KV head."""
     w = synth.WORKLOADS[name]
     say(f"{w.name} generate")
     inp, geom, cache = T.setup(w, gpu_device)
-    say(f"{w.name} run")
-    res = T.run_gpu(w, inp, geom, cache, gpu_device)
+    say(f"{w.name} run" + (" staged" if staged else ""))
+    res = T.run_gpu(w, inp, geom, cache, gpu_device, staged=staged)
     units = O.prefill_units(w.seq_lens, w.q_lens)
     bt_all = inp["block_table"].cpu().numpy()
     Hs, G = w.num_idx_heads // w.num_sel_groups, w.num_q_heads // w.num_kv_heads

@@ -27,9 +27,10 @@ def capture(fn):
     return g
 
 
-def make_step(w, inp, geom, cache, dev, static=False):
+def make_step(w, inp, geom, cache, dev, static=False, staged=False):
     """Pre-allocated outputs and a step that writes them (no allocation inside).
-    static: decode attention through msa_sparse_attn_decode_static (no workspace)."""
+    static: decode attention through msa_sparse_attn_decode_static (no workspace);
+    staged: prefill attention through msa_sparse_attn_prefill_staged."""
     T = w.tokens_per_seq
     if w.is_decode:
         rows, batch = w.total_q, None
@@ -46,6 +47,9 @@ def make_step(w, inp, geom, cache, dev, static=False):
     elif w.per_token:
         ws = msa.workspace(msa.msa_prefill_tokens_workspace_size(geom, batch.total_units,
                                                                  batch.total_q, w.topk), dev)
+    elif staged:
+        ws = msa.workspace(msa.msa_prefill_workspace_size(geom, cache, batch.total_units,
+                                                          w.topk), dev)
     else:
         ws = None
 
@@ -68,6 +72,9 @@ def make_step(w, inp, geom, cache, dev, static=False):
                                        ws, bufs["lse"])
         elif w.per_token:
             msa.msa_sparse_attn_prefill_tokens(geom, cache, batch, inp["q"], bufs["ids"], w.topk,
+                                               bufs["out"], ws, bufs["lse"])
+        elif staged:
+            msa.msa_sparse_attn_prefill_staged(geom, cache, batch, inp["q"], bufs["ids"], w.topk,
                                                bufs["out"], ws, bufs["lse"])
         else:
             msa.msa_sparse_attn_prefill(geom, cache, batch, inp["q"], bufs["ids"], w.topk,
@@ -94,6 +101,17 @@ CASES = {
                                          num_q_heads=16, num_kv_heads=4, num_idx_heads=8,
                                          num_sel_groups=1, topk=5, cache_format="fp8",
                                          per_token=True),
+    # FP8 prefill through the staged attention: the slot map is reset, kept blocks
+    # claimed and converted, then attended, on every replay
+    "prefill_fp8_staged": dict(seq_lens=(1500, 700), q_lens=(600, 700), topk=4,
+                               cache_format="fp8", staged=True),
+    "prefill_fp8_staged_one_group": dict(seq_lens=(1500, 300), q_lens=(400, 300),
+                                         num_q_heads=16, num_kv_heads=4, num_idx_heads=8,
+                                         num_sel_groups=1, topk=5, cache_format="fp8",
+                                         staged=True),
+    # more cache blocks than kept entries: slots claimed through the slot map
+    "prefill_fp8_staged_claimed": dict(seq_lens=(20000, 700), q_lens=(200, 700), topk=4,
+                                       cache_format="fp8", staged=True),
     # the decode attention that keeps its partials in the library's static scratch
     "decode_static": dict(seq_lens=(3000, 700, 129, 20000), q_lens=None, topk=5,
                           static=True),
@@ -104,10 +122,11 @@ CASES = {
 def test_graph_replays_match_eager(name, gpu_device):
     kw = dict(CASES[name])
     static = kw.pop("static", False)
+    staged = kw.pop("staged", False)
     w = synth.small_workload(**kw)
     say(f"graph {name}")
     inp, geom, cache = T_.setup(w, gpu_device, permute=True)
-    step, bufs = make_step(w, inp, geom, cache, gpu_device, static)
+    step, bufs = make_step(w, inp, geom, cache, gpu_device, static, staged)
     step()
     torch.cuda.synchronize()
     eager = {k: v.clone() for k, v in bufs.items()}

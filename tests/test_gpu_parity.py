@@ -37,12 +37,12 @@ def setup(w, dev, permute=False):
     return inp, geometry(w), cache_of(inp)
 
 
-def run_gpu(w, inp, geom, cache, dev, num_splits=0):
+def run_gpu(w, inp, geom, cache, dev, num_splits=0, staged=False):
     if w.is_decode:
         res = msa.decode(geom, cache, inp["q"], inp["q_idx"], w.topk, num_splits)
     else:
         batch = msa.make_batch(w.seq_lens, w.q_lens, dev)
-        res = msa.prefill(geom, cache, batch, inp["q"], inp["q_idx"], w.topk)
+        res = msa.prefill(geom, cache, batch, inp["q"], inp["q_idx"], w.topk, staged=staged)
     torch.cuda.synchronize()
     return {k: v.cpu() for k, v in res.items()}
 
