@@ -58,9 +58,13 @@ def measured_peaks(dev):
     lib.msa_probe_stream_read.restype = ctypes.c_int
     lib.msa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                           ctypes.c_void_p, ctypes.c_void_p]
-    lib.msa_probe_mfma_bf16.restype = ctypes.c_int
-    lib.msa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                        ctypes.c_void_p]
+    for name in ("msa_probe_mfma_bf16", "msa_probe_mfma_bf16_random"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    lib.msa_probe_mfma_valu.restype = ctypes.c_int
+    lib.msa_probe_mfma_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p]
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     nbytes = 4 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -93,12 +97,29 @@ def measured_peaks(dev):
                                           stream), 1)      # clock ramp
     t = timed(lambda: lib.msa_probe_mfma_bf16(groups, iters, ctypes.c_void_p(sink.data_ptr()),
                                               stream), 3)
+    t_rand = timed(lambda: lib.msa_probe_mfma_bf16_random(
+        groups, iters, ctypes.c_void_p(sink.data_ptr()), stream), 3)
+    # MFMA and softmax-like fp32 VALU work of two waves on one SIMD: alone and together
+    co_groups, co_iters = 1024, 2000
+    co = {mode: timed(lambda: lib.msa_probe_mfma_valu(co_groups, co_iters, mode,
+                                                      ctypes.c_void_p(sink.data_ptr()), stream),
+                      3) * 1e3 for mode in (1, 2, 3)}
+    hidden = (co[1] + co[2] - co[3]) / min(co[1], co[2])
     best_g = max(hbm, key=hbm.get)
     return dict(hbm_gbs=hbm[best_g], mfma_bf16_tflops=flops / t / 1e12,
+                mfma_bf16_random_tflops=flops / t_rand / 1e12,
+                mfma_valu_coexec=dict(mfma_ms=co[1], valu_ms=co[2], both_ms=co[3],
+                                      hidden_frac_of_smaller=hidden,
+                                      probe="one work-group of 8 waves per CU; waves 0-3: "
+                                            f"{co_iters} rounds of 16 random-operand MFMAs, "
+                                            "waves 4-7: as many rounds of a softmax tile's "
+                                            "fp32 work (max3 tree, 16 x fma+exp2+add, 8 packs)"),
                 hbm_probe=f"streaming read of 4 GiB, 16-byte non-temporal loads, 8 in flight "
                           f"per thread, best of {sorted(hbm)} work-groups (best {best_g})",
                 mfma_probe="v_mfma_f32_32x32x16_bf16, 8 independent chains per wave, "
-                           f"{groups} work-groups of 4 waves, register operands")
+                           f"{groups} work-groups of 4 waves, register operands (small "
+                           "constants; the random-operand figure uses full-mantissa values "
+                           "uniform in (-1.7, 1.7))")
 
 
 def geometry(w):
@@ -542,8 +563,11 @@ def main():
     peaks = None
     if not args.no_probes:
         peaks = measured_peaks(dev)
+        co = peaks["mfma_valu_coexec"]
         log(f"measured peaks: HBM read {peaks['hbm_gbs']:.0f} GB/s, bf16 MFMA "
-            f"{peaks['mfma_bf16_tflops']:.0f} TFLOP/s")
+            f"{peaks['mfma_bf16_tflops']:.0f} TFLOP/s (random operands "
+            f"{peaks['mfma_bf16_random_tflops']:.0f}); MFMA {co['mfma_ms']:.3f} ms, VALU "
+            f"{co['valu_ms']:.3f} ms, both {co['both_ms']:.3f} ms on one SIMD")
         torch.cuda.empty_cache()
 
     w = synth.WORKLOADS[args.workload]
@@ -592,6 +616,9 @@ def main():
         mp = peaks["hbm_gbs"] if rf["bound"] == "hbm" else peaks["mfma_bf16_tflops"]
         rf["measured_peak"] = mp
         rf["frac_of_measured_peak"] = rf["achieved"] / mp
+        if rf["bound"] == "mfma":
+            rf["frac_of_random_operand_mfma_peak"] = \
+                rf["achieved"] / peaks["mfma_bf16_random_tflops"]
 
     for r in [main_res] + ([second] if second else []) + extra:
         add_measured(r)

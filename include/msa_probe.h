@@ -1,6 +1,7 @@
 /*
  * msa_probe.h - peak-rate probes of the MI355X (gfx950) for the measurement of
- * libmsa: a plain streaming read of device memory and a dense bf16 MFMA loop.
+ * libmsa: a plain streaming read of device memory, dense bf16 MFMA loops on
+ * constant and on random operands, and MFMA next to fp32 VALU work on one SIMD.
  * They give the practical ceilings the kernels' roofline fractions are also
  * quoted against (next to the published peaks: 8 TB/s HBM3E, 2.5 PFLOP/s dense
  * bf16). Built as libmsa_probe.so; not part of the attention path.
@@ -34,6 +35,21 @@ int msa_probe_stream_read(const void *buf, size_t bytes, int groups, uint32_t *s
  * sink[groups * 4]. Floating-point work: groups * 4 * iters * 8 * 32768 flop.
  * groups in [1, 65536], iters >= 1. Returns as msa_probe_stream_read. */
 int msa_probe_mfma_bf16(int groups, int iters, float *sink, void *stream);
+
+/* As msa_probe_mfma_bf16 with random operands: every lane holds 8 operand pairs
+ * uniform in (-1.7, 1.7) that use all bf16 mantissa bits (the MFMA rate depends on
+ * the data: small constant operands run faster). Same flop count and sink. */
+int msa_probe_mfma_bf16_random(int groups, int iters, float *sink, void *stream);
+
+/* MFMA and fp32 VALU work of two waves on one SIMD: `groups` work-groups of 8
+ * waves holding 128 KiB of LDS each (one per CU; waves w and w + 4 share a SIMD).
+ * mode 1: waves 0-3 run `iters` rounds of 16 random-operand 32x32x16 bf16 MFMAs
+ * (groups * 4 * iters * 16 * 32768 flop); mode 2: waves 4-7 run `iters` rounds of
+ * a softmax tile's fp32 work on 16 values per lane (max3 tree, 16 x (fma, exp2,
+ * add), 8 bf16 packs); mode 3: both at once. Comparing the three times shows how
+ * much of the smaller one the SIMD hides. Writes sink[groups * 8]. groups in [1,
+ * 32768], iters >= 1, mode in {1, 2, 3}. Returns as msa_probe_stream_read. */
+int msa_probe_mfma_valu(int groups, int iters, int mode, float *sink, void *stream);
 
 #ifdef __cplusplus
 }

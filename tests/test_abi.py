@@ -377,3 +377,33 @@ def test_prefill_staged_checks(lib):
     assert lib.msa_sparse_attn_prefill_staged(ctypes.byref(fp8), ctypes.byref(c),
                                               ctypes.byref(empty), None, None, 16, 0.0, None, 0,
                                               None, None, None) == OK
+
+
+def test_probe_library_exports_and_checks():
+    """libmsa_probe.so (the bench's peak-rate probes) exports every function of
+    include/msa_probe.h and rejects bad arguments before any launch (-1)."""
+    path = os.path.join(ROOT, "block_sparse_long_11_amd", "libmsa_probe.so")
+    if not os.path.exists(path):
+        pytest.fail("libmsa_probe.so is not built (run __graft_entry__.build())")
+    text = open(os.path.join(ROOT, "include", "msa_probe.h")).read()
+    names = sorted(set(re.findall(r"^int\s+(msa_probe_[a-z0-9_]+)\s*\(", text, re.M)))
+    assert names == ["msa_probe_mfma_bf16", "msa_probe_mfma_bf16_random", "msa_probe_mfma_valu",
+                     "msa_probe_stream_read"]
+    plib = ctypes.CDLL(path)
+    for n in names:
+        getattr(plib, n).restype = ctypes.c_int
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    plib.msa_probe_stream_read.argtypes = [vp, sz, ctypes.c_int, vp, vp]
+    assert plib.msa_probe_stream_read(FAKE, 1000, 64, FAKE, None) == -1      # not 32 KiB units
+    assert plib.msa_probe_stream_read(FAKE, 32768, 0, FAKE, None) == -1
+    assert plib.msa_probe_stream_read(None, 32768, 64, FAKE, None) == -1
+    for n in ("msa_probe_mfma_bf16", "msa_probe_mfma_bf16_random"):
+        fn = getattr(plib, n)
+        fn.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+        assert fn(0, 10, FAKE, None) == -1
+        assert fn(64, 0, FAKE, None) == -1
+        assert fn(64, 10, None, None) == -1
+    plib.msa_probe_mfma_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    assert plib.msa_probe_mfma_valu(64, 10, 0, FAKE, None) == -1
+    assert plib.msa_probe_mfma_valu(64, 10, 4, FAKE, None) == -1
+    assert plib.msa_probe_mfma_valu(32769, 10, 3, FAKE, None) == -1
