@@ -306,6 +306,14 @@ def measured_traffic(kernel_key, source_file):
         return None
 
 
+def attn_prefill_traffic(workload, staged):
+    """Prefill attention's HBM bytes per call; the staged call adds its slot marking
+    and block conversion launches to the attention's."""
+    keys = ["attn_prefill"] + (["stage_mark", "stage_convert"] if staged else [])
+    parts = [measured_traffic(f"{workload}:{k}", "attn_prefill.hip") for k in keys]
+    return None if any(v is None for v in parts) else sum(parts)
+
+
 def graph_ms_per_step(runner, steps, warmup):
     """The same step captured once in a HIP graph and replayed: the time per
     replay, without the launch gaps between the step's kernels."""
@@ -387,8 +395,7 @@ def measure(w, dev, steps, warmup, permute=False):
         res["roofline"] = dict(kernel=kname, bound="mfma",
                                achieved=flops / t / 1e12, peak=MFMA_BF16_PEAK_TFLOPS,
                                unit="TFLOP/s", frac=flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                               traffic=measured_traffic(f"{w.name}:attn_prefill",
-                                                        "attn_prefill.hip"),
+                               traffic=attn_prefill_traffic(w.name, r.staged),
                                traffic_source=TRAFFIC_SOURCE, algorithmic_flops=flops)
     res["_runner"] = r
     return res
