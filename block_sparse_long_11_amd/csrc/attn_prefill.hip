@@ -330,10 +330,15 @@ void attn_prefill_bf16_kernel(
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
-  f32x16 s = f32x16{};
+  // S^T of the even and the odd tiles: a tile's scores stay in place from its M
+  // phase, through its softmax phase, to the next M phase, which forms its
+  // probabilities while it accumulates the next tile's scores in the other half
+  f32x16 sc[2] = {f32x16{}, f32x16{}};
   bf16x8 kf[KS], vf[2 * DT], pf[2];
   float m_ref = kMaxFloor;                // reference maximum, log2 units
   float l_run = 0.f;                      // this lane's share of the row sum
+  float msub = 0.f;                       // per token: +inf when this lane's row does not
+                                          // keep the block of the tile in its softmax phase
 
   auto read_k = [&](auto r, int kt2) __attribute__((always_inline)) {
     constexpr int R = decltype(r)::value % 4;
@@ -351,26 +356,66 @@ void attn_prefill_bf16_kernel(
                                                            dt * 32 * VC * 16);
   };
 
-  // M phase: S^T = K Q^T of the current tile and O^T += V^T P^T of the previous
-  // one, interleaved so that neither accumulation chain waits on itself.
-  auto mphase = [&](auto pv_tag, auto qk_tag) __attribute__((always_inline)) {
+  // M phase: S^T = K Q^T of the current tile into sc[P], and for the previous tile
+  // (scores in sc[1 - P], its softmax phase done) the probabilities against the
+  // reference maximum that phase left, their row sum and O^T += V^T P^T. The
+  // score MFMAs do not wait for the probabilities, so the exponentials run while
+  // the matrix core is busy with them.
+  auto mphase = [&](auto pv_tag, auto qk_tag, auto par) __attribute__((always_inline)) {
     constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
-    if constexpr (QK) s = f32x16{};
-    constexpr int NI = KS > 2 * DT ? KS : 2 * DT;
+    constexpr int P = decltype(par)::value;
+    if constexpr (QK) {
+      sc[P] = f32x16{};
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      if constexpr (QK)
-        if (i < KS) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i], s, 0, 0, 0);
-      if constexpr (PV)
-        if (i < 2 * DT)
-          o[i / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i % 2], o[i / 2], 0, 0, 0);
+      for (int i = 0; i < KS; ++i)
+        sc[P] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i], sc[P], 0, 0, 0);
+    }
+    if constexpr (PV) {
+      const float mr = PT ? m_ref + msub : m_ref;   // a row without the block: exp2(-inf) = 0
+      float ls = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t w[4];
+#pragma unroll
+        for (int jj = 0; jj < 8; jj += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[1 - P][8 * h + jj], c, -mr));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[1 - P][8 * h + jj + 1], c, -mr));
+          w[jj / 2] = cvt_pk_bf16(p0, p1);
+          ls += p0 + p1;
+        }
+        pf[h] = as_bf16x8(uint4{w[0], w[1], w[2], w[3]});
+      }
+      l_run += ls;
+      asm volatile("" : "+v"(l_run));   // summed here, not where the next phase uses it
+#pragma unroll
+      for (int i = 0; i < 2 * DT; ++i)
+        o[i / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i % 2], o[i / 2], 0, 0, 0);
+    }
+    if constexpr (PV && QK) {
+      // issue order: each score MFMA followed by a pair of probabilities (fma, exp),
+      // each P.V MFMA by the packing and summing work, so that the VALU work fills
+      // the matrix core's cycles instead of following them
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 32 / KS, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * DT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 24 / (2 * DT), 0);
+      }
     }
   };
 
-  // Softmax of tile kt (0..3) of the block at position bp; the first block is
-  // always masked (MASK), any other one only when it reaches the unit's first query.
-  auto softmax = [&](auto mask_tag, int kt, int bp) __attribute__((always_inline)) {
+  // Softmax phase of tile kt (0..3) of the block at position bp, scores in sc[P]:
+  // the causal mask (the first block always, MASK; any other one only when it
+  // reaches the unit's first query), the tile's row maximum and, when it grew by
+  // more than the slack, the rescale of O and the row sum.
+  auto softmax = [&](auto mask_tag, auto par, int kt, int bp) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int P = decltype(par)::value;
+    f32x16 &s = sc[P];
     bool do_mask = MASK;
     if constexpr (!MASK || PT) {
       const bool lt = late_at(bp);
@@ -394,7 +439,6 @@ void attn_prefill_bf16_kernel(
     }
     // per token: a row that does not keep this block sees none of its keys (its
     // maximum ignores the tile, its probabilities are exp2(-inf) = 0)
-    float msub = 0.f;
     if constexpr (PT) {
       const bool keep = ((__builtin_amdgcn_readlane(keepw, bp & 63) >> n) & 1u) != 0;
       x = keep ? x : neg_inf();
@@ -409,44 +453,33 @@ void attn_prefill_bf16_kernel(
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
     }
-    const float mr = PT ? m_ref + msub : m_ref;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t w[4];
-#pragma unroll
-      for (int jj = 0; jj < 8; jj += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj], c, -mr));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + jj + 1], c, -mr));
-        w[jj / 2] = cvt_pk_bf16(p0, p1);
-        l_run += p0 + p1;
-      }
-      pf[h] = as_bf16x8(uint4{w[0], w[1], w[2], w[3]});
-    }
   };
 
   // Tiles 4 bp .. 4 bp + 3 of block position bp, whose half-blocks sit in ring
-  // slots R0 and R0 + 1; the next block's are R0 + 2 and R0 + 3.
+  // slots R0 and R0 + 1; the next block's are R0 + 2 and R0 + 3. Tile kt's scores
+  // use sc[kt % 2] (four tiles a block keep the parity of every block's tiles).
   auto block_step = [&](auto mask_tag, auto r0, int bp) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int R0 = decltype(r0)::value;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    auto tile = [&](auto ktc) __attribute__((always_inline)) {
+      constexpr int kt = decltype(ktc)::value;
+      constexpr int P = kt % 2;
       const int T = 4 * bp + kt;
       if (MASK && kt == 0)
-        mphase(std::false_type{}, std::true_type{});     // first tile: no previous P
+        mphase(std::false_type{}, std::true_type{}, ic<P>{});   // first tile: no previous P
       else
-        mphase(std::true_type{}, std::true_type{});
+        mphase(std::true_type{}, std::true_type{}, ic<P>{});
       phase_barrier();
-      if (kt == 0) read_k(ic<R0>{}, 1);
-      else if (kt == 1) read_k(ic<R0 + 1>{}, 0);
-      else if (kt == 2) read_k(ic<R0 + 1>{}, 1);
+      if constexpr (kt == 0) read_k(ic<R0>{}, 1);
+      else if constexpr (kt == 1) read_k(ic<R0 + 1>{}, 0);
+      else if constexpr (kt == 2) read_k(ic<R0 + 1>{}, 1);
       else if (T + 1 < 4 * nk) read_k(ic<R0 + 2>{}, 0);
-      if (kt < 2) read_v(ic<R0>{}, kt);
+      if constexpr (kt < 2) read_v(ic<R0>{}, kt);
       else read_v(ic<R0 + 1>{}, kt - 2);
-      softmax(mask_tag, kt, bp);
-      if (kt == 1) {
+      softmax(mask_tag, ic<P>{}, kt, bp);
+      if constexpr (kt == 1) {
         if (2 * bp + 3 < NH) issue(2 * bp + 3, ic<R0 + 3>{});
-      } else if (kt == 3) {
+      } else if constexpr (kt == 3) {
         if (2 * bp + 4 < NH) issue(2 * bp + 4, ic<R0 + 4>{});
       } else {
         const int hb = 2 * bp + kt / 2 + 1;   // first read in S(T + 1)
@@ -456,7 +489,11 @@ void attn_prefill_bf16_kernel(
         }
       }
       phase_barrier();
-    }
+    };
+    tile(ic<0>{});
+    tile(ic<1>{});
+    tile(ic<2>{});
+    tile(ic<3>{});
   };
 
   // Prologue: half-blocks 0..2 requested, 0 waited for, K of tile 0 read.
@@ -478,7 +515,8 @@ void attn_prefill_bf16_kernel(
     if (bp + 1 >= nk) break;
     block_step(std::false_type{}, ic<0>{}, bp + 1);
   }
-  mphase(std::true_type{}, std::false_type{});          // O^T += V^T P^T of the last tile
+  // probabilities and O^T += V^T P^T of the last tile (odd: its scores are in sc[1])
+  mphase(std::true_type{}, std::false_type{}, ic<0>{});
   if (grp == 0) phase_barrier();
 
   if (!active) return;

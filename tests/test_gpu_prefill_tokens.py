@@ -130,7 +130,9 @@ def test_prefill_tokens_pool_to_the_tile_scores(gpu_device):
         tile = b["scores"][u].numpy()
         inf = ~np.isfinite(tile)
         assert np.array_equal(pooled[inf], tile[inf])
-        assert (np.abs(pooled - tile)[~inf] <= 2 * np.broadcast_to(tol[:, None], tile.shape)[~inf]).all()
+        fin = ~inf
+        assert (np.abs(pooled[fin] - tile[fin]) <=
+                2 * np.broadcast_to(tol[:, None], tile.shape)[fin]).all()
 
 
 @pytest.mark.parametrize("name", ["prefill_32k", "prefill_32k_sel1"])
