@@ -286,20 +286,31 @@ class Runner:
 
 TRAFFIC_SOURCE = ("committed rocprofv3 counter profile (profiles/pmc_traffic.json: FETCH_SIZE and "
                   "WRITE_SIZE per launch, scaled by a plain-copy calibration), used only while the "
-                  "kernel's source file is unchanged; not measured in this run")
+                  "code of the kernel's source file (comments aside) is unchanged; not measured in "
+                  "this run")
+
+
+def source_code_hash(path):
+    """sha256 of a source file's code: comments removed and whitespace runs
+    collapsed, so that an edit of comments alone keeps the hash."""
+    import re
+    with open(path, encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
 def measured_traffic(kernel_key, source_file):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a plain copy), or
-    None when there is no entry or the kernel's source changed since it was taken."""
+    None when there is no entry or the kernel's source code changed since it was
+    taken."""
     try:
         with open(PMC_SUMMARY) as f:
             summ = json.load(f)
         e = summ["kernels"][kernel_key]
-        with open(os.path.join(CSRC, source_file), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        if sha != e["source_sha256"]:
+        if source_code_hash(os.path.join(CSRC, source_file)) != e["source_code_sha256"]:
             return None
         return e["hbm_bytes_per_launch"]
     except (OSError, KeyError, ValueError):

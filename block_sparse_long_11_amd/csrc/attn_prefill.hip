@@ -25,11 +25,16 @@
 // half a, register 8h+jj holds key 16h + 8a + jj, which is exactly the k-index
 // the P^T operand needs, so V^T is read in natural key order.
 //
-// Ping-pong: every tile T is split into an MFMA phase M(T) (S^T of tile T and
-// O^T += V^T P^T of tile T-1) and a softmax phase S(T) (mask, row maximum,
-// exponentials, P, and the LDS reads of the operands of M(T+1)). Phases end at
+// Ping-pong: every tile T is split into an MFMA phase M(T) and a softmax phase
+// S(T). M(T) accumulates S^T of tile T and, for tile T-1, forms the probabilities
+// (against the reference maximum S(T-1) left), packs P, adds the row sum and
+// accumulates O^T += V^T P^T, each score MFMA followed by a pair of exponentials
+// so that the VALU work fills the matrix core's cycles. S(T) masks tile T, takes
+// its row maximum, rescales O and the row sum when needed, and reads the operands
+// of M(T+1) from LDS. Scores of even and odd tiles alternate between two
+// accumulators, so tile T's scores wait in place for M(T+1). Phases end at
 // work-group barriers, and waves 4..7 run one phase behind waves 0..3, so on
-// every SIMD one wave issues MFMAs while the other does the softmax.
+// every SIMD one wave is in an MFMA phase while the other is in a softmax phase.
 //
 // K/V staging: half-blocks of 64 keys (K as [key][d], V as the cache's d-major
 // [d][key]) go through a ring of 4 LDS slots by direct global->LDS loads,
