@@ -669,10 +669,11 @@ constexpr int kChunk2 = 32;   // blocks per work-group (16: 1-3% slower, 64: slo
 constexpr int kTiles = 2;
 constexpr int kIdxThreads = kTiles * 2 * kWave;
 // x-block sizes of ItemOrder: 32 tile pairs (their query rows of one group, 2 MiB
-// at 128 channels, and the current 1 MiB key chunk fit one XCD's 4 MB L2); 8 tile
-// pairs for the wide kernel (512 channels: 2 MiB of query rows, 2 MiB chunks)
+// at 128 channels, and the current 1 MiB key chunk fit one XCD's 4 MB L2); 4 tile
+// pairs for the wide kernel (512 channels: 1 MiB of query rows beside 2 MiB key
+// chunks; 8 measured 3-5% slower, 2 and 1 far slower)
 constexpr int kPairBlock = 32;
-constexpr int kWidePairBlock = 8;
+constexpr int kWidePairBlock = 4;
 
 template <int DI, int HS, bool FP8, bool PT>
 __global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
