@@ -385,6 +385,9 @@ hipError_t launch_attn_decode(const Geom &g, const msa_cache_t &c, int T, const 
       qb, c.k_cache, c.v_cache, c.k_scale, c.v_scale, c.block_table, c.seq_lens, ids,     \
       topk, c.max_blocks_per_seq, g.Hq, g.Hkv, g.nsel, T, num_splits, per, sl2, o_part,    \
       lse_part)
+  MSA_LOG_LAUNCH(g.fp8 ? "attn_decode_bf16_kernel (FP8 caches)" : "attn_decode_bf16_kernel", grid,
+                 kDecThreads, 0);
+  MSA_LOG_LAUNCH("combine_kernel", rows * g.Hq, g.D, 0);
   if (g.D == 64) {
     if (g.fp8) MSA_DEC(64, true); else MSA_DEC(64, false);
     combine_kernel<64, true><<<rows * g.Hq, 64, 0, st>>>(o_part, lse_part, num_splits, out,

@@ -836,6 +836,7 @@ hipError_t launch_attn_f32(const Geom &g, const msa_cache_t &c, const msa_unit_t
   const float *qf = static_cast<const float *>(q);
   const float *kf = static_cast<const float *>(c.k_cache);
   const float *vf = static_cast<const float *>(c.v_cache);
+  MSA_LOG_LAUNCH("attn_f32_kernel", grid, 128, 0);
   if (g.D == 64)
     attn_f32_kernel<64><<<grid, 128, 0, st>>>(qf, kf, vf, c.block_table, c.seq_lens, units,
                                               T, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,
@@ -1126,6 +1127,8 @@ void stage_kept_blocks(const Geom &g, const msa_cache_t &c, const msa_batch_t &b
   const uint8_t *v8 = static_cast<const uint8_t *>(c.v_cache);
   const dim3 cgrid(static_cast<unsigned>(sg.S));
   if (sg.direct) {
+    MSA_LOG_LAUNCH("stage_mark_kernel (in place)", mark_groups, kStageThreads, 0);
+    MSA_LOG_LAUNCH("stage_convert_kernel (in place)", cgrid, kStageThreads, 0);
     stage_mark_kernel<true><<<mark_groups, kStageThreads, 0, st>>>(
         b.units, ids, topk, g.nsel, g.Hkv, c.block_table, c.max_blocks_per_seq,
         c.num_phys_blocks, rows, sg);
@@ -1136,6 +1139,9 @@ void stage_kept_blocks(const Geom &g, const msa_cache_t &c, const msa_batch_t &b
   const int64_t n = c.num_phys_blocks * g.Hkv;
   const int reset_groups = static_cast<int>(std::min<int64_t>((n + kStageThreads - 1) /
                                                               kStageThreads, 1024));
+  MSA_LOG_LAUNCH("stage_reset_kernel", reset_groups, kStageThreads, 0);
+  MSA_LOG_LAUNCH("stage_mark_kernel (claimed slots)", mark_groups, kStageThreads, 0);
+  MSA_LOG_LAUNCH("stage_convert_kernel (claimed slots)", cgrid, kStageThreads, 0);
   stage_reset_kernel<<<reset_groups, kStageThreads, 0, st>>>(sg, n);
   stage_mark_kernel<false><<<mark_groups, kStageThreads, 0, st>>>(
       b.units, ids, topk, g.nsel, g.Hkv, c.block_table, c.max_blocks_per_seq, c.num_phys_blocks,
@@ -1201,6 +1207,8 @@ hipError_t launch_prefill_attention(const Geom &g, const msa_cache_t &c, const m
                                                  al(entries * 4));
     tu = TokenUnion{cnt, uids, msk};
     const int W = c.max_blocks_per_seq / 32 + 1;   // bitmap words for any tau of the table
+    MSA_LOG_LAUNCH("token_union_kernel", dim3(b.total_units, g.nsel), kUnionThreads,
+                   2 * W * sizeof(uint32_t));
     token_union_kernel<<<dim3(b.total_units, g.nsel), kUnionThreads,
                          2 * W * sizeof(uint32_t), st>>>(b.units, ids, topk, g.nsel, tu, cnt,
                                                          uids, msk);
@@ -1229,6 +1237,8 @@ hipError_t launch_prefill_attention(const Geom &g, const msa_cache_t &c, const m
   } else if (g.fp8) {
     const uint8_t *k8 = static_cast<const uint8_t *>(c.k_cache);
     const uint8_t *v8 = static_cast<const uint8_t *>(c.v_cache);
+    MSA_LOG_LAUNCH(PT ? "attn_prefill_fp8_kernel (per token)" : "attn_prefill_fp8_kernel", grid,
+                   NW * 64, 0);
     if (g.D == 64)
       attn_prefill_fp8_kernel<64, PT><<<grid, NW * 64, 0, st>>>(
           qb, k8, v8, c.k_scale, c.v_scale, c.block_table, b.units, ids, topk,
@@ -1239,6 +1249,8 @@ hipError_t launch_prefill_attention(const Geom &g, const msa_cache_t &c, const m
           c.max_blocks_per_seq, g.Hq, g.Hkv, g.nsel, num_uj, pairs, sl2, tu, ob, lse);
     return hipGetLastError();
   }
+  MSA_LOG_LAUNCH(PT ? "attn_prefill_bf16_kernel (per token)" : "attn_prefill_bf16_kernel", grid,
+                 NW * 64, 0);
   if (g.D == 64)
     attn_prefill_bf16_kernel<64, PT><<<grid, NW * 64, 0, st>>>(
         qb, kb, vb, c.block_table, remap, b.units, ids, topk, c.max_blocks_per_seq, g.Hq, g.Hkv,

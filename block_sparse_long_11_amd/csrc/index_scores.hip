@@ -1005,6 +1005,7 @@ hipError_t dispatch_decode_hs(const Geom &g, const msa_cache_t &c, int T, const 
   case HS:                                                                               \
     {                                                                                    \
     const DecodeLaunch dl = decode_launch(c, index_decode_kernel<BF16, DI, HS>);        \
+    MSA_LOG_LAUNCH("index_decode_kernel", dl.grid, 256, dl.lds);                          \
     index_decode_kernel<BF16, DI, HS><<<dl.grid, 256, dl.lds, st>>>(                     \
         q_idx, c.k_idx_cache, c.block_table, c.seq_lens, c.num_seqs,                     \
         c.max_blocks_per_seq, g.nsel, T, dl.compact, scores);                            \
@@ -1028,6 +1029,7 @@ hipError_t dispatch_decode_fp8(const Geom &g, const msa_cache_t &c, int T, const
     {                                                                                    \
     const DecodeLaunch dl = decode_launch(c, index_decode_fp8_kernel<DI, HS>,           \
                                           static_cast<size_t>(g.Hi) * kBlk * (DI / 32)); \
+    MSA_LOG_LAUNCH("index_decode_fp8_kernel", dl.grid, 256, dl.lds);                      \
     index_decode_fp8_kernel<DI, HS><<<dl.grid, 256, dl.lds, st>>>(                       \
         q, k, c.k_idx_scale, c.block_table, c.seq_lens, c.num_seqs, c.max_blocks_per_seq, \
         g.nsel, T, dl.compact, scores);                                                  \
@@ -1051,6 +1053,8 @@ hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_
                                           g.nsel, kPairBlock);
     if (ord.grid() > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(ord.grid()));
+    MSA_LOG_LAUNCH(PT ? "index_prefill_bf16_kernel (per token)" : "index_prefill_bf16_kernel", grid,
+                   kIdxThreads, 0);
     switch (hs) {
 #define MSA_CASE(HS)                                                                     \
   case HS:                                                                               \
@@ -1070,6 +1074,8 @@ hipError_t dispatch_prefill_bf16(const Geom &g, const msa_cache_t &c, const msa_
                                         kWidePairBlock);
   if (ord.grid() > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(ord.grid()));
+  MSA_LOG_LAUNCH(PT ? "index_prefill_wide_kernel (per token)" : "index_prefill_wide_kernel", grid,
+                 kWideThreads, 0);
   switch (hs) {
 #define MSA_CASE(HS)                                                                     \
   case HS:                                                                               \
@@ -1116,6 +1122,7 @@ hipError_t launch_prefill_scores(const Geom &g, const msa_cache_t &c, const msa_
                       : dispatch_prefill_bf16<32, false, PT>(g, c, b, q_idx, scores, st);
   }
   const dim3 grid(b.total_units, c.max_blocks_per_seq, g.nsel);
+  MSA_LOG_LAUNCH("index_prefill_f32_kernel", grid, 128, 0);
   index_prefill_f32_kernel<<<grid, 128, 0, st>>>(
       static_cast<const float *>(q_idx), static_cast<const float *>(c.k_idx_cache),
       c.block_table, b.units, c.max_blocks_per_seq, g.nsel, g.Hi, g.Di, PT, scores);

@@ -5,11 +5,26 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
 #include "msa.h"
 #include "msa_launch.h"
+
+namespace msa {
+
+bool log_enabled() {
+  const char *v = std::getenv("MSA_LOG");
+  return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+}
+
+void log_launch(const char *kernel, dim3 grid, dim3 block, size_t lds) {
+  std::fprintf(stderr, "msa: launch %s grid (%u, %u, %u) block (%u, %u, %u) lds %zu\n", kernel,
+               grid.x, grid.y, grid.z, block.x, block.y, block.z, lds);
+}
+
+}  // namespace msa
 
 namespace {
 
@@ -22,6 +37,7 @@ msa_status_t fail(msa_status_t st, const char *fmt, ...) {
   vsnprintf(buf, sizeof(buf), fmt, ap);
   va_end(ap);
   g_last_error = buf;
+  if (msa::log_enabled()) std::fprintf(stderr, "msa: refused (status %d): %s\n", st, buf);
   return st;
 }
 

@@ -9,6 +9,17 @@
 
 namespace msa {
 
+// Debugging aid: with MSA_LOG set to a non-zero value in the environment, every
+// kernel launch prints its kernel, grid, block and dynamic LDS bytes to stderr,
+// and every refused call its reason. Off by default; the variable is read at every
+// launch, so a process can switch it on and off.
+bool log_enabled();
+void log_launch(const char *kernel, dim3 grid, dim3 block, size_t lds);
+#define MSA_LOG_LAUNCH(kernel, grid, block, lds)                                      \
+  do {                                                                               \
+    if (::msa::log_enabled()) ::msa::log_launch(kernel, dim3(grid), dim3(block), lds); \
+  } while (0)
+
 struct Geom {
   int Hq, Hkv, D, Hi, Di, nsel;
   bool bf16;

@@ -395,6 +395,8 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_insert_kernel(InsertArg
 
 template <bool BF, int D, bool FP8 = false>
 hipError_t launch_one(const InsertArgs &a, dim3 grid, size_t lds, hipStream_t st) {
+  MSA_LOG_LAUNCH(FP8 ? "qk_norm_rope_insert_kernel (FP8 caches)" : "qk_norm_rope_insert_kernel", grid,
+                 kThreads, lds);
   hipLaunchKernelGGL((qk_norm_rope_insert_kernel<BF, D, FP8>), grid, dim3(kThreads), lds, st,
                      a);
   return hipGetLastError();

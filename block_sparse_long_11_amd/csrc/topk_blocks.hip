@@ -314,6 +314,7 @@ hipError_t launch_topk(const float *scores, int rows, int row_len, int topk, int
   const int per_lane = (row_len + kWave - 1) / kWave;
 #define MSA_TOPK_WAVE(E)                                                              \
   if (per_lane <= E) {                                                                \
+    MSA_LOG_LAUNCH("topk_rows_wave_kernel", (rows + 3) / 4, 256, 0);                   \
     topk_rows_wave_kernel<E><<<(rows + 3) / 4, 256, 0, st>>>(scores, rows, row_len, topk, \
                                                              ids);                    \
     return hipGetLastError();                                                         \
@@ -323,11 +324,13 @@ hipError_t launch_topk(const float *scores, int rows, int row_len, int topk, int
   const int per = (row_len + kTopkThreads - 1) / kTopkThreads;   // entries per thread
 #define MSA_TOPK(KPT)                                                                 \
   if (per <= KPT) {                                                                   \
+    MSA_LOG_LAUNCH("topk_rows_reg_kernel", rows, kTopkThreads, 0);                     \
     topk_rows_reg_kernel<KPT><<<rows, kTopkThreads, 0, st>>>(scores, row_len, topk, ids); \
     return hipGetLastError();                                                         \
   }
   MSA_TOPK(1) MSA_TOPK(2) MSA_TOPK(4) MSA_TOPK(8) MSA_TOPK(16) MSA_TOPK(32)
 #undef MSA_TOPK
+  MSA_LOG_LAUNCH("topk_rows_kernel", rows, kTopkThreads, 0);
   topk_rows_kernel<<<rows, kTopkThreads, 0, st>>>(scores, row_len, topk, ids);
   return hipGetLastError();
 }

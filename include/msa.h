@@ -29,6 +29,10 @@
  *     as MSA_ERR_HIP. Device-side values (seq_lens, block_table, ids) are not
  *     checked: out-of-range entries are undefined behaviour.
  *   - Calls are re-entrant and thread-safe.
+ *   - Debugging aid: with the environment variable MSA_LOG set to a non-zero
+ *     value, every kernel launch prints its kernel, grid, block and dynamic LDS
+ *     bytes to stderr, and every refused call its status and reason (read at
+ *     every call; off by default).
  *
  * Data layout (block-major paged caches, [dd] "Serving options", [vllm]):
  *   k_cache            [num_phys_blocks][H_kv][128][D]     (dtype), token-major

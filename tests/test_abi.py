@@ -407,3 +407,34 @@ def test_probe_library_exports_and_checks():
     assert plib.msa_probe_mfma_valu(64, 10, 0, FAKE, None) == -1
     assert plib.msa_probe_mfma_valu(64, 10, 4, FAKE, None) == -1
     assert plib.msa_probe_mfma_valu(32769, 10, 3, FAKE, None) == -1
+
+
+def _stderr_of(fn):
+    """Runs fn() with file descriptor 2 redirected to a temporary file; returns the
+    text written there (the library prints with stdio, below Python's sys.stderr)."""
+    import tempfile
+    with tempfile.TemporaryFile(mode="w+b") as tmp:
+        saved = os.dup(2)
+        try:
+            os.dup2(tmp.fileno(), 2)
+            fn()
+        finally:
+            ctypes.CDLL(None).fflush(None)
+            os.dup2(saved, 2)
+            os.close(saved)
+        tmp.seek(0)
+        return tmp.read().decode()
+
+
+def test_msa_log_reports_refused_calls(lib, monkeypatch):
+    """MSA_LOG=1: a refused call prints its reason to stderr; unset, nothing."""
+    c, b = _cache(), msa._Batch(FAKE, 3, 300)
+    call = lambda: lib.msa_sparse_attn_prefill(None, ctypes.byref(c), ctypes.byref(b), FAKE, FAKE,
+                                               16, 0.0, FAKE, None, None)
+    monkeypatch.delenv("MSA_LOG", raising=False)
+    assert _stderr_of(call) == ""
+    monkeypatch.setenv("MSA_LOG", "1")
+    text = _stderr_of(call)
+    assert "msa: refused (status 1): geom is NULL" in text
+    monkeypatch.setenv("MSA_LOG", "0")
+    assert _stderr_of(call) == ""

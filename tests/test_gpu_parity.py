@@ -367,3 +367,25 @@ def test_decode_many_sequences(gpu_device):
     assert np.isfinite(s0[cols < tau[:, None]]).all()
     assert np.isposinf(s0[cols == tau[:, None]]).all()
     assert np.isneginf(s0[cols > tau[:, None]]).all()
+
+
+def test_msa_log_prints_launches(gpu_device, monkeypatch):
+    """MSA_LOG=1: every launch of a prefill and a decode step prints its kernel and
+    launch geometry to stderr (the library's debugging aid)."""
+    import test_abi as A
+    monkeypatch.setenv("MSA_LOG", "1")
+    pre = synth.small_workload(seq_lens=(700, 300), q_lens=(300, 300))
+    dec = synth.small_workload(seq_lens=(3000, 700), q_lens=None, topk=5)
+    say("MSA_LOG launches")
+
+    def run():
+        for w in (pre, dec):
+            inp, geom, cache = setup(w, gpu_device)
+            run_gpu(w, inp, geom, cache, gpu_device)
+        torch.cuda.synchronize()
+
+    text = A._stderr_of(run)
+    for kernel in ("index_prefill_bf16_kernel", "topk_rows_", "attn_prefill_bf16_kernel",
+                   "index_decode_kernel", "attn_decode_bf16_kernel", "combine_kernel"):
+        assert f"msa: launch {kernel}" in text, (kernel, text[:2000])
+    assert "grid (" in text and "block (" in text
