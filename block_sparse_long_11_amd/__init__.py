@@ -113,6 +113,10 @@ EXPORTS = {
         ctypes.POINTER(_Geom), ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "msa_validate_block_table": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]),
+    "msa_validate_ids": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int32]),
     "msa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "msa_last_error": (ctypes.c_char_p, []),
     "msa_version": (ctypes.c_int32, []),
@@ -590,6 +594,23 @@ def prefill_tokens(geom: Geometry, cache: Cache, batch: Batch, q, q_idx, topk, s
     msa_sparse_attn_prefill_tokens(geom, cache, batch, q, ids, topk, out, ws, lse, softmax_scale,
                                    stream)
     return dict(scores=scores, ids=ids, out=out, lse=lse)
+
+
+def msa_validate_block_table(block_table, seq_lens, num_phys_blocks):
+    """Host check of a block table (debugging aid): raises MsaError naming the first
+    entry that is not a physical block. Tensors may live on any device."""
+    bt = np.ascontiguousarray(block_table.cpu().numpy(), dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens.cpu().numpy(), dtype=np.int32)
+    _check(lib().msa_validate_block_table(bt.ctypes.data, sl.ctypes.data, bt.shape[0],
+                                          bt.shape[1], int(num_phys_blocks)))
+
+
+def msa_validate_ids(ids, max_blocks_per_seq):
+    """Host check of id lists [rows][n_sel][topk] (debugging aid): raises MsaError
+    naming the first list with an out-of-range or repeated entry."""
+    a = np.ascontiguousarray(ids.cpu().numpy(), dtype=np.int32)
+    _check(lib().msa_validate_ids(a.ctypes.data, a.shape[0], a.shape[1], a.shape[2],
+                                  int(max_blocks_per_seq)))
 
 
 def workspace(nbytes, device):

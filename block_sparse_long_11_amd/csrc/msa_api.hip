@@ -2,12 +2,14 @@
 // Every check here runs before anything is enqueued; see msa.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "msa.h"
 #include "msa_launch.h"
@@ -247,6 +249,55 @@ msa_status_t msa_prefill_plan(const int32_t *h_seq_lens, const int32_t *h_q_lens
     }
   }
   *h_num_units = static_cast<int32_t>(count);
+  return ok();
+}
+
+msa_status_t msa_validate_block_table(const int32_t *h_block_table, const int32_t *h_seq_lens,
+                                      int32_t num_seqs, int32_t max_blocks_per_seq,
+                                      int64_t num_phys_blocks) {
+  MSA_REQUIRE(h_block_table != nullptr && h_seq_lens != nullptr, MSA_ERR_INVALID_ARG,
+              "validate: NULL argument");
+  MSA_REQUIRE(num_seqs > 0 && max_blocks_per_seq > 0 && num_phys_blocks > 0,
+              MSA_ERR_INVALID_ARG, "validate: sizes must be positive");
+  for (int r = 0; r < num_seqs; ++r) {
+    const int L = h_seq_lens[r];
+    MSA_REQUIRE(L > 0 && (static_cast<int64_t>(L) + MSA_BLOCK_SIZE - 1) / MSA_BLOCK_SIZE <=
+                             max_blocks_per_seq,
+                MSA_ERR_INVALID_ARG, "validate: sequence %d has %d tokens, more than %d blocks",
+                r, L, max_blocks_per_seq);
+    const int nb = (L + MSA_BLOCK_SIZE - 1) / MSA_BLOCK_SIZE;
+    const int32_t *row = h_block_table + static_cast<size_t>(r) * max_blocks_per_seq;
+    for (int b = 0; b < nb; ++b)
+      MSA_REQUIRE(row[b] >= 0 && row[b] < num_phys_blocks, MSA_ERR_INVALID_ARG,
+                  "validate: block_table[%d][%d] = %d is not a physical block (0 .. %lld)", r, b,
+                  row[b], static_cast<long long>(num_phys_blocks - 1));
+  }
+  return ok();
+}
+
+msa_status_t msa_validate_ids(const int32_t *h_ids, int32_t num_rows, int32_t num_sel_groups,
+                              int32_t topk, int32_t max_blocks_per_seq) {
+  MSA_REQUIRE(h_ids != nullptr || num_rows == 0, MSA_ERR_INVALID_ARG, "validate: ids is NULL");
+  MSA_REQUIRE(num_rows >= 0 && num_sel_groups > 0 && topk > 0 && max_blocks_per_seq > 0,
+              MSA_ERR_INVALID_ARG, "validate: bad sizes");
+  std::vector<int32_t> seen;
+  for (int64_t l = 0; l < static_cast<int64_t>(num_rows) * num_sel_groups; ++l) {
+    const int32_t *row = h_ids + l * topk;
+    seen.clear();
+    for (int i = 0; i < topk && row[i] != -1; ++i) {
+      MSA_REQUIRE(row[i] >= 0 && row[i] < max_blocks_per_seq, MSA_ERR_INVALID_ARG,
+                  "validate: row %lld group %lld entry %d is %d, outside 0 .. %d (end a list "
+                  "with -1)", static_cast<long long>(l / num_sel_groups),
+                  static_cast<long long>(l % num_sel_groups), i, row[i],
+                  max_blocks_per_seq - 1);
+      seen.push_back(row[i]);
+    }
+    std::sort(seen.begin(), seen.end());
+    MSA_REQUIRE(std::adjacent_find(seen.begin(), seen.end()) == seen.end(), MSA_ERR_INVALID_ARG,
+                "validate: row %lld group %lld lists a block twice",
+                static_cast<long long>(l / num_sel_groups),
+                static_cast<long long>(l % num_sel_groups));
+  }
   return ok();
 }
 

@@ -154,6 +154,22 @@ msa_status_t msa_prefill_plan(const int32_t *h_seq_lens, const int32_t *h_q_lens
                               int32_t num_seqs, msa_unit_t *h_units, int32_t capacity,
                               int32_t *h_num_units);
 
+/* Debugging aids for the device-side values the calls trust (out-of-range
+ * entries are undefined behaviour there): pure host code over HOST copies, to be
+ * run on a batch that misbehaves. Each returns MSA_OK, or MSA_ERR_INVALID_ARG with
+ * msa_last_error() naming the first violation.
+ * msa_validate_block_table: for every sequence r, seq_lens[r] >= 1 fits in
+ *   max_blocks_per_seq blocks of 128 and the entries of its blocks, block_table[r]
+ *   [0 .. ceil(seq_lens[r] / 128) - 1], are physical blocks in [0, num_phys_blocks).
+ * msa_validate_ids: every list of ids [num_rows][num_sel_groups][topk] (the
+ *   selection's output, or a caller's own) holds distinct entries in
+ *   [0, max_blocks_per_seq) before its first -1. */
+msa_status_t msa_validate_block_table(const int32_t *h_block_table, const int32_t *h_seq_lens,
+                                      int32_t num_seqs, int32_t max_blocks_per_seq,
+                                      int64_t num_phys_blocks);
+msa_status_t msa_validate_ids(const int32_t *h_ids, int32_t num_rows, int32_t num_sel_groups,
+                              int32_t topk, int32_t max_blocks_per_seq);
+
 /* Step 1, indexer block scores ([feat] row "Indexer-selected sparse attention":
  * a lightning indexer scores keys per head and pools them into blocks; [vllm]:
  * each query or GQA query group scores every available block).

@@ -438,3 +438,35 @@ def test_msa_log_reports_refused_calls(lib, monkeypatch):
     assert "msa: refused (status 1): geom is NULL" in text
     monkeypatch.setenv("MSA_LOG", "0")
     assert _stderr_of(call) == ""
+
+
+def test_validate_block_table_and_ids(lib):
+    """Host debugging aids: a block table whose sequences' blocks are physical blocks
+    passes; the first entry outside [0, num_phys_blocks) is named; id lists pass with
+    distinct in-range entries before their first -1 (entries after it are ignored) and
+    fail on an out-of-range or repeated entry."""
+    bt = torch.tensor([[3, 0, 7, -5], [1, 2, -1, -1]], dtype=torch.int32)
+    sl = torch.tensor([300, 200], dtype=torch.int32)     # 3 and 2 blocks
+    msa.msa_validate_block_table(bt, sl, 8)
+    with pytest.raises(msa.MsaError, match=r"block_table\[0\]\[2\] = 7"):
+        msa.msa_validate_block_table(bt, sl, 7)
+    with pytest.raises(msa.MsaError, match="more than 4 blocks"):
+        msa.msa_validate_block_table(bt, torch.tensor([600, 1], dtype=torch.int32), 8)
+    bt2 = bt.clone()
+    bt2[1, 1] = -1
+    with pytest.raises(msa.MsaError, match=r"block_table\[1\]\[1\] = -1"):
+        msa.msa_validate_block_table(bt2, sl, 8)
+    ids = torch.tensor([[[0, 3, 2, -1]], [[5, -1, 5, 99]]], dtype=torch.int32)
+    msa.msa_validate_ids(ids, 6)
+    with pytest.raises(msa.MsaError, match="row 0 group 0 entry 1 is 3"):
+        msa.msa_validate_ids(ids, 3)
+    bad = ids.clone()
+    bad[0, 0, 2] = 0
+    with pytest.raises(msa.MsaError, match="row 0 group 0 lists a block twice"):
+        msa.msa_validate_ids(bad, 6)
+    # the oracle's selection (ascending, the diagonal last, -1 padded) passes
+    rng = np.random.default_rng(3)
+    rows = [[O.select_blocks(rng.standard_normal(8), tau, 5) for tau in (0, 2, 7)]]
+    msa.msa_validate_ids(torch.tensor(np.asarray(rows, dtype=np.int32).transpose(1, 0, 2)), 8)
+    assert lib.msa_validate_ids(None, 0, 1, 4, 8) == OK
+    assert lib.msa_validate_ids(None, 1, 1, 4, 8) == INVALID
