@@ -106,7 +106,7 @@ def test_prefill_tokens_equal_chunks_match_per_token_decode(gpu_device):
     sa, sb = a["scores"].numpy(), b["scores"].numpy()
     inf = ~np.isfinite(sb)
     assert np.array_equal(sa[inf], sb[inf])
-    assert (np.abs(sa - sb)[~inf] <= 2 * np.broadcast_to(tol[None, :, None], sb.shape)[~inf]).all()
+    assert (np.abs(sa[~inf] - sb[~inf]) <= 2 * np.broadcast_to(tol[None, :, None], sb.shape)[~inf]).all()
     same = (a["ids"] == b["ids"]).all(dim=2).all(dim=1)      # rows selecting the same blocks
     assert same.float().mean().item() >= 0.5
     d = (a["out"][same].float() - b["out"][same].float()).abs().max().item()
