@@ -827,9 +827,11 @@ void index_prefill_bf16_kernel(
                                          src[key * CHG + ((2 * ks + lane / 32) ^ swz(key))]);
         }
       };
+      // one chain of three-input maxima (8 per accumulator): the pairwise form,
+      // max(m, max(a, b)), compiled to 12 instructions
       auto pool = [&](float &mm, const f32x16 &v) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) mm = fmaxf(mm, fmaxf(v[i], v[i + 1]));
+        for (int i = 0; i < 16; i += 2) mm = fmaxf(fmaxf(mm, v[i]), v[i + 1]);
       };
       rd(0, kf[0]);
 #pragma unroll
