@@ -35,9 +35,9 @@ def _hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def _compile(src: pathlib.Path, extra):
-    obj = BUILD / (src.stem + ".o")
-    cmd = [_hipcc(), *CFLAGS, *extra, "-c", str(src), "-o", str(obj)]
+def _compile(src: pathlib.Path, extra, flags=CFLAGS, out_dir=BUILD):
+    obj = out_dir / (src.stem + ".o")
+    cmd = [_hipcc(), *flags, *extra, "-c", str(src), "-o", str(obj)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src.name}:\n{res.stderr}")
@@ -68,6 +68,25 @@ def build(verbose=False, extra=()):
     if verbose:
         print(f"built {LIB}" + (f" and {PROBE_LIB.name}" if probes else ""))
     return LIB
+
+
+def build_host_asan(verbose=False):
+    """A copy of libmsa.so whose host code (argument checks, plan, validators,
+    launch set-up) is built with AddressSanitizer, for the CPU tests of the C ABI:
+    `_build/asan/libmsa.so`. Its device code is the same source at -O1 and is never
+    launched from those tests. Loading it needs the ASan runtime preloaded."""
+    out = BUILD / "asan"
+    out.mkdir(parents=True, exist_ok=True)
+    flags = [f if f != "-O3" else "-O1" for f in CFLAGS] + [
+        "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+    srcs = sorted(CSRC.glob("*.hip"))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, [], flags, out), srcs))
+    lib = out / "libmsa.so"
+    _link(objs, lib)
+    if verbose:
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
