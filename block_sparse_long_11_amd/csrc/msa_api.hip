@@ -225,14 +225,19 @@ msa_status_t msa_prefill_plan(const int32_t *h_seq_lens, const int32_t *h_q_lens
   MSA_REQUIRE(h_seq_lens != nullptr && h_q_lens != nullptr && h_num_units != nullptr,
               MSA_ERR_INVALID_ARG, "plan: NULL argument");
   MSA_REQUIRE(num_seqs > 0, MSA_ERR_INVALID_ARG, "plan: num_seqs must be positive");
-  int64_t count = 0;
+  int64_t count = 0, total_q = 0;
   for (int r = 0; r < num_seqs; ++r) {
     const int L = h_seq_lens[r], n = h_q_lens[r];
     MSA_REQUIRE(L > 0 && n >= 0 && n <= L, MSA_ERR_INVALID_ARG,
                 "plan: request %d has seq_len %d and q_len %d", r, L, n);
     if (n > 0) count += (L - 1) / MSA_BLOCK_SIZE - (L - n) / MSA_BLOCK_SIZE + 1;
+    total_q += n;
   }
   MSA_REQUIRE(count <= 2147483647, MSA_ERR_INVALID_ARG, "plan: too many units");
+  // unit rows are int32 offsets into the batch's query rows
+  MSA_REQUIRE(total_q <= 2147483647, MSA_ERR_INVALID_ARG,
+              "plan: %lld query rows in all, more than an int32 row index holds",
+              static_cast<long long>(total_q));
   if (h_units != nullptr) {
     MSA_REQUIRE(capacity >= count, MSA_ERR_INVALID_ARG,
                 "plan: capacity %d < %lld units", capacity, static_cast<long long>(count));

@@ -149,7 +149,8 @@ typedef struct {
  * 128-position boundaries ([dd]: 128-token blocks; the first unit of a chunk that
  * starts mid-block is partial). With h_units == NULL only *h_num_units is set.
  * Otherwise up to `capacity` units are written in request order, tiles ascending.
- * Needs 0 <= h_q_lens[r] <= h_seq_lens[r]. Pure host code. */
+ * Needs 0 <= h_q_lens[r] <= h_seq_lens[r], and at most 2^31 - 1 units and query
+ * rows in all (row offsets are int32); else MSA_ERR_INVALID_ARG. Pure host code. */
 msa_status_t msa_prefill_plan(const int32_t *h_seq_lens, const int32_t *h_q_lens,
                               int32_t num_seqs, msa_unit_t *h_units, int32_t capacity,
                               int32_t *h_num_units);

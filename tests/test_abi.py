@@ -159,6 +159,11 @@ def test_prefill_plan_rejects_bad_lengths(lib):
     assert e.value.status == INVALID
     with pytest.raises(msa.MsaError):
         msa.msa_prefill_plan([0], [0])
+    # query rows past an int32 row index: refused while counting, before any unit
+    big = 2**31 - 1
+    with pytest.raises(msa.MsaError) as e:
+        msa.msa_prefill_plan([big, big], [big, 2])
+    assert e.value.status == INVALID and "query rows" in str(e.value)
 
 
 def test_binding_checks_tensors_before_calling(lib):
