@@ -596,11 +596,27 @@ def prefill_tokens(geom: Geometry, cache: Cache, batch: Batch, q, q_idx, topk, s
     return dict(scores=scores, ids=ids, out=out, lse=lse)
 
 
+def _host_int32(t, name, ndim):
+    """A C-contiguous int32 host copy of an integer tensor or array of `ndim`
+    dimensions; values outside int32 are refused rather than wrapped."""
+    a = t.detach().cpu().numpy() if isinstance(t, torch.Tensor) else np.asarray(t)
+    if a.ndim != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {a.shape}")
+    if a.dtype != np.int32:
+        if not np.issubdtype(a.dtype, np.integer):
+            raise ValueError(f"{name} must hold integers, got {a.dtype}")
+        if a.size and (a.min() < -2**31 or a.max() > 2**31 - 1):
+            raise ValueError(f"{name} holds values outside int32")
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
 def msa_validate_block_table(block_table, seq_lens, num_phys_blocks):
     """Host check of a block table (debugging aid): raises MsaError naming the first
     entry that is not a physical block. Tensors may live on any device."""
-    bt = np.ascontiguousarray(block_table.cpu().numpy(), dtype=np.int32)
-    sl = np.ascontiguousarray(seq_lens.cpu().numpy(), dtype=np.int32)
+    bt = _host_int32(block_table, "block_table", 2)
+    sl = _host_int32(seq_lens, "seq_lens", 1)
+    if sl.shape[0] != bt.shape[0]:
+        raise ValueError(f"seq_lens has {sl.shape[0]} entries for {bt.shape[0]} table rows")
     _check(lib().msa_validate_block_table(bt.ctypes.data, sl.ctypes.data, bt.shape[0],
                                           bt.shape[1], int(num_phys_blocks)))
 
@@ -608,9 +624,9 @@ def msa_validate_block_table(block_table, seq_lens, num_phys_blocks):
 def msa_validate_ids(ids, max_blocks_per_seq):
     """Host check of id lists [rows][n_sel][topk] (debugging aid): raises MsaError
     naming the first list with an out-of-range or repeated entry."""
-    a = np.ascontiguousarray(ids.cpu().numpy(), dtype=np.int32)
-    _check(lib().msa_validate_ids(a.ctypes.data, a.shape[0], a.shape[1], a.shape[2],
-                                  int(max_blocks_per_seq)))
+    a = _host_int32(ids, "ids", 3)
+    _check(lib().msa_validate_ids(a.ctypes.data if a.size else None, a.shape[0], a.shape[1],
+                                  a.shape[2], int(max_blocks_per_seq)))
 
 
 def workspace(nbytes, device):

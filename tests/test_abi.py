@@ -475,3 +475,13 @@ def test_validate_block_table_and_ids(lib):
     msa.msa_validate_ids(torch.tensor(np.asarray(rows, dtype=np.int32).transpose(1, 0, 2)), 8)
     assert lib.msa_validate_ids(None, 0, 1, 4, 8) == OK
     assert lib.msa_validate_ids(None, 1, 1, 4, 8) == INVALID
+    # the binding refuses what the C call would misread: a short seq_lens, wrong
+    # ranks, and values that a cast to int32 would wrap
+    with pytest.raises(ValueError, match="entries for"):
+        msa.msa_validate_block_table(bt, sl[:1], 8)
+    with pytest.raises(ValueError, match="2-D"):
+        msa.msa_validate_block_table(bt[0], sl, 8)
+    with pytest.raises(ValueError, match="outside int32"):
+        msa.msa_validate_ids(torch.tensor([[[2**32 + 1, -1]]], dtype=torch.int64), 8)
+    msa.msa_validate_ids(torch.tensor([[[1, 0, -1]]], dtype=torch.int64), 8)
+    msa.msa_validate_ids(torch.zeros(0, 1, 4, dtype=torch.int32), 8)
