@@ -286,10 +286,10 @@ class Batch:
 
 def msa_prefill_plan(seq_lens, q_lens):
     """Host plan of a prefill batch: int32 [U][5] rows (r, tau, row0, num_rows, pos0)."""
-    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
-    ql = np.ascontiguousarray(q_lens, dtype=np.int32)
-    if sl.shape != ql.shape or sl.ndim != 1:
-        raise ValueError("seq_lens and q_lens must be 1-D and of equal length")
+    sl = _host_int32(seq_lens, "seq_lens", 1)
+    ql = _host_int32(q_lens, "q_lens", 1)
+    if sl.shape != ql.shape:
+        raise ValueError("seq_lens and q_lens must be of equal length")
     n = ctypes.c_int32(0)
     _check(lib().msa_prefill_plan(sl.ctypes.data, ql.ctypes.data, len(sl), None, 0,
                                   ctypes.byref(n)))

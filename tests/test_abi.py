@@ -164,6 +164,8 @@ def test_prefill_plan_rejects_bad_lengths(lib):
     with pytest.raises(msa.MsaError) as e:
         msa.msa_prefill_plan([big, big], [big, 2])
     assert e.value.status == INVALID and "query rows" in str(e.value)
+    with pytest.raises(ValueError, match="outside int32"):
+        msa.msa_prefill_plan(np.array([2**32 + 300]), np.array([10]))
 
 
 def test_binding_checks_tensors_before_calling(lib):
