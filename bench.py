@@ -51,8 +51,9 @@ def log(msg):
 
 def measured_peaks(dev):
     """Practical ceilings on this GPU: a streaming read of 4 GiB with 16-byte
-    non-temporal loads (best of several grid sizes) and a dense bf16 MFMA loop on
-    register operands. Timed with HIP events on the launch stream."""
+    non-temporal loads and a device copy of 1 GiB (each the best of several grid
+    sizes), dense bf16 MFMA loops on register operands and MFMA next to VALU work on
+    one SIMD. Timed with HIP events on the launch stream."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_long_11_amd", "libmsa_probe.so"))
     lib.msa_probe_stream_read.restype = ctypes.c_int
@@ -62,6 +63,9 @@ def measured_peaks(dev):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                        ctypes.c_void_p]
+    lib.msa_probe_copy.restype = ctypes.c_int
+    lib.msa_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_int, ctypes.c_void_p]
     lib.msa_probe_mfma_valu.restype = ctypes.c_int
     lib.msa_probe_mfma_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_void_p, ctypes.c_void_p]
@@ -90,6 +94,14 @@ def measured_peaks(dev):
                                                      groups, ctypes.c_void_p(sink.data_ptr()),
                                                      stream), 4)
         hbm[groups] = nbytes / t / 1e9
+    # a plain copy of 1 GiB between the buffer's first and third quarter
+    cbytes = 1 << 30
+    copy = {}
+    for groups in (2048, 4096, 8192):
+        t = timed(lambda: lib.msa_probe_copy(ctypes.c_void_p(buf.data_ptr()),
+                                             ctypes.c_void_p(buf.data_ptr() + 2 * cbytes),
+                                             cbytes, groups, stream), 3)
+        copy[groups] = 2 * cbytes / t / 1e9
     del buf
     groups, iters = 1024, 20000
     flops = groups * 4 * iters * 8 * 32768
@@ -106,7 +118,8 @@ def measured_peaks(dev):
                       3) * 1e3 for mode in (1, 2, 3)}
     hidden = (co[1] + co[2] - co[3]) / min(co[1], co[2])
     best_g = max(hbm, key=hbm.get)
-    return dict(hbm_gbs=hbm[best_g], mfma_bf16_tflops=flops / t / 1e12,
+    best_c = max(copy, key=copy.get)
+    return dict(hbm_gbs=hbm[best_g], copy_gbs=copy[best_c], mfma_bf16_tflops=flops / t / 1e12,
                 mfma_bf16_random_tflops=flops / t_rand / 1e12,
                 mfma_valu_coexec=dict(mfma_ms=co[1], valu_ms=co[2], both_ms=co[3],
                                       hidden_frac_of_smaller=hidden,
@@ -116,6 +129,9 @@ def measured_peaks(dev):
                                             "fp32 work (max3 tree, 16 x fma+exp2+add, 8 packs)"),
                 hbm_probe=f"streaming read of 4 GiB, 16-byte non-temporal loads, 8 in flight "
                           f"per thread, best of {sorted(hbm)} work-groups (best {best_g})",
+                copy_probe=f"device copy of 1 GiB (read + write bytes counted), 16-byte loads and "
+                           f"stores, 8 in flight per thread, best of {sorted(copy)} work-groups "
+                           f"(best {best_c})",
                 mfma_probe="v_mfma_f32_32x32x16_bf16, 8 independent chains per wave, "
                            f"{groups} work-groups of 4 waves, register operands (small "
                            "constants; the random-operand figure uses full-mantissa values "
@@ -582,7 +598,8 @@ def main():
     if not args.no_probes:
         peaks = measured_peaks(dev)
         co = peaks["mfma_valu_coexec"]
-        log(f"measured peaks: HBM read {peaks['hbm_gbs']:.0f} GB/s, bf16 MFMA "
+        log(f"measured peaks: HBM read {peaks['hbm_gbs']:.0f} GB/s, copy "
+            f"{peaks['copy_gbs']:.0f} GB/s, bf16 MFMA "
             f"{peaks['mfma_bf16_tflops']:.0f} TFLOP/s (random operands "
             f"{peaks['mfma_bf16_random_tflops']:.0f}); MFMA {co['mfma_ms']:.3f} ms, VALU "
             f"{co['valu_ms']:.3f} ms, both {co['both_ms']:.3f} ms on one SIMD")
@@ -640,6 +657,11 @@ def main():
 
     for r in [main_res] + ([second] if second else []) + extra:
         add_measured(r)
+    if peaks is not None:
+        # the insert writes as many bytes as it reads: a plain copy is its ceiling
+        for ins in inserts:
+            ins["copy_rate_gbs"] = peaks["copy_gbs"]
+            ins["frac_of_copy_rate"] = ins["achieved"] / peaks["copy_gbs"]
 
     config = dict(workload=w.name, batch=w.num_seqs,
                   seq_lens=w.seq_lens if len(set(w.seq_lens)) > 1 else w.seq_lens[0],

@@ -1,5 +1,5 @@
 // Peak-rate probes of gfx950 (see include/msa_probe.h): the practical ceilings of
-// a streaming HBM read and of dense bf16 MFMA issue (on small constant operands
+// a streaming HBM read, of a plain device copy and of dense bf16 MFMA issue (on small constant operands
 // and on random full-mantissa operands), and the co-execution of MFMA and fp32
 // VALU work of two waves on one SIMD, measured on the same GPU as the kernels
 // they bound.
@@ -40,6 +40,27 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4 *__re
     uint32_t r = 0;
     for (int i = 0; i < kThreads; ++i) r ^= red[i];
     sink[blockIdx.x] = r;
+  }
+}
+
+// Device copy: 16-byte loads, 8 in flight per thread, then 16-byte stores of the
+// same chunks, grid-stride (no non-temporal hints: a plain copy's own rate).
+__global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4 *__restrict__ src,
+                                                        u32x4 *__restrict__ dst, size_t n16) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * kThreads * kInFlight;
+  for (size_t base = static_cast<size_t>(blockIdx.x) * kThreads * kInFlight + threadIdx.x;
+       base < n16; base += stride) {
+    u32x4 v[kInFlight];
+#pragma unroll
+    for (int i = 0; i < kInFlight; ++i) {
+      const size_t e = base + static_cast<size_t>(i) * kThreads;
+      if (e < n16) v[i] = src[e];
+    }
+#pragma unroll
+    for (int i = 0; i < kInFlight; ++i) {
+      const size_t e = base + static_cast<size_t>(i) * kThreads;
+      if (e < n16) dst[e] = v[i];
+    }
   }
 }
 
@@ -179,6 +200,16 @@ int msa_probe_stream_read(const void *buf, size_t bytes, int groups, uint32_t *s
     return -1;
   stream_read_kernel<<<groups, kThreads, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const u32x4 *>(buf), bytes / 16, sink);
+  return static_cast<int>(hipGetLastError());
+}
+
+int msa_probe_copy(const void *src, void *dst, size_t bytes, int groups, void *stream) {
+  const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+  if (src == nullptr || dst == nullptr || bytes == 0 || bytes % 16 != 0 || groups < 1 ||
+      groups > 65536 || s % 16 != 0 || d % 16 != 0 || (s < d + bytes && d < s + bytes))
+    return -1;
+  copy_kernel<<<groups, kThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), bytes / 16);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -1,7 +1,8 @@
 /*
  * msa_probe.h - peak-rate probes of the MI355X (gfx950) for the measurement of
- * libmsa: a plain streaming read of device memory, dense bf16 MFMA loops on
- * constant and on random operands, and MFMA next to fp32 VALU work on one SIMD.
+ * libmsa: a plain streaming read of device memory, a plain device copy, dense
+ * bf16 MFMA loops on constant and on random operands, and MFMA next to fp32 VALU
+ * work on one SIMD.
  * They give the practical ceilings the kernels' roofline fractions are also
  * quoted against (next to the published peaks: 8 TB/s HBM3E, 2.5 PFLOP/s dense
  * bf16). Built as libmsa_probe.so; not part of the attention path.
@@ -28,6 +29,13 @@ extern "C" {
  * launch's hipError_t. */
 int msa_probe_stream_read(const void *buf, size_t bytes, int groups, uint32_t *sink,
                           void *stream);
+
+/* Copies `bytes` from src to dst (device buffers that do not overlap) with 16-byte
+ * loads, 8 in flight per thread, and 16-byte stores, grid-stride over `groups`
+ * work-groups of 256 threads: the rate of a plain copy, the ceiling of a kernel
+ * that writes as many bytes as it reads. bytes a positive multiple of 16, both
+ * pointers 16-byte aligned; groups in [1, 65536]. Returns as msa_probe_stream_read. */
+int msa_probe_copy(const void *src, void *dst, size_t bytes, int groups, void *stream);
 
 /* Dense bf16 MFMA issue: `groups` work-groups of 256 threads (4 waves); every
  * wave runs `iters` rounds of 8 independent v_mfma_f32_32x32x16_bf16 chains on

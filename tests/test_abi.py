@@ -394,8 +394,8 @@ def test_probe_library_exports_and_checks():
         pytest.fail("libmsa_probe.so is not built (run __graft_entry__.build())")
     text = open(os.path.join(ROOT, "include", "msa_probe.h")).read()
     names = sorted(set(re.findall(r"^int\s+(msa_probe_[a-z0-9_]+)\s*\(", text, re.M)))
-    assert names == ["msa_probe_mfma_bf16", "msa_probe_mfma_bf16_random", "msa_probe_mfma_valu",
-                     "msa_probe_stream_read"]
+    assert names == ["msa_probe_copy", "msa_probe_mfma_bf16", "msa_probe_mfma_bf16_random",
+                     "msa_probe_mfma_valu", "msa_probe_stream_read"]
     plib = ctypes.CDLL(path)
     for n in names:
         getattr(plib, n).restype = ctypes.c_int
@@ -404,6 +404,13 @@ def test_probe_library_exports_and_checks():
     assert plib.msa_probe_stream_read(FAKE, 1000, 64, FAKE, None) == -1      # not 32 KiB units
     assert plib.msa_probe_stream_read(FAKE, 32768, 0, FAKE, None) == -1
     assert plib.msa_probe_stream_read(None, 32768, 64, FAKE, None) == -1
+    plib.msa_probe_copy.argtypes = [vp, vp, sz, ctypes.c_int, vp]
+    far = FAKE + (1 << 30)
+    assert plib.msa_probe_copy(FAKE, far, 1000, 64, None) == -1           # not 16-byte units
+    assert plib.msa_probe_copy(FAKE, FAKE + 4096, 8192, 64, None) == -1   # overlap
+    assert plib.msa_probe_copy(FAKE + 8, far, 4096, 64, None) == -1       # unaligned
+    assert plib.msa_probe_copy(FAKE, far, 4096, 0, None) == -1
+    assert plib.msa_probe_copy(None, far, 4096, 64, None) == -1
     for n in ("msa_probe_mfma_bf16", "msa_probe_mfma_bf16_random"):
         fn = getattr(plib, n)
         fn.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
