@@ -695,6 +695,12 @@ void index_prefill_bf16_kernel(
   __shared__ u32x4 Kb0[kBlk * CHG], Kb1[kBlk * CHG];
   __shared__ u32x4 Ks0[SCH], Ks1[SCH];
   __shared__ float red[NW][kChunk2];
+  // per token: the scores of up to kFlushB blocks of the tile pair's rows, written
+  // out as runs of a score row instead of one scattered float per row and block
+  // (row stride kFlushB + 1, odd, so 64 consecutive rows hit 64 distinct banks)
+  constexpr int kFlushB = 8, kPStride = kFlushB + 1;
+  __shared__ float pts[PT ? kTiles * kBlk * kPStride : 1];
+  static_assert(kTiles * kBlk == kIdxThreads, "one thread per staged row");
   const uint16_t *k_idx = static_cast<const uint16_t *>(k_idx_);
   const uint8_t *k_idx8 = static_cast<const uint8_t *>(k_idx_);
   // FP8 row swizzle: keys sharing a 256-byte bank row get distinct chunk slots
@@ -869,8 +875,30 @@ void index_prefill_bf16_kernel(
                                                          false, false);
         const float v = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         const int rit = (wave % 2) * 64 + lane;
-        if (rit < mine.num_rows)
-          scores[(static_cast<size_t>(mine.row0 + rit) * nsel + g) * max_blocks + b] = v;
+        if (rit < mine.num_rows) pts[(tt * kBlk + rit) * kPStride + bi % kFlushB] = v;
+      }
+      // every kFlushB blocks (and after the last): each thread writes one row's
+      // staged scores, the blocks before that row's diagonal, as one run
+      if (bi % kFlushB == kFlushB - 1 || bi == nblk - 1) {
+        __syncthreads();
+        const int fb = bi - bi % kFlushB, cnt = bi % kFlushB + 1;
+        const int tt2 = t / kBlk, i = t % kBlk;
+        if (tt2 < ntile) {
+          const msa_unit_t ut = units[u0 + tt2];
+          if (i < ut.num_rows) {
+            float *dst = scores + (static_cast<size_t>(ut.row0 + i) * nsel + g) * max_blocks +
+                         b0 + fb;
+            const float *srcp = pts + t * kPStride;
+            const int nv = min(cnt, ut.tau - b0 - fb);
+            if (nv == kFlushB && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+              *reinterpret_cast<float4 *>(dst) = make_float4(srcp[0], srcp[1], srcp[2], srcp[3]);
+              *reinterpret_cast<float4 *>(dst + 4) =
+                  make_float4(srcp[4], srcp[5], srcp[6], srcp[7]);
+            } else {
+              for (int k = 0; k < nv; ++k) dst[k] = srcp[k];
+            }
+          }
+        }
       }
     } else {
       m = group_max<kWave>(m);
