@@ -861,8 +861,9 @@ constexpr int kUnionThreads = 256;
 __global__ __launch_bounds__(kUnionThreads) void token_union_kernel(
     const msa_unit_t *__restrict__ units, const int32_t *__restrict__ ids, int topk, int nsel,
     TokenUnion tu, int32_t *__restrict__ count, int32_t *__restrict__ uids,
-    uint32_t *__restrict__ masks) {
-  extern __shared__ uint32_t bits[];      // [W] bitmap, then [W] exclusive prefix
+    uint32_t *__restrict__ masks, int mcap) {
+  // [W] bitmap, [W] exclusive prefix, then mcap entries' row masks [mcap][4]
+  extern __shared__ uint32_t bits[];
   __shared__ int nkr[kBlk];               // each row's list length
   __shared__ int wsum[kUnionThreads / kWave];
   const int u = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
@@ -876,11 +877,13 @@ __global__ __launch_bounds__(kUnionThreads) void token_union_kernel(
     return ids + (static_cast<size_t>(un.row0 + i) * nsel + g) * topk;
   };
   for (int w = t; w < W; w += kUnionThreads) bits[w] = 0u;
-  for (int i = t; i < n; i += kUnionThreads) {
-    const int32_t *r = row_ids(i);
-    int k = 0;
-    while (k < topk && r[k] >= 0) ++k;
-    nkr[i] = k;
+  // each row's list length: the position of its first -1 (topk if none), from
+  // independent loads rather than a walk along the row
+  for (int i = t; i < n; i += kUnionThreads) nkr[i] = topk;
+  __syncthreads();
+  for (int e = t; e < n * topk; e += kUnionThreads) {
+    const int i = e / topk, k = e % topk;
+    if (row_ids(i)[k] < 0) atomicMin(&nkr[i], k);
   }
   __syncthreads();
   for (int e = t; e < n * topk; e += kUnionThreads) {
@@ -916,9 +919,17 @@ __global__ __launch_bounds__(kUnionThreads) void token_union_kernel(
       m &= m - 1u;
     }
   }
-  for (int e = t; e < total * 4; e += kUnionThreads) masks[base * 4 + e] = 0u;
+  // the row masks are ORed together in LDS when the union fits there (then
+  // written out whole), else in place with global atomics
+  uint32_t *lm = pre + W;
+  const bool in_lds = total <= mcap;
+  if (in_lds) {
+    for (int e = t; e < total * 4; e += kUnionThreads) lm[e] = 0u;
+  } else {
+    for (int e = t; e < total * 4; e += kUnionThreads) masks[base * 4 + e] = 0u;
+  }
   if (t == 0) count[static_cast<size_t>(u) * nsel + g] = total;
-  __threadfence();                        // the zeros reach L2 before the ORs below
+  if (!in_lds) __threadfence();           // the zeros reach L2 before the ORs below
   __syncthreads();
   for (int e = t; e < n * topk; e += kUnionThreads) {
     const int i = e / topk, k = e % topk;
@@ -926,7 +937,14 @@ __global__ __launch_bounds__(kUnionThreads) void token_union_kernel(
     const int b = row_ids(i)[k];
     if (b < 0 || b > tau) continue;
     const int pos = pre[b / 32] + __popc(bits[b / 32] & ((1u << (b % 32)) - 1u));
-    atomicOr(&masks[(base + pos) * 4 + i / 32], 1u << (i % 32));
+    if (in_lds)
+      atomicOr(&lm[pos * 4 + i / 32], 1u << (i % 32));
+    else
+      atomicOr(&masks[(base + pos) * 4 + i / 32], 1u << (i % 32));
+  }
+  if (in_lds) {
+    __syncthreads();
+    for (int e = t; e < total * 4; e += kUnionThreads) masks[base * 4 + e] = lm[e];
   }
 }
 
@@ -1207,11 +1225,14 @@ hipError_t launch_prefill_attention(const Geom &g, const msa_cache_t &c, const m
                                                  al(entries * 4));
     tu = TokenUnion{cnt, uids, msk};
     const int W = c.max_blocks_per_seq / 32 + 1;   // bitmap words for any tau of the table
-    MSA_LOG_LAUNCH("token_union_kernel", dim3(b.total_units, g.nsel), kUnionThreads,
-                   2 * W * sizeof(uint32_t));
-    token_union_kernel<<<dim3(b.total_units, g.nsel), kUnionThreads,
-                         2 * W * sizeof(uint32_t), st>>>(b.units, ids, topk, g.nsel, tu, cnt,
-                                                         uids, msk);
+    // LDS row masks for unions of up to mcap blocks (a union holds at most W * 32
+    // ids, and at most 128 rows times topk), when those fit in 32 KiB
+    const int64_t most = std::min<int64_t>(int64_t(W) * 32, int64_t(kBlk) * topk);
+    const int mcap = most * 16 <= 32768 ? static_cast<int>(most) : 0;
+    const size_t lds = (2 * size_t(W) + 4 * size_t(mcap)) * sizeof(uint32_t);
+    MSA_LOG_LAUNCH("token_union_kernel", dim3(b.total_units, g.nsel), kUnionThreads, lds);
+    token_union_kernel<<<dim3(b.total_units, g.nsel), kUnionThreads, lds, st>>>(
+        b.units, ids, topk, g.nsel, tu, cnt, uids, msk, mcap);
   }
   constexpr int NW = kPrefWaves;
   const int pairs = (g.G() + NW / 4 - 1) / (NW / 4);   // work-groups per (unit, KV head)
