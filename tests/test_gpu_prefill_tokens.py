@@ -66,6 +66,9 @@ CASES = {
     "topk_one": dict(seq_lens=(1000,), q_lens=(500,), topk=1),
     # unions of more than 64 blocks: the kernel's union ids come in chunks of 64
     "union_over_64": dict(seq_lens=(12000,), q_lens=(300,), topk=40),
+    # a table of 2063 blocks and top-20: unions may outgrow the 2048 row-mask entries
+    # the union kernel keeps in LDS, so it ORs the masks with global atomics
+    "union_global_masks": dict(seq_lens=(264000,), q_lens=(140,), topk=20),
     "f32_ragged": dict(dtype="f32", seq_lens=(700, 300), q_lens=(300, 300), num_q_heads=4,
                        num_kv_heads=1, head_dim=64, num_idx_heads=2, idx_head_dim=32,
                        num_sel_groups=1),
