@@ -29,9 +29,11 @@
 // S(T). M(T) accumulates S^T of tile T and, for tile T-1, forms the probabilities
 // (against the reference maximum S(T-1) left), packs P, adds the row sum and
 // accumulates O^T += V^T P^T, each score MFMA followed by a pair of exponentials
-// so that the VALU work fills the matrix core's cycles. S(T) masks tile T, takes
-// its row maximum, rescales O and the row sum when needed, and reads the operands
-// of M(T+1) from LDS. Scores of even and odd tiles alternate between two
+// so that the VALU work fills the matrix core's cycles, and (for a tile no mask
+// touches) takes tile T's row maximum behind its P.V MFMAs. S(T) masks tile T (and
+// then takes its row maximum), rescales O and the row sum when needed, and reads
+// the operands of M(T+1) from LDS: it is kept short, since the softmax phase is
+// the one that both waves of a SIMD end up waiting for at the barrier. Scores of even and odd tiles alternate between two
 // accumulators, so tile T's scores wait in place for M(T+1). Phases end at
 // work-group barriers, and waves 4..7 run one phase behind waves 0..3, so on
 // every SIMD one wave is in an MFMA phase while the other is in a softmax phase.
@@ -342,6 +344,7 @@ void attn_prefill_bf16_kernel(
   bf16x8 kf[KS], vf[2 * DT], pf[2];
   float m_ref = kMaxFloor;                // reference maximum, log2 units
   float l_run = 0.f;                      // this lane's share of the row sum
+  float xm = 0.f;                         // the tile maximum an M phase formed
   float msub = 0.f;                       // per token: +inf when this lane's row does not
                                           // keep the block of the tile in its softmax phase
 
@@ -365,9 +368,12 @@ void attn_prefill_bf16_kernel(
   // (scores in sc[1 - P], its softmax phase done) the probabilities against the
   // reference maximum that phase left, their row sum and O^T += V^T P^T. The
   // score MFMAs do not wait for the probabilities, so the exponentials run while
-  // the matrix core is busy with them.
-  auto mphase = [&](auto pv_tag, auto qk_tag, auto par) __attribute__((always_inline)) {
+  // the matrix core is busy with them. With MX (a tile no mask will touch) the
+  // phase also takes the new tile's row maximum, behind the P.V MFMAs, so that
+  // the softmax phase, the one both waves of a SIMD wait for, does not.
+  auto mphase = [&](auto pv_tag, auto qk_tag, auto par, auto mx_tag) __attribute__((always_inline)) {
     constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
+    constexpr bool MX = decltype(mx_tag)::value && QK;
     constexpr int P = decltype(par)::value;
     if constexpr (QK) {
       sc[P] = f32x16{};
@@ -396,6 +402,16 @@ void attn_prefill_bf16_kernel(
       for (int i = 0; i < 2 * DT; ++i)
         o[i / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i % 2], o[i / 2], 0, 0, 0);
     }
+    if constexpr (MX) {
+      const f32x16 &s = sc[P];
+      float x = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) x = fmaxf(fmaxf(x, s[i]), s[i + 1]);
+      x = fmaxf(x, s[15]);
+      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+      xm = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * c;
+    }
     if constexpr (PV && QK) {
       // issue order: each score MFMA followed by a pair of probabilities (fma, exp),
       // each P.V MFMA by the packing and summing work, so that the VALU work fills
@@ -408,15 +424,16 @@ void attn_prefill_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < 2 * DT; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 24 / (2 * DT), 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, (24 + (MX ? 12 : 0)) / (2 * DT), 0);
       }
     }
   };
 
   // Softmax phase of tile kt (0..3) of the block at position bp, scores in sc[P]:
   // the causal mask (the first block always, MASK; any other one only when it
-  // reaches the unit's first query), the tile's row maximum and, when it grew by
-  // more than the slack, the rescale of O and the row sum.
+  // reaches the unit's first query), the tile's row maximum (taken here only for a
+  // masked tile; the M phase took it for the others) and, when it grew by more than
+  // the slack, the rescale of O and the row sum.
   auto softmax = [&](auto mask_tag, auto par, int kt, int bp) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int P = decltype(par)::value;
@@ -433,14 +450,19 @@ void attn_prefill_bf16_kernel(
       for (int i = 0; i < 16; ++i)
         if (16 * (i / 8) + 8 * a + (i % 8) > lim) s[i] = neg_inf();
     }
-    float x = fmaxf(fmaxf(s[0], s[1]), s[2]);
+    float x;
+    if (!MASK && !do_mask) {
+      x = xm;                               // formed in the tile's M phase
+    } else {
+      x = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-    for (int i = 3; i < 15; i += 2) x = fmaxf(fmaxf(x, s[i]), s[i + 1]);
-    x = fmaxf(x, s[15]);
-    {   // max with the other half of the wave (same query column)
-      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                        false, false);
-      x = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * c;
+      for (int i = 3; i < 15; i += 2) x = fmaxf(fmaxf(x, s[i]), s[i + 1]);
+      x = fmaxf(x, s[15]);
+      {   // max with the other half of the wave (same query column)
+        const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                          false, false);
+        x = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * c;
+      }
     }
     // per token: a row that does not keep this block sees none of its keys (its
     // maximum ignores the tile, its probabilities are exp2(-inf) = 0)
@@ -470,10 +492,12 @@ void attn_prefill_bf16_kernel(
       constexpr int kt = decltype(ktc)::value;
       constexpr int P = kt % 2;
       const int T = 4 * bp + kt;
+      // the tile maximum in the M phase for the blocks with no static mask
+      using MXT = std::integral_constant<bool, !MASK>;
       if (MASK && kt == 0)
-        mphase(std::false_type{}, std::true_type{}, ic<P>{});   // first tile: no previous P
+        mphase(std::false_type{}, std::true_type{}, ic<P>{}, MXT{});   // no previous P
       else
-        mphase(std::true_type{}, std::true_type{}, ic<P>{});
+        mphase(std::true_type{}, std::true_type{}, ic<P>{}, MXT{});
       phase_barrier();
       if constexpr (kt == 0) read_k(ic<R0>{}, 1);
       else if constexpr (kt == 1) read_k(ic<R0 + 1>{}, 0);
@@ -521,7 +545,7 @@ void attn_prefill_bf16_kernel(
     block_step(std::false_type{}, ic<0>{}, bp + 1);
   }
   // probabilities and O^T += V^T P^T of the last tile (odd: its scores are in sc[1])
-  mphase(std::true_type{}, std::false_type{}, ic<0>{});
+  mphase(std::true_type{}, std::false_type{}, ic<0>{}, std::false_type{});
   if (grp == 0) phase_barrier();
 
   if (!active) return;
