@@ -345,6 +345,7 @@ void attn_prefill_bf16_kernel(
   float m_ref = kMaxFloor;                // reference maximum, log2 units
   float l_run = 0.f;                      // this lane's share of the row sum
   float xm = 0.f;                         // the tile maximum an M phase formed
+  float thr = kMaxFloor + kSlack;         // m_ref + kSlack, kept with m_ref
   float msub = 0.f;                       // per token: +inf when this lane's row does not
                                           // keep the block of the tile in its softmax phase
 
@@ -411,6 +412,7 @@ void attn_prefill_bf16_kernel(
       const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                                         false, false);
       xm = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * c;
+      asm volatile("" : "+v"(xm));          // finished here, not in the softmax phase
     }
     if constexpr (PV && QK) {
       // issue order: each score MFMA followed by a pair of probabilities (fma, exp),
@@ -471,11 +473,12 @@ void attn_prefill_bf16_kernel(
       x = keep ? x : neg_inf();
       msub = keep ? 0.f : pos_inf();
     }
-    const bool need = x > m_ref + kSlack;
+    const bool need = x > thr;
     if (__any(need)) {
       const float nm = need ? x : m_ref;
       const float al = __builtin_amdgcn_exp2f(m_ref - nm);
       m_ref = nm;
+      thr = m_ref + kSlack;
       l_run *= al;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
