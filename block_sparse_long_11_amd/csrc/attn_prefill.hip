@@ -33,8 +33,9 @@
 // touches) takes tile T's row maximum behind its P.V MFMAs. S(T) masks tile T (and
 // then takes its row maximum), rescales O and the row sum when needed, and reads
 // the operands of M(T+1) from LDS: it is kept short, since the softmax phase is
-// the one that both waves of a SIMD end up waiting for at the barrier. Scores of even and odd tiles alternate between two
-// accumulators, so tile T's scores wait in place for M(T+1). Phases end at
+// the one that both waves of a SIMD end up waiting for at the barrier. Scores of
+// even and odd tiles alternate between two accumulators, so tile T's scores wait
+// in place for M(T+1). Phases end at
 // work-group barriers, and waves 4..7 run one phase behind waves 0..3, so on
 // every SIMD one wave is in an MFMA phase while the other is in a softmax phase.
 //
