@@ -840,6 +840,44 @@ void index_prefill_bf16_kernel(
         for (int i = 0; i < 16; i += 2) mm = fmaxf(fmaxf(mm, v[i]), v[i + 1]);
       };
       rd(0, kf[0]);
+      if constexpr (!FP8) {
+        // row set a's chain while row set b's previous sub-tile is pooled, then row
+        // set b's chain while a's is pooled: one max3 beside each MFMA, and the wave
+        // no longer waits for a sub-tile's results before the next sub-tile's MFMAs
+        // (FP8 keys keep the alternating chains below, whose conversions fill the
+        // MFMA shadow instead)
+        auto chain = [&](f32x16 &acc, const bf16x8 *q, int cb) __attribute__((always_inline)) {
+          acc = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            if constexpr (PT)
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cb][ks], q[ks], acc, 0, 0, 0);
+            else
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q[ks], kf[cb][ks], acc, 0, 0, 0);
+          }
+        };
+        float &pa = PT ? ma : m, &pb = PT ? mb : m;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int cb = nt & 1;
+          if (nt < 3) rd(nt + 1, kf[cb ^ 1]);
+          chain(acc0, qa, cb);
+          if (nt > 0) pool(pb, acc1);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+          }
+          chain(acc1, qb, cb);
+          pool(pa, acc0);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+          }
+        }
+        pool(pb, acc1);
+      } else
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int cb = nt & 1;
