@@ -649,9 +649,10 @@ void index_prefill_wide_kernel(
 // next block is in flight while this one is scored; one staged block serves every
 // query row of the group. Wave w owns 64 rows (two 32-row MFMA tiles) of tile
 // w/2: every key fragment read from LDS feeds two MFMAs. A = query rows in
-// registers, B = key rows from LDS. Per 32-key sub-tile the two rows' MFMA
-// chains alternate (no MFMA waits on the result of the one just issued), then
-// both accumulators are max-pooled, and the next sub-tile's fragments are read
+// registers, B = key rows from LDS. Per 32-key sub-tile, with bf16 keys, row set
+// a's MFMA chain runs while row set b's accumulator of the previous sub-tile is
+// max-pooled, then b's chain while a's is pooled (FP8 keys: the two chains
+// alternate, then both are pooled); the next sub-tile's fragments are read
 // meanwhile. Rows past a unit's end repeat its last row, so they never change a
 // maximum.
 //
