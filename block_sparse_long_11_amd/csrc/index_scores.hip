@@ -649,11 +649,10 @@ void index_prefill_wide_kernel(
 // next block is in flight while this one is scored; one staged block serves every
 // query row of the group. Wave w owns 64 rows (two 32-row MFMA tiles) of tile
 // w/2: every key fragment read from LDS feeds two MFMAs. A = query rows in
-// registers, B = key rows from LDS. Per 32-key sub-tile, with bf16 keys, row set
-// a's MFMA chain runs while row set b's accumulator of the previous sub-tile is
-// max-pooled, then b's chain while a's is pooled (FP8 keys: the two chains
-// alternate, then both are pooled); the next sub-tile's fragments are read
-// meanwhile. Rows past a unit's end repeat its last row, so they never change a
+// registers, B = key rows from LDS. Per 32-key sub-tile, row set a's MFMA chain
+// runs while row set b's accumulator of the previous sub-tile is max-pooled, then
+// b's chain while a's is pooled; the next sub-tile's fragments are read (and, for
+// FP8 keys, converted) meanwhile. Rows past a unit's end repeat its last row, so they never change a
 // maximum.
 //
 // FP8 indexer keys: the staged rows are the group's E4M3 codes (GD bytes a key,
@@ -841,70 +840,43 @@ void index_prefill_bf16_kernel(
         for (int i = 0; i < 16; i += 2) mm = fmaxf(fmaxf(mm, v[i]), v[i + 1]);
       };
       rd(0, kf[0]);
-      if constexpr (!FP8) {
-        // row set a's chain while row set b's previous sub-tile is pooled, then row
-        // set b's chain while a's is pooled: one max3 beside each MFMA, and the wave
-        // no longer waits for a sub-tile's results before the next sub-tile's MFMAs
-        // (FP8 keys keep the alternating chains below, whose conversions fill the
-        // MFMA shadow instead)
-        auto chain = [&](f32x16 &acc, const bf16x8 *q, int cb) __attribute__((always_inline)) {
-          acc = f32x16{};
+      // row set a's chain while row set b's previous sub-tile is pooled, then row
+      // set b's chain while a's is pooled, so the wave does not wait for a
+      // sub-tile's results before the next sub-tile's MFMAs: beside each MFMA one
+      // max3 (bf16 keys), or three VALU instructions of the pooling and of the next
+      // fragments' FP8 conversions
+      auto chain = [&](f32x16 &acc, const bf16x8 *q, int cb) __attribute__((always_inline)) {
+        acc = f32x16{};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            if constexpr (PT)
-              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cb][ks], q[ks], acc, 0, 0, 0);
-            else
-              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q[ks], kf[cb][ks], acc, 0, 0, 0);
-          }
-        };
-        float &pa = PT ? ma : m, &pb = PT ? mb : m;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int cb = nt & 1;
-          if (nt < 3) rd(nt + 1, kf[cb ^ 1]);
-          chain(acc0, qa, cb);
-          if (nt > 0) pool(pb, acc1);
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
-          }
-          chain(acc1, qb, cb);
-          pool(pa, acc0);
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
-          }
+        for (int ks = 0; ks < KS; ++ks) {
+          if constexpr (PT)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cb][ks], q[ks], acc, 0, 0, 0);
+          else
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q[ks], kf[cb][ks], acc, 0, 0, 0);
         }
-        pool(pb, acc1);
-      } else
+      };
+      float &pa = PT ? ma : m, &pb = PT ? mb : m;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int cb = nt & 1;
         if (nt < 3) rd(nt + 1, kf[cb ^ 1]);
-        // the two rows' chains alternate, so no MFMA waits on the one just issued
-        acc0 = f32x16{};
-        acc1 = f32x16{};
+        constexpr int NV = FP8 ? 3 : 1;   // VALU instructions beside each MFMA
+        chain(acc0, qa, cb);
+        if (nt > 0) pool(pb, acc1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          if constexpr (PT) {
-            // keys x queries: a lane holds one query column and 16 keys of the tile
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cb][ks], qa[ks], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cb][ks], qb[ks], acc1, 0, 0, 0);
-          } else {
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[cb][ks], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], kf[cb][ks], acc1, 0, 0, 0);
-          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
         }
-        if constexpr (PT) {
-          pool(ma, acc0);
-          pool(mb, acc1);
-        } else {
-          pool(m, acc0);
-          pool(m, acc1);
+        chain(acc1, qb, cb);
+        pool(pa, acc0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
         }
       }
+      pool(pb, acc1);
     }
     if constexpr (PT) {
       // lanes 0..31 take the other half's keys of row set a, lanes 32..63 those of
