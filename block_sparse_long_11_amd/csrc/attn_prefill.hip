@@ -416,18 +416,23 @@ void attn_prefill_bf16_kernel(
       asm volatile("" : "+v"(xm));          // finished here, not in the softmax phase
     }
     if constexpr (PV && QK) {
-      // issue order: each score MFMA followed by a pair of probabilities (fma, exp),
-      // each P.V MFMA by the packing and summing work, so that the VALU work fills
-      // the matrix core's cycles instead of following them
+      // issue order: each score MFMA followed by VALU work of the probabilities (fma,
+      // exp), each P.V MFMA by the rest of it, the packing, the sums and the row
+      // maximum, so that the VALU work fills the matrix core's cycles instead of
+      // following them. At head_dim 128, 3 VALU instructions beside each score MFMA
+      // and 5 beside each P.V MFMA measured best (4 and 4: 0.8-1.4% slower; 2-6 and
+      // 6-3 slower still)
+      constexpr int kSV = KS == 8 ? 3 : 32 / KS;
+      constexpr int kPV = KS == 8 ? 5 : (24 + (MX ? 12 : 0)) / (2 * DT);
 #pragma unroll
       for (int i = 0; i < KS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 32 / KS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kSV, 0);
       }
 #pragma unroll
       for (int i = 0; i < 2 * DT; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, (24 + (MX ? 12 : 0)) / (2 * DT), 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kPV, 0);
       }
     }
   };
