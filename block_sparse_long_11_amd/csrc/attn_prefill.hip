@@ -18,7 +18,9 @@
 //
 // bf16 path (MFMA 32x32x16, fp32 accumulate). A work-group of 8 waves owns (unit,
 // KV head j, 2 query heads): 128 token rows x 2 heads, one wave per (head, 32
-// tokens); waves w and w + 4 share a SIMD. Per 32-key tile each wave computes
+// tokens); waves w and w + 4 share a SIMD. With per-token selection it owns 32
+// rows x 8 heads instead (the same query rows per K/V tile), and reads the union
+// of those 32 rows' kept blocks. Per 32-key tile each wave computes
 //   S^T = K . Q^T           (A = K rows from LDS, B = Q held in registers)
 //   O^T += V^T . P^T        (A = V^T rows from LDS, B = P from S^T's registers)
 // The S^T row m of a tile is fed key (m with bits 2 and 3 swapped): then lane
@@ -127,17 +129,18 @@ using ic = std::integral_constant<int, V>;
 }  // namespace
 
 // Per-query-token prefill (each token row keeps its own blocks): for every (unit,
-// group) the union of its rows' kept ids, ascending, and for each union entry
-// four 32-bit row masks (bit n of word w: tile row 32 w + n keeps the block).
-// Entry lists of unit u, group g start at base(): the same extent as the rows'
-// own id lists, which bound the union's size.
+// group, 32-row slab s of the unit's rows) the union of the slab's rows' kept ids,
+// ascending, and for each union entry a 32-bit row mask (bit n: row 32 s + n
+// keeps the block). The list of slab s starts at base(): inside the extent of its
+// rows' own id lists, which bound the union's size.
 struct TokenUnion {
-  const int32_t *count;     // [U][n_sel] union sizes
+  const int32_t *count;     // [U][n_sel][4] union sizes
   const int32_t *ids;       // union ids
-  const uint32_t *masks;    // [entry][4]
-  __device__ __forceinline__ size_t base(const msa_unit_t &un, int nsel, int g,
-                                         int topk) const {
-    return (static_cast<size_t>(un.row0) * nsel + static_cast<size_t>(g) * un.num_rows) * topk;
+  const uint32_t *masks;    // [entry]
+  __device__ __forceinline__ size_t base(const msa_unit_t &un, int nsel, int g, int topk,
+                                         int slab) const {
+    return (static_cast<size_t>(un.row0) * nsel + static_cast<size_t>(g) * un.num_rows +
+            static_cast<size_t>(32 * slab)) * topk;
   }
 };
 
@@ -212,17 +215,21 @@ void attn_prefill_bf16_kernel(
   const msa_unit_t un = units[u];
   const int G = Hq / Hkv;
   const int g = (nsel == Hkv) ? j : 0;
-  // per token: the union of the unit's rows' lists (ascending) and its row masks
-  const size_t ubase = PT ? tu.base(un, nsel, g, topk) : 0;
-  const int32_t *sel = PT ? tu.ids + ubase : ids + (static_cast<size_t>(u) * nsel + g) * topk;
-  const int32_t *bt = block_table + static_cast<size_t>(un.r) * max_blocks;
 
   const int t = threadIdx.x, lane = t % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
   const int a = lane / 32, n = lane % 32;
   const int grp = wave / 4;               // 0 leads, 1 trails by one phase
-  const int hl = 2 * hp + grp;            // head inside the group
-  const int slab = wave % 4;              // 32-token slab of the tile
+  // Work-group hp of (unit, KV head j) takes 2 heads x the tile's 4 slabs of 32
+  // rows (wave w: head 2 hp + w / 4, slab w % 4); per token, 8 heads x one slab
+  // (slab hp % 4, heads 8 (hp / 4) + 2 (w % 4) + w / 4), so that its waves read
+  // the union of that slab's lists alone
+  const int slab = PT ? hp % 4 : wave % 4;
+  const int hl = PT ? 8 * (hp / 4) + 2 * (wave % 4) + grp : 2 * hp + grp;
+  // per token: the union of the slab's rows' lists (ascending) and its row masks
+  const size_t ubase = PT ? tu.base(un, nsel, g, topk, slab) : 0;
+  const int32_t *sel = PT ? tu.ids + ubase : ids + (static_cast<size_t>(u) * nsel + g) * topk;
+  const int32_t *bt = block_table + static_cast<size_t>(un.r) * max_blocks;
   // Waves past the group's heads or the unit's rows compute on clamped (valid)
   // rows like the others and store nothing.
   const bool active = hl < G && slab * 32 < un.num_rows;
@@ -241,7 +248,7 @@ void attn_prefill_bf16_kernel(
   // takes the causal test.
   int nk = 0;
   if constexpr (PT)
-    nk = tu.count[static_cast<size_t>(u) * nsel + g];
+    nk = tu.count[(static_cast<size_t>(u) * nsel + g) * 4 + slab];
   else
     while (nk < topk && sel[nk] >= 0) ++nk;
   if (nk == 0) {                          // nothing kept: no visible key
@@ -284,7 +291,7 @@ void attn_prefill_bf16_kernel(
       const int pl = 64 * late_chunk + lane;
       const int ix = pl == 0 ? nk - 1 : pl - 1;
       logical = pl < nk ? sel[ix] : 0;
-      if constexpr (PT) keepw = pl < nk ? tu.masks[(ubase + ix) * 4 + slab] : 0u;
+      if constexpr (PT) keepw = pl < nk ? tu.masks[ubase + ix] : 0u;
       late = __ballot(pl < nk && logical >= un.tau);
     }
     return ((late >> (p & 63)) & 1) != 0;
@@ -604,15 +611,16 @@ void attn_prefill_fp8_kernel(
   const msa_unit_t un = units[u];
   const int G = Hq / Hkv;
   const int g = (nsel == Hkv) ? j : 0;
-  const size_t ubase = PT ? tu.base(un, nsel, g, topk) : 0;
-  const int32_t *sel = PT ? tu.ids + ubase : ids + (static_cast<size_t>(u) * nsel + g) * topk;
-  const int32_t *bt = block_table + static_cast<size_t>(un.r) * max_blocks;
 
   const int t = threadIdx.x, lane = t % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
   const int a = lane / 32, n = lane % 32;
-  const int hl = 2 * hp + wave / 4;
-  const int slab = wave % 4;
+  // heads and slabs of the waves as in the bf16 kernel
+  const int slab = PT ? hp % 4 : wave % 4;
+  const int hl = PT ? 8 * (hp / 4) + 2 * (wave % 4) + wave / 4 : 2 * hp + wave / 4;
+  const size_t ubase = PT ? tu.base(un, nsel, g, topk, slab) : 0;
+  const int32_t *sel = PT ? tu.ids + ubase : ids + (static_cast<size_t>(u) * nsel + g) * topk;
+  const int32_t *bt = block_table + static_cast<size_t>(un.r) * max_blocks;
   const bool active = hl < G && slab * 32 < un.num_rows;
   const int head = j * G + min(hl, G - 1);
   const int row_in_tile = slab * 32 + n;
@@ -622,7 +630,7 @@ void attn_prefill_fp8_kernel(
 
   int nk = 0;
   if constexpr (PT)
-    nk = tu.count[static_cast<size_t>(u) * nsel + g];
+    nk = tu.count[(static_cast<size_t>(u) * nsel + g) * 4 + slab];
   else
     while (nk < topk && sel[nk] >= 0) ++nk;
   if (nk == 0) {                          // nothing kept: no visible key
@@ -728,7 +736,7 @@ void attn_prefill_fp8_kernel(
     const bool late = blk_id >= un.tau;
     // per token: whether this lane's row keeps the block
     bool keep = true;
-    if constexpr (PT) keep = ((tu.masks[(ubase + ix_of(hb >> 1)) * 4 + slab] >> n) & 1u) != 0;
+    if constexpr (PT) keep = ((tu.masks[ubase + ix_of(hb >> 1)] >> n) & 1u) != 0;
 #pragma unroll
     for (int kt2 = 0; kt2 < 2; ++kt2) {
       bf16x8 kf[KS], vf[2 * DT], pf[2];
@@ -883,36 +891,43 @@ hipError_t launch_attn_f32(const Geom &g, const msa_cache_t &c, const msa_unit_t
   return hipGetLastError();
 }
 
-// Union of the kept lists of one (unit, group) for the per-token prefill: one
-// work-group per pair. Each row's list ends at its first -1; ids outside [0, tau]
-// hold no key visible to the unit's rows and are left out. The ids set bits of an
-// LDS bitmap over [0, tau]; an exclusive scan of the words' popcounts gives every
-// block its rank, so the union comes out ascending; each kept (row, id) then ORs
-// the row's bit into the mask words of its block's entry (zeroed first).
+// Union of the kept lists of one (unit, group, 32-row slab) for the per-token
+// prefill: one work-group per triple. Each row's list ends at its first -1; ids
+// outside [0, tau] hold no key visible to the unit's rows and are left out. The
+// ids set bits of an LDS bitmap over [0, tau]; an exclusive scan of the words'
+// popcounts gives every block its rank, so the union comes out ascending; each
+// kept (row, id) then ORs the row's bit into the mask word of its block's entry
+// (zeroed first).
 constexpr int kUnionThreads = 256;
+constexpr int kUnionLdsMasks = 2048;      // most row-mask words a union keeps in LDS
 
 __global__ __launch_bounds__(kUnionThreads) void token_union_kernel(
     const msa_unit_t *__restrict__ units, const int32_t *__restrict__ ids, int topk, int nsel,
     TokenUnion tu, int32_t *__restrict__ count, int32_t *__restrict__ uids,
     uint32_t *__restrict__ masks, int mcap) {
-  // [W] bitmap, [W] exclusive prefix, then mcap entries' row masks [mcap][4]
+  // [W] bitmap, [W] exclusive prefix, then mcap entries' row masks
   extern __shared__ uint32_t bits[];
-  __shared__ int nkr[kBlk];               // each row's list length
+  __shared__ int nkr[32];                 // each row's list length
   __shared__ int wsum[kUnionThreads / kWave];
-  const int u = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  const int u = blockIdx.x, g = blockIdx.y, slab = blockIdx.z, t = threadIdx.x;
   const int lane = t % kWave, wave = t / kWave;
   const msa_unit_t un = units[u];
-  const int n = un.num_rows, tau = un.tau;
+  const int n = min(32, un.num_rows - 32 * slab), tau = un.tau;   // rows of the slab
+  const size_t ci = (static_cast<size_t>(u) * nsel + g) * 4 + slab;
+  if (n <= 0) {                           // a slab past the unit's rows
+    if (t == 0) count[ci] = 0;
+    return;
+  }
   const int W = tau / 32 + 1;             // words covering blocks [0, tau]
   uint32_t *pre = bits + W;
-  const size_t base = tu.base(un, nsel, g, topk);
+  const size_t base = tu.base(un, nsel, g, topk, slab);
   auto row_ids = [&](int i) {
-    return ids + (static_cast<size_t>(un.row0 + i) * nsel + g) * topk;
+    return ids + (static_cast<size_t>(un.row0 + 32 * slab + i) * nsel + g) * topk;
   };
   for (int w = t; w < W; w += kUnionThreads) bits[w] = 0u;
   // each row's list length: the position of its first -1 (topk if none), from
   // independent loads rather than a walk along the row
-  for (int i = t; i < n; i += kUnionThreads) nkr[i] = topk;
+  if (t < n) nkr[t] = topk;
   __syncthreads();
   for (int e = t; e < n * topk; e += kUnionThreads) {
     const int i = e / topk, k = e % topk;
@@ -957,11 +972,11 @@ __global__ __launch_bounds__(kUnionThreads) void token_union_kernel(
   uint32_t *lm = pre + W;
   const bool in_lds = total <= mcap;
   if (in_lds) {
-    for (int e = t; e < total * 4; e += kUnionThreads) lm[e] = 0u;
+    for (int e = t; e < total; e += kUnionThreads) lm[e] = 0u;
   } else {
-    for (int e = t; e < total * 4; e += kUnionThreads) masks[base * 4 + e] = 0u;
+    for (int e = t; e < total; e += kUnionThreads) masks[base + e] = 0u;
   }
-  if (t == 0) count[static_cast<size_t>(u) * nsel + g] = total;
+  if (t == 0) count[ci] = total;
   if (!in_lds) __threadfence();           // the zeros reach L2 before the ORs below
   __syncthreads();
   for (int e = t; e < n * topk; e += kUnionThreads) {
@@ -971,13 +986,13 @@ __global__ __launch_bounds__(kUnionThreads) void token_union_kernel(
     if (b < 0 || b > tau) continue;
     const int pos = pre[b / 32] + __popc(bits[b / 32] & ((1u << (b % 32)) - 1u));
     if (in_lds)
-      atomicOr(&lm[pos * 4 + i / 32], 1u << (i % 32));
+      atomicOr(&lm[pos], 1u << i);
     else
-      atomicOr(&masks[(base + pos) * 4 + i / 32], 1u << (i % 32));
+      atomicOr(&masks[base + pos], 1u << i);
   }
   if (in_lds) {
     __syncthreads();
-    for (int e = t; e < total * 4; e += kUnionThreads) masks[base * 4 + e] = lm[e];
+    for (int e = t; e < total; e += kUnionThreads) masks[base + e] = lm[e];
   }
 }
 
@@ -1214,7 +1229,7 @@ size_t tokens_workspace_bytes(const Geom &g, int total_units, int total_q, int t
   if (!g.bf16) return 0;
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   const size_t entries = static_cast<size_t>(total_q) * g.nsel * topk;
-  return al(static_cast<size_t>(total_units) * g.nsel * 4) + al(entries * 4) + al(entries * 16);
+  return al(static_cast<size_t>(total_units) * g.nsel * 16) + al(entries * 4) + al(entries * 4);
 }
 
 template <bool PT>
@@ -1253,22 +1268,24 @@ hipError_t launch_prefill_attention(const Geom &g, const msa_cache_t &c, const m
     char *ws = static_cast<char *>(workspace);
     int32_t *cnt = reinterpret_cast<int32_t *>(ws);
     int32_t *uids = reinterpret_cast<int32_t *>(ws + al(static_cast<size_t>(b.total_units) *
-                                                         g.nsel * 4));
+                                                         g.nsel * 16));
     uint32_t *msk = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(uids) +
                                                  al(entries * 4));
     tu = TokenUnion{cnt, uids, msk};
     const int W = c.max_blocks_per_seq / 32 + 1;   // bitmap words for any tau of the table
-    // LDS row masks for unions of up to mcap blocks (a union holds at most W * 32
-    // ids, and at most 128 rows times topk), when those fit in 32 KiB
-    const int64_t most = std::min<int64_t>(int64_t(W) * 32, int64_t(kBlk) * topk);
-    const int mcap = most * 16 <= 32768 ? static_cast<int>(most) : 0;
-    const size_t lds = (2 * size_t(W) + 4 * size_t(mcap)) * sizeof(uint32_t);
-    MSA_LOG_LAUNCH("token_union_kernel", dim3(b.total_units, g.nsel), kUnionThreads, lds);
-    token_union_kernel<<<dim3(b.total_units, g.nsel), kUnionThreads, lds, st>>>(
-        b.units, ids, topk, g.nsel, tu, cnt, uids, msk, mcap);
+    // LDS row masks for unions of up to mcap blocks (a slab's union holds at most
+    // W * 32 ids, and at most 32 rows times topk), when there are at most 2048
+    const int64_t most = std::min<int64_t>(int64_t(W) * 32, int64_t(32) * topk);
+    const int mcap = most <= kUnionLdsMasks ? static_cast<int>(most) : 0;
+    const size_t lds = (2 * size_t(W) + size_t(mcap)) * sizeof(uint32_t);
+    const dim3 ugrid(b.total_units, g.nsel, 4);
+    MSA_LOG_LAUNCH("token_union_kernel", ugrid, kUnionThreads, lds);
+    token_union_kernel<<<ugrid, kUnionThreads, lds, st>>>(b.units, ids, topk, g.nsel, tu, cnt,
+                                                          uids, msk, mcap);
   }
   constexpr int NW = kPrefWaves;
-  const int pairs = (g.G() + NW / 4 - 1) / (NW / 4);   // work-groups per (unit, KV head)
+  // work-groups per (unit, KV head): of 2 heads each, per token of 8 heads x 4 slabs
+  const int pairs = PT ? 4 * ((g.G() + 7) / 8) : (g.G() + NW / 4 - 1) / (NW / 4);
   const int num_uj = b.total_units * g.Hkv;
   const int groups8 = (num_uj + 7) / 8;
   const dim3 grid(groups8 * 8 * pairs);

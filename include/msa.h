@@ -346,8 +346,8 @@ msa_status_t msa_sparse_attn_decode_per_token(const msa_geom_t *geom, const msa_
  *   msa_sparse_attn_prefill_tokens: q [total_q][H_q][D], ids as above (rows as
  *       for msa_sparse_attn_prefill: distinct ids, ended by the first -1,
  *       masked by position) -> out [total_q][H_q][D], lse fp32 [total_q][H_q] or
- *       NULL. The 128 rows of a unit are attended together over the union of
- *       their lists, each row over its own blocks only. workspace (device,
+ *       NULL. Every 32 rows of a unit are attended together over the union
+ *       of their lists, each row over its own blocks only. workspace (device,
  *       256-byte aligned) of msa_prefill_tokens_workspace_size(geom, total_units,
  *       total_q, topk) bytes holds the unions (0 bytes for fp32: workspace may
  *       be NULL). max_blocks_per_seq <= 131072.

@@ -337,7 +337,8 @@ def test_prefill_tokens_checks(lib):
                                                ctypes.byref(empty), None, None, None) == OK
     need = lib.msa_prefill_tokens_workspace_size(ctypes.byref(g), 3, 300, 16)
     al = lambda x: (x + 255) // 256 * 256
-    assert need == al(3 * 4 * 4) + al(300 * 4 * 16 * 4) + al(300 * 4 * 16 * 16)
+    # union sizes per (unit, group, 32-row slab), union ids, one row-mask word per id
+    assert need == al(3 * 4 * 4 * 4) + al(300 * 4 * 16 * 4) + al(300 * 4 * 16 * 4)
     assert lib.msa_prefill_tokens_workspace_size(ctypes.byref(_geom(dtype=msa.MSA_F32)), 3, 300,
                                                  16) == 0
     call = lambda ws, nbytes, **kw: lib.msa_sparse_attn_prefill_tokens(

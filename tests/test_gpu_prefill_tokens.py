@@ -1,7 +1,7 @@
 """Per-query-token selection in prefill on MI355X through the C ABI, against the
 oracle's prefill_token_units path: every new token scores the blocks with its own
 indexer query, keeps its own top-k and attends over its own blocks (the unit's
-rows are attended together over the union of their lists). Bars of the tile
+rows are attended 32 at a time over the union of their lists). Bars of the tile
 path: scores within the dot-product bound, ids exact outside near ties (then
 attention is compared on the GPU's ids), out max-abs 2e-2 (bf16) or 1e-5
 (fp32), lse 1e-3. Small cases are compared in full; the 32k prefill on a seeded
@@ -66,9 +66,9 @@ CASES = {
     "topk_one": dict(seq_lens=(1000,), q_lens=(500,), topk=1),
     # unions of more than 64 blocks: the kernel's union ids come in chunks of 64
     "union_over_64": dict(seq_lens=(12000,), q_lens=(300,), topk=40),
-    # a table of 2063 blocks and top-20: unions may outgrow the 2048 row-mask entries
-    # the union kernel keeps in LDS, so it ORs the masks with global atomics
-    "union_global_masks": dict(seq_lens=(264000,), q_lens=(140,), topk=20),
+    # a table of 2063 blocks and top-80: a slab's union may outgrow the 2048 row-mask
+    # words the union kernel keeps in LDS, so it ORs the masks with global atomics
+    "union_global_masks": dict(seq_lens=(264000,), q_lens=(140,), topk=80),
     "f32_ragged": dict(dtype="f32", seq_lens=(700, 300), q_lens=(300, 300), num_q_heads=4,
                        num_kv_heads=1, head_dim=64, num_idx_heads=2, idx_head_dim=32,
                        num_sel_groups=1),
