@@ -242,11 +242,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_reg_kernel(
 
 // Rows of at most 64 * E entries: one wave per row, four rows per work-group, no
 // LDS and no barriers. Lane l holds the E consecutive entries from l * E. The
-// K-th largest key is found bit by bit from the top: the largest threshold with
-// at least K keys at or above it, each count being the popcounts of one ballot
-// per register. Entries above it are kept, and of those equal to it the lowest
-// indices, counted with v_mbcnt (set bits of lower lanes); the same counts give
-// every kept entry its output slot, so the ids come out ascending.
+// threshold is built bit by bit from the top: the largest with at least K keys at
+// or above it (the K-th largest key), each count being the popcounts of one ballot
+// per register; the search stops early once exactly K keys are at or above it,
+// which then separates the K largest from the rest. Entries above it are kept,
+// and of those equal to it the lowest indices, counted with v_mbcnt (set bits of
+// lower lanes); the same counts give every kept entry its output slot, so the ids
+// come out ascending.
 template <int E>
 __global__ __launch_bounds__(256) void topk_rows_wave_kernel(const float *__restrict__ scores,
                                                              int rows, int row_len, int topk,
@@ -276,10 +278,14 @@ __global__ __launch_bounds__(256) void topk_rows_wave_kernel(const float *__rest
       int c = 0;
 #pragma unroll
       for (int j = 0; j < E; ++j) c += __popcll(__ballot(key[j] >= cand));
-      if (c >= K) thr = cand;
+      if (c >= K) {
+        thr = cand;
+        if (c == K) break;                     // the same for every lane
+      }
     }
     // thr is the key of the K-th largest entry (every one of the K largest is
-    // above -inf); `remaining` entries equal to it are taken, lowest index first
+    // above -inf), or a threshold with exactly the K largest at or above it;
+    // `remaining` entries equal to it are taken, lowest index first
     int n_gt = 0, eq_before = 0;
     uint64_t eq[E];
 #pragma unroll

@@ -63,6 +63,13 @@ CASES = {
     "g16_d64_di32": dict(seq_lens=(1300,), q_lens=(700,), num_q_heads=16, num_kv_heads=1,
                          head_dim=64, num_idx_heads=2, idx_head_dim=32, num_sel_groups=1),
     "topk_covers_all": dict(seq_lens=(1000,), q_lens=(1000,), topk=16),
+    # 12 query heads per KV head: a work-group of one 32-row slab takes 8 heads, so the
+    # second group of 8 has 4 waves without a head; tiles of 56 and 4 rows leave
+    # slabs without rows
+    "g12_partial_heads": dict(seq_lens=(900,), q_lens=(700,), num_q_heads=24, num_kv_heads=2,
+                              topk=5),
+    "fp8_g12_partial_heads": dict(seq_lens=(900,), q_lens=(700,), num_q_heads=24,
+                                  num_kv_heads=2, topk=5, cache_format="fp8"),
     "topk_one": dict(seq_lens=(1000,), q_lens=(500,), topk=1),
     # unions of more than 64 blocks: the kernel's union ids come in chunks of 64
     "union_over_64": dict(seq_lens=(12000,), q_lens=(300,), topk=40),
