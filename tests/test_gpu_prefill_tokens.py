@@ -154,7 +154,10 @@ def test_prefill_tokens_full_size_sampled(name, gpu_device):
     res = run_tokens(w, inp, geom, cache, gpu_device)
     units = O.prefill_token_units(w.seq_lens, w.q_lens)
     rng = np.random.default_rng(3)
-    rows = sorted({0, 127, 128, len(units) - 1} | set(rng.choice(len(units), 12, False).tolist()))
+    rows = sorted({0, 127, 128, len(units) - 1} | set(rng.choice(len(units), 12, False).tolist())
+                  # the last and first rows of neighbouring 32-row slabs (each slab's rows
+                  # are attended over their own union) in an early, a middle and a late tile
+                  | {b + o for b in (1024, 16384, 30720) for o in (31, 32, 63, 64, 95, 96)})
     bt = inp["block_table"].cpu().numpy()
     nsel, Hs = w.num_sel_groups, w.num_idx_heads // w.num_sel_groups
     G = w.num_q_heads // w.num_kv_heads
